@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE layer on one MI355X.
+
+A step is one whole layer (router GEMV -> softmax/top-k -> bucket -> MXFP4 gate/up +
+SwiGLU -> MXFP4 down + gate-weighted combine) over one batch of synthetic tokens,
+through k3moe_layer_forward. Inputs sit in HBM before the timed region; each step
+takes a fresh token set so routing (and the experts read) changes from step to step
+and the 256 MB last-level cache cannot serve a repeated working set.
+
+Prints ONE JSON line. `value` is the algorithmic weight stream of a step (the k
+selected experts' MXFP4 bytes + the bf16 router) divided by the measured step time.
+`roofline` reports the dominant kernel (the MXFP4 gate/up GEMV) timed live with HIP
+events around its own launch; `cpu_baseline` times the fp64 CPU oracle on a small
+sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+
+
+class Hip:
+    """Minimal ctypes access to HIP events (on the stream the library launches on)."""
+
+    def __init__(self):
+        self.L = ctypes.CDLL("libamdhip64.so")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.L.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        if self.L.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e
+
+    def elapsed_ms(self, a, b) -> float:
+        self.L.hipEventSynchronize(b)
+        ms = ctypes.c_float()
+        if self.L.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, e):
+        self.L.hipEventDestroy(e)
+
+
+def workload_desc(w) -> str:
+    s = f"d={w.d} f={w.f} E={w.E} k={w.k} T={w.T}"
+    if w.zipf_alpha:
+        s += f" zipf={w.zipf_alpha}"
+    return s
+
+
+def expert_bytes_per_step(w, ids_np) -> int:
+    """Algorithmic MXFP4 bytes: every distinct selected expert read once."""
+    import numpy as np
+    return int(len(np.unique(ids_np))) * w.expert_bytes
+
+
+def cpu_baseline(w, n_tokens: int):
+    import numpy as np
+
+    import oracle
+    x = w.x_bf16(token_set=1000, T=n_tokens)
+    wr = w.router_w(0)
+    ids, _, _, _ = oracle.layer_route(x, wr, w.bias(0), w.k)
+    experts = {int(e): w.expert_host(0, int(e)) for e in np.unique(ids)}
+    t0 = time.perf_counter()
+    oracle.layer_route(x, wr, w.bias(0), w.k)
+    oracle.layer_forward(x, wr, w.bias(0), experts, w.d, w.f, w.E, w.k)
+    sec = time.perf_counter() - t0
+    # the decode metric counts each token's own k experts and the router, per token
+    bytes_total = n_tokens * (w.k * w.expert_bytes + w.d * w.E * 2)
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": bytes_total / sec / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_tokens} single-token decode layers ({workload_desc(w)}), fp64 oracle, "
+                      f"{sec:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode", choices=["decode", "batched"])
+    ap.add_argument("--token-sets", type=int, default=64)
+    ap.add_argument("--cpu-tokens", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one MI355X: this build runs the layer on a single GPU "
+              "(expert-parallel sharding across GPUs is not implemented); use --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import mxfp4_expert_matmul_k3moe_amd as k3
+    from k3gen import device as gdev
+    from k3gen.workloads import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    dims = k3.make_dims(w.d, w.f, w.E, w.k)
+    ex = k3.MxExperts(**gdev.experts(w, 0, dev))
+    wr = gdev.router_w(w, 0, dev)
+    bias = gdev.bias(w, 0, dev)
+    nsets = max(1, args.token_sets)
+    xs = torch.stack([gdev.x_bf16(w, token_set=i, device=dev) for i in range(nsets)])
+    ws = k3.make_workspace(dims, w.T, dev)
+    y = torch.empty((w.T, w.d), dtype=torch.float32, device=dev)
+    ybf = torch.empty((w.T, w.d), dtype=torch.bfloat16, device=dev)
+    ids = torch.empty((nsets, w.T, w.k), dtype=torch.int32, device=dev)
+    gates = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+
+    def step(i):
+        s = i % nsets
+        k3.layer_forward(dims, xs[s], wr, bias, ex, y=y, y_bf16=ybf, ids=ids[s], gates=gates,
+                         ws=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    ids_np = ids.cpu().numpy()
+    router_bytes = w.d * w.E * 2
+    per_set = [expert_bytes_per_step(w, ids_np[s]) + router_bytes for s in range(nsets)]
+    bytes_timed = sum(per_set[(args.warmup + i) % nsets] for i in range(args.steps))
+    value = bytes_timed / (t1 - t0) / 1e9
+
+    # dominant kernel: MXFP4 gate/up GEMV, HIP events around its own launch
+    hip = Hip()
+    nprobe = min(args.steps, 100)
+    kern = {}
+    for which, name in ((k3.KERNEL_GATE_UP, "gate_up"), (k3.KERNEL_DOWN, "down")):
+        evs = [(hip.event(), hip.event()) for _ in range(nprobe)]
+        for i in range(nprobe):
+            k3.time_next_kernel(which, evs[i][0], evs[i][1])
+            step(args.warmup + i)
+        torch.cuda.synchronize()
+        times = [hip.elapsed_ms(a, b) for a, b in evs]
+        for a, b in evs:
+            hip.destroy(a)
+            hip.destroy(b)
+        kern[name] = sum(times) / len(times)
+    # algorithmic bytes per launch: gate+up rows of the distinct selected experts
+    sel = np.mean([len(np.unique(ids_np[(args.warmup + i) % nsets])) for i in range(nprobe)])
+    gu_bytes = sel * 2 * w.f * (w.d // 2 + w.d // 32)
+    dn_bytes = sel * w.d * (w.f // 2 + w.f // 32)
+    gu_gbs = gu_bytes / (kern["gate_up"] * 1e-3) / 1e9
+    dn_gbs = dn_bytes / (kern["down"] * 1e-3) / 1e9
+    traffic = None
+    prof_traffic = os.path.join(ROOT, "profiles", "gateup_decode_traffic.json")
+    if os.path.exists(prof_traffic):
+        with open(prof_traffic) as fh:
+            tr = json.load(fh)
+        if tr.get("kernel_source_hash") == _kernel_hash():
+            traffic = tr.get("bytes_per_launch")
+
+    out = {
+        "metric": "MoE layer MXFP4 weight-stream GB/s (decode) + TFLOP/s (prefill), % of peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4*bf16->fp32 (router fp64)",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {workload_desc(w)}",
+                   "bytes_per_step": int(round(bytes_timed / args.steps)),
+                   "token_sets": nsets},
+        "roofline": {"bound": "hbm", "kernel": "gateup_gemv (MXFP4 gate/up GEMV + SwiGLU)",
+                     "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "bytes_per_launch": int(gu_bytes), "avg_launch_us": round(kern["gate_up"] * 1e3, 2)},
+        "kernels": {"down_us": round(kern["down"] * 1e3, 2), "down_GBps": round(dn_gbs, 1),
+                    "layer_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def _kernel_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for n in ("ffn_gemv.hip", "k3moe_device.h"):
+        with open(os.path.join(ROOT, "mxfp4_expert_matmul_k3moe_amd", "csrc", n), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    sys.exit(main())

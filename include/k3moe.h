@@ -1,0 +1,166 @@
+/*
+ * k3moe.h — C ABI of the MI355X (gfx950) routed-expert MoE FFN on MXFP4 weights.
+ *
+ * What it computes. For each token t with activation x_t (d_model wide):
+ *     logits_t = W_router^T x_t (+ bias)           router GEMV over all E experts
+ *     p_t      = softmax(logits_t) over all E       max-subtracted
+ *     ids_t    = the top_k experts by logit, largest first, equal logits -> lower id
+ *     gates_t  = p_t[ids_t]                         full-softmax probabilities, no renorm
+ *     y_t      = sum_{slot} gates_t[slot] * E_{ids_t[slot]}(x_t)
+ *     E_e(x)   = D_e (silu(G_e x) * (U_e x))        SwiGLU expert, silu(z) = z/(1+e^-z)
+ * with G_e, U_e, D_e stored as MXFP4 and multiplied from the packed form.
+ * Sources: "Kimi K3 纯 C 语言 CPU 推理实战" (chenxutan.com/d/5901.html) §1.2 (the routing
+ * formula y = sum_i g_i(x) E_i(x), g = TopK(Softmax(W_gate x)), K = 16) and §2.4 (router
+ * GEMV over a [hidden][experts] gate matrix, stable softmax over all experts,
+ * strict-greater top-k selection, combine weighted by the full probability);
+ * project card "P053 FareedKhan-dev/kimi-k3-in-c", core features (MXFP4 = E2M1 nibble +
+ * shared E8M0 scale, 0.53125 B/weight; packed nibbles are multiplied, never dequantised).
+ *
+ * Data formats (all row-major, little-endian):
+ *   MXFP4 matrix [R][K]: nibbles uint8 [R][K/2], element 2j in bits 3..0 of byte j,
+ *     element 2j+1 in bits 7..4; scales uint8 [R][K/32], one E8M0 byte per 32
+ *     consecutive K-elements of a row. E2M1 code: bit 3 sign, bits 2..1 exponent
+ *     (bias 1), bit 0 mantissa (values 0, .5, 1, 1.5, 2, 3, 4, 6 and negatives).
+ *     E8M0 byte s: 2^(s-127); s = 255 is NaN and propagates as NaN.
+ *   Expert tensors of one layer: gate, up [E][d_ff][d_model] and down [E][d_model][d_ff]
+ *     as MXFP4 matrices stacked over experts (so gate_q is [E][d_ff][d_model/2]).
+ *   Router weight: bf16 [d_model][E]. Optional logit bias: fp32 [E], added before softmax.
+ *   Activations: bf16 (K3MOE_BF16) or fp32 (K3MOE_F32), [T][d_model].
+ *   Routing: topk_ids int32 [T][top_k], topk_gates fp32 [T][top_k].
+ *   Bucketing: expert_offsets int32 [E+1] (prefix sums of per-expert token counts),
+ *     bucket_rows int32 [T*top_k] holding pair ids t*top_k+slot, grouped by expert in
+ *     ascending expert id and ascending t within each expert.
+ *   Output y: fp32 [T][d_model], overwritten. y_bf16, when given, holds the
+ *     round-to-nearest-even bf16 of y.
+ *
+ * Conventions of every entry point:
+ *   - Every pointer argument except `stream` and the structs' host copies is DEVICE
+ *     memory owned by the caller. The library never allocates device memory and keeps
+ *     no state beyond cached device properties; calls with distinct workspaces may run
+ *     concurrently on distinct streams.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = default
+ *     stream). The caller synchronises. Results are bit-identical from run to run.
+ *   - Arguments are validated on the host before anything is enqueued; nothing is
+ *     defaulted. Errors: K3MOE_EINVAL (null required pointer, negative T, d_model or
+ *     d_ff not a positive multiple of 32, n_experts < 1, top_k outside
+ *     [1, min(n_experts, 32)], unknown dtype), K3MOE_EUNSUPPORTED (valid but outside
+ *     what the kernels implement, e.g. T or E above the limits below),
+ *     K3MOE_EWORKSPACE (ws_bytes below k3moe_workspace_bytes(dims, T)), K3MOE_EHIP (a
+ *     HIP launch failed). T = 0 returns K3MOE_OK and enqueues nothing.
+ *     k3moe_last_error() gives a message for the calling thread's last failure.
+ *   - Input values are not scanned: NaN inputs and E8M0 255 propagate as NaN.
+ *   - Alignment: x, y and the MXFP4 nibble arrays must be 16-byte aligned (EINVAL).
+ *   - Limits (EUNSUPPORTED beyond): n_experts <= 4096, T <= 1048576, d_model <= 16384,
+ *     d_ff <= 16384; the expert kernels also need (d_ff/32)/p <= 4, with p the largest
+ *     power of two <= 64 dividing d_ff/32 (true for d_ff = 1536, 256, 32, any multiple
+ *     of 2048, ...).
+ */
+#ifndef K3MOE_H
+#define K3MOE_H
+#include <stddef.h>
+#include <stdint.h>
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define K3MOE_VERSION 1
+
+#if defined(__GNUC__)
+#define K3MOE_API __attribute__((visibility("default")))
+#else
+#define K3MOE_API
+#endif
+
+typedef struct {
+  int32_t d_model;   /* hidden width d (7168 for the K3 layer)   */
+  int32_t d_ff;      /* expert inner width f (1536)              */
+  int32_t n_experts; /* routed experts E (896)                   */
+  int32_t top_k;     /* experts per token k (16)                 */
+} k3moe_dims;
+
+typedef struct { /* one layer of routed experts, device pointers, caller-owned */
+  const uint8_t *gate_q, *gate_s; /* [E][d_ff][d_model/2], [E][d_ff][d_model/32] */
+  const uint8_t *up_q, *up_s;     /* same shapes as gate                        */
+  const uint8_t *down_q, *down_s; /* [E][d_model][d_ff/2], [E][d_model][d_ff/32] */
+} k3moe_mx_experts;
+
+typedef struct { /* extras of a full block; device pointers except rms_eps */
+  const uint16_t* rms_gamma; /* bf16 [d_model]                          */
+  float rms_eps;             /* added to mean(h^2) inside the sqrt      */
+  const uint16_t* sh_gate;   /* bf16 [d_ff][d_model] shared expert      */
+  const uint16_t* sh_up;     /* bf16 [d_ff][d_model]                    */
+  const uint16_t* sh_down;   /* bf16 [d_model][d_ff]                    */
+} k3moe_block;
+
+enum {
+  K3MOE_OK = 0,
+  K3MOE_EINVAL = -1,
+  K3MOE_EUNSUPPORTED = -2,
+  K3MOE_EWORKSPACE = -3,
+  K3MOE_EHIP = -4
+};
+enum { K3MOE_BF16 = 0, K3MOE_F32 = 1 };
+
+/* Library version (K3MOE_VERSION). */
+K3MOE_API int k3moe_version(void);
+
+/* Device workspace, in bytes, that any entry point needs for up to max_tokens
+ * tokens with these dims; 0 when dims are invalid. Pure host function. */
+K3MOE_API size_t k3moe_workspace_bytes(const k3moe_dims* dims, int32_t max_tokens);
+
+/* Router GEMV + softmax + top-k ("Kimi K3 纯 C 语言 CPU 推理实战" §2.4, compute_gate_scores
+ * followed by the softmax and top-k steps of moe_forward).
+ * x: [T][d_model] of x_dtype. w_router: bf16 [d_model][E]. logit_bias: fp32 [E] or NULL.
+ * Logits are accumulated in fp64 (bf16*bf16 and bf16*fp32 products are exact there), so
+ * the selected ids and their order are those of the exact-arithmetic definition.
+ * Writes topk_ids [T][k] and topk_gates [T][k]. */
+K3MOE_API int k3moe_router(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
+                 const uint16_t* w_router, const float* logit_bias, int32_t* topk_ids,
+                 float* topk_gates, void* ws, size_t ws_bytes, void* stream);
+
+/* Stable counting sort of the T*k (token, slot) pairs by expert (the token lists the
+ * grouped expert matmuls consume). topk_ids: [T][k], each in [0, E) and distinct within a
+ * token (ids outside [0, E) are a caller error; the kernels ignore such pairs).
+ * Writes expert_offsets [E+1] and bucket_rows [T*k]. */
+K3MOE_API int k3moe_route_bucket(const k3moe_dims* dims, int32_t T, const int32_t* topk_ids,
+                       int32_t* expert_offsets, int32_t* bucket_rows, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Routed experts + gate-weighted combine for already-routed tokens:
+ * y_t = sum_slot topk_gates[t][slot] * E_e(x_t), e the expert whose bucket holds pair
+ * t*k+slot. Each expert's MXFP4 weights are read once per call for all of its tokens and
+ * decoded in registers; nothing dequantised is written to memory. Slots are summed in slot
+ * order. x: [T][d_model] of x_dtype. y: fp32 [T][d_model], overwritten. */
+K3MOE_API int k3moe_expert_ffn(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
+                     const k3moe_mx_experts* experts, const int32_t* expert_offsets,
+                     const int32_t* bucket_rows, const float* topk_gates, float* y,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* One whole layer: router -> top-k -> bucket -> experts -> combine.
+ * blk == NULL: y = MoE(x).
+ * blk != NULL (block mode): x must be fp32 (x_dtype K3MOE_F32), the residual h;
+ *   xhat = h / sqrt(mean(h^2) + rms_eps) * rms_gamma feeds the router, the routed experts
+ *   and the shared bf16 SwiGLU expert S; y = h + S(xhat) + MoE(xhat) (fp32).
+ * y_bf16 [T][d_model] (nullable) receives RNE(y). topk_ids / topk_gates (nullable)
+ * receive the routing. */
+K3MOE_API int k3moe_layer_forward(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
+                        const uint16_t* w_router, const float* logit_bias,
+                        const k3moe_mx_experts* experts, const k3moe_block* blk, float* y,
+                        uint16_t* y_bf16, int32_t* topk_ids, float* topk_gates, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* Diagnostics for live per-kernel timing. Arms a one-shot probe on the calling thread:
+ * the next entry-point call that launches kernel `which` records hipEvent_t ev_start on
+ * its stream right before that launch and ev_stop right after it, then disarms. The
+ * events are created and owned by the caller. which: K3MOE_KERNEL_*. Passing NULL events
+ * disarms. Returns K3MOE_EINVAL for an unknown `which`. */
+enum { K3MOE_KERNEL_ROUTER = 1, K3MOE_KERNEL_GATE_UP = 2, K3MOE_KERNEL_DOWN = 3 };
+K3MOE_API int k3moe_time_next_kernel(int which, void* ev_start, void* ev_stop);
+
+/* Message describing the calling thread's last non-OK status ("" if none). */
+K3MOE_API const char* k3moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

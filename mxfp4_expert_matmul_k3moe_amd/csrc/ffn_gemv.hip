@@ -1,0 +1,436 @@
+// ffn_gemv.hip — MXFP4 expert GEMVs for few tokens per expert (decode, batched decode).
+//
+// The expert weights are streamed from HBM with 16-byte loads: one load is one
+// 32-element MXFP4 block of one row (16 packed bytes), whose E8M0 scale is one more
+// byte. The block is decoded in registers (gfx950 scaled FP4 conversion), multiplied
+// against 32 activations, summed, and only then scaled by the block's power of two.
+// Nothing dequantised is written anywhere. Rows are split over aligned groups of
+// `lpr` lanes (the largest power of two dividing the row's block count), so a row's
+// partial sums are reduced inside its lane group with a fixed shuffle tree.
+//
+// Expert form: E(x) = D (silu(G x) * (U x)) (SwiGLU without biases); combine:
+// y_t = sum over slots in slot order of gate * E(x_t), following "Kimi K3 纯 C 语言 CPU
+// 推理实战" (chenxutan.com/d/5901.html) §1.2 and §2.4, with the weight layout [N][K] and
+// 32-element scale groups of its §2.3 quantised GEMM.
+#include "k3moe_device.h"
+#include "k3moe_launch.h"
+
+namespace k3moe {
+namespace {
+
+constexpr int kGateUpWaves = 4;
+constexpr int kMaxTokGroup = 4;
+constexpr int kLdsBudget = 64 * 1024;
+
+struct GateUpArgs {
+  int T, d, f, k;
+  const void* x;
+  const uint8_t *gq, *gs, *uq, *us;
+  const int32_t *offsets, *rows, *act, *n_act;
+  int nchunk, rc, tg;
+  float* h;
+};
+
+// LDS layout of one staged activation row: block cb = sub + lpr*i, 16-byte piece qq of
+// that block goes to chunk ((i*Q + qq)*lpr + sub), so the lanes of a row group read
+// consecutive 16-byte chunks (no bank conflicts). Q = pieces per block (4 bf16 / 8 f32).
+__device__ __forceinline__ int x_chunk(int cb, int qq, int lpr, int Q) {
+  const int i = cb / lpr, sub = cb - i * lpr;
+  return (i * Q + qq) * lpr + sub;
+}
+
+template <bool XF32, int BPLC, int TGM>
+__global__ __launch_bounds__(256) void gateup_gemv_kernel(GateUpArgs a) {
+  extern __shared__ __attribute__((aligned(16))) u32x4 xs[];
+  constexpr int Q = XF32 ? 8 : 4;  // 16-byte pieces per 32-element block
+  const int item = blockIdx.x;
+  const int ai = item / a.nchunk, c = item - ai * a.nchunk;
+  if (ai >= *a.n_act) return;
+  const int e = a.act[ai];
+  const int P = a.T * a.k;
+  const int p0 = min(max(a.offsets[e], 0), P), p1 = min(max(a.offsets[e + 1], p0), P);
+  const int d = a.d, f = a.f;
+  const int NB = d >> 5;
+  const int lpr = lanes_per_row(NB), bpl = NB / lpr, rpw = 64 / lpr;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane & (lpr - 1), rsel = lane / lpr;
+  const int j0 = c * a.rc, j1 = min(f, j0 + a.rc);
+  const size_t rq = (size_t)(d >> 1), rs = (size_t)NB;
+  const uint8_t* gq = a.gq + (size_t)e * f * rq;
+  const uint8_t* uq = a.uq + (size_t)e * f * rq;
+  const uint8_t* gs = a.gs + (size_t)e * f * rs;
+  const uint8_t* us = a.us + (size_t)e * f * rs;
+  const int chunks_per_tok = NB * Q;
+
+  for (int pg = p0; pg < p1; pg += a.tg) {
+    const int ntok = min(a.tg, p1 - pg);
+    __syncthreads();
+    for (int tok = 0; tok < ntok; ++tok) {
+      const int pair = a.rows[pg + tok];
+      const bool ok = pair >= 0 && pair < P;  // caller-supplied buckets are not trusted
+      const int t = ok ? pair / a.k : 0;
+      const u32x4* src = reinterpret_cast<const u32x4*>(
+          static_cast<const uint8_t*>(a.x) + (size_t)t * d * (XF32 ? 4 : 2));
+      for (int v = threadIdx.x; v < chunks_per_tok; v += 256) {
+        const int cb = v / Q, qq = v - cb * Q;
+        xs[tok * chunks_per_tok + x_chunk(cb, qq, lpr, Q)] = ok ? src[v] : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    __syncthreads();
+    for (int jb = j0 + wave * rpw; jb < j1; jb += kGateUpWaves * rpw) {
+      const int j = jb + rsel;
+      const bool rv = j < j1;
+      float gacc[TGM], uacc[TGM];
+#pragma unroll
+      for (int tk = 0; tk < TGM; ++tk) gacc[tk] = uacc[tk] = 0.0f;
+      for (int i0 = 0; i0 < bpl; i0 += BPLC) {
+        u32x4 gw[BPLC], uw[BPLC];
+        uint32_t gsc[BPLC], usc[BPLC];
+#pragma unroll
+        for (int ii = 0; ii < BPLC; ++ii) {
+          const int i = i0 + ii;
+          const int cb = sub + lpr * i;
+          if (rv && i < bpl) {
+            gw[ii] = load_u32x4_nt(gq + (size_t)j * rq + (size_t)cb * 16);
+            uw[ii] = load_u32x4_nt(uq + (size_t)j * rq + (size_t)cb * 16);
+            gsc[ii] = gs[(size_t)j * rs + cb];
+            usc[ii] = us[(size_t)j * rs + cb];
+          }
+        }
+#pragma unroll
+        for (int tk = 0; tk < TGM; ++tk) {
+          if (tk < ntok) {
+            const u32x4* xt = xs + tk * chunks_per_tok;
+#pragma unroll
+            for (int ii = 0; ii < BPLC; ++ii) {
+              const int i = i0 + ii;
+              if (rv && i < bpl) {
+                const int cb = sub + lpr * i;
+                if constexpr (XF32) {
+                  float xv[32];
+#pragma unroll
+                  for (int qq = 0; qq < 8; ++qq) {
+                    const u32x4 v = xt[x_chunk(cb, qq, lpr, 8)];
+                    xv[4 * qq + 0] = __uint_as_float(v[0]);
+                    xv[4 * qq + 1] = __uint_as_float(v[1]);
+                    xv[4 * qq + 2] = __uint_as_float(v[2]);
+                    xv[4 * qq + 3] = __uint_as_float(v[3]);
+                  }
+                  gacc[tk] = fmaf(e8m0_to_f32(gsc[ii]), block_dot_f32(gw[ii], xv), gacc[tk]);
+                  uacc[tk] = fmaf(e8m0_to_f32(usc[ii]), block_dot_f32(uw[ii], xv), uacc[tk]);
+                } else {
+                  uint32_t xp[16];
+#pragma unroll
+                  for (int qq = 0; qq < 4; ++qq) {
+                    const u32x4 v = xt[x_chunk(cb, qq, lpr, 4)];
+                    xp[4 * qq + 0] = v[0];
+                    xp[4 * qq + 1] = v[1];
+                    xp[4 * qq + 2] = v[2];
+                    xp[4 * qq + 3] = v[3];
+                  }
+                  gacc[tk] = fmaf(e8m0_to_f32(gsc[ii]), block_dot_bf16(gw[ii], xp), gacc[tk]);
+                  uacc[tk] = fmaf(e8m0_to_f32(usc[ii]), block_dot_bf16(uw[ii], xp), uacc[tk]);
+                }
+              }
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int tk = 0; tk < TGM; ++tk) {
+        if (tk < ntok) {
+          const float g = group_sum_rt(gacc[tk], lpr);
+          const float u = group_sum_rt(uacc[tk], lpr);
+          if (rv && sub == 0) a.h[(size_t)(pg + tk) * f + j] = silu_f32(g) * u;
+        }
+      }
+    }
+  }
+}
+
+// ---- down projection, T == 1, all slots of the token + ordered combine --------------------
+struct DownT1Args {
+  int d, f, k;
+  const uint8_t *dq, *ds;
+  const float* h;
+  const int32_t *pair_pos, *pair_exp;
+  const float* gates;
+  const float *resid, *shared;
+  float* y;
+  uint16_t* y_bf16;
+  int rc;
+};
+
+constexpr int kMaxSlots = 32;
+constexpr int kDownRowsT1 = 16;
+
+template <int BPL>
+__global__ __launch_bounds__(512) void down_fused_t1_kernel(DownT1Args a) {
+  __shared__ float zs[kMaxSlots][kDownRowsT1];
+  __shared__ float gs[kMaxSlots];
+  const int d = a.d, f = a.f, k = a.k;
+  const int NB = f >> 5;
+  const int lpr = lanes_per_row(NB);
+  const int gtid = threadIdx.x;
+  const int lane = gtid & 63;
+  const int q = gtid / lpr;            // slot handled by this lane group
+  const int sub = lane & (lpr - 1);
+  const int r0 = blockIdx.x * kDownRowsT1;
+  const int nr = min(kDownRowsT1, d - r0);
+  if (gtid < k) gs[gtid] = a.gates[gtid];
+  const int pos = (q < k) ? a.pair_pos[q] : -1;
+  const int e = (q < k) ? a.pair_exp[q] : -1;
+  const bool sv = pos >= 0 && e >= 0;
+  // h of this slot for this lane's blocks, in registers
+  float hv[BPL][32];
+#pragma unroll
+  for (int i = 0; i < BPL; ++i) {
+    const int cb = sub + lpr * i;
+    const f32x4* src = reinterpret_cast<const f32x4*>(a.h + (size_t)(sv ? pos : 0) * f + cb * 32);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const f32x4 t = sv ? src[v] : f32x4{0.f, 0.f, 0.f, 0.f};
+      hv[i][4 * v + 0] = t[0];
+      hv[i][4 * v + 1] = t[1];
+      hv[i][4 * v + 2] = t[2];
+      hv[i][4 * v + 3] = t[3];
+    }
+  }
+  const size_t rq = (size_t)(f >> 1), rs = (size_t)NB;
+  const uint8_t* dq = a.dq + (size_t)(sv ? e : 0) * d * rq;
+  const uint8_t* dsc = a.ds + (size_t)(sv ? e : 0) * d * rs;
+  for (int rr = 0; rr < nr; rr += 2) {
+    u32x4 w[2][BPL];
+    uint32_t sc[2][BPL];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int r = r0 + rr + u;
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) {
+        const int cb = sub + lpr * i;
+        if (sv && rr + u < nr) {
+          w[u][i] = load_u32x4_nt(dq + (size_t)r * rq + (size_t)cb * 16);
+          sc[u][i] = dsc[(size_t)r * rs + cb];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float p = 0.0f;
+      if (sv && rr + u < nr) {
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) p = fmaf(e8m0_to_f32(sc[u][i]), block_dot_f32(w[u][i], hv[i]), p);
+      }
+      const float z = group_sum_rt(p, lpr);
+      if (q < k && sub == 0 && rr + u < nr) zs[q][rr + u] = sv ? z : 0.0f;
+    }
+  }
+  __syncthreads();
+  if (gtid < nr) {
+    const int r = r0 + gtid;
+    float acc = 0.0f;
+    for (int s = 0; s < k; ++s) acc = fmaf(gs[s], zs[s][gtid], acc);
+    float out = acc;
+    if (a.resid) out = (a.resid[r] + (a.shared ? a.shared[r] : 0.0f)) + acc;
+    a.y[r] = out;
+    if (a.y_bf16) a.y_bf16[r] = f32_to_bf16_rne(out);
+  }
+}
+
+// ---- down projection per expert (any T) into pair-indexed z --------------------------------
+struct DownArgs {
+  int T, d, f, k;
+  const uint8_t *dq, *ds;
+  const float* h;
+  const int32_t *offsets, *rows, *act, *n_act;
+  int nchunk, rc;
+  float* z;
+};
+
+template <int BPL>
+__global__ __launch_bounds__(256) void down_gemv_kernel(DownArgs a) {
+  const int item = blockIdx.x;
+  const int ai = item / a.nchunk, c = item - ai * a.nchunk;
+  if (ai >= *a.n_act) return;
+  const int e = a.act[ai];
+  const int P = a.T * a.k;
+  const int p0 = min(max(a.offsets[e], 0), P), p1 = min(max(a.offsets[e + 1], p0), P);
+  const int d = a.d, f = a.f;
+  const int NB = f >> 5;
+  const int lpr = lanes_per_row(NB), rpw = 64 / lpr;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane & (lpr - 1), rsel = lane / lpr;
+  const int i0r = c * a.rc, i1r = min(d, i0r + a.rc);
+  const size_t rq = (size_t)(f >> 1), rs = (size_t)NB;
+  const uint8_t* dq = a.dq + (size_t)e * d * rq;
+  const uint8_t* dsc = a.ds + (size_t)e * d * rs;
+  for (int p = p0; p < p1; ++p) {
+    const int pair = a.rows[p];
+    if (pair < 0 || pair >= P) continue;
+    float hv[BPL][32];
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) {
+      const int cb = sub + lpr * i;
+      const f32x4* src = reinterpret_cast<const f32x4*>(a.h + (size_t)p * f + cb * 32);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const f32x4 t = src[v];
+        hv[i][4 * v + 0] = t[0];
+        hv[i][4 * v + 1] = t[1];
+        hv[i][4 * v + 2] = t[2];
+        hv[i][4 * v + 3] = t[3];
+      }
+    }
+    for (int rb = i0r + wave * rpw; rb < i1r; rb += 4 * rpw) {
+      const int r = rb + rsel;
+      const bool rv = r < i1r;
+      u32x4 w[BPL];
+      uint32_t sc[BPL];
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) {
+        const int cb = sub + lpr * i;
+        if (rv) {
+          w[i] = load_u32x4(dq + (size_t)r * rq + (size_t)cb * 16);
+          sc[i] = dsc[(size_t)r * rs + cb];
+        }
+      }
+      float acc = 0.0f;
+      if (rv) {
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) acc = fmaf(e8m0_to_f32(sc[i]), block_dot_f32(w[i], hv[i]), acc);
+      }
+      const float zz = group_sum_rt(acc, lpr);
+      if (rv && sub == 0) a.z[(size_t)pair * d + r] = zz;
+    }
+  }
+}
+
+// ---- combine -----------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void combine_kernel(int T, int d, int k, const float* __restrict__ z,
+                                                      const float* __restrict__ gates,
+                                                      const int32_t* __restrict__ pair_pos,
+                                                      const float* __restrict__ resid,
+                                                      const float* __restrict__ shared,
+                                                      float* __restrict__ y,
+                                                      uint16_t* __restrict__ y_bf16) {
+  const int t = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= d) return;
+  float acc = 0.0f;
+  for (int s = 0; s < k; ++s) {
+    const int pr = t * k + s;
+    if (pair_pos[pr] >= 0) acc = fmaf(gates[pr], z[(size_t)pr * d + i], acc);
+  }
+  float out = acc;
+  if (resid) out = (resid[(size_t)t * d + i] + (shared ? shared[(size_t)t * d + i] : 0.0f)) + acc;
+  y[(size_t)t * d + i] = out;
+  if (y_bf16) y_bf16[(size_t)t * d + i] = f32_to_bf16_rne(out);
+}
+
+int bpl_of(int nb) { return nb / lanes_per_row(nb); }
+
+}  // namespace
+
+bool down_fused_supported(int f, int k) { return k * lanes_per_row(f >> 5) <= 512; }
+
+bool gemv_shape_supported(int d, int f) {
+  // down projections keep a row slice of h in registers: at most 4 blocks per lane
+  const int bd = bpl_of(f >> 5);
+  return (d % 32 == 0) && (f % 32 == 0) && bd >= 1 && bd <= 4 &&
+         (size_t)d * 4 <= (size_t)kLdsBudget;
+}
+
+hipError_t launch_gateup_gemv(int T, int d, int f, int E, int k, const void* x, int xf32,
+                              const MxPtrs& w, const int32_t* offsets, const int32_t* rows,
+                              const int32_t* act, const int32_t* n_act, int max_act, float* h,
+                              hipStream_t s) {
+  GateUpArgs a;
+  a.T = T; a.d = d; a.f = f; a.k = k; a.x = x;
+  a.gq = w.gate_q; a.gs = w.gate_s; a.uq = w.up_q; a.us = w.up_s;
+  a.offsets = offsets; a.rows = rows; a.act = act; a.n_act = n_act; a.h = h;
+  const int NB = d >> 5;
+  const int lpr = lanes_per_row(NB), bpl = NB / lpr, rpw = 64 / lpr;
+  const size_t xrow = (size_t)d * (xf32 ? 4 : 2);
+  int tg = (T == 1) ? 1 : (int)(kLdsBudget / xrow);
+  tg = tg < 1 ? 1 : (tg > kMaxTokGroup ? kMaxTokGroup : tg);
+  a.tg = tg;
+  // rows per block: two row-iterations per wave
+  a.rc = kGateUpWaves * rpw * 2;
+  a.nchunk = (f + a.rc - 1) / a.rc;
+  const size_t lds = (size_t)tg * xrow;
+  dim3 grid((unsigned)(max_act * a.nchunk));
+  const int bplc = bpl <= 8 ? bpl : 8;
+#define K3_GU(XF, B, TG) \
+  gateup_gemv_kernel<XF, B, TG><<<grid, 256, lds, s>>>(a)
+#define K3_GU_B(XF, TG)                   \
+  switch (bplc) {                         \
+    case 1: K3_GU(XF, 1, TG); break;      \
+    case 2: K3_GU(XF, 2, TG); break;      \
+    case 3: K3_GU(XF, 3, TG); break;      \
+    case 4: K3_GU(XF, 4, TG); break;      \
+    case 5: K3_GU(XF, 5, TG); break;      \
+    case 6: K3_GU(XF, 6, TG); break;      \
+    case 7: K3_GU(XF, 7, TG); break;      \
+    default: K3_GU(XF, 8, TG); break;     \
+  }
+  if (xf32) {
+    if (tg == 1) { K3_GU_B(true, 1) } else { K3_GU_B(true, 4) }
+  } else {
+    if (tg == 1) { K3_GU_B(false, 1) } else { K3_GU_B(false, 4) }
+  }
+#undef K3_GU_B
+#undef K3_GU
+  return hipGetLastError();
+}
+
+hipError_t launch_down_fused_t1(int d, int f, int k, const MxPtrs& w, const float* h,
+                                const int32_t* pair_pos, const int32_t* pair_exp,
+                                const float* gates, const float* resid, const float* shared,
+                                float* y, uint16_t* y_bf16, hipStream_t s) {
+  DownT1Args a;
+  a.d = d; a.f = f; a.k = k; a.dq = w.down_q; a.ds = w.down_s; a.h = h;
+  a.pair_pos = pair_pos; a.pair_exp = pair_exp; a.gates = gates;
+  a.resid = resid; a.shared = shared; a.y = y; a.y_bf16 = y_bf16; a.rc = kDownRowsT1;
+  const int NB = f >> 5;
+  const int lpr = lanes_per_row(NB);
+  const int lanes = k * lpr;
+  const int threads = ((lanes + 63) / 64) * 64;
+  dim3 grid((unsigned)((d + kDownRowsT1 - 1) / kDownRowsT1));
+  switch (bpl_of(NB)) {
+    case 1: down_fused_t1_kernel<1><<<grid, threads, 0, s>>>(a); break;
+    case 2: down_fused_t1_kernel<2><<<grid, threads, 0, s>>>(a); break;
+    case 3: down_fused_t1_kernel<3><<<grid, threads, 0, s>>>(a); break;
+    default: down_fused_t1_kernel<4><<<grid, threads, 0, s>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_down_gemv(int T, int d, int f, int E, int k, const MxPtrs& w, const float* h,
+                            const int32_t* offsets, const int32_t* rows, const int32_t* act,
+                            const int32_t* n_act, int max_act, float* z, hipStream_t s) {
+  DownArgs a;
+  a.T = T; a.d = d; a.f = f; a.k = k; a.dq = w.down_q; a.ds = w.down_s; a.h = h;
+  a.offsets = offsets; a.rows = rows; a.act = act; a.n_act = n_act; a.z = z;
+  const int NB = f >> 5;
+  const int rpw = 64 / lanes_per_row(NB);
+  a.rc = 4 * rpw * 4;
+  a.nchunk = (d + a.rc - 1) / a.rc;
+  dim3 grid((unsigned)(max_act * a.nchunk));
+  switch (bpl_of(NB)) {
+    case 1: down_gemv_kernel<1><<<grid, 256, 0, s>>>(a); break;
+    case 2: down_gemv_kernel<2><<<grid, 256, 0, s>>>(a); break;
+    case 3: down_gemv_kernel<3><<<grid, 256, 0, s>>>(a); break;
+    default: down_gemv_kernel<4><<<grid, 256, 0, s>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(int T, int d, int k, const float* z, const float* gates,
+                          const int32_t* pair_pos, const float* resid, const float* shared,
+                          float* y, uint16_t* y_bf16, hipStream_t s) {
+  dim3 grid((unsigned)((d + 255) / 256), (unsigned)T);
+  combine_kernel<<<grid, 256, 0, s>>>(T, d, k, z, gates, pair_pos, resid, shared, y, y_bf16);
+  return hipGetLastError();
+}
+
+}  // namespace k3moe

@@ -1,0 +1,391 @@
+// k3moe_api.cpp — the C ABI of include/k3moe.h: host-side argument validation,
+// workspace carving and kernel dispatch. No device memory is allocated here; every
+// launch goes onto the caller's stream.
+#include "k3moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "k3moe_launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+// One-shot timing probe (k3moe_time_next_kernel).
+thread_local int g_probe_which = 0;
+thread_local hipEvent_t g_probe_start = nullptr, g_probe_stop = nullptr;
+
+struct Probe {  // records around one launch when armed for `which`
+  int which;
+  hipStream_t s;
+  bool armed;
+  Probe(int w, hipStream_t st) : which(w), s(st), armed(g_probe_which == w) {
+    if (armed) (void)hipEventRecord(g_probe_start, s);
+  }
+  ~Probe() {
+    if (armed) {
+      (void)hipEventRecord(g_probe_stop, s);
+      g_probe_which = 0;
+    }
+  }
+};
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+constexpr int kMaxE = 4096;
+constexpr int kMaxK = 32;
+constexpr int kMaxT = 1 << 20;
+constexpr int kMaxWidth = 16384;
+
+enum Region {
+  R_PART, R_IDS, R_GATES, R_OFFS, R_ROWS, R_ACT, R_NACT, R_PPOS, R_PEXP, R_HIST, R_BASE,
+  R_MASK, R_H, R_Z, R_XHAT, R_HSH, R_SSH, R_COUNT
+};
+
+struct Layout {
+  size_t off[R_COUNT];
+  size_t total;
+};
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+Layout layout_for(const k3moe_dims& dm, int64_t T) {
+  const int64_t d = dm.d_model, f = dm.d_ff, E = dm.n_experts, k = dm.top_k;
+  const int64_t P = T * k;
+  const int64_t NB = (T + k3moe::kBucketTokens - 1) / k3moe::kBucketTokens;
+  const int64_t NC = k3moe::router_num_chunks((int)d);
+  const int64_t tg = T < k3moe::kRouterGemvMaxT ? T : k3moe::kRouterGemvMaxT;
+  const size_t part_small = (size_t)(NC * tg * E * 8), part_big = (size_t)(T * E * 8);
+  size_t sz[R_COUNT];
+  sz[R_PART] = part_small > part_big ? part_small : part_big;
+  sz[R_IDS] = (size_t)P * 4;
+  sz[R_GATES] = (size_t)P * 4;
+  sz[R_OFFS] = (size_t)(E + 1) * 4;
+  sz[R_ROWS] = (size_t)P * 4;
+  sz[R_ACT] = (size_t)E * 4;
+  sz[R_NACT] = 16;
+  sz[R_PPOS] = (size_t)P * 4;
+  sz[R_PEXP] = (size_t)P * 4;
+  sz[R_HIST] = (size_t)(NB * E * 4);
+  sz[R_BASE] = (size_t)(NB * E * 4);
+  sz[R_MASK] = (size_t)(NB * E * 8);
+  sz[R_H] = (size_t)(P * f * 4);
+  sz[R_Z] = (size_t)(P * d * 4);
+  sz[R_XHAT] = (size_t)(T * d * 4);
+  sz[R_HSH] = (size_t)(T * f * 4);
+  sz[R_SSH] = (size_t)(T * d * 4);
+  Layout L;
+  size_t o = 0;
+  for (int r = 0; r < R_COUNT; ++r) {
+    L.off[r] = o;
+    o = align_up(o + sz[r], 256);
+  }
+  L.total = o + 256;  // slack to align the caller's base pointer
+  return L;
+}
+
+struct Ws {
+  char* base;
+  Layout L;
+  template <class P>
+  P* at(Region r) const { return reinterpret_cast<P*>(base + L.off[r]); }
+};
+
+int check_dims(const k3moe_dims* dims) {
+  if (!dims) return fail(K3MOE_EINVAL, "dims is NULL");
+  const k3moe_dims& d = *dims;
+  if (d.d_model <= 0 || d.d_model % 32)
+    return fail(K3MOE_EINVAL, "d_model=%d must be a positive multiple of 32", d.d_model);
+  if (d.d_ff <= 0 || d.d_ff % 32)
+    return fail(K3MOE_EINVAL, "d_ff=%d must be a positive multiple of 32", d.d_ff);
+  if (d.n_experts < 1) return fail(K3MOE_EINVAL, "n_experts=%d must be >= 1", d.n_experts);
+  const int kmax = d.n_experts < kMaxK ? d.n_experts : kMaxK;
+  if (d.top_k < 1 || d.top_k > kmax)
+    return fail(K3MOE_EINVAL, "top_k=%d outside [1, %d]", d.top_k, kmax);
+  if (d.n_experts > kMaxE) return fail(K3MOE_EUNSUPPORTED, "n_experts=%d > %d", d.n_experts, kMaxE);
+  if (d.d_model > kMaxWidth || d.d_ff > kMaxWidth)
+    return fail(K3MOE_EUNSUPPORTED, "d_model/d_ff above %d", kMaxWidth);
+  return K3MOE_OK;
+}
+
+int check_T(int32_t T) {
+  if (T < 0) return fail(K3MOE_EINVAL, "T=%d is negative", T);
+  if (T > kMaxT) return fail(K3MOE_EUNSUPPORTED, "T=%d > %d", T, kMaxT);
+  return K3MOE_OK;
+}
+
+int check_dtype(int x_dtype) {
+  if (x_dtype != K3MOE_BF16 && x_dtype != K3MOE_F32)
+    return fail(K3MOE_EINVAL, "unknown x_dtype %d", x_dtype);
+  return K3MOE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int need_ptr(const void* p, const char* name, bool align16 = false) {
+  if (!p) return fail(K3MOE_EINVAL, "%s is NULL", name);
+  if (align16 && !aligned16(p)) return fail(K3MOE_EINVAL, "%s is not 16-byte aligned", name);
+  return K3MOE_OK;
+}
+
+int check_experts(const k3moe_mx_experts* ex) {
+  if (!ex) return fail(K3MOE_EINVAL, "experts is NULL");
+  int rc;
+  if ((rc = need_ptr(ex->gate_q, "experts->gate_q", true))) return rc;
+  if ((rc = need_ptr(ex->gate_s, "experts->gate_s"))) return rc;
+  if ((rc = need_ptr(ex->up_q, "experts->up_q", true))) return rc;
+  if ((rc = need_ptr(ex->up_s, "experts->up_s"))) return rc;
+  if ((rc = need_ptr(ex->down_q, "experts->down_q", true))) return rc;
+  if ((rc = need_ptr(ex->down_s, "experts->down_s"))) return rc;
+  return K3MOE_OK;
+}
+
+int check_expert_shape(const k3moe_dims& dm) {
+  if (!k3moe::gemv_shape_supported(dm.d_model, dm.d_ff))
+    return fail(K3MOE_EUNSUPPORTED, "expert shape d_model=%d d_ff=%d not supported", dm.d_model,
+                dm.d_ff);
+  return K3MOE_OK;
+}
+
+int get_ws(const k3moe_dims& dm, int32_t T, void* ws, size_t ws_bytes, Ws* out) {
+  out->L = layout_for(dm, T);
+  if (ws_bytes < out->L.total)
+    return fail(K3MOE_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, out->L.total);
+  if (!ws) return fail(K3MOE_EINVAL, "ws is NULL");
+  out->base = reinterpret_cast<char*>(align_up(reinterpret_cast<uintptr_t>(ws), 256));
+  return K3MOE_OK;
+}
+
+int hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(K3MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return K3MOE_OK;
+}
+
+int run_router(const k3moe_dims& dm, int32_t T, const void* x, int xf32, const uint16_t* w,
+               const float* bias, int32_t* ids, float* gates, const Ws& ws, hipStream_t s) {
+  double* part = ws.at<double>(R_PART);
+  int nsum = 1;
+  hipError_t e;
+  Probe probe(K3MOE_KERNEL_ROUTER, s);
+  if (T <= k3moe::kRouterGemvMaxT) {
+    e = k3moe::launch_router_gemv(T, dm.d_model, dm.n_experts, x, xf32, w, part, s);
+    nsum = k3moe::router_num_chunks(dm.d_model);
+  } else {
+    e = k3moe::launch_router_gemm(T, dm.d_model, dm.n_experts, x, xf32, w, part, s);
+  }
+  int rc = hip_check(e, "router logits");
+  if (rc) return rc;
+  return hip_check(k3moe::launch_route_topk(T, dm.n_experts, dm.top_k, part, nsum, bias, ids,
+                                            gates, s),
+                   "softmax/top-k");
+}
+
+k3moe::BucketOut bucket_out(const Ws& ws, int32_t* offsets, int32_t* rows) {
+  k3moe::BucketOut o;
+  o.offsets = offsets;
+  o.rows = rows;
+  o.act = ws.at<int32_t>(R_ACT);
+  o.n_act = ws.at<int32_t>(R_NACT);
+  o.pair_pos = ws.at<int32_t>(R_PPOS);
+  o.pair_exp = ws.at<int32_t>(R_PEXP);
+  return o;
+}
+
+int run_ffn(const k3moe_dims& dm, int32_t T, const void* x, int xf32,
+            const k3moe_mx_experts* ex, const int32_t* offsets, const int32_t* rows,
+            const float* gates, const float* resid, const float* shared, float* y,
+            uint16_t* y_bf16, const Ws& ws, hipStream_t s) {
+  const int d = dm.d_model, f = dm.d_ff, E = dm.n_experts, k = dm.top_k;
+  k3moe::MxPtrs w{ex->gate_q, ex->gate_s, ex->up_q, ex->up_s, ex->down_q, ex->down_s};
+  const int64_t P = (int64_t)T * k;
+  const int max_act = (int)(P < E ? P : E);
+  float* h = ws.at<float>(R_H);
+  int rc;
+  {
+    Probe probe(K3MOE_KERNEL_GATE_UP, s);
+    rc = hip_check(k3moe::launch_gateup_gemv(T, d, f, E, k, x, xf32, w, offsets, rows,
+                                             ws.at<int32_t>(R_ACT), ws.at<int32_t>(R_NACT),
+                                             max_act, h, s),
+                   "gate/up");
+  }
+  if (rc) return rc;
+  if (T == 1 && k3moe::down_fused_supported(f, k)) {
+    Probe probe(K3MOE_KERNEL_DOWN, s);
+    return hip_check(k3moe::launch_down_fused_t1(d, f, k, w, h, ws.at<int32_t>(R_PPOS),
+                                                 ws.at<int32_t>(R_PEXP), gates, resid, shared, y,
+                                                 y_bf16, s),
+                     "down+combine");
+  }
+  float* z = ws.at<float>(R_Z);
+  {
+    Probe probe(K3MOE_KERNEL_DOWN, s);
+    rc = hip_check(k3moe::launch_down_gemv(T, d, f, E, k, w, h, offsets, rows,
+                                           ws.at<int32_t>(R_ACT), ws.at<int32_t>(R_NACT),
+                                           max_act, z, s),
+                   "down");
+  }
+  if (rc) return rc;
+  return hip_check(k3moe::launch_combine(T, d, k, z, gates, ws.at<int32_t>(R_PPOS), resid,
+                                         shared, y, y_bf16, s),
+                   "combine");
+}
+
+}  // namespace
+
+extern "C" {
+
+int k3moe_version(void) { return K3MOE_VERSION; }
+
+int k3moe_time_next_kernel(int which, void* ev_start, void* ev_stop) {
+  if (which != K3MOE_KERNEL_ROUTER && which != K3MOE_KERNEL_GATE_UP && which != K3MOE_KERNEL_DOWN)
+    return fail(K3MOE_EINVAL, "unknown kernel id %d", which);
+  if (!ev_start || !ev_stop) {
+    g_probe_which = 0;
+    return K3MOE_OK;
+  }
+  g_probe_which = which;
+  g_probe_start = (hipEvent_t)ev_start;
+  g_probe_stop = (hipEvent_t)ev_stop;
+  return K3MOE_OK;
+}
+
+const char* k3moe_last_error(void) { return g_err.c_str(); }
+
+size_t k3moe_workspace_bytes(const k3moe_dims* dims, int32_t max_tokens) {
+  if (check_dims(dims) || max_tokens < 0 || max_tokens > kMaxT) return 0;
+  return layout_for(*dims, max_tokens < 1 ? 1 : max_tokens).total;
+}
+
+int k3moe_router(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
+                 const uint16_t* w_router, const float* logit_bias, int32_t* topk_ids,
+                 float* topk_gates, void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_T(T)) || (rc = check_dtype(x_dtype))) return rc;
+  if (T == 0) return K3MOE_OK;
+  if ((rc = need_ptr(x, "x")) || (rc = need_ptr(w_router, "w_router")) ||
+      (rc = need_ptr(topk_ids, "topk_ids")) || (rc = need_ptr(topk_gates, "topk_gates")))
+    return rc;
+  Ws w;
+  if ((rc = get_ws(*dims, T, ws, ws_bytes, &w))) return rc;
+  return run_router(*dims, T, x, x_dtype == K3MOE_F32, w_router, logit_bias, topk_ids,
+                    topk_gates, w, (hipStream_t)stream);
+}
+
+int k3moe_route_bucket(const k3moe_dims* dims, int32_t T, const int32_t* topk_ids,
+                       int32_t* expert_offsets, int32_t* bucket_rows, void* ws, size_t ws_bytes,
+                       void* stream) {
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_T(T))) return rc;
+  if (T == 0) return K3MOE_OK;
+  if ((rc = need_ptr(topk_ids, "topk_ids")) || (rc = need_ptr(expert_offsets, "expert_offsets")) ||
+      (rc = need_ptr(bucket_rows, "bucket_rows")))
+    return rc;
+  Ws w;
+  if ((rc = get_ws(*dims, T, ws, ws_bytes, &w))) return rc;
+  return hip_check(k3moe::launch_bucket(T, dims->n_experts, dims->top_k, topk_ids,
+                                        bucket_out(w, expert_offsets, bucket_rows),
+                                        w.at<uint32_t>(R_HIST), w.at<uint32_t>(R_BASE),
+                                        w.at<uint64_t>(R_MASK), (hipStream_t)stream),
+                   "bucket");
+}
+
+int k3moe_expert_ffn(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
+                     const k3moe_mx_experts* experts, const int32_t* expert_offsets,
+                     const int32_t* bucket_rows, const float* topk_gates, float* y, void* ws,
+                     size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_T(T)) || (rc = check_dtype(x_dtype))) return rc;
+  if (T == 0) return K3MOE_OK;
+  if ((rc = check_expert_shape(*dims))) return rc;
+  if ((rc = need_ptr(x, "x", true)) || (rc = check_experts(experts)) ||
+      (rc = need_ptr(expert_offsets, "expert_offsets")) ||
+      (rc = need_ptr(bucket_rows, "bucket_rows")) || (rc = need_ptr(topk_gates, "topk_gates")) ||
+      (rc = need_ptr(y, "y", true)))
+    return rc;
+  Ws w;
+  if ((rc = get_ws(*dims, T, ws, ws_bytes, &w))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const k3moe::BucketOut o = bucket_out(w, const_cast<int32_t*>(expert_offsets),
+                                        const_cast<int32_t*>(bucket_rows));
+  rc = hip_check(k3moe::launch_pairs_from_bucket(T, dims->n_experts, dims->top_k,
+                                                 expert_offsets, bucket_rows, o, s),
+                 "bucket index");
+  if (rc) return rc;
+  return run_ffn(*dims, T, x, x_dtype == K3MOE_F32, experts, expert_offsets, bucket_rows,
+                 topk_gates, nullptr, nullptr, y, nullptr, w, s);
+}
+
+int k3moe_layer_forward(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
+                        const uint16_t* w_router, const float* logit_bias,
+                        const k3moe_mx_experts* experts, const k3moe_block* blk, float* y,
+                        uint16_t* y_bf16, int32_t* topk_ids, float* topk_gates, void* ws,
+                        size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_dims(dims)) || (rc = check_T(T)) || (rc = check_dtype(x_dtype))) return rc;
+  if (T == 0) return K3MOE_OK;
+  if ((rc = check_expert_shape(*dims))) return rc;
+  if ((rc = need_ptr(x, "x", true)) || (rc = need_ptr(w_router, "w_router")) ||
+      (rc = check_experts(experts)) || (rc = need_ptr(y, "y", true)))
+    return rc;
+  if (blk) {
+    if (x_dtype != K3MOE_F32) return fail(K3MOE_EINVAL, "block mode needs an fp32 residual x");
+    if ((rc = need_ptr(blk->rms_gamma, "blk->rms_gamma")) ||
+        (rc = need_ptr(blk->sh_gate, "blk->sh_gate", true)) ||
+        (rc = need_ptr(blk->sh_up, "blk->sh_up", true)) ||
+        (rc = need_ptr(blk->sh_down, "blk->sh_down", true)))
+      return rc;
+    if (!(blk->rms_eps >= 0.0f)) return fail(K3MOE_EINVAL, "rms_eps must be >= 0");
+  }
+  Ws w;
+  if ((rc = get_ws(*dims, T, ws, ws_bytes, &w))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const int d = dims->d_model;
+  int32_t* ids = topk_ids ? topk_ids : w.at<int32_t>(R_IDS);
+  float* gates = topk_gates ? topk_gates : w.at<float>(R_GATES);
+  const void* xin = x;
+  int xf32 = x_dtype == K3MOE_F32;
+  if (blk) {
+    float* xhat = w.at<float>(R_XHAT);
+    rc = hip_check(k3moe::launch_rmsnorm(T, d, static_cast<const float*>(x), blk->rms_gamma,
+                                         blk->rms_eps, xhat, s),
+                   "rmsnorm");
+    if (rc) return rc;
+    xin = xhat;
+    xf32 = 1;
+  }
+  if ((rc = run_router(*dims, T, xin, xf32, w_router, logit_bias, ids, gates, w, s))) return rc;
+  int32_t* offs = w.at<int32_t>(R_OFFS);
+  int32_t* rows = w.at<int32_t>(R_ROWS);
+  rc = hip_check(k3moe::launch_bucket(T, dims->n_experts, dims->top_k, ids,
+                                      bucket_out(w, offs, rows), w.at<uint32_t>(R_HIST),
+                                      w.at<uint32_t>(R_BASE), w.at<uint64_t>(R_MASK), s),
+                 "bucket");
+  if (rc) return rc;
+  const float* resid = nullptr;
+  const float* shared = nullptr;
+  if (blk) {
+    float* ssh = w.at<float>(R_SSH);
+    rc = hip_check(k3moe::launch_dense_swiglu(T, d, dims->d_ff, static_cast<const float*>(xin),
+                                              blk->sh_gate, blk->sh_up, blk->sh_down,
+                                              w.at<float>(R_HSH), ssh, s),
+                   "shared expert");
+    if (rc) return rc;
+    resid = static_cast<const float*>(x);
+    shared = ssh;
+  }
+  return run_ffn(*dims, T, xin, xf32, experts, offs, rows, gates, resid, shared, y, y_bf16, w, s);
+}
+
+}  // extern "C"

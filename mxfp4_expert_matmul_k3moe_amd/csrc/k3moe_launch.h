@@ -1,0 +1,74 @@
+// k3moe_launch.h — host-side launch wrappers of the gfx950 kernels (internal).
+// Every wrapper enqueues on `stream` and returns hipGetLastError().
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace k3moe {
+
+// ---- router (router.hip) -------------------------------------------------------
+// Rows of W handled per partial-sum chunk of the small-T router.
+int router_chunk_rows(int d);
+int router_num_chunks(int d);
+constexpr int kRouterGemvMaxT = 64;   // above this the tiled fp64 GEMM is used
+
+hipError_t launch_router_gemv(int T, int d, int E, const void* x, int xf32,
+                              const uint16_t* w, double* part, hipStream_t s);
+hipError_t launch_router_gemm(int T, int d, int E, const void* x, int xf32,
+                              const uint16_t* w, double* logits, hipStream_t s);
+// nsum: number of fp64 partial arrays [nsum][T][E] to add (1 = plain logits).
+hipError_t launch_route_topk(int T, int E, int k, const double* part, int nsum,
+                             const float* bias, int32_t* ids, float* gates, hipStream_t s);
+
+// ---- bucketing (bucket.hip) ----------------------------------------------------
+constexpr int kBucketTokens = 64;  // tokens per bucketing block
+struct BucketOut {
+  int32_t* offsets;   // [E+1]
+  int32_t* rows;      // [P] pair ids by bucket position
+  int32_t* act;       // [E] active experts, ascending
+  int32_t* n_act;     // [1]
+  int32_t* pair_pos;  // [P] bucket position of pair id
+  int32_t* pair_exp;  // [P] expert of pair id
+};
+hipError_t launch_bucket(int T, int E, int k, const int32_t* ids, const BucketOut& o,
+                         uint32_t* hist, uint32_t* base, uint64_t* masks, hipStream_t s);
+// From caller-supplied offsets/rows (k3moe_expert_ffn): act, n_act, pair_pos, pair_exp.
+hipError_t launch_pairs_from_bucket(int T, int E, int k, const int32_t* offsets,
+                                    const int32_t* rows, const BucketOut& o, hipStream_t s);
+
+// ---- expert FFN, GEMV family (ffn_gemv.hip) -----------------------------------------
+struct MxPtrs {
+  const uint8_t *gate_q, *gate_s, *up_q, *up_s, *down_q, *down_s;
+};
+bool gemv_shape_supported(int d, int f);
+// The T == 1 fused down kernel puts one lane group per slot in one block.
+bool down_fused_supported(int f, int k);
+hipError_t launch_gateup_gemv(int T, int d, int f, int E, int k, const void* x, int xf32,
+                              const MxPtrs& w, const int32_t* offsets, const int32_t* rows,
+                              const int32_t* act, const int32_t* n_act, int max_act,
+                              float* h, hipStream_t s);
+// T == 1: down projection of all k slots + ordered combine (+ optional residual terms).
+hipError_t launch_down_fused_t1(int d, int f, int k, const MxPtrs& w, const float* h,
+                                const int32_t* pair_pos, const int32_t* pair_exp,
+                                const float* gates, const float* resid, const float* shared,
+                                float* y, uint16_t* y_bf16, hipStream_t s);
+// Any T: per-expert down projection into z [P][d] (pair-indexed).
+hipError_t launch_down_gemv(int T, int d, int f, int E, int k, const MxPtrs& w,
+                            const float* h, const int32_t* offsets, const int32_t* rows,
+                            const int32_t* act, const int32_t* n_act, int max_act, float* z,
+                            hipStream_t s);
+// y[t] = (resid + shared) + sum_slot g * z[t*k+slot], slot order.
+hipError_t launch_combine(int T, int d, int k, const float* z, const float* gates,
+                          const int32_t* pair_pos, const float* resid, const float* shared,
+                          float* y, uint16_t* y_bf16, hipStream_t s);
+
+// ---- block extras (block.hip) ---------------------------------------------------------
+hipError_t launch_rmsnorm(int T, int d, const float* h, const uint16_t* gamma, float eps,
+                          float* xhat, hipStream_t s);
+// Dense bf16 SwiGLU: out [T][d] = Wd (silu(Wg x) * (Wu x)); hbuf [T][f] scratch.
+hipError_t launch_dense_swiglu(int T, int d, int f, const float* x, const uint16_t* wg,
+                               const uint16_t* wu, const uint16_t* wd, float* hbuf,
+                               float* out, hipStream_t s);
+
+}  // namespace k3moe

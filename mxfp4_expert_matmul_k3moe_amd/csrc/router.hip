@@ -1,0 +1,284 @@
+// router.hip — router logits (fp64 accumulation), softmax and top-k on gfx950.
+//
+// Follows "Kimi K3 纯 C 语言 CPU 推理实战" (chenxutan.com/d/5901.html) §2.4: logits are
+// the GEMV of the token against the [hidden][experts] gate matrix, the softmax is
+// max-subtracted over all experts, and top-k picks the largest logits with the lower
+// index winning a tie; the gate of a chosen expert is its full-softmax probability.
+// Every product bf16*bf16 or bf16*fp32 is exact in fp64, and the sums are carried in
+// fp64, so the ranking is that of the exact logits barring ties closer than fp64
+// rounding.
+#include "k3moe_device.h"
+#include "k3moe_launch.h"
+
+namespace k3moe {
+namespace {
+
+constexpr int kRouterRows = 512;  // W rows per partial chunk (4 waves x 128)
+constexpr int kRouterCols = 64;   // W columns per block (one lane each)
+constexpr int kTokGroup = 8;      // tokens per pass over a chunk
+
+template <bool XF32>
+__device__ __forceinline__ double load_x(const void* x, size_t i) {
+  if (XF32) return (double)static_cast<const float*>(x)[i];
+  return (double)bf16_bits_to_f32(static_cast<const uint16_t*>(x)[i]);
+}
+
+// part[chunk][t][e] = sum over rows k of this chunk of x[t][k] * W[k][e].
+// Block: 4 waves; lane = column; wave w sums rows [w*128, w*128+128) of the chunk; the
+// four wave sums are added in wave order. Grid: (chunks, column blocks).
+template <bool XF32, int NT>
+__global__ __launch_bounds__(256) void router_gemv_kernel(int T, int d, int E,
+                                                          const void* __restrict__ x,
+                                                          const uint16_t* __restrict__ w,
+                                                          double* __restrict__ part) {
+  __shared__ double xs[kRouterRows][NT];
+  __shared__ double ws[4][NT][kRouterCols];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int chunk = blockIdx.x;
+  const int k0 = chunk * kRouterRows;
+  const int nrows = min(kRouterRows, d - k0);
+  const int col = blockIdx.y * kRouterCols + lane;
+  const int r0 = wave * (kRouterRows / 4);
+  const int r1 = min(r0 + kRouterRows / 4, nrows);
+  for (int t0 = 0; t0 < T; t0 += NT) {
+    const int nt = min(NT, T - t0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < nrows * NT; i += 256) {
+      const int r = i / NT, tt = i % NT;
+      xs[r][tt] = (tt < nt) ? load_x<XF32>(x, (size_t)(t0 + tt) * d + k0 + r) : 0.0;
+    }
+    __syncthreads();
+    double acc[NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) acc[tt] = 0.0;
+    if (col < E) {
+      const uint16_t* wp = w + (size_t)k0 * E + col;
+      int r = r0;
+      for (; r + 8 <= r1; r += 8) {
+        uint16_t wv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) wv[u] = wp[(size_t)(r + u) * E];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const double wd = (double)bf16_bits_to_f32(wv[u]);
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) acc[tt] = fma(xs[r + u][tt], wd, acc[tt]);
+        }
+      }
+      for (; r < r1; ++r) {
+        const double wd = (double)bf16_bits_to_f32(wp[(size_t)r * E]);
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) acc[tt] = fma(xs[r][tt], wd, acc[tt]);
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) ws[wave][tt][lane] = acc[tt];
+    __syncthreads();
+    if (wave == 0 && col < E) {
+      for (int tt = 0; tt < nt; ++tt) {
+        const double s = ((ws[0][tt][lane] + ws[1][tt][lane]) + ws[2][tt][lane]) + ws[3][tt][lane];
+        part[((size_t)chunk * T + t0 + tt) * E + col] = s;
+      }
+    }
+  }
+}
+
+// Tiled fp64 GEMM for many tokens: logits[t][e] = sum_k x[t][k] W[k][e], k ascending
+// within each 16-row step, steps ascending. Tile 64 tokens x 64 experts; each thread
+// owns a 4x4 patch.
+template <bool XF32>
+__global__ __launch_bounds__(256) void router_gemm_kernel(int T, int d, int E,
+                                                          const void* __restrict__ x,
+                                                          const uint16_t* __restrict__ w,
+                                                          double* __restrict__ logits) {
+  constexpr int TM = 64, TN = 64, TK = 16;
+  __shared__ double xs[TK][TM + 1];
+  __shared__ double wsh[TK][TN + 1];
+  const int tid = threadIdx.x;
+  const int tm0 = blockIdx.x * TM, tn0 = blockIdx.y * TN;
+  const int ty = tid / 16, tx = tid % 16;  // 16 x 16 threads, 4x4 each
+  double acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+  for (int k0 = 0; k0 < d; k0 += TK) {
+    __syncthreads();
+    for (int i = tid; i < TM * TK; i += 256) {
+      const int m = i / TK, kk = i % TK;
+      const int t = tm0 + m, k = k0 + kk;
+      xs[kk][m] = (t < T && k < d) ? load_x<XF32>(x, (size_t)t * d + k) : 0.0;
+    }
+    for (int i = tid; i < TN * TK; i += 256) {
+      const int kk = i / TN, n = i % TN;
+      const int e = tn0 + n, k = k0 + kk;
+      wsh[kk][n] = (e < E && k < d) ? (double)bf16_bits_to_f32(w[(size_t)k * E + e]) : 0.0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < TK; ++kk) {
+      double a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = xs[kk][ty + 16 * i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = wsh[kk][tx + 16 * j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = tm0 + ty + 16 * i;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = tn0 + tx + 16 * j;
+      if (t < T && e < E) logits[(size_t)t * E + e] = acc[i][j];
+    }
+  }
+}
+
+// Total-order key of an fp64 logit: larger logit -> larger key; +0 and -0 share a
+// key; NaN gets key 0, below every number.
+__device__ __forceinline__ uint64_t order_key(double v) {
+  if (v != v) return 0ull;
+  v = v + 0.0;  // -0 -> +0
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+__device__ __forceinline__ bool better(uint64_t ka, int ia, uint64_t kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+constexpr int kMaxE = 4096;
+
+// One block (256 threads) per token. Phase 1 (all waves): logits = sum of partials
+// (+ bias) into LDS. Phase 2 (wave 0): the k-th best of the 64 lane maxima bounds the
+// k-th best logit from below, so every top-k element ranks at or above it; those
+// candidates are ranked exactly against each other. Softmax gates follow.
+__global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
+                                                         const double* __restrict__ part,
+                                                         int nsum, const float* __restrict__ bias,
+                                                         int32_t* __restrict__ ids,
+                                                         float* __restrict__ gates) {
+  __shared__ double lg[kMaxE];
+  __shared__ int cid[kMaxE];
+  __shared__ int s_total;
+  __shared__ uint64_t s_tk;
+  __shared__ int s_ti;
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < E; e += 256) {
+    double s = part[(size_t)t * E + e];
+    for (int c = 1; c < nsum; ++c) s += part[((size_t)c * T + t) * E + e];
+    if (bias) s += (double)bias[e];
+    lg[e] = s;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    uint64_t bk = 0;
+    int bi = -1;
+    for (int e = lane; e < E; e += 64) {
+      const uint64_t kv = order_key(lg[e]);
+      if (bi < 0 || better(kv, e, bk, bi)) { bk = kv; bi = e; }
+    }
+    int rank = 0;
+    for (int j = 0; j < 64; ++j) {
+      const uint64_t ok = __shfl(bk, j, 64);
+      const int oi = __shfl(bi, j, 64);
+      if (oi >= 0 && bi >= 0 && better(ok, oi, bk, bi)) ++rank;
+    }
+    const int kk = min(k, min(E, 64));
+    if (bi >= 0 && rank == kk - 1) { s_tk = bk; s_ti = bi; }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const uint64_t tk = s_tk;
+    const int ti = s_ti;
+    int mine = 0;
+    for (int e = lane; e < E; e += 64)
+      if (!better(tk, ti, order_key(lg[e]), e)) ++mine;
+    int pre = mine;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(pre, off, 64);
+      if (lane >= off) pre += v;
+    }
+    if (lane == 63) s_total = pre;
+    pre -= mine;
+    for (int e = lane; e < E; e += 64) {
+      const uint64_t kv = order_key(lg[e]);
+      if (!better(tk, ti, kv, e)) cid[pre++] = e;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int total = s_total;
+    // softmax: max over non-NaN logits, per-lane ordered sums, fixed xor tree
+    double m = -__builtin_huge_val();
+    int anynan = 0;
+    for (int e = lane; e < E; e += 64) {
+      const double v = lg[e];
+      anynan |= (v != v);
+      m = (v > m) ? v : m;
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+      const double o = __shfl_xor(m, off, 64);
+      m = (o > m) ? o : m;
+    }
+    double se = 0.0;
+    for (int e = lane; e < E; e += 64) se += exp(lg[e] - m);
+    for (int off = 32; off >= 1; off >>= 1) se += __shfl_xor(se, off, 64);
+    if (__any(anynan)) se = __builtin_nan("");
+    for (int c0 = 0; c0 < total; c0 += 64) {
+      const int c = c0 + lane;
+      if (c < total) {
+        const int id = cid[c];
+        const uint64_t kv = order_key(lg[id]);
+        int r = 0;
+        for (int j = 0; j < total; ++j) {
+          const int oj = cid[j];
+          r += better(order_key(lg[oj]), oj, kv, id) ? 1 : 0;
+        }
+        if (r < k) {
+          ids[(size_t)t * k + r] = id;
+          gates[(size_t)t * k + r] = (float)(exp(lg[id] - m) / se);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+int router_chunk_rows(int) { return kRouterRows; }
+int router_num_chunks(int d) { return (d + kRouterRows - 1) / kRouterRows; }
+
+hipError_t launch_router_gemv(int T, int d, int E, const void* x, int xf32, const uint16_t* w,
+                              double* part, hipStream_t s) {
+  dim3 grid(router_num_chunks(d), (E + kRouterCols - 1) / kRouterCols);
+  if (T == 1) {
+    if (xf32) router_gemv_kernel<true, 1><<<grid, 256, 0, s>>>(T, d, E, x, w, part);
+    else router_gemv_kernel<false, 1><<<grid, 256, 0, s>>>(T, d, E, x, w, part);
+  } else {
+    if (xf32) router_gemv_kernel<true, kTokGroup><<<grid, 256, 0, s>>>(T, d, E, x, w, part);
+    else router_gemv_kernel<false, kTokGroup><<<grid, 256, 0, s>>>(T, d, E, x, w, part);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_router_gemm(int T, int d, int E, const void* x, int xf32, const uint16_t* w,
+                              double* logits, hipStream_t s) {
+  dim3 grid((T + 63) / 64, (E + 63) / 64);
+  if (xf32) router_gemm_kernel<true><<<grid, 256, 0, s>>>(T, d, E, x, w, logits);
+  else router_gemm_kernel<false><<<grid, 256, 0, s>>>(T, d, E, x, w, logits);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_topk(int T, int E, int k, const double* part, int nsum,
+                             const float* bias, int32_t* ids, float* gates, hipStream_t s) {
+  route_topk_kernel<<<T, 256, 0, s>>>(T, E, k, part, nsum, bias, ids, gates);
+  return hipGetLastError();
+}
+
+}  // namespace k3moe

@@ -1,0 +1,307 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bars (the oracle is the reference):
+  - routing: expert ids and their order bit-exact; gates within 2 fp32 ulps;
+  - bucketing: offsets and rows bit-exact;
+  - layer output: max over tokens of ||y_gpu - y_ref||_2 / ||y_ref||_2 <= 2e-3 on the
+    fp32 output (the 2e-3 relative bound, read per token in the L2 norm);
+  - the bf16 copy equals round-to-nearest-even of the fp32 output;
+  - repeated runs are bit-identical.
+Every case prints its name before touching the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_expert_matmul_k3moe_amd as k3
+import oracle
+from k3gen import device as gdev
+from k3gen.workloads import BATCHED, DECODE, PREFILL, STACK8, TINY, TOY, Workload
+from oracle import harness
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def dims_of(w: Workload):
+    return k3.make_dims(w.d, w.f, w.E, w.k)
+
+
+def rel_l2(yg: np.ndarray, yr: np.ndarray) -> np.ndarray:
+    return np.linalg.norm(yg - yr, axis=1) / np.maximum(np.linalg.norm(yr, axis=1), 1e-300)
+
+
+def check_routing(ids_g, gates_g, ids_r, gates_r):
+    assert np.array_equal(ids_g, ids_r), "expert ids/order differ from the oracle"
+    g32 = gates_r.astype(np.float32)
+    ulp = np.spacing(np.abs(g32))
+    assert np.all(np.abs(gates_g - g32) <= 2 * ulp), "gates differ by more than 2 ulp"
+
+
+def run_gpu_layer(w: Workload, x_np, dev, layer=0, experts=None, block=False, x_dtype="bf16"):
+    dims = dims_of(w)
+    ex = k3.MxExperts(**(experts if experts is not None else gdev.experts(w, layer, dev)))
+    if x_dtype == "bf16":
+        x = gdev.bf16_tensor(x_np, dev)
+    else:
+        x = torch.from_numpy(np.ascontiguousarray(x_np, dtype=np.float32)).to(dev)
+    T = x.shape[0]
+    ids = torch.empty((T, w.k), dtype=torch.int32, device=dev)
+    gates = torch.empty((T, w.k), dtype=torch.float32, device=dev)
+    ybf = torch.empty((T, w.d), dtype=torch.bfloat16, device=dev)
+    blk = None
+    if block:
+        b = gdev.block_extras(w, layer, dev)
+        blk = k3.BlockWeights(b["rms_gamma"], b["sh_gate"], b["sh_up"], b["sh_down"], 1e-6)
+    y = k3.layer_forward(dims, x, gdev.router_w(w, layer, dev), gdev.bias(w, layer, dev), ex,
+                         blk, y_bf16=ybf, ids=ids, gates=gates)
+    torch.cuda.synchronize()
+    return {"y": y, "ybf": ybf, "ids": ids.cpu().numpy(), "gates": gates.cpu().numpy()}
+
+
+def assert_layer(w: Workload, g, ref, rows=None, tol=TOL):
+    ids_g, gates_g = g["ids"], g["gates"]
+    yg = g["y"].cpu().double().numpy()
+    if rows is not None:
+        ids_g, gates_g, yg = ids_g[rows], gates_g[rows], yg[rows]
+    check_routing(ids_g, gates_g, ref["ids"], ref["gates"])
+    err = rel_l2(yg, ref["y"])
+    print(f"    max rel L2 err {err.max():.3e}  (tokens {len(err)})", flush=True)
+    assert err.max() <= tol
+    assert torch.equal(g["ybf"], g["y"].to(torch.bfloat16)), "bf16 copy is not RNE(fp32)"
+    return err
+
+
+# ---- generator ----------------------------------------------------------------------------
+def test_device_generator_matches_host(dev):
+    say("device generator vs host generator")
+    for w, es in [(TOY, range(TOY.E)), (DECODE.with_(E=3), range(3))]:
+        d = gdev.experts(w, 0, dev)
+        for e in es:
+            h = w.expert_host(0, e)
+            for n, t in d.items():
+                assert np.array_equal(t[e].cpu().numpy(), h[n]), (w.name, e, n)
+
+
+# ---- small layers -------------------------------------------------------------------------
+SHAPES = [
+    TINY,                                                   # T=3, multi-token GEMV path
+    TOY,                                                    # the toy layer, T=1
+    Workload("ragged1", 11, d=96, f=64, E=13, k=3, T=37),   # 3 blocks/row, ragged tails
+    Workload("k_eq_e", 12, d=160, f=96, E=5, k=5, T=1),     # k = E
+    Workload("prefill_small", 13, d=512, f=256, E=40, k=8, T=70, zipf_alpha=1.1),
+    Workload("one_expert", 14, d=64, f=32, E=1, k=1, T=4),
+    Workload("k3_widths", 15, d=7168, f=1536, E=24, k=4, T=5),
+    Workload("k3_widths_t1", 16, d=7168, f=1536, E=40, k=16, T=1),
+    Workload("many_tokens", 17, d=256, f=128, E=16, k=2, T=130),
+]
+
+
+@pytest.mark.parametrize("w", SHAPES, ids=[s.name for s in SHAPES])
+def test_layer_matches_oracle(dev, w):
+    say(f"layer {w.name} d={w.d} f={w.f} E={w.E} k={w.k} T={w.T}")
+    x = w.x_bf16()
+    g = run_gpu_layer(w, x, dev)
+    ref = harness.run_layer(w, x)
+    err = assert_layer(w, g, ref)
+    assert err.max() < 1e-4  # fp32 accumulation throughout these GEMV paths
+
+
+def test_entry_points_separately(dev):
+    w = TOY.with_(T=9, name="toy9")
+    say("router / route_bucket / expert_ffn separately on toy T=9")
+    dims = dims_of(w)
+    xh = w.x_bf16()
+    x = gdev.bf16_tensor(xh, dev)
+    ids, gates = k3.router(dims, x, gdev.router_w(w, 0, dev))
+    ref = harness.run_layer(w, xh)
+    torch.cuda.synchronize()
+    check_routing(ids.cpu().numpy(), gates.cpu().numpy(), ref["ids"], ref["gates"])
+    offs, rows = k3.route_bucket(dims, ids)
+    ro, rr = oracle.bucket(ref["ids"], w.E)
+    assert np.array_equal(offs.cpu().numpy(), ro) and np.array_equal(rows.cpu().numpy(), rr)
+    ex = k3.MxExperts(**gdev.experts(w, 0, dev))
+    y = k3.expert_ffn(dims, x, ex, offs, rows, gates)
+    torch.cuda.synchronize()
+    assert rel_l2(y.cpu().double().numpy(), ref["y"]).max() < 1e-4
+    # the same with a single token (fused down + combine path)
+    y1 = k3.expert_ffn(dims, x[:1].contiguous(), ex, *k3.route_bucket(dims, ids[:1].contiguous()),
+                       gates[:1].contiguous())
+    torch.cuda.synchronize()
+    assert rel_l2(y1.cpu().double().numpy(), ref["y"][:1]).max() < 1e-4
+
+
+def test_bucket_large_T_exact(dev):
+    say("route_bucket T=300 (multi-block) vs oracle")
+    rng = np.random.default_rng(9)
+    E, k, T = 50, 6, 300
+    ids_np = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    dims = k3.make_dims(64, 32, E, k)
+    offs, rows = k3.route_bucket(dims, torch.from_numpy(ids_np).to(dev))
+    torch.cuda.synchronize()
+    ro, rr = oracle.bucket(ids_np, E)
+    assert np.array_equal(offs.cpu().numpy(), ro) and np.array_equal(rows.cpu().numpy(), rr)
+
+
+def test_zero_input_routes_first_k(dev):
+    w = TOY.with_(T=2, name="toy_zero")
+    say("x = 0")
+    x = np.zeros((2, w.d), dtype=np.uint16)
+    g = run_gpu_layer(w, x, dev)
+    assert g["ids"].tolist() == [list(range(w.k))] * 2
+    assert np.all(g["gates"] == np.float32(1.0 / w.E))
+    ref = harness.run_layer(w, x)
+    assert_layer(w, g, ref)
+
+
+def test_nan_scale_propagates(dev):
+    w = TOY
+    say("E8M0 255 in one down row of a selected expert")
+    x = w.x_bf16()
+    ref0 = harness.run_layer(w, x)
+    e = int(ref0["ids"][0, 0])
+    ex = gdev.experts(w, 0, dev)
+    ex["down_s"][e, 5, 0] = 255
+    g = run_gpu_layer(w, x, dev, experts=ex)
+    over = w.expert_host(0, e)
+    over["down_s"][5, 0] = 255
+    ref = harness.run_layer(w, x, expert_override={e: over})
+    yg = g["y"].cpu().numpy()[0]
+    assert np.array_equal(np.isnan(yg), np.isnan(ref["y"][0]))
+    assert np.isnan(yg[5]) and np.isfinite(np.delete(yg, 5)).all()
+
+
+def test_down_scale_plus_one_doubles_exactly(dev):
+    for w in (TOY, TINY):
+        say(f"down scales +1 doubles y exactly ({w.name})")
+        x = w.x_bf16()
+        ex = gdev.experts(w, 0, dev)
+        y1 = run_gpu_layer(w, x, dev, experts=ex)["y"].clone()
+        ex["down_s"] += 1
+        y2 = run_gpu_layer(w, x, dev, experts=ex)["y"]
+        assert torch.equal(y2, 2 * y1)
+
+
+def test_repeat_runs_bit_identical(dev):
+    for w in (TOY, TINY, SHAPES[4]):
+        say(f"determinism {w.name}")
+        x = w.x_bf16()
+        ex = gdev.experts(w, 0, dev)
+        a = run_gpu_layer(w, x, dev, experts=ex)
+        b = run_gpu_layer(w, x, dev, experts=ex)
+        assert torch.equal(a["y"], b["y"]) and np.array_equal(a["ids"], b["ids"])
+        assert np.array_equal(a["gates"], b["gates"])
+
+
+def test_fp32_activations(dev):
+    w = TOY.with_(T=3, name="toy_f32")
+    say("fp32 activations")
+    x = w.resid0()
+    g = run_gpu_layer(w, x, dev, x_dtype="f32")
+    ref = harness.run_layer(w, x)
+    assert_layer(w, g, ref)
+
+
+def test_block_mode_small_chain(dev):
+    w = TINY.with_(block=True, layers=3, T=2, name="tiny_block")
+    say("block mode, 3 chained tiny blocks")
+    h0 = w.resid0()
+    ref = harness.run_stack(w, h0)
+    h = torch.from_numpy(h0).to(dev)
+    for layer in range(w.layers):
+        g = run_gpu_layer(w, h.cpu().numpy(), dev, layer=layer, block=True, x_dtype="f32")
+        assert np.array_equal(g["ids"], ref["ids"][layer]), f"routing differs at layer {layer}"
+        h = g["y"]
+    err = rel_l2(h.cpu().double().numpy(), ref["y"])
+    print(f"    max rel L2 err {err.max():.3e}", flush=True)
+    assert err.max() < 1e-4
+
+
+def test_workspace_too_small_reports(dev):
+    w = TOY
+    dims = dims_of(w)
+    small = torch.empty(64, dtype=torch.uint8, device=dev)
+    with pytest.raises(k3.K3MoEError) as ei:
+        k3.router(dims, gdev.x_bf16(w, device=dev), gdev.router_w(w, 0, dev), ws=small)
+    assert ei.value.code == k3.EWORKSPACE
+
+
+# ---- K3-shaped workloads ------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def k3_decode_layer(dev):
+    ex = gdev.experts(DECODE, 0, dev)
+    yield ex
+    del ex
+    torch.cuda.empty_cache()
+
+
+def test_decode_k3(dev, k3_decode_layer):
+    w = DECODE
+    say("decode: d=7168 f=1536 E=896 k=16 T=1")
+    for ts in (0, 1):
+        x = w.x_bf16(token_set=ts)
+        g = run_gpu_layer(w, x, dev, experts=k3_decode_layer)
+        ref = harness.run_layer(w, x)
+        assert_layer(w, g, ref)
+        g2 = run_gpu_layer(w, x, dev, experts=k3_decode_layer)
+        assert torch.equal(g["y"], g2["y"])
+
+
+def test_batched_k3(dev):
+    w = BATCHED
+    say("batched decode: T=32")
+    x = w.x_bf16()
+    ex = gdev.experts(w, 0, dev)
+    g = run_gpu_layer(w, x, dev, experts=ex)
+    rows = [0, 11, 31]
+    ref = harness.run_layer(w, x, tokens=rows)
+    assert_layer(w, g, ref, rows=rows)
+    ids_all, _, _, _ = oracle.layer_route(x, w.router_w(0), None, w.k)
+    assert np.array_equal(g["ids"], ids_all)
+    del ex
+    torch.cuda.empty_cache()
+
+
+def test_prefill_k3(dev):
+    w = PREFILL
+    say("prefill: T=2048 with Zipf(1.1) logit bias")
+    x = w.x_bf16()
+    ex = gdev.experts(w, 0, dev)
+    g = run_gpu_layer(w, x, dev, experts=ex)
+    ids_all, gates_all, _, _ = oracle.layer_route(x, w.router_w(0), w.bias(0), w.k)
+    check_routing(g["ids"], g["gates"], ids_all, gates_all)
+    counts = np.bincount(ids_all.ravel(), minlength=w.E)
+    print(f"    touched experts {int((counts > 0).sum())}, max load {counts.max()}", flush=True)
+    rows = [0, 1023, 2047]
+    ref = harness.run_layer(w, x, tokens=rows)
+    assert_layer(w, g, ref, rows=rows)
+    del ex
+    torch.cuda.empty_cache()
+
+
+def test_stack8_k3(dev):
+    w = STACK8
+    say("8 stacked blocks, T=1, ~126 GB of MXFP4 experts resident")
+    h0 = w.resid0()
+    ref = harness.run_stack(w, h0)
+    layers = [gdev.experts(w, l, dev) for l in range(w.layers)]
+    h = h0
+    for l in range(w.layers):
+        g = run_gpu_layer(w, h, dev, layer=l, experts=layers[l], block=True, x_dtype="f32")
+        assert np.array_equal(g["ids"], ref["ids"][l]), f"routing differs at layer {l}"
+        h = g["y"].cpu().numpy()
+    err = rel_l2(h.astype(np.float64), ref["y"])
+    print(f"    max rel L2 err after 8 blocks {err.max():.3e}", flush=True)
+    assert err.max() <= TOL
+    del layers
+    torch.cuda.empty_cache()
