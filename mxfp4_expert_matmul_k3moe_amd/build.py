@@ -13,7 +13,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libk3moe.so")
 
-SOURCES = ["router.hip", "bucket.hip", "ffn_gemv.hip", "block.hip", "k3moe_api.cpp"]
+SOURCES = ["router.hip", "bucket.hip", "ffn_gemv.hip", "ffn_mfma.hip", "block.hip",
+           "k3moe_api.cpp"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
          "-Wno-unused-function", "-fvisibility=hidden",
          # no packed fp32 instructions in any generated code

@@ -81,32 +81,47 @@ __device__ void place_pairs(int T, int E, int k, int b, const int32_t* ids,
   }
 }
 
-// Counts per expert -> offsets [E+1], active list, n_act (one 1024-thread block).
-// cnt_to_base: on return holds the first position of each expert.
-__device__ void offsets_and_active(int E, int* cnt_to_base, int32_t* offsets, int32_t* act,
-                                   int32_t* n_act, int* s_wave) {
-  int v[4], o[4], f[4], fo[4];
+// Active-expert list and M-tile prefix of the grouped GEMM from per-expert counts v[].
+__device__ void active_and_tiles(int E, const int v[4], int32_t* act, int32_t* n_act,
+                                 int32_t* mtile_off, int* s_wave) {
+  int f[4], fo[4], mt[4], mo[4];
   const int e0 = threadIdx.x * 4;
   for (int i = 0; i < 4; ++i) {
-    const int e = e0 + i;
-    v[i] = (e < E) ? cnt_to_base[e] : 0;
-    f[i] = (e < E && v[i] > 0) ? 1 : 0;
+    f[i] = (e0 + i < E && v[i] > 0) ? 1 : 0;
+    mt[i] = f[i] ? (v[i] + kMfmaTileM - 1) / kMfmaTileM : 0;
   }
-  int total, nact;
-  block_scan4(v, o, s_wave, &total);
+  int nact, ntiles;
   block_scan4(f, fo, s_wave, &nact);
+  block_scan4(mt, mo, s_wave, &ntiles);
+  for (int i = 0; i < 4; ++i)
+    if (f[i]) {
+      act[fo[i]] = e0 + i;
+      mtile_off[fo[i]] = mo[i];
+    }
+  if (threadIdx.x == 0) {
+    *n_act = nact;
+    mtile_off[nact] = ntiles;
+  }
+  __syncthreads();
+}
+
+// Counts per expert -> offsets [E+1], active list, n_act, M-tile prefix (one 1024-thread
+// block). cnt_to_base: on return holds the first position of each expert.
+__device__ void offsets_and_active(int E, int* cnt_to_base, const BucketOut& ob, int* s_wave) {
+  int v[4], o[4];
+  const int e0 = threadIdx.x * 4;
+  for (int i = 0; i < 4; ++i) v[i] = (e0 + i < E) ? cnt_to_base[e0 + i] : 0;
+  int total;
+  block_scan4(v, o, s_wave, &total);
+  active_and_tiles(E, v, ob.act, ob.n_act, ob.mtile_off, s_wave);
   for (int i = 0; i < 4; ++i) {
     const int e = e0 + i;
     if (e < E) {
-      offsets[e] = o[i];
+      ob.offsets[e] = o[i];
       cnt_to_base[e] = o[i];
-      if (f[i]) act[fo[i]] = e;
     }
   }
-  if (threadIdx.x == 0) {
-    offsets[E] = total;
-    *n_act = nact;
-  }
+  if (threadIdx.x == 0) ob.offsets[E] = total;
   __syncthreads();
 }
 
@@ -120,7 +135,7 @@ __global__ __launch_bounds__(1024) void bucket_single_kernel(int T, int E, int k
   build_masks(T, E, k, 0, ids, mask);
   for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = __popcll(mask[e]);
   __syncthreads();
-  offsets_and_active(E, cnt, o.offsets, o.act, o.n_act, s_wave);
+  offsets_and_active(E, cnt, o, s_wave);
   place_pairs(T, E, k, 0, ids, mask, cnt, o.rows, o.pair_pos, o.pair_exp);
 }
 
@@ -152,7 +167,7 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(int NB, int E,
     cnt[e] = run;
   }
   __syncthreads();
-  offsets_and_active(E, cnt, o.offsets, o.act, o.n_act, s_wave);
+  offsets_and_active(E, cnt, o, s_wave);
   for (int e = threadIdx.x; e < E; e += blockDim.x)
     for (int b = 0; b < NB; ++b) base[(size_t)b * E + e] += (uint32_t)cnt[e];
 }
@@ -190,21 +205,11 @@ __global__ __launch_bounds__(1024) void pairs_from_bucket_kernel(int T, int E, i
     cnt[e] = max(z - a, 0);
   }
   __syncthreads();
-  // offsets_and_active rewrites offsets; keep the caller's by scanning into scratch
-  int v[4], ofs[4], f[4], fo[4];
+  // the caller's offsets stay as they are; only the active list and tiles are derived
+  int v[4];
   const int e0 = threadIdx.x * 4;
-  for (int i = 0; i < 4; ++i) {
-    const int e = e0 + i;
-    v[i] = (e < E) ? cnt[e] : 0;
-    f[i] = (v[i] > 0) ? 1 : 0;
-  }
-  int total, nact;
-  block_scan4(v, ofs, s_wave, &total);
-  block_scan4(f, fo, s_wave, &nact);
-  for (int i = 0; i < 4; ++i)
-    if (e0 + i < E && f[i]) o.act[fo[i]] = e0 + i;
-  if (threadIdx.x == 0) *o.n_act = nact;
-  __syncthreads();
+  for (int i = 0; i < 4; ++i) v[i] = (e0 + i < E) ? cnt[e0 + i] : 0;
+  active_and_tiles(E, v, o.act, o.n_act, o.mtile_off, s_wave);
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     const int a = min(max(offsets[e], 0), P), z = min(max(offsets[e + 1], 0), P);
     for (int p = a; p < z; ++p) {

@@ -148,7 +148,6 @@ __global__ __launch_bounds__(256) void gateup_gemv_kernel(GateUpArgs a) {
   }
 }
 
-// ---- down projection, T == 1, all slots of the token + ordered combine --------------------
 struct DownT1Args {
   int d, f, k;
   const uint8_t *dq, *ds;
@@ -162,26 +161,111 @@ struct DownT1Args {
 };
 
 constexpr int kMaxSlots = 32;
-constexpr int kDownRowsT1 = 16;
+
+// ---- gate/up, T == 1: one token, persistent over (expert, row group) ----------------------
+// The token is staged in LDS once per block. Each wave walks row groups (rpw rows of G and
+// the same rows of U of one selected expert) with a stride of all waves in the grid, and
+// issues the loads of its next group before computing the current one.
+struct GateUpDecodeArgs {
+  int d, f;
+  const void* x;
+  const uint8_t *gq, *gs, *uq, *us;
+  const int32_t *offsets, *act, *n_act;
+  float* h;
+};
+
+template <bool XF32, int BPL>
+__global__ __launch_bounds__(256) void gateup_decode_kernel(GateUpDecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) u32x4 xs[];
+  constexpr int Q = XF32 ? 8 : 4;
+  const int d = a.d, f = a.f;
+  const int NB = d >> 5;
+  const int lpr = lanes_per_row(NB), rpw = 64 / lpr;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane & (lpr - 1), rsel = lane / lpr;
+  const size_t rq = (size_t)(d >> 1), rs = (size_t)NB;
+  {
+    const u32x4* src = static_cast<const u32x4*>(a.x);
+    for (int v = threadIdx.x; v < NB * Q; v += 256) {
+      const int cb = v / Q, qq = v - cb * Q;
+      xs[x_chunk(cb, qq, lpr, Q)] = src[v];
+    }
+  }
+  __syncthreads();
+  const int rgpe = (f + rpw - 1) / rpw;  // row groups per expert
+  const int total = *a.n_act * rgpe;
+  const int stride = gridDim.x * kGateUpWaves;
+  for (int rg = blockIdx.x * kGateUpWaves + wave; rg < total; rg += stride) {
+    const int ai = rg / rgpe;
+    const int j = (rg - ai * rgpe) * rpw + rsel;
+    const int e = a.act[ai];
+    const bool rv = j < f;
+    const size_t row = (size_t)e * f + (rv ? j : 0);
+    u32x4 gw[BPL], uw[BPL];
+    uint32_t gsc[BPL], usc[BPL];
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) {
+      const size_t cb = (size_t)(sub + lpr * i);
+      gw[i] = load_u32x4_nt(a.gq + row * rq + cb * 16);
+      uw[i] = load_u32x4_nt(a.uq + row * rq + cb * 16);
+      gsc[i] = a.gs[row * rs + cb];
+      usc[i] = a.us[row * rs + cb];
+    }
+    float gacc = 0.0f, uacc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) {
+      const u32x4* xb = xs + (i * Q) * lpr + sub;  // piece qq of this lane's block i
+      if constexpr (XF32) {
+        float xv[32];
+#pragma unroll
+        for (int qq = 0; qq < 8; ++qq) {
+          const u32x4 v = xb[qq * lpr];
+          xv[4 * qq + 0] = __uint_as_float(v[0]);
+          xv[4 * qq + 1] = __uint_as_float(v[1]);
+          xv[4 * qq + 2] = __uint_as_float(v[2]);
+          xv[4 * qq + 3] = __uint_as_float(v[3]);
+        }
+        gacc = fmaf(e8m0_to_f32(gsc[i]), block_dot_f32(gw[i], xv), gacc);
+        uacc = fmaf(e8m0_to_f32(usc[i]), block_dot_f32(uw[i], xv), uacc);
+      } else {
+        uint32_t xp[16];
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const u32x4 v = xb[qq * lpr];
+          xp[4 * qq + 0] = v[0];
+          xp[4 * qq + 1] = v[1];
+          xp[4 * qq + 2] = v[2];
+          xp[4 * qq + 3] = v[3];
+        }
+        gacc = fmaf(e8m0_to_f32(gsc[i]), block_dot_bf16(gw[i], xp), gacc);
+        uacc = fmaf(e8m0_to_f32(usc[i]), block_dot_bf16(uw[i], xp), uacc);
+      }
+    }
+    const float g = group_sum_rt(gacc, lpr);
+    const float u = group_sum_rt(uacc, lpr);
+    if (sub == 0 && rv) a.h[(size_t)a.offsets[e] * f + j] = silu_f32(g) * u;
+  }
+}
+
+// ---- down, T == 1: all slots, persistent over 4-row chunks, ordered combine -----------------
+// Lane group q owns slot q and keeps that slot's h row slice in registers for the whole
+// kernel. A block walks 4-row chunks of the output with the grid stride; the k partial
+// results of a row meet in LDS and one thread adds them in slot order.
+constexpr int kDecRows = 4;
 
 template <int BPL>
-__global__ __launch_bounds__(512) void down_fused_t1_kernel(DownT1Args a) {
-  __shared__ float zs[kMaxSlots][kDownRowsT1];
-  __shared__ float gs[kMaxSlots];
+__global__ __launch_bounds__(512) void down_decode_kernel(DownT1Args a) {
+  __shared__ float zs[2][kMaxSlots][kDecRows];
+  __shared__ float gsh[kMaxSlots];
   const int d = a.d, f = a.f, k = a.k;
   const int NB = f >> 5;
   const int lpr = lanes_per_row(NB);
-  const int gtid = threadIdx.x;
-  const int lane = gtid & 63;
-  const int q = gtid / lpr;            // slot handled by this lane group
-  const int sub = lane & (lpr - 1);
-  const int r0 = blockIdx.x * kDownRowsT1;
-  const int nr = min(kDownRowsT1, d - r0);
-  if (gtid < k) gs[gtid] = a.gates[gtid];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int q = tid / lpr, sub = lane & (lpr - 1);
+  if (tid < k) gsh[tid] = a.gates[tid];
   const int pos = (q < k) ? a.pair_pos[q] : -1;
   const int e = (q < k) ? a.pair_exp[q] : -1;
   const bool sv = pos >= 0 && e >= 0;
-  // h of this slot for this lane's blocks, in registers
   float hv[BPL][32];
 #pragma unroll
   for (int i = 0; i < BPL; ++i) {
@@ -199,41 +283,63 @@ __global__ __launch_bounds__(512) void down_fused_t1_kernel(DownT1Args a) {
   const size_t rq = (size_t)(f >> 1), rs = (size_t)NB;
   const uint8_t* dq = a.dq + (size_t)(sv ? e : 0) * d * rq;
   const uint8_t* dsc = a.ds + (size_t)(sv ? e : 0) * d * rs;
-  for (int rr = 0; rr < nr; rr += 2) {
-    u32x4 w[2][BPL];
-    uint32_t sc[2][BPL];
+  const int nchunk = (d + kDecRows - 1) / kDecRows;
+  u32x4 w0[kDecRows][BPL], w1[kDecRows][BPL];
+  uint32_t s0[kDecRows][BPL], s1[kDecRows][BPL];
+  auto load = [&](int ch, u32x4 (&w)[kDecRows][BPL], uint32_t (&sc)[kDecRows][BPL]) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int r = r0 + rr + u;
+    for (int u = 0; u < kDecRows; ++u) {
+      const int r = ch * kDecRows + u;
 #pragma unroll
       for (int i = 0; i < BPL; ++i) {
         const int cb = sub + lpr * i;
-        if (sv && rr + u < nr) {
+        if (sv && r < d) {
           w[u][i] = load_u32x4_nt(dq + (size_t)r * rq + (size_t)cb * 16);
           sc[u][i] = dsc[(size_t)r * rs + cb];
         }
       }
     }
+  };
+  auto compute = [&](int ch, const u32x4 (&w)[kDecRows][BPL],
+                     const uint32_t (&sc)[kDecRows][BPL], float (&z)[kMaxSlots][kDecRows]) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < kDecRows; ++u) {
       float p = 0.0f;
-      if (sv && rr + u < nr) {
+      const int r = ch * kDecRows + u;
+      if (sv && r < d) {
 #pragma unroll
         for (int i = 0; i < BPL; ++i) p = fmaf(e8m0_to_f32(sc[u][i]), block_dot_f32(w[u][i], hv[i]), p);
       }
-      const float z = group_sum_rt(p, lpr);
-      if (q < k && sub == 0 && rr + u < nr) zs[q][rr + u] = sv ? z : 0.0f;
+      const float zz = group_sum_rt(p, lpr);
+      if (q < k && sub == 0) z[q][u] = sv ? zz : 0.0f;
     }
-  }
+    __syncthreads();
+    if (tid < kDecRows) {
+      const int r = ch * kDecRows + tid;
+      if (r < d) {
+        float acc = 0.0f;
+        for (int s2 = 0; s2 < k; ++s2) acc = fmaf(gsh[s2], z[s2][tid], acc);
+        float out = acc;
+        if (a.resid) out = (a.resid[r] + (a.shared ? a.shared[r] : 0.0f)) + acc;
+        a.y[r] = out;
+        if (a.y_bf16) a.y_bf16[r] = f32_to_bf16_rne(out);
+      }
+    }
+  };
+  // chunks ch, ch + G, ch + 2G, ... alternate between two register buffers and two LDS
+  // slots; one barrier per chunk separates a slot's writes from its next reuse
+  const int G = gridDim.x;
+  int ch = blockIdx.x;
+  if (ch < nchunk) load(ch, w0, s0);
   __syncthreads();
-  if (gtid < nr) {
-    const int r = r0 + gtid;
-    float acc = 0.0f;
-    for (int s = 0; s < k; ++s) acc = fmaf(gs[s], zs[s][gtid], acc);
-    float out = acc;
-    if (a.resid) out = (a.resid[r] + (a.shared ? a.shared[r] : 0.0f)) + acc;
-    a.y[r] = out;
-    if (a.y_bf16) a.y_bf16[r] = f32_to_bf16_rne(out);
+  while (ch < nchunk) {
+    if (ch + G < nchunk) load(ch + G, w1, s1);
+    compute(ch, w0, s0, zs[0]);
+    ch += G;
+    if (ch >= nchunk) break;
+    if (ch + G < nchunk) load(ch + G, w0, s0);
+    compute(ch, w1, s1, zs[1]);
+    ch += G;
   }
 }
 
@@ -383,24 +489,58 @@ hipError_t launch_gateup_gemv(int T, int d, int f, int E, int k, const void* x, 
   return hipGetLastError();
 }
 
-hipError_t launch_down_fused_t1(int d, int f, int k, const MxPtrs& w, const float* h,
-                                const int32_t* pair_pos, const int32_t* pair_exp,
-                                const float* gates, const float* resid, const float* shared,
-                                float* y, uint16_t* y_bf16, hipStream_t s) {
+hipError_t launch_gateup_decode(int d, int f, int k, const void* x, int xf32, const MxPtrs& w,
+                                const int32_t* offsets, const int32_t* act, const int32_t* n_act,
+                                float* h, int n_cu, hipStream_t s) {
+  GateUpDecodeArgs a;
+  a.d = d; a.f = f; a.x = x;
+  a.gq = w.gate_q; a.gs = w.gate_s; a.uq = w.up_q; a.us = w.up_s;
+  a.offsets = offsets; a.act = act; a.n_act = n_act; a.h = h;
+  const int NB = d >> 5;
+  const int lpr = lanes_per_row(NB), bpl = NB / lpr, rpw = 64 / lpr;
+  const int rgpe = (f + rpw - 1) / rpw;
+  const int waves = k * rgpe;  // upper bound of row groups
+  int grid = (waves + kGateUpWaves - 1) / kGateUpWaves;
+  const int cap = 2 * n_cu;
+  if (grid > cap) grid = cap;
+  const size_t lds = (size_t)d * (xf32 ? 4 : 2);
+#define K3_GD(XF, B) gateup_decode_kernel<XF, B><<<grid, 256, lds, s>>>(a)
+#define K3_GD_B(XF)                   \
+  switch (bpl) {                      \
+    case 1: K3_GD(XF, 1); break;      \
+    case 2: K3_GD(XF, 2); break;      \
+    case 3: K3_GD(XF, 3); break;      \
+    case 4: K3_GD(XF, 4); break;      \
+    case 5: K3_GD(XF, 5); break;      \
+    case 6: K3_GD(XF, 6); break;      \
+    case 7: K3_GD(XF, 7); break;      \
+    default: K3_GD(XF, 8); break;     \
+  }
+  if (xf32) { K3_GD_B(true) } else { K3_GD_B(false) }
+#undef K3_GD_B
+#undef K3_GD
+  return hipGetLastError();
+}
+
+hipError_t launch_down_decode(int d, int f, int k, const MxPtrs& w, const float* h,
+                              const int32_t* pair_pos, const int32_t* pair_exp,
+                              const float* gates, const float* resid, const float* shared,
+                              float* y, uint16_t* y_bf16, int n_cu, hipStream_t s) {
   DownT1Args a;
   a.d = d; a.f = f; a.k = k; a.dq = w.down_q; a.ds = w.down_s; a.h = h;
   a.pair_pos = pair_pos; a.pair_exp = pair_exp; a.gates = gates;
-  a.resid = resid; a.shared = shared; a.y = y; a.y_bf16 = y_bf16; a.rc = kDownRowsT1;
+  a.resid = resid; a.shared = shared; a.y = y; a.y_bf16 = y_bf16; a.rc = kDecRows;
   const int NB = f >> 5;
   const int lpr = lanes_per_row(NB);
-  const int lanes = k * lpr;
-  const int threads = ((lanes + 63) / 64) * 64;
-  dim3 grid((unsigned)((d + kDownRowsT1 - 1) / kDownRowsT1));
+  const int threads = ((k * lpr + 63) / 64) * 64;
+  const int nchunk = (d + kDecRows - 1) / kDecRows;
+  int grid = 2 * n_cu;
+  if (grid > nchunk) grid = nchunk;
   switch (bpl_of(NB)) {
-    case 1: down_fused_t1_kernel<1><<<grid, threads, 0, s>>>(a); break;
-    case 2: down_fused_t1_kernel<2><<<grid, threads, 0, s>>>(a); break;
-    case 3: down_fused_t1_kernel<3><<<grid, threads, 0, s>>>(a); break;
-    default: down_fused_t1_kernel<4><<<grid, threads, 0, s>>>(a); break;
+    case 1: down_decode_kernel<1><<<grid, threads, 0, s>>>(a); break;
+    case 2: down_decode_kernel<2><<<grid, threads, 0, s>>>(a); break;
+    case 3: down_decode_kernel<3><<<grid, threads, 0, s>>>(a); break;
+    default: down_decode_kernel<4><<<grid, threads, 0, s>>>(a); break;
   }
   return hipGetLastError();
 }

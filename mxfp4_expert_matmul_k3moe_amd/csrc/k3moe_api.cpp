@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -48,10 +49,12 @@ constexpr int kMaxE = 4096;
 constexpr int kMaxK = 32;
 constexpr int kMaxT = 1 << 20;
 constexpr int kMaxWidth = 16384;
+// Above this many tokens, bf16 activations go through the MFMA grouped GEMMs.
+constexpr int kGemvMaxTokens = 64;
 
 enum Region {
   R_PART, R_IDS, R_GATES, R_OFFS, R_ROWS, R_ACT, R_NACT, R_PPOS, R_PEXP, R_HIST, R_BASE,
-  R_MASK, R_H, R_Z, R_XHAT, R_HSH, R_SSH, R_COUNT
+  R_MASK, R_H, R_Z, R_XHAT, R_HSH, R_SSH, R_MTILE, R_COUNT
 };
 
 struct Layout {
@@ -86,6 +89,7 @@ Layout layout_for(const k3moe_dims& dm, int64_t T) {
   sz[R_XHAT] = (size_t)(T * d * 4);
   sz[R_HSH] = (size_t)(T * f * 4);
   sz[R_SSH] = (size_t)(T * d * 4);
+  sz[R_MTILE] = (size_t)(E + 1) * 4;
   Layout L;
   size_t o = 0;
   for (int r = 0; r < R_COUNT; ++r) {
@@ -168,13 +172,40 @@ int get_ws(const k3moe_dims& dm, int32_t T, void* ws, size_t ws_bytes, Ws* out) 
   return K3MOE_OK;
 }
 
+// Compute units of the current device (cached per device ordinal).
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 int hip_check(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(K3MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
   return K3MOE_OK;
 }
 
+k3moe::BucketOut bucket_out(const Ws& ws, int32_t* offsets, int32_t* rows) {
+  k3moe::BucketOut o;
+  o.offsets = offsets;
+  o.rows = rows;
+  o.act = ws.at<int32_t>(R_ACT);
+  o.n_act = ws.at<int32_t>(R_NACT);
+  o.pair_pos = ws.at<int32_t>(R_PPOS);
+  o.pair_exp = ws.at<int32_t>(R_PEXP);
+  o.mtile_off = ws.at<int32_t>(R_MTILE);
+  return o;
+}
+
 int run_router(const k3moe_dims& dm, int32_t T, const void* x, int xf32, const uint16_t* w,
-               const float* bias, int32_t* ids, float* gates, const Ws& ws, hipStream_t s) {
+               const float* bias, int32_t* ids, float* gates, const Ws& ws, hipStream_t s,
+               const k3moe::BucketOut* bucket1 = nullptr) {
   double* part = ws.at<double>(R_PART);
   int nsum = 1;
   hipError_t e;
@@ -188,20 +219,10 @@ int run_router(const k3moe_dims& dm, int32_t T, const void* x, int xf32, const u
   int rc = hip_check(e, "router logits");
   if (rc) return rc;
   return hip_check(k3moe::launch_route_topk(T, dm.n_experts, dm.top_k, part, nsum, bias, ids,
-                                            gates, s),
+                                            gates, bucket1, s),
                    "softmax/top-k");
 }
 
-k3moe::BucketOut bucket_out(const Ws& ws, int32_t* offsets, int32_t* rows) {
-  k3moe::BucketOut o;
-  o.offsets = offsets;
-  o.rows = rows;
-  o.act = ws.at<int32_t>(R_ACT);
-  o.n_act = ws.at<int32_t>(R_NACT);
-  o.pair_pos = ws.at<int32_t>(R_PPOS);
-  o.pair_exp = ws.at<int32_t>(R_PEXP);
-  return o;
-}
 
 int run_ffn(const k3moe_dims& dm, int32_t T, const void* x, int xf32,
             const k3moe_mx_experts* ex, const int32_t* offsets, const int32_t* rows,
@@ -213,6 +234,47 @@ int run_ffn(const k3moe_dims& dm, int32_t T, const void* x, int xf32,
   const int max_act = (int)(P < E ? P : E);
   float* h = ws.at<float>(R_H);
   int rc;
+  if (T > kGemvMaxTokens && !xf32) {
+    // many tokens per expert: grouped GEMMs on bf16 MFMA, h kept in bf16
+    uint16_t* hb = ws.at<uint16_t>(R_H);
+    float* z = ws.at<float>(R_Z);
+    const int32_t* mt = ws.at<int32_t>(R_MTILE);
+    {
+      Probe probe(K3MOE_KERNEL_GATE_UP, s);
+      rc = hip_check(k3moe::launch_gateup_mfma(T, d, f, E, k, static_cast<const uint16_t*>(x), w,
+                                               offsets, rows, ws.at<int32_t>(R_ACT),
+                                               ws.at<int32_t>(R_NACT), mt, hb, s),
+                     "gate/up (MFMA)");
+    }
+    if (rc) return rc;
+    {
+      Probe probe(K3MOE_KERNEL_DOWN, s);
+      rc = hip_check(k3moe::launch_down_mfma(T, d, f, E, k, w, hb, offsets, rows,
+                                             ws.at<int32_t>(R_ACT), ws.at<int32_t>(R_NACT), mt, z,
+                                             s),
+                     "down (MFMA)");
+    }
+    if (rc) return rc;
+    return hip_check(k3moe::launch_combine(T, d, k, z, gates, ws.at<int32_t>(R_PPOS), resid,
+                                           shared, y, y_bf16, s),
+                     "combine");
+  }
+  if (T == 1 && k3moe::down_fused_supported(f, k)) {
+    // single token: persistent decode kernels
+    {
+      Probe probe(K3MOE_KERNEL_GATE_UP, s);
+      rc = hip_check(k3moe::launch_gateup_decode(d, f, k, x, xf32, w, offsets,
+                                                 ws.at<int32_t>(R_ACT), ws.at<int32_t>(R_NACT),
+                                                 h, cu_count(), s),
+                     "gate/up (decode)");
+    }
+    if (rc) return rc;
+    Probe probe(K3MOE_KERNEL_DOWN, s);
+    return hip_check(k3moe::launch_down_decode(d, f, k, w, h, ws.at<int32_t>(R_PPOS),
+                                               ws.at<int32_t>(R_PEXP), gates, resid, shared, y,
+                                               y_bf16, cu_count(), s),
+                     "down+combine (decode)");
+  }
   {
     Probe probe(K3MOE_KERNEL_GATE_UP, s);
     rc = hip_check(k3moe::launch_gateup_gemv(T, d, f, E, k, x, xf32, w, offsets, rows,
@@ -221,13 +283,6 @@ int run_ffn(const k3moe_dims& dm, int32_t T, const void* x, int xf32,
                    "gate/up");
   }
   if (rc) return rc;
-  if (T == 1 && k3moe::down_fused_supported(f, k)) {
-    Probe probe(K3MOE_KERNEL_DOWN, s);
-    return hip_check(k3moe::launch_down_fused_t1(d, f, k, w, h, ws.at<int32_t>(R_PPOS),
-                                                 ws.at<int32_t>(R_PEXP), gates, resid, shared, y,
-                                                 y_bf16, s),
-                     "down+combine");
-  }
   float* z = ws.at<float>(R_Z);
   {
     Probe probe(K3MOE_KERNEL_DOWN, s);
@@ -365,14 +420,20 @@ int k3moe_layer_forward(const k3moe_dims* dims, int32_t T, const void* x, int x_
     xin = xhat;
     xf32 = 1;
   }
-  if ((rc = run_router(*dims, T, xin, xf32, w_router, logit_bias, ids, gates, w, s))) return rc;
   int32_t* offs = w.at<int32_t>(R_OFFS);
   int32_t* rows = w.at<int32_t>(R_ROWS);
-  rc = hip_check(k3moe::launch_bucket(T, dims->n_experts, dims->top_k, ids,
-                                      bucket_out(w, offs, rows), w.at<uint32_t>(R_HIST),
-                                      w.at<uint32_t>(R_BASE), w.at<uint64_t>(R_MASK), s),
-                 "bucket");
-  if (rc) return rc;
+  const k3moe::BucketOut bo = bucket_out(w, offs, rows);
+  // a single token's bucket is written by the top-k kernel itself
+  if ((rc = run_router(*dims, T, xin, xf32, w_router, logit_bias, ids, gates, w, s,
+                       T == 1 ? &bo : nullptr)))
+    return rc;
+  if (T > 1) {
+    rc = hip_check(k3moe::launch_bucket(T, dims->n_experts, dims->top_k, ids, bo,
+                                        w.at<uint32_t>(R_HIST), w.at<uint32_t>(R_BASE),
+                                        w.at<uint64_t>(R_MASK), s),
+                   "bucket");
+    if (rc) return rc;
+  }
   const float* resid = nullptr;
   const float* shared = nullptr;
   if (blk) {

@@ -17,20 +17,23 @@ hipError_t launch_router_gemv(int T, int d, int E, const void* x, int xf32,
                               const uint16_t* w, double* part, hipStream_t s);
 hipError_t launch_router_gemm(int T, int d, int E, const void* x, int xf32,
                               const uint16_t* w, double* logits, hipStream_t s);
-// nsum: number of fp64 partial arrays [nsum][T][E] to add (1 = plain logits).
-hipError_t launch_route_topk(int T, int E, int k, const double* part, int nsum,
-                             const float* bias, int32_t* ids, float* gates, hipStream_t s);
-
 // ---- bucketing (bucket.hip) ----------------------------------------------------
 constexpr int kBucketTokens = 64;  // tokens per bucketing block
+constexpr int kMfmaTileM = 64;     // tokens per grouped-GEMM tile
 struct BucketOut {
-  int32_t* offsets;   // [E+1]
-  int32_t* rows;      // [P] pair ids by bucket position
-  int32_t* act;       // [E] active experts, ascending
-  int32_t* n_act;     // [1]
-  int32_t* pair_pos;  // [P] bucket position of pair id
-  int32_t* pair_exp;  // [P] expert of pair id
+  int32_t* offsets;    // [E+1]
+  int32_t* rows;       // [P] pair ids by bucket position
+  int32_t* act;        // [E] active experts, ascending
+  int32_t* n_act;      // [1]
+  int32_t* pair_pos;   // [P] bucket position of pair id
+  int32_t* pair_exp;   // [P] expert of pair id
+  int32_t* mtile_off;  // [E+1] prefix over active experts of ceil(count / kMfmaTileM)
 };
+// nsum: number of fp64 partial arrays [nsum][T][E] to add (1 = plain logits).
+// bucket1 (T == 1 only, may be NULL): also write the single token's bucket.
+hipError_t launch_route_topk(int T, int E, int k, const double* part, int nsum,
+                             const float* bias, int32_t* ids, float* gates,
+                             const BucketOut* bucket1, hipStream_t s);
 hipError_t launch_bucket(int T, int E, int k, const int32_t* ids, const BucketOut& o,
                          uint32_t* hist, uint32_t* base, uint64_t* masks, hipStream_t s);
 // From caller-supplied offsets/rows (k3moe_expert_ffn): act, n_act, pair_pos, pair_exp.
@@ -42,17 +45,20 @@ struct MxPtrs {
   const uint8_t *gate_q, *gate_s, *up_q, *up_s, *down_q, *down_s;
 };
 bool gemv_shape_supported(int d, int f);
-// The T == 1 fused down kernel puts one lane group per slot in one block.
+// The T == 1 down kernel puts one lane group per slot in one block.
 bool down_fused_supported(int f, int k);
 hipError_t launch_gateup_gemv(int T, int d, int f, int E, int k, const void* x, int xf32,
                               const MxPtrs& w, const int32_t* offsets, const int32_t* rows,
                               const int32_t* act, const int32_t* n_act, int max_act,
                               float* h, hipStream_t s);
-// T == 1: down projection of all k slots + ordered combine (+ optional residual terms).
-hipError_t launch_down_fused_t1(int d, int f, int k, const MxPtrs& w, const float* h,
-                                const int32_t* pair_pos, const int32_t* pair_exp,
-                                const float* gates, const float* resid, const float* shared,
-                                float* y, uint16_t* y_bf16, hipStream_t s);
+// T == 1, persistent decode kernels (grid sized from the CU count).
+hipError_t launch_gateup_decode(int d, int f, int k, const void* x, int xf32, const MxPtrs& w,
+                                const int32_t* offsets, const int32_t* act, const int32_t* n_act,
+                                float* h, int n_cu, hipStream_t s);
+hipError_t launch_down_decode(int d, int f, int k, const MxPtrs& w, const float* h,
+                              const int32_t* pair_pos, const int32_t* pair_exp,
+                              const float* gates, const float* resid, const float* shared,
+                              float* y, uint16_t* y_bf16, int n_cu, hipStream_t s);
 // Any T: per-expert down projection into z [P][d] (pair-indexed).
 hipError_t launch_down_gemv(int T, int d, int f, int E, int k, const MxPtrs& w,
                             const float* h, const int32_t* offsets, const int32_t* rows,
@@ -62,6 +68,21 @@ hipError_t launch_down_gemv(int T, int d, int f, int E, int k, const MxPtrs& w,
 hipError_t launch_combine(int T, int d, int k, const float* z, const float* gates,
                           const int32_t* pair_pos, const float* resid, const float* shared,
                           float* y, uint16_t* y_bf16, hipStream_t s);
+
+// ---- expert FFN, grouped GEMM on bf16 MFMA (ffn_mfma.hip) ---------------------------
+// Upper bound on the number of M tiles over all active experts.
+int mfma_mtiles_bound(int T, int E, int k);
+bool mfma_shape_supported(int d, int f);
+// h (bf16 [P][f], bucket order) = silu(G x) * (U x) for every (expert, token) pair.
+hipError_t launch_gateup_mfma(int T, int d, int f, int E, int k, const uint16_t* x,
+                              const MxPtrs& w, const int32_t* offsets, const int32_t* rows,
+                              const int32_t* act, const int32_t* n_act,
+                              const int32_t* mtile_off, uint16_t* h, hipStream_t s);
+// z (fp32 [P][d], pair-indexed) = D h.
+hipError_t launch_down_mfma(int T, int d, int f, int E, int k, const MxPtrs& w,
+                            const uint16_t* h, const int32_t* offsets, const int32_t* rows,
+                            const int32_t* act, const int32_t* n_act, const int32_t* mtile_off,
+                            float* z, hipStream_t s);
 
 // ---- block extras (block.hip) ---------------------------------------------------------
 hipError_t launch_rmsnorm(int T, int d, const float* h, const uint16_t* gamma, float eps,

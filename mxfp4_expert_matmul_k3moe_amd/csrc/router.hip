@@ -15,7 +15,7 @@ namespace {
 
 constexpr int kRouterRows = 512;  // W rows per partial chunk (4 waves x 128)
 constexpr int kRouterCols = 64;   // W columns per block (one lane each)
-constexpr int kTokGroup = 8;      // tokens per pass over a chunk
+constexpr int kTokGroup = 4;      // tokens per pass over a chunk
 
 template <bool XF32>
 __device__ __forceinline__ double load_x(const void* x, size_t i) {
@@ -77,6 +77,92 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(int T, int d, int E,
     if (wave == 0 && col < E) {
       for (int tt = 0; tt < nt; ++tt) {
         const double s = ((ws[0][tt][lane] + ws[1][tt][lane]) + ws[2][tt][lane]) + ws[3][tt][lane];
+        part[((size_t)chunk * T + t0 + tt) * E + col] = s;
+      }
+    }
+  }
+}
+
+// Same partials with 16-byte loads: a block covers 512 rows x 64 columns; lane l reads
+// columns 8*(l%8) .. +7 of rows l/8, l/8 + 8, ... (16 rows per lane, all loads issued
+// before the first FMA). Row sums: per lane in row order, then a fixed xor tree over
+// the 8 lanes sharing a column group, then the four waves in order. Needs E % 8 == 0.
+template <bool XF32, int NT>
+__global__ __launch_bounds__(256) void router_gemv_vec_kernel(int T, int d, int E,
+                                                              const void* __restrict__ x,
+                                                              const uint16_t* __restrict__ w,
+                                                              double* __restrict__ part) {
+  constexpr int RPL = kRouterRows / 4 / 8;  // rows per lane (16)
+  __shared__ double xs[kRouterRows][NT];
+  __shared__ double wsum[4][NT][kRouterCols];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int chunk = blockIdx.x;
+  const int k0 = chunk * kRouterRows;
+  const int nrows = min(kRouterRows, d - k0);
+  const int cg = lane & 7, rl = lane >> 3;
+  const int col0 = blockIdx.y * kRouterCols + cg * 8;
+  const bool cv = col0 < E;
+  for (int t0 = 0; t0 < T; t0 += NT) {
+    const int nt = min(NT, T - t0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < nrows * NT; i += 256) {
+      const int r = i / NT, tt = i % NT;
+      xs[r][tt] = (tt < nt) ? load_x<XF32>(x, (size_t)(t0 + tt) * d + k0 + r) : 0.0;
+    }
+    __syncthreads();
+    u32x4 wv[RPL];
+#pragma unroll
+    for (int u = 0; u < RPL; ++u) {
+      const int r = wave * (kRouterRows / 4) + rl + 8 * u;
+      wv[u] = (cv && r < nrows)
+                  ? *reinterpret_cast<const u32x4*>(w + (size_t)(k0 + r) * E + col0)
+                  : u32x4{0u, 0u, 0u, 0u};
+    }
+    double acc[NT][8];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[tt][c] = 0.0;
+#pragma unroll
+    for (int u = 0; u < RPL; ++u) {
+      const int r = wave * (kRouterRows / 4) + rl + 8 * u;
+      if (r < nrows) {
+        double wd[8];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          wd[2 * c] = (double)__uint_as_float(wv[u][c] << 16);
+          wd[2 * c + 1] = (double)__uint_as_float(wv[u][c] & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          const double xv = xs[r][tt];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) acc[tt][c] = fma(xv, wd[c], acc[tt][c]);
+        }
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        double v = acc[tt][c];
+        v += __shfl_xor(v, 8, 64);
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        acc[tt][c] = v;
+      }
+    if (rl == 0) {
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) wsum[wave][tt][cg * 8 + c] = acc[tt][c];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nt * kRouterCols; i += 256) {
+      const int tt = i / kRouterCols, c = i % kRouterCols;
+      const int col = blockIdx.y * kRouterCols + c;
+      if (col < E) {
+        const double s = ((wsum[0][tt][c] + wsum[1][tt][c]) + wsum[2][tt][c]) + wsum[3][tt][c];
         part[((size_t)chunk * T + t0 + tt) * E + col] = s;
       }
     }
@@ -152,45 +238,72 @@ __device__ __forceinline__ bool better(uint64_t ka, int ia, uint64_t kb, int ib)
 }
 
 constexpr int kMaxE = 4096;
+constexpr int kMaxSlots = 32;
+constexpr int kMaxChunks = 32;  // d <= 16384 in 512-row chunks
 
-// One block (256 threads) per token. Phase 1 (all waves): logits = sum of partials
-// (+ bias) into LDS. Phase 2 (wave 0): the k-th best of the 64 lane maxima bounds the
-// k-th best logit from below, so every top-k element ranks at or above it; those
-// candidates are ranked exactly against each other. Softmax gates follow.
+// One block (256 threads) per token.
+//  1. logits = sum of the fp64 partials in chunk order (+ bias), kept as order keys in LDS;
+//  2. wave 0: the k-th best of the 64 lane maxima bounds the k-th best logit from below,
+//     so every top-k element ranks at or above it; those candidates are ranked exactly;
+//  3. all waves: softmax denominator (per-thread ordered sums, fixed tree); gates.
+// With `bk` (T == 1) the same block also writes the expert bucket of the single token.
+struct Bucket1 {
+  int32_t *offsets, *rows, *act, *n_act, *pair_pos, *pair_exp, *mtile_off;
+};
+
+__device__ __forceinline__ double key_to_double(uint64_t kv) {
+  const uint64_t b = (kv >> 63) ? (kv & 0x7FFFFFFFFFFFFFFFull) : ~kv;
+  return __longlong_as_double((long long)b);
+}
+
 __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
                                                          const double* __restrict__ part,
                                                          int nsum, const float* __restrict__ bias,
                                                          int32_t* __restrict__ ids,
-                                                         float* __restrict__ gates) {
-  __shared__ double lg[kMaxE];
+                                                         float* __restrict__ gates, Bucket1 bk) {
+  __shared__ uint64_t keys[kMaxE];
   __shared__ int cid[kMaxE];
-  __shared__ int s_total;
+  __shared__ double red[256];
+  __shared__ double s_max;
+  __shared__ int s_total, s_nan, s_ids[kMaxSlots];
   __shared__ uint64_t s_tk;
   __shared__ int s_ti;
   const int t = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int e = threadIdx.x; e < E; e += 256) {
-    double s = part[(size_t)t * E + e];
-    for (int c = 1; c < nsum; ++c) s += part[((size_t)c * T + t) * E + e];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) s_nan = 0;
+  __syncthreads();
+  int nan_here = 0;
+  for (int e = tid; e < E; e += 256) {
+    double v[kMaxChunks];
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c)
+      v[c] = (c < nsum) ? part[((size_t)c * T + t) * E + e] : 0.0;
+    double s = v[0];
+#pragma unroll
+    for (int c = 1; c < kMaxChunks; ++c)
+      if (c < nsum) s += v[c];
     if (bias) s += (double)bias[e];
-    lg[e] = s;
+    nan_here |= (s != s);
+    keys[e] = order_key(s);
   }
+  if (nan_here) s_nan = 1;
   __syncthreads();
   if (wave == 0) {
-    uint64_t bk = 0;
+    uint64_t bkey = 0;
     int bi = -1;
     for (int e = lane; e < E; e += 64) {
-      const uint64_t kv = order_key(lg[e]);
-      if (bi < 0 || better(kv, e, bk, bi)) { bk = kv; bi = e; }
+      const uint64_t kv = keys[e];
+      if (bi < 0 || better(kv, e, bkey, bi)) { bkey = kv; bi = e; }
     }
     int rank = 0;
     for (int j = 0; j < 64; ++j) {
-      const uint64_t ok = __shfl(bk, j, 64);
+      const uint64_t ok = __shfl(bkey, j, 64);
       const int oi = __shfl(bi, j, 64);
-      if (oi >= 0 && bi >= 0 && better(ok, oi, bk, bi)) ++rank;
+      if (oi >= 0 && bi >= 0 && better(ok, oi, bkey, bi)) ++rank;
     }
+    if (bi >= 0 && rank == 0) s_max = key_to_double(bkey);
     const int kk = min(k, min(E, 64));
-    if (bi >= 0 && rank == kk - 1) { s_tk = bk; s_ti = bi; }
+    if (bi >= 0 && rank == kk - 1) { s_tk = bkey; s_ti = bi; }
   }
   __syncthreads();
   if (wave == 0) {
@@ -198,7 +311,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
     const int ti = s_ti;
     int mine = 0;
     for (int e = lane; e < E; e += 64)
-      if (!better(tk, ti, order_key(lg[e]), e)) ++mine;
+      if (!better(tk, ti, keys[e], e)) ++mine;
     int pre = mine;
     for (int off = 1; off < 64; off <<= 1) {
       const int v = __shfl_up(pre, off, 64);
@@ -206,46 +319,56 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
     }
     if (lane == 63) s_total = pre;
     pre -= mine;
-    for (int e = lane; e < E; e += 64) {
-      const uint64_t kv = order_key(lg[e]);
-      if (!better(tk, ti, kv, e)) cid[pre++] = e;
+    for (int e = lane; e < E; e += 64)
+      if (!better(tk, ti, keys[e], e)) cid[pre++] = e;
+  }
+  // softmax denominator over all experts (NaN-free max = top logit)
+  const double m = s_max;
+  double se = 0.0;
+  for (int e = tid; e < E; e += 256) se += exp(key_to_double(keys[e]) - m);
+  red[tid] = se;
+  __syncthreads();
+  for (int off = 128; off >= 1; off >>= 1) {
+    if (tid < off) red[tid] += red[tid + off];
+    __syncthreads();
+  }
+  const double sum = s_nan ? __builtin_nan("") : red[0];
+  const int total = s_total;
+  for (int c = tid; c < total; c += 256) {
+    const int id = cid[c];
+    const uint64_t kv = keys[id];
+    int r = 0;
+    for (int j = 0; j < total; ++j) {
+      const int oj = cid[j];
+      r += better(keys[oj], oj, kv, id) ? 1 : 0;
+    }
+    if (r < k) {
+      ids[(size_t)t * k + r] = id;
+      gates[(size_t)t * k + r] = (float)(exp(key_to_double(kv) - m) / sum);
+      if (bk.offsets) s_ids[r] = id;
     }
   }
+  if (!bk.offsets) return;
+  // T == 1: bucket of the single token. Ranks of the k ids in ascending id order.
   __syncthreads();
-  if (wave == 0) {
-    const int total = s_total;
-    // softmax: max over non-NaN logits, per-lane ordered sums, fixed xor tree
-    double m = -__builtin_huge_val();
-    int anynan = 0;
-    for (int e = lane; e < E; e += 64) {
-      const double v = lg[e];
-      anynan |= (v != v);
-      m = (v > m) ? v : m;
-    }
-    for (int off = 32; off >= 1; off >>= 1) {
-      const double o = __shfl_xor(m, off, 64);
-      m = (o > m) ? o : m;
-    }
-    double se = 0.0;
-    for (int e = lane; e < E; e += 64) se += exp(lg[e] - m);
-    for (int off = 32; off >= 1; off >>= 1) se += __shfl_xor(se, off, 64);
-    if (__any(anynan)) se = __builtin_nan("");
-    for (int c0 = 0; c0 < total; c0 += 64) {
-      const int c = c0 + lane;
-      if (c < total) {
-        const int id = cid[c];
-        const uint64_t kv = order_key(lg[id]);
-        int r = 0;
-        for (int j = 0; j < total; ++j) {
-          const int oj = cid[j];
-          r += better(order_key(lg[oj]), oj, kv, id) ? 1 : 0;
-        }
-        if (r < k) {
-          ids[(size_t)t * k + r] = id;
-          gates[(size_t)t * k + r] = (float)(exp(lg[id] - m) / se);
-        }
-      }
-    }
+  if (tid < k) {
+    const int id = s_ids[tid];
+    int pos = 0;
+    for (int j = 0; j < k; ++j) pos += (s_ids[j] < id) ? 1 : 0;
+    bk.rows[pos] = tid;
+    bk.act[pos] = id;
+    bk.pair_pos[tid] = pos;
+    bk.pair_exp[tid] = id;
+    bk.mtile_off[pos] = pos;
+  }
+  if (tid == 0) {
+    *bk.n_act = k;
+    bk.mtile_off[k] = k;
+  }
+  for (int e = tid; e <= E; e += 256) {
+    int c = 0;
+    for (int j = 0; j < k; ++j) c += (s_ids[j] < e) ? 1 : 0;
+    bk.offsets[e] = c;
   }
 }
 
@@ -257,6 +380,16 @@ int router_num_chunks(int d) { return (d + kRouterRows - 1) / kRouterRows; }
 hipError_t launch_router_gemv(int T, int d, int E, const void* x, int xf32, const uint16_t* w,
                               double* part, hipStream_t s) {
   dim3 grid(router_num_chunks(d), (E + kRouterCols - 1) / kRouterCols);
+  if (E % 8 == 0) {
+    if (T == 1) {
+      if (xf32) router_gemv_vec_kernel<true, 1><<<grid, 256, 0, s>>>(T, d, E, x, w, part);
+      else router_gemv_vec_kernel<false, 1><<<grid, 256, 0, s>>>(T, d, E, x, w, part);
+    } else {
+      if (xf32) router_gemv_vec_kernel<true, kTokGroup><<<grid, 256, 0, s>>>(T, d, E, x, w, part);
+      else router_gemv_vec_kernel<false, kTokGroup><<<grid, 256, 0, s>>>(T, d, E, x, w, part);
+    }
+    return hipGetLastError();
+  }
   if (T == 1) {
     if (xf32) router_gemv_kernel<true, 1><<<grid, 256, 0, s>>>(T, d, E, x, w, part);
     else router_gemv_kernel<false, 1><<<grid, 256, 0, s>>>(T, d, E, x, w, part);
@@ -276,8 +409,15 @@ hipError_t launch_router_gemm(int T, int d, int E, const void* x, int xf32, cons
 }
 
 hipError_t launch_route_topk(int T, int E, int k, const double* part, int nsum,
-                             const float* bias, int32_t* ids, float* gates, hipStream_t s) {
-  route_topk_kernel<<<T, 256, 0, s>>>(T, E, k, part, nsum, bias, ids, gates);
+                             const float* bias, int32_t* ids, float* gates,
+                             const BucketOut* bucket1, hipStream_t s) {
+  Bucket1 b{};
+  if (bucket1 && T == 1) {
+    b.offsets = bucket1->offsets; b.rows = bucket1->rows; b.act = bucket1->act;
+    b.n_act = bucket1->n_act; b.pair_pos = bucket1->pair_pos; b.pair_exp = bucket1->pair_exp;
+    b.mtile_off = bucket1->mtile_off;
+  }
+  route_topk_kernel<<<T, 256, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
   return hipGetLastError();
 }
 
