@@ -105,7 +105,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode", choices=["decode", "batched"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "batched", "prefill"])
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
+                    help="only run a plain device copy of MB megabytes 20 times (counter scale)")
     ap.add_argument("--token-sets", type=int, default=64)
     ap.add_argument("--cpu-tokens", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -119,6 +121,17 @@ def main() -> int:
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * 1000 * 1000
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(20):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 20}), flush=True)
+        return 0
 
     import mxfp4_expert_matmul_k3moe_amd as k3
     from k3gen import device as gdev

@@ -326,20 +326,22 @@ __global__ __launch_bounds__(512) void down_decode_kernel(DownT1Args a) {
       }
     }
   };
-  // chunks ch, ch + G, ch + 2G, ... alternate between two register buffers and two LDS
-  // slots; one barrier per chunk separates a slot's writes from its next reuse
-  const int G = gridDim.x;
-  int ch = blockIdx.x;
-  if (ch < nchunk) load(ch, w0, s0);
+  // block b owns the contiguous chunk range [c0, c1) (consecutive rows of every selected
+  // expert); chunks alternate between two register buffers and two LDS slots, and one
+  // barrier per chunk separates a slot's writes from its next reuse
+  const int per = (nchunk + gridDim.x - 1) / gridDim.x;
+  const int c0 = blockIdx.x * per, c1 = min(nchunk, c0 + per);
+  int ch = c0;
+  if (ch < c1) load(ch, w0, s0);
   __syncthreads();
-  while (ch < nchunk) {
-    if (ch + G < nchunk) load(ch + G, w1, s1);
+  while (ch < c1) {
+    if (ch + 1 < c1) load(ch + 1, w1, s1);
     compute(ch, w0, s0, zs[0]);
-    ch += G;
-    if (ch >= nchunk) break;
-    if (ch + G < nchunk) load(ch + G, w0, s0);
+    ++ch;
+    if (ch >= c1) break;
+    if (ch + 1 < c1) load(ch + 1, w0, s0);
     compute(ch, w1, s1, zs[1]);
-    ch += G;
+    ++ch;
   }
 }
 
@@ -534,8 +536,8 @@ hipError_t launch_down_decode(int d, int f, int k, const MxPtrs& w, const float*
   const int lpr = lanes_per_row(NB);
   const int threads = ((k * lpr + 63) / 64) * 64;
   const int nchunk = (d + kDecRows - 1) / kDecRows;
-  int grid = 2 * n_cu;
-  if (grid > nchunk) grid = nchunk;
+  const int per = (nchunk + 2 * n_cu - 1) / (2 * n_cu);  // chunks per block
+  const int grid = (nchunk + per - 1) / per;
   switch (bpl_of(NB)) {
     case 1: down_decode_kernel<1><<<grid, threads, 0, s>>>(a); break;
     case 2: down_decode_kernel<2><<<grid, threads, 0, s>>>(a); break;

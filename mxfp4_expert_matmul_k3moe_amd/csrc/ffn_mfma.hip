@@ -11,8 +11,10 @@
 // owns block g and feeds its 32 elements to four MFMAs, 8 per MFMA; the activation
 // operand uses the same permutation of k, which leaves every dot product unchanged.
 //
-// Gate/up: h = silu(G x) * (U x), written as bf16 (the MFMA A operand of the down GEMM).
-// Down: z = D h, fp32, one row per (token, slot) pair, combined later in slot order.
+// Gate/up: h = silu(G x) * (U x), written as a pair of bf16 arrays h_hi = bf16(h),
+// h_lo = bf16(h - h_hi), which together carry h to about 2^-16 relative.
+// Down: z = D h_hi + D h_lo (two MFMAs per step on the same decoded B operand), fp32,
+// one row per (token, slot) pair, combined later in slot order.
 // Source of the form: "Kimi K3 纯 C 语言 CPU 推理实战" (chenxutan.com/d/5901.html) §1.2, §2.3.
 #include "k3moe_device.h"
 #include "k3moe_launch.h"
@@ -52,11 +54,13 @@ __device__ __forceinline__ void decode_b(const u32x4 q, float sc, bf16x8 out[4])
 
 struct MfmaArgs {
   int T, d, f, k;
-  const uint16_t* a_src;  // gate/up: x [T][d]; down: h [P][f]
+  const uint16_t* a_src;  // gate/up: x [T][d]; down: h_hi [P][f]
+  const uint16_t* a_lo;   // down: h_lo [P][f]
   const uint8_t *q0, *s0, *q1, *s1;  // gate/up: G and U; down: D (q1 unused)
   const int32_t *offsets, *rows, *act, *n_act, *mtile_off;
   int nblk_n;
-  uint16_t* h_out;  // gate/up output
+  uint16_t* h_out;  // gate/up output: h_hi
+  uint16_t* h_lo;   // gate/up output: h_lo
   float* z_out;     // down output
 };
 
@@ -64,7 +68,8 @@ struct MfmaArgs {
 // DOWN:   N slice = 256 rows i (each wave 64 i, as 4 tiles).
 template <bool GATEUP>
 __global__ __launch_bounds__(256) void mfma_ffn_kernel(MfmaArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * APITCH];
+  constexpr int NA = GATEUP ? 1 : 2;  // activation tiles per stage: x, or h_hi and h_lo
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][NA][BM * APITCH];
   const int n_act = *a.n_act;
   const int mt_glob = blockIdx.x / a.nblk_n;
   const int nb = blockIdx.x - mt_glob * a.nblk_n;
@@ -84,13 +89,16 @@ __global__ __launch_bounds__(256) void mfma_ffn_kernel(MfmaArgs a) {
 
   // staging assignment: 4 threads per tile row, 32 k (64 bytes) each
   const int sr = tid >> 2, sq = tid & 3;
-  const uint16_t* srow = nullptr;
+  const uint16_t* srow[NA];
+#pragma unroll
+  for (int v = 0; v < NA; ++v) srow[v] = nullptr;
   if (sr < pn) {
     if (GATEUP) {
       const int pair = a.rows[p0 + sr];
-      if (pair >= 0 && pair < P) srow = a.a_src + (size_t)(pair / a.k) * a.d;
+      if (pair >= 0 && pair < P) srow[0] = a.a_src + (size_t)(pair / a.k) * a.d;
     } else {
-      srow = a.a_src + (size_t)(p0 + sr) * a.f;
+      srow[0] = a.a_src + (size_t)(p0 + sr) * a.f;
+      srow[NA - 1] = a.a_lo + (size_t)(p0 + sr) * a.f;
     }
   }
 
@@ -126,19 +134,25 @@ __global__ __launch_bounds__(256) void mfma_ffn_kernel(MfmaArgs a) {
     for (int nt = 0; nt < NT; ++nt) acc[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = (K + BK - 1) / BK;
-  u32x4 stg[4];
+  u32x4 stg[NA][4];
   auto load_a = [&](int ks) {
     const int k0 = ks * BK + sq * 32;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const bool ok = srow != nullptr && (k0 + 8 * c) < K;
-      stg[c] = ok ? *reinterpret_cast<const u32x4*>(srow + k0 + 8 * c) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int v = 0; v < NA; ++v)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bool ok = srow[v] != nullptr && (k0 + 8 * c) < K;
+        stg[v][c] = ok ? *reinterpret_cast<const u32x4*>(srow[v] + k0 + 8 * c)
+                       : u32x4{0u, 0u, 0u, 0u};
+      }
   };
   auto store_a = [&](int buf) {
-    uint16_t* dst = &As[buf][sr * APITCH + sq * 32];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(dst + 8 * c) = stg[c];
+    for (int v = 0; v < NA; ++v) {
+      uint16_t* dst = &As[buf][v][sr * APITCH + sq * 32];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(dst + 8 * c) = stg[v][c];
+    }
   };
   u32x4 bq[NT];
   uint32_t bs[NT];
@@ -167,15 +181,19 @@ __global__ __launch_bounds__(256) void mfma_ffn_kernel(MfmaArgs a) {
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const uint16_t* arow = &As[buf][(16 * m + ln) * APITCH + 32 * g];
-      bf16x8 aop[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) aop[i] = *reinterpret_cast<const bf16x8*>(arow + 8 * i);
+      for (int v = 0; v < NA; ++v) {
+        const uint16_t* arow = &As[buf][v][(16 * m + ln) * APITCH + 32 * g];
+        bf16x8 aop[4];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+        for (int i = 0; i < 4; ++i) aop[i] = *reinterpret_cast<const bf16x8*>(arow + 8 * i);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[m][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[i], bop[nt][i], acc[m][nt], 0, 0, 0);
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[m][nt] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[i], bop[nt][i], acc[m][nt], 0, 0, 0);
+      }
     }
     if (ks + 1 < nk) {
       store_a(buf ^ 1);
@@ -196,7 +214,10 @@ __global__ __launch_bounds__(256) void mfma_ffn_kernel(MfmaArgs a) {
           const int j = nb * 128 + wave * 32 + nt * 16 + ln;
           if (j < a.f) {
             const float hv = silu_f32(acc[m][nt][r]) * acc[m][nt + 2][r];
-            a.h_out[(size_t)(p0 + row) * a.f + j] = f32_to_bf16_rne(hv);
+            const uint16_t hi = f32_to_bf16_rne(hv);
+            const size_t o = (size_t)(p0 + row) * a.f + j;
+            a.h_out[o] = hi;
+            a.h_lo[o] = f32_to_bf16_rne(hv - bf16_bits_to_f32(hi));
           }
         }
       } else {
@@ -232,6 +253,7 @@ hipError_t launch_gateup_mfma(int T, int d, int f, int E, int k, const uint16_t*
   a.offsets = offsets; a.rows = rows; a.act = act; a.n_act = n_act; a.mtile_off = mtile_off;
   a.nblk_n = (f + 127) / 128;
   a.h_out = h;
+  a.h_lo = h + (size_t)T * k * f;
   dim3 grid((unsigned)(mfma_mtiles_bound(T, E, k) * a.nblk_n));
   mfma_ffn_kernel<true><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
@@ -243,6 +265,7 @@ hipError_t launch_down_mfma(int T, int d, int f, int E, int k, const MxPtrs& w,
                             float* z, hipStream_t s) {
   MfmaArgs a{};
   a.T = T; a.d = d; a.f = f; a.k = k; a.a_src = h;
+  a.a_lo = h + (size_t)T * k * f;
   a.q0 = w.down_q; a.s0 = w.down_s;
   a.offsets = offsets; a.rows = rows; a.act = act; a.n_act = n_act; a.mtile_off = mtile_off;
   a.nblk_n = (d + 255) / 256;

@@ -73,12 +73,13 @@ hipError_t launch_combine(int T, int d, int k, const float* z, const float* gate
 // Upper bound on the number of M tiles over all active experts.
 int mfma_mtiles_bound(int T, int E, int k);
 bool mfma_shape_supported(int d, int f);
-// h (bf16 [P][f], bucket order) = silu(G x) * (U x) for every (expert, token) pair.
+// h = silu(G x) * (U x) for every (expert, token) pair, bucket order, as two bf16 arrays
+// h[0 .. P*f) = bf16(h) and h[P*f .. 2*P*f) = bf16(h - bf16(h)).
 hipError_t launch_gateup_mfma(int T, int d, int f, int E, int k, const uint16_t* x,
                               const MxPtrs& w, const int32_t* offsets, const int32_t* rows,
                               const int32_t* act, const int32_t* n_act,
                               const int32_t* mtile_off, uint16_t* h, hipStream_t s);
-// z (fp32 [P][d], pair-indexed) = D h.
+// z (fp32 [P][d], pair-indexed) = D h, from both halves of h.
 hipError_t launch_down_mfma(int T, int d, int f, int E, int k, const MxPtrs& w,
                             const uint16_t* h, const int32_t* offsets, const int32_t* rows,
                             const int32_t* act, const int32_t* n_act, const int32_t* mtile_off,

@@ -240,6 +240,7 @@ __device__ __forceinline__ bool better(uint64_t ka, int ia, uint64_t kb, int ib)
 constexpr int kMaxE = 4096;
 constexpr int kMaxSlots = 32;
 constexpr int kMaxChunks = 32;  // d <= 16384 in 512-row chunks
+constexpr int kMaxCand = 2048;  // candidate buffer; the exact ranking covers any count
 
 // One block (256 threads) per token.
 //  1. logits = sum of the fp64 partials in chunk order (+ bias), kept as order keys in LDS;
@@ -262,7 +263,10 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
                                                          int32_t* __restrict__ ids,
                                                          float* __restrict__ gates, Bucket1 bk) {
   __shared__ uint64_t keys[kMaxE];
-  __shared__ int cid[kMaxE];
+  __shared__ uint64_t ckey[kMaxCand];
+  __shared__ int cid[kMaxCand];
+  __shared__ uint64_t lm_key[64];
+  __shared__ int lm_id[64];
   __shared__ double red[256];
   __shared__ double s_max;
   __shared__ int s_total, s_nan, s_ids[kMaxSlots];
@@ -295,11 +299,19 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
       const uint64_t kv = keys[e];
       if (bi < 0 || better(kv, e, bkey, bi)) { bkey = kv; bi = e; }
     }
+    lm_key[lane] = bkey;
+    lm_id[lane] = bi;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // rank of this lane's maximum among the 64 lane maxima (broadcast LDS reads)
+    const uint64_t bkey = lm_key[lane];
+    const int bi = lm_id[lane];
     int rank = 0;
+#pragma unroll 8
     for (int j = 0; j < 64; ++j) {
-      const uint64_t ok = __shfl(bkey, j, 64);
-      const int oi = __shfl(bi, j, 64);
-      if (oi >= 0 && bi >= 0 && better(ok, oi, bkey, bi)) ++rank;
+      const int oi = lm_id[j];
+      rank += (oi >= 0 && bi >= 0 && better(lm_key[j], oi, bkey, bi)) ? 1 : 0;
     }
     if (bi >= 0 && rank == 0) s_max = key_to_double(bkey);
     const int kk = min(k, min(E, 64));
@@ -320,7 +332,13 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
     if (lane == 63) s_total = pre;
     pre -= mine;
     for (int e = lane; e < E; e += 64)
-      if (!better(tk, ti, keys[e], e)) cid[pre++] = e;
+      if (!better(tk, ti, keys[e], e)) {
+        if (pre < kMaxCand) {
+          cid[pre] = e;
+          ckey[pre] = keys[e];
+        }
+        ++pre;
+      }
   }
   // softmax denominator over all experts (NaN-free max = top logit)
   const double m = s_max;
@@ -334,18 +352,33 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
   }
   const double sum = s_nan ? __builtin_nan("") : red[0];
   const int total = s_total;
-  for (int c = tid; c < total; c += 256) {
-    const int id = cid[c];
-    const uint64_t kv = keys[id];
-    int r = 0;
-    for (int j = 0; j < total; ++j) {
-      const int oj = cid[j];
-      r += better(keys[oj], oj, kv, id) ? 1 : 0;
+  if (total <= kMaxCand) {
+    for (int c = tid; c < total; c += 256) {
+      const int id = cid[c];
+      const uint64_t kv = ckey[c];
+      int r = 0;
+#pragma unroll 8
+      for (int j = 0; j < total; ++j) r += better(ckey[j], cid[j], kv, id) ? 1 : 0;
+      if (r < k) {
+        ids[(size_t)t * k + r] = id;
+        gates[(size_t)t * k + r] = (float)(exp(key_to_double(kv) - m) / sum);
+        if (bk.offsets) s_ids[r] = id;
+      }
     }
-    if (r < k) {
-      ids[(size_t)t * k + r] = id;
-      gates[(size_t)t * k + r] = (float)(exp(key_to_double(kv) - m) / sum);
-      if (bk.offsets) s_ids[r] = id;
+  } else {
+    // very many exact ties: rank every candidate against all logits
+    const uint64_t tk = s_tk;
+    const int ti = s_ti;
+    for (int e = tid; e < E; e += 256) {
+      const uint64_t kv = keys[e];
+      if (better(tk, ti, kv, e)) continue;
+      int r = 0;
+      for (int j = 0; j < E; ++j) r += better(keys[j], j, kv, e) ? 1 : 0;
+      if (r < k) {
+        ids[(size_t)t * k + r] = e;
+        gates[(size_t)t * k + r] = (float)(exp(key_to_double(kv) - m) / sum);
+        if (bk.offsets) s_ids[r] = e;
+      }
     }
   }
   if (!bk.offsets) return;
