@@ -247,15 +247,17 @@ __global__ __launch_bounds__(256) void gateup_decode_kernel(GateUpDecodeArgs a) 
   }
 }
 
-// ---- down, T == 1: all slots, persistent over 4-row chunks, ordered combine -----------------
-// Lane group q owns slot q and keeps that slot's h row slice in registers for the whole
-// kernel. A block walks 4-row chunks of the output with the grid stride; the k partial
-// results of a row meet in LDS and one thread adds them in slot order.
-constexpr int kDecRows = 4;
+// ---- down, T == 1: all slots of the token, ordered combine ---------------------------------
+// Lane group q (lpr lanes) owns slot q and keeps that slot's slice of h in registers. A
+// block owns `rpb` consecutive output rows: it walks them R rows at a time (all R*BPL
+// loads of a step issued together), parks each row's k partial results in LDS, and after
+// one barrier adds them per row in slot order. No barrier and no global store sits inside
+// the row loop, so loads of consecutive steps overlap across the block's waves.
+constexpr int kDecMaxRows = 64;  // rows per block (LDS holds k x rpb partials)
 
-template <int BPL>
+template <int BPL, int R>
 __global__ __launch_bounds__(512) void down_decode_kernel(DownT1Args a) {
-  __shared__ float zs[2][kMaxSlots][kDecRows];
+  __shared__ float zs[kMaxSlots][kDecMaxRows];
   __shared__ float gsh[kMaxSlots];
   const int d = a.d, f = a.f, k = a.k;
   const int NB = f >> 5;
@@ -266,6 +268,9 @@ __global__ __launch_bounds__(512) void down_decode_kernel(DownT1Args a) {
   const int pos = (q < k) ? a.pair_pos[q] : -1;
   const int e = (q < k) ? a.pair_exp[q] : -1;
   const bool sv = pos >= 0 && e >= 0;
+  // loads are unconditional (clamped to valid addresses) and masked afterwards, so the
+  // compiler can keep many of them in flight
+  const float hmask = sv ? 1.0f : 0.0f;
   float hv[BPL][32];
 #pragma unroll
   for (int i = 0; i < BPL; ++i) {
@@ -273,75 +278,50 @@ __global__ __launch_bounds__(512) void down_decode_kernel(DownT1Args a) {
     const f32x4* src = reinterpret_cast<const f32x4*>(a.h + (size_t)(sv ? pos : 0) * f + cb * 32);
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
-      const f32x4 t = sv ? src[v] : f32x4{0.f, 0.f, 0.f, 0.f};
-      hv[i][4 * v + 0] = t[0];
-      hv[i][4 * v + 1] = t[1];
-      hv[i][4 * v + 2] = t[2];
-      hv[i][4 * v + 3] = t[3];
+      const f32x4 t = src[v];
+      hv[i][4 * v + 0] = t[0] * hmask;
+      hv[i][4 * v + 1] = t[1] * hmask;
+      hv[i][4 * v + 2] = t[2] * hmask;
+      hv[i][4 * v + 3] = t[3] * hmask;
     }
   }
   const size_t rq = (size_t)(f >> 1), rs = (size_t)NB;
   const uint8_t* dq = a.dq + (size_t)(sv ? e : 0) * d * rq;
   const uint8_t* dsc = a.ds + (size_t)(sv ? e : 0) * d * rs;
-  const int nchunk = (d + kDecRows - 1) / kDecRows;
-  u32x4 w0[kDecRows][BPL], w1[kDecRows][BPL];
-  uint32_t s0[kDecRows][BPL], s1[kDecRows][BPL];
-  auto load = [&](int ch, u32x4 (&w)[kDecRows][BPL], uint32_t (&sc)[kDecRows][BPL]) {
+  const int r0 = blockIdx.x * a.rc;
+  const int r1 = min(d, r0 + a.rc);
+  for (int rb = r0; rb < r1; rb += R) {
+    u32x4 w[R][BPL];
+    uint32_t sc[R][BPL];
 #pragma unroll
-    for (int u = 0; u < kDecRows; ++u) {
-      const int r = ch * kDecRows + u;
+    for (int u = 0; u < R; ++u) {
+      const int r = min(rb + u, r1 - 1);
 #pragma unroll
       for (int i = 0; i < BPL; ++i) {
         const int cb = sub + lpr * i;
-        if (sv && r < d) {
-          w[u][i] = load_u32x4_nt(dq + (size_t)r * rq + (size_t)cb * 16);
-          sc[u][i] = dsc[(size_t)r * rs + cb];
-        }
+        w[u][i] = load_u32x4_nt(dq + (size_t)r * rq + (size_t)cb * 16);
+        sc[u][i] = dsc[(size_t)r * rs + cb];
       }
     }
-  };
-  auto compute = [&](int ch, const u32x4 (&w)[kDecRows][BPL],
-                     const uint32_t (&sc)[kDecRows][BPL], float (&z)[kMaxSlots][kDecRows]) {
 #pragma unroll
-    for (int u = 0; u < kDecRows; ++u) {
+    for (int u = 0; u < R; ++u) {
+      const int r = rb + u;
       float p = 0.0f;
-      const int r = ch * kDecRows + u;
-      if (sv && r < d) {
 #pragma unroll
-        for (int i = 0; i < BPL; ++i) p = fmaf(e8m0_to_f32(sc[u][i]), block_dot_f32(w[u][i], hv[i]), p);
-      }
+      for (int i = 0; i < BPL; ++i) p = fmaf(e8m0_to_f32(sc[u][i]), block_dot_f32(w[u][i], hv[i]), p);
       const float zz = group_sum_rt(p, lpr);
-      if (q < k && sub == 0) z[q][u] = sv ? zz : 0.0f;
+      if (q < k && sub == 0 && r < r1) zs[q][r - r0] = sv ? zz : 0.0f;
     }
-    __syncthreads();
-    if (tid < kDecRows) {
-      const int r = ch * kDecRows + tid;
-      if (r < d) {
-        float acc = 0.0f;
-        for (int s2 = 0; s2 < k; ++s2) acc = fmaf(gsh[s2], z[s2][tid], acc);
-        float out = acc;
-        if (a.resid) out = (a.resid[r] + (a.shared ? a.shared[r] : 0.0f)) + acc;
-        a.y[r] = out;
-        if (a.y_bf16) a.y_bf16[r] = f32_to_bf16_rne(out);
-      }
-    }
-  };
-  // block b owns the contiguous chunk range [c0, c1) (consecutive rows of every selected
-  // expert); chunks alternate between two register buffers and two LDS slots, and one
-  // barrier per chunk separates a slot's writes from its next reuse
-  const int per = (nchunk + gridDim.x - 1) / gridDim.x;
-  const int c0 = blockIdx.x * per, c1 = min(nchunk, c0 + per);
-  int ch = c0;
-  if (ch < c1) load(ch, w0, s0);
+  }
   __syncthreads();
-  while (ch < c1) {
-    if (ch + 1 < c1) load(ch + 1, w1, s1);
-    compute(ch, w0, s0, zs[0]);
-    ++ch;
-    if (ch >= c1) break;
-    if (ch + 1 < c1) load(ch + 1, w0, s0);
-    compute(ch, w1, s1, zs[1]);
-    ++ch;
+  for (int rl = tid; rl < r1 - r0; rl += blockDim.x) {
+    const int r = r0 + rl;
+    float acc = 0.0f;
+    for (int s2 = 0; s2 < k; ++s2) acc = fmaf(gsh[s2], zs[s2][rl], acc);
+    float out = acc;
+    if (a.resid) out = (a.resid[r] + (a.shared ? a.shared[r] : 0.0f)) + acc;
+    a.y[r] = out;
+    if (a.y_bf16) a.y_bf16[r] = f32_to_bf16_rne(out);
   }
 }
 
@@ -493,7 +473,7 @@ hipError_t launch_gateup_gemv(int T, int d, int f, int E, int k, const void* x, 
 
 hipError_t launch_gateup_decode(int d, int f, int k, const void* x, int xf32, const MxPtrs& w,
                                 const int32_t* offsets, const int32_t* act, const int32_t* n_act,
-                                float* h, int n_cu, hipStream_t s) {
+                                float* h, int n_cu, hipStream_t s, int blocks_per_cu) {
   GateUpDecodeArgs a;
   a.d = d; a.f = f; a.x = x;
   a.gq = w.gate_q; a.gs = w.gate_s; a.uq = w.up_q; a.us = w.up_s;
@@ -503,7 +483,7 @@ hipError_t launch_gateup_decode(int d, int f, int k, const void* x, int xf32, co
   const int rgpe = (f + rpw - 1) / rpw;
   const int waves = k * rgpe;  // upper bound of row groups
   int grid = (waves + kGateUpWaves - 1) / kGateUpWaves;
-  const int cap = 2 * n_cu;
+  const int cap = (blocks_per_cu > 0 ? blocks_per_cu : 2) * n_cu;
   if (grid > cap) grid = cap;
   const size_t lds = (size_t)d * (xf32 ? 4 : 2);
 #define K3_GD(XF, B) gateup_decode_kernel<XF, B><<<grid, 256, lds, s>>>(a)
@@ -527,23 +507,39 @@ hipError_t launch_gateup_decode(int d, int f, int k, const void* x, int xf32, co
 hipError_t launch_down_decode(int d, int f, int k, const MxPtrs& w, const float* h,
                               const int32_t* pair_pos, const int32_t* pair_exp,
                               const float* gates, const float* resid, const float* shared,
-                              float* y, uint16_t* y_bf16, int n_cu, hipStream_t s) {
+                              float* y, uint16_t* y_bf16, int n_cu, hipStream_t s,
+                              int rows_per_block, int rows_per_step) {
   DownT1Args a;
   a.d = d; a.f = f; a.k = k; a.dq = w.down_q; a.ds = w.down_s; a.h = h;
   a.pair_pos = pair_pos; a.pair_exp = pair_exp; a.gates = gates;
-  a.resid = resid; a.shared = shared; a.y = y; a.y_bf16 = y_bf16; a.rc = kDecRows;
+  a.resid = resid; a.shared = shared; a.y = y; a.y_bf16 = y_bf16;
   const int NB = f >> 5;
   const int lpr = lanes_per_row(NB);
   const int threads = ((k * lpr + 63) / 64) * 64;
-  const int nchunk = (d + kDecRows - 1) / kDecRows;
-  const int per = (nchunk + 2 * n_cu - 1) / (2 * n_cu);  // chunks per block
-  const int grid = (nchunk + per - 1) / per;
-  switch (bpl_of(NB)) {
-    case 1: down_decode_kernel<1><<<grid, threads, 0, s>>>(a); break;
-    case 2: down_decode_kernel<2><<<grid, threads, 0, s>>>(a); break;
-    case 3: down_decode_kernel<3><<<grid, threads, 0, s>>>(a); break;
-    default: down_decode_kernel<4><<<grid, threads, 0, s>>>(a); break;
+  int rpb = rows_per_block;
+  if (rpb <= 0) {  // about two blocks per CU
+    rpb = (d + 2 * n_cu - 1) / (2 * n_cu);
+    rpb = (rpb + 3) / 4 * 4;
   }
+  if (rpb > kDecMaxRows) rpb = kDecMaxRows;
+  if (rpb < 1) rpb = 1;
+  a.rc = rpb;
+  const int grid = (d + rpb - 1) / rpb;
+#define K3_DD(B, R) down_decode_kernel<B, R><<<grid, threads, 0, s>>>(a)
+#define K3_DD_R(B)                         \
+  switch (rows_per_step) {                 \
+    case 2: K3_DD(B, 2); break;            \
+    case 8: K3_DD(B, 8); break;            \
+    default: K3_DD(B, 4); break;           \
+  }
+  switch (bpl_of(NB)) {
+    case 1: K3_DD_R(1) break;
+    case 2: K3_DD_R(2) break;
+    case 3: K3_DD_R(3) break;
+    default: K3_DD_R(4) break;
+  }
+#undef K3_DD_R
+#undef K3_DD
   return hipGetLastError();
 }
 

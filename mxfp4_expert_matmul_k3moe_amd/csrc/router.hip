@@ -242,11 +242,15 @@ constexpr int kMaxSlots = 32;
 constexpr int kMaxChunks = 32;  // d <= 16384 in 512-row chunks
 constexpr int kMaxCand = 2048;  // candidate buffer; the exact ranking covers any count
 
-// One block (256 threads) per token.
-//  1. logits = sum of the fp64 partials in chunk order (+ bias), kept as order keys in LDS;
-//  2. wave 0: the k-th best of the 64 lane maxima bounds the k-th best logit from below,
-//     so every top-k element ranks at or above it; those candidates are ranked exactly;
-//  3. all waves: softmax denominator (per-thread ordered sums, fixed tree); gates.
+// One block (256 threads) per token; thread t holds the logits of experts t + 256*j
+// (j < KPT) in registers.
+//  1. logits = sum of the fp64 partials in chunk order (+ bias), as order keys;
+//  2. each wave ranks its 64 lane maxima (readlane broadcasts): the k-th best of them is
+//     at most the k-th best of all E, so the best such bound over the waves is a valid
+//     threshold, and every top-k element ranks at or above it;
+//  3. candidates at or above the threshold are compacted into LDS (wave scans) and ranked
+//     exactly against each other; the softmax denominator is a per-thread ordered sum and
+//     a fixed reduction tree.
 // With `bk` (T == 1) the same block also writes the expert bucket of the single token.
 struct Bucket1 {
   int32_t *offsets, *rows, *act, *n_act, *pair_pos, *pair_exp, *mtile_off;
@@ -257,6 +261,13 @@ __device__ __forceinline__ double key_to_double(uint64_t kv) {
   return __longlong_as_double((long long)b);
 }
 
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+template <int KPT>
 __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
                                                          const double* __restrict__ part,
                                                          int nsum, const float* __restrict__ bias,
@@ -265,93 +276,125 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
   __shared__ uint64_t keys[kMaxE];
   __shared__ uint64_t ckey[kMaxCand];
   __shared__ int cid[kMaxCand];
-  __shared__ uint64_t lm_key[64];
-  __shared__ int lm_id[64];
-  __shared__ double red[256];
-  __shared__ double s_max;
-  __shared__ int s_total, s_nan, s_ids[kMaxSlots];
-  __shared__ uint64_t s_tk;
-  __shared__ int s_ti;
+  __shared__ uint64_t w_tk[4], w_mk[4];
+  __shared__ int w_ti[4], w_ok[4], w_cnt[4], w_nan[4];
+  __shared__ double w_sum[4];
+  __shared__ int s_ids[kMaxSlots];
   const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) s_nan = 0;
-  __syncthreads();
+
+  // 1. logits: all loads of a chunk issued before any add; chunks summed in order
+  double acc[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) acc[j] = 0.0;
+  for (int c = 0; c < nsum; ++c) {
+    double v[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int e = tid + 256 * j;
+      v[j] = (e < E) ? part[((size_t)c * T + t) * E + e] : 0.0;
+    }
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) acc[j] = (c == 0) ? v[j] : acc[j] + v[j];
+  }
+  uint64_t key[KPT];
   int nan_here = 0;
-  for (int e = tid; e < E; e += 256) {
-    double v[kMaxChunks];
+  uint64_t bkey = 0;
+  int bi = -1;
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c)
-      v[c] = (c < nsum) ? part[((size_t)c * T + t) * E + e] : 0.0;
-    double s = v[0];
-#pragma unroll
-    for (int c = 1; c < kMaxChunks; ++c)
-      if (c < nsum) s += v[c];
-    if (bias) s += (double)bias[e];
-    nan_here |= (s != s);
-    keys[e] = order_key(s);
-  }
-  if (nan_here) s_nan = 1;
-  __syncthreads();
-  if (wave == 0) {
-    uint64_t bkey = 0;
-    int bi = -1;
-    for (int e = lane; e < E; e += 64) {
-      const uint64_t kv = keys[e];
-      if (bi < 0 || better(kv, e, bkey, bi)) { bkey = kv; bi = e; }
+  for (int j = 0; j < KPT; ++j) {
+    const int e = tid + 256 * j;
+    if (e < E) {
+      const double l = bias ? acc[j] + (double)bias[e] : acc[j];
+      nan_here |= (l != l);
+      key[j] = order_key(l);
+      keys[e] = key[j];
+      if (bi < 0 || better(key[j], e, bkey, bi)) { bkey = key[j]; bi = e; }
+    } else {
+      key[j] = 0;
     }
-    lm_key[lane] = bkey;
-    lm_id[lane] = bi;
   }
-  __syncthreads();
-  if (wave == 0) {
-    // rank of this lane's maximum among the 64 lane maxima (broadcast LDS reads)
-    const uint64_t bkey = lm_key[lane];
-    const int bi = lm_id[lane];
+
+  // 2. per-wave threshold from the 64 lane maxima
+  {
     int rank = 0;
-#pragma unroll 8
-    for (int j = 0; j < 64; ++j) {
-      const int oi = lm_id[j];
-      rank += (oi >= 0 && bi >= 0 && better(lm_key[j], oi, bkey, bi)) ? 1 : 0;
+    for (int l = 0; l < 64; ++l) {
+      const int oi = __builtin_amdgcn_readlane(bi, l);
+      const uint64_t ok = readlane64(bkey, l);
+      rank += (oi >= 0 && bi >= 0 && better(ok, oi, bkey, bi)) ? 1 : 0;
     }
-    if (bi >= 0 && rank == 0) s_max = key_to_double(bkey);
-    const int kk = min(k, min(E, 64));
-    if (bi >= 0 && rank == kk - 1) { s_tk = bkey; s_ti = bi; }
+    const int nvalid = __popcll(__ballot(bi >= 0));
+    if (lane == 0) {
+      w_ok[wave] = nvalid >= k;
+      w_nan[wave] = 0;
+    }
+    if (bi >= 0 && rank == 0) w_mk[wave] = bkey;
+    if (bi >= 0 && rank == k - 1) {
+      w_tk[wave] = bkey;
+      w_ti[wave] = bi;
+    }
+    if (__any(nan_here) && lane == 0) w_nan[wave] = 1;
+    if (nvalid == 0 && lane == 0) w_mk[wave] = 0;
   }
   __syncthreads();
-  if (wave == 0) {
-    const uint64_t tk = s_tk;
-    const int ti = s_ti;
-    int mine = 0;
-    for (int e = lane; e < E; e += 64)
-      if (!better(tk, ti, keys[e], e)) ++mine;
-    int pre = mine;
-    for (int off = 1; off < 64; off <<= 1) {
-      const int v = __shfl_up(pre, off, 64);
-      if (lane >= off) pre += v;
+  uint64_t tk = 0, mk = 0;
+  int ti = 0x7FFFFFFF;
+  bool have = false;
+  int anynan = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (w_ok[w] && (!have || better(w_tk[w], w_ti[w], tk, ti))) {
+      tk = w_tk[w];
+      ti = w_ti[w];
+      have = true;
     }
-    if (lane == 63) s_total = pre;
-    pre -= mine;
-    for (int e = lane; e < E; e += 64)
-      if (!better(tk, ti, keys[e], e)) {
-        if (pre < kMaxCand) {
-          cid[pre] = e;
-          ckey[pre] = keys[e];
-        }
-        ++pre;
-      }
+    mk = (w_mk[w] > mk) ? w_mk[w] : mk;
+    anynan |= w_nan[w];
   }
-  // softmax denominator over all experts (NaN-free max = top logit)
-  const double m = s_max;
+  const double m = key_to_double(mk);
+
+  // 3. candidates (wave scan) and softmax denominator
+  int mine = 0;
   double se = 0.0;
-  for (int e = tid; e < E; e += 256) se += exp(key_to_double(keys[e]) - m);
-  red[tid] = se;
-  __syncthreads();
-  for (int off = 128; off >= 1; off >>= 1) {
-    if (tid < off) red[tid] += red[tid + off];
-    __syncthreads();
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int e = tid + 256 * j;
+    if (e < E) {
+      mine += better(tk, ti, key[j], e) ? 0 : 1;
+      se += exp(key_to_double(key[j]) - m);
+    }
   }
-  const double sum = s_nan ? __builtin_nan("") : red[0];
-  const int total = s_total;
+  int pre = mine;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(pre, off, 64);
+    if (lane >= off) pre += v;
+  }
+  for (int off = 32; off >= 1; off >>= 1) se += __shfl_xor(se, off, 64);
+  if (lane == 63) w_cnt[wave] = pre;
+  if (lane == 0) w_sum[wave] = se;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    base += (w < wave) ? w_cnt[w] : 0;
+    total += w_cnt[w];
+  }
+  const double sum = anynan ? __builtin_nan("") : ((w_sum[0] + w_sum[1]) + w_sum[2]) + w_sum[3];
+  pre = base + pre - mine;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int e = tid + 256 * j;
+    if (e < E && !better(tk, ti, key[j], e)) {
+      if (pre < kMaxCand) {
+        cid[pre] = e;
+        ckey[pre] = key[j];
+      }
+      ++pre;
+    }
+  }
+  __syncthreads();
+
+  // 4. exact ranks of the candidates
   if (total <= kMaxCand) {
     for (int c = tid; c < total; c += 256) {
       const int id = cid[c];
@@ -367,8 +410,6 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
     }
   } else {
     // very many exact ties: rank every candidate against all logits
-    const uint64_t tk = s_tk;
-    const int ti = s_ti;
     for (int e = tid; e < E; e += 256) {
       const uint64_t kv = keys[e];
       if (better(tk, ti, kv, e)) continue;
@@ -382,7 +423,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
     }
   }
   if (!bk.offsets) return;
-  // T == 1: bucket of the single token. Ranks of the k ids in ascending id order.
+  // 5. T == 1: bucket of the single token (ranks of the k ids in ascending id order)
   __syncthreads();
   if (tid < k) {
     const int id = s_ids[tid];
@@ -398,9 +439,13 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
     *bk.n_act = k;
     bk.mtile_off[k] = k;
   }
+  int sid[kMaxSlots];
+#pragma unroll
+  for (int j = 0; j < kMaxSlots; ++j) sid[j] = (j < k) ? s_ids[j] : 0x7FFFFFFF;
   for (int e = tid; e <= E; e += 256) {
     int c = 0;
-    for (int j = 0; j < k; ++j) c += (s_ids[j] < e) ? 1 : 0;
+#pragma unroll
+    for (int j = 0; j < kMaxSlots; ++j) c += (sid[j] < e) ? 1 : 0;
     bk.offsets[e] = c;
   }
 }
@@ -450,7 +495,12 @@ hipError_t launch_route_topk(int T, int E, int k, const double* part, int nsum,
     b.n_act = bucket1->n_act; b.pair_pos = bucket1->pair_pos; b.pair_exp = bucket1->pair_exp;
     b.mtile_off = bucket1->mtile_off;
   }
-  route_topk_kernel<<<T, 256, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
+  const int kpt = (E + 255) / 256;
+  if (kpt <= 1) route_topk_kernel<1><<<T, 256, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
+  else if (kpt <= 2) route_topk_kernel<2><<<T, 256, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
+  else if (kpt <= 4) route_topk_kernel<4><<<T, 256, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
+  else if (kpt <= 8) route_topk_kernel<8><<<T, 256, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
+  else route_topk_kernel<16><<<T, 256, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
   return hipGetLastError();
 }
 
