@@ -104,20 +104,19 @@ __global__ __launch_bounds__(256) void router_gemv_vec_kernel(int T, int d, int 
   const bool cv = col0 < E;
   for (int t0 = 0; t0 < T; t0 += NT) {
     const int nt = min(NT, T - t0);
+    // weight loads first (clamped to valid rows/columns, masked below), then the activations
+    u32x4 wv[RPL];
+#pragma unroll
+    for (int u = 0; u < RPL; ++u) {
+      const int r = min(wave * (kRouterRows / 4) + rl + 8 * u, nrows - 1);
+      wv[u] = *reinterpret_cast<const u32x4*>(w + (size_t)(k0 + r) * E + (cv ? col0 : 0));
+    }
     __syncthreads();
     for (int i = threadIdx.x; i < nrows * NT; i += 256) {
       const int r = i / NT, tt = i % NT;
       xs[r][tt] = (tt < nt) ? load_x<XF32>(x, (size_t)(t0 + tt) * d + k0 + r) : 0.0;
     }
     __syncthreads();
-    u32x4 wv[RPL];
-#pragma unroll
-    for (int u = 0; u < RPL; ++u) {
-      const int r = wave * (kRouterRows / 4) + rl + 8 * u;
-      wv[u] = (cv && r < nrows)
-                  ? *reinterpret_cast<const u32x4*>(w + (size_t)(k0 + r) * E + col0)
-                  : u32x4{0u, 0u, 0u, 0u};
-    }
     double acc[NT][8];
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt)
@@ -284,18 +283,25 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   // 1. logits: all loads of a chunk issued before any add; chunks summed in order
+  constexpr int CB = (32 / KPT) > 1 ? (32 / KPT) : 1;  // chunks whose loads go out together
   double acc[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) acc[j] = 0.0;
-  for (int c = 0; c < nsum; ++c) {
-    double v[KPT];
+  for (int c0 = 0; c0 < nsum; c0 += CB) {
+    double v[CB][KPT];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int e = tid + 256 * j;
-      v[j] = (e < E) ? part[((size_t)c * T + t) * E + e] : 0.0;
-    }
+    for (int u = 0; u < CB; ++u)
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) acc[j] = (c == 0) ? v[j] : acc[j] + v[j];
+      for (int j = 0; j < KPT; ++j) {
+        const int e = min(tid + 256 * j, E - 1);
+        const int c = min(c0 + u, nsum - 1);
+        v[u][j] = part[((size_t)c * T + t) * E + e];  // clamped: always a valid address
+      }
+#pragma unroll
+    for (int u = 0; u < CB; ++u)
+#pragma unroll
+      for (int j = 0; j < KPT; ++j)
+        if (c0 + u < nsum) acc[j] = (c0 + u == 0) ? v[u][j] : acc[j] + v[u][j];
   }
   uint64_t key[KPT];
   int nan_here = 0;
