@@ -184,28 +184,6 @@ __global__ __launch_bounds__(256) void gateup_decode_kernel(GateUpDecodeArgs a) 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane & (lpr - 1), rsel = lane / lpr;
   const size_t rq = (size_t)(d >> 1), rs = (size_t)NB;
-  const int rgpe = (f + rpw - 1) / rpw;  // row groups per expert
-  const int total = *a.n_act * rgpe;
-  const int stride = gridDim.x * kGateUpWaves;
-  u32x4 gw[BPL], uw[BPL];
-  uint32_t gsc[BPL], usc[BPL];
-  auto load = [&](int rg) {  // clamped: always valid addresses
-    const int rgc = min(rg, total - 1);
-    const int ai = rgc / rgpe;
-    const int j = min((rgc - ai * rgpe) * rpw + rsel, f - 1);
-    const size_t row = (size_t)a.act[ai] * f + j;
-#pragma unroll
-    for (int i = 0; i < BPL; ++i) {
-      const size_t cb = (size_t)(sub + lpr * i);
-      gw[i] = load_u32x4_nt(a.gq + row * rq + cb * 16);
-      uw[i] = load_u32x4_nt(a.uq + row * rq + cb * 16);
-      gsc[i] = a.gs[row * rs + cb];
-      usc[i] = a.us[row * rs + cb];
-    }
-  };
-  int rg = blockIdx.x * kGateUpWaves + wave;
-  // the first row group's weights are requested before the token is staged
-  if (total > 0) load(rg);
   {
     const u32x4* src = static_cast<const u32x4*>(a.x);
     for (int v = threadIdx.x; v < NB * Q; v += 256) {
@@ -214,7 +192,25 @@ __global__ __launch_bounds__(256) void gateup_decode_kernel(GateUpDecodeArgs a) 
     }
   }
   __syncthreads();
-  for (; rg < total; rg += stride) {
+  const int rgpe = (f + rpw - 1) / rpw;  // row groups per expert
+  const int total = *a.n_act * rgpe;
+  const int stride = gridDim.x * kGateUpWaves;
+  for (int rg = blockIdx.x * kGateUpWaves + wave; rg < total; rg += stride) {
+    const int ai = rg / rgpe;
+    const int j = (rg - ai * rgpe) * rpw + rsel;
+    const int e = a.act[ai];
+    const bool rv = j < f;
+    const size_t row = (size_t)e * f + (rv ? j : 0);
+    u32x4 gw[BPL], uw[BPL];
+    uint32_t gsc[BPL], usc[BPL];
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) {
+      const size_t cb = (size_t)(sub + lpr * i);
+      gw[i] = load_u32x4_nt(a.gq + row * rq + cb * 16);
+      uw[i] = load_u32x4_nt(a.uq + row * rq + cb * 16);
+      gsc[i] = a.gs[row * rs + cb];
+      usc[i] = a.us[row * rs + cb];
+    }
     float gacc = 0.0f, uacc = 0.0f;
 #pragma unroll
     for (int i = 0; i < BPL; ++i) {
@@ -245,13 +241,9 @@ __global__ __launch_bounds__(256) void gateup_decode_kernel(GateUpDecodeArgs a) 
         uacc = fmaf(e8m0_to_f32(usc[i]), block_dot_bf16(uw[i], xp), uacc);
       }
     }
-    const int ai = rg / rgpe;
-    const int j = (rg - ai * rgpe) * rpw + rsel;
-    const int e = a.act[ai];
-    if (rg + stride < total) load(rg + stride);
     const float g = group_sum_rt(gacc, lpr);
     const float u = group_sum_rt(uacc, lpr);
-    if (sub == 0 && j < f) a.h[(size_t)a.offsets[e] * f + j] = silu_f32(g) * u;
+    if (sub == 0 && rv) a.h[(size_t)a.offsets[e] * f + j] = silu_f32(g) * u;
   }
 }
 
@@ -276,27 +268,6 @@ __global__ __launch_bounds__(512) void down_decode_kernel(DownT1Args a) {
   const int pos = (q < k) ? a.pair_pos[q] : -1;
   const int e = (q < k) ? a.pair_exp[q] : -1;
   const bool sv = pos >= 0 && e >= 0;
-  const size_t rq = (size_t)(f >> 1), rs = (size_t)NB;
-  const uint8_t* dq = a.dq + (size_t)(sv ? e : 0) * d * rq;
-  const uint8_t* dsc = a.ds + (size_t)(sv ? e : 0) * d * rs;
-  const int r0 = blockIdx.x * a.rc;
-  const int r1 = min(d, r0 + a.rc);
-  u32x4 w[R][BPL];
-  uint32_t sc[R][BPL];
-  auto load = [&](int rb) {  // clamped to valid rows; results of extra rows are dropped
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-      const int r = min(rb + u, r1 - 1);
-#pragma unroll
-      for (int i = 0; i < BPL; ++i) {
-        const int cb = sub + lpr * i;
-        w[u][i] = load_u32x4_nt(dq + (size_t)r * rq + (size_t)cb * 16);
-        sc[u][i] = dsc[(size_t)r * rs + cb];
-      }
-    }
-  };
-  // the first step's weights are requested before this slot's h
-  if (r0 < r1) load(r0);
   // loads are unconditional (clamped to valid addresses) and masked afterwards, so the
   // compiler can keep many of them in flight
   const float hmask = sv ? 1.0f : 0.0f;
@@ -314,19 +285,31 @@ __global__ __launch_bounds__(512) void down_decode_kernel(DownT1Args a) {
       hv[i][4 * v + 3] = t[3] * hmask;
     }
   }
+  const size_t rq = (size_t)(f >> 1), rs = (size_t)NB;
+  const uint8_t* dq = a.dq + (size_t)(sv ? e : 0) * d * rq;
+  const uint8_t* dsc = a.ds + (size_t)(sv ? e : 0) * d * rs;
+  const int r0 = blockIdx.x * a.rc;
+  const int r1 = min(d, r0 + a.rc);
   for (int rb = r0; rb < r1; rb += R) {
-    float p[R];
+    u32x4 w[R][BPL];
+    uint32_t sc[R][BPL];
 #pragma unroll
     for (int u = 0; u < R; ++u) {
-      p[u] = 0.0f;
+      const int r = min(rb + u, r1 - 1);
 #pragma unroll
-      for (int i = 0; i < BPL; ++i) p[u] = fmaf(e8m0_to_f32(sc[u][i]), block_dot_f32(w[u][i], hv[i]), p[u]);
+      for (int i = 0; i < BPL; ++i) {
+        const int cb = sub + lpr * i;
+        w[u][i] = load_u32x4_nt(dq + (size_t)r * rq + (size_t)cb * 16);
+        sc[u][i] = dsc[(size_t)r * rs + cb];
+      }
     }
-    if (rb + R < r1) load(rb + R);
 #pragma unroll
     for (int u = 0; u < R; ++u) {
       const int r = rb + u;
-      const float zz = group_sum_rt(p[u], lpr);
+      float p = 0.0f;
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) p = fmaf(e8m0_to_f32(sc[u][i]), block_dot_f32(w[u][i], hv[i]), p);
+      const float zz = group_sum_rt(p, lpr);
       if (q < k && sub == 0 && r < r1) zs[q][r - r0] = sv ? zz : 0.0f;
     }
   }

@@ -283,7 +283,10 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   // 1. logits: all loads of a chunk issued before any add; chunks summed in order
-  constexpr int CB = (32 / KPT) > 1 ? (32 / KPT) : 1;  // chunks whose loads go out together
+  constexpr int CB = (64 / KPT) > 1 ? (64 / KPT) : 1;  // chunks whose loads go out together
+  float bv[KPT];  // bias requested together with the first partials
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) bv[j] = bias ? bias[min(tid + 256 * j, E - 1)] : 0.0f;
   double acc[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) acc[j] = 0.0;
@@ -311,7 +314,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
   for (int j = 0; j < KPT; ++j) {
     const int e = tid + 256 * j;
     if (e < E) {
-      const double l = bias ? acc[j] + (double)bias[e] : acc[j];
+      const double l = bias ? acc[j] + (double)bv[j] : acc[j];
       nan_here |= (l != l);
       key[j] = order_key(l);
       keys[e] = key[j];
@@ -445,14 +448,13 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
     *bk.n_act = k;
     bk.mtile_off[k] = k;
   }
-  int sid[kMaxSlots];
-#pragma unroll
-  for (int j = 0; j < kMaxSlots; ++j) sid[j] = (j < k) ? s_ids[j] : 0x7FFFFFFF;
-  for (int e = tid; e <= E; e += 256) {
-    int c = 0;
-#pragma unroll
-    for (int j = 0; j < kMaxSlots; ++j) c += (sid[j] < e) ? 1 : 0;
-    bk.offsets[e] = c;
+  // only the selected experts' offsets are read on the single-token path
+  if (tid < k) {
+    const int id = s_ids[tid];
+    int pos = 0;
+    for (int j = 0; j < k; ++j) pos += (s_ids[j] < id) ? 1 : 0;
+    bk.offsets[id] = pos;
+    bk.offsets[id + 1] = pos + 1;
   }
 }
 
