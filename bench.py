@@ -193,13 +193,19 @@ def main() -> int:
     dn_bytes = sel * w.d * (w.f // 2 + w.f // 32)
     gu_gbs = gu_bytes / (kern["gate_up"] * 1e-3) / 1e9
     dn_gbs = dn_bytes / (kern["down"] * 1e-3) / 1e9
+    # HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE record, used only while
+    # the kernel source it was measured on is unchanged
     traffic = None
-    prof_traffic = os.path.join(ROOT, "profiles", "gateup_decode_traffic.json")
-    if os.path.exists(prof_traffic):
+    prof_traffic = os.path.join(ROOT, "profiles", "gateup_decode_traffic.txt")
+    if args.workload == "decode" and os.path.exists(prof_traffic):
+        tr = {}
         with open(prof_traffic) as fh:
-            tr = json.load(fh)
+            for line in fh:
+                if ":" in line and not line.startswith("#"):
+                    key, val = line.split(":", 1)
+                    tr[key.strip()] = val.strip()
         if tr.get("kernel_source_hash") == _kernel_hash():
-            traffic = tr.get("bytes_per_launch")
+            traffic = int(tr["bytes_per_launch"])
 
     out = {
         "metric": "MoE layer MXFP4 weight-stream GB/s (decode) + TFLOP/s (prefill), % of peak",
@@ -217,7 +223,7 @@ def main() -> int:
         "config": {"workload": f"{w.name}: {workload_desc(w)}",
                    "bytes_per_step": int(round(bytes_timed / args.steps)),
                    "token_sets": nsets},
-        "roofline": {"bound": "hbm", "kernel": "gateup_gemv (MXFP4 gate/up GEMV + SwiGLU)",
+        "roofline": {"bound": "hbm", "kernel": "gateup_decode_kernel (MXFP4 gate/up GEMV + SwiGLU)",
                      "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": int(gu_bytes), "avg_launch_us": round(kern["gate_up"] * 1e3, 2)},
