@@ -143,7 +143,8 @@ def main() -> int:
     ex = k3.MxExperts(**gdev.experts(w, 0, dev))
     wr = gdev.router_w(w, 0, dev)
     bias = gdev.bias(w, 0, dev)
-    nsets = max(1, args.token_sets)
+    # fresh tokens every step; prefill steps read most experts anyway, so fewer sets suffice
+    nsets = max(1, args.token_sets if w.T <= 64 else min(args.token_sets, 4))
     xs = torch.stack([gdev.x_bf16(w, token_set=i, device=dev) for i in range(nsets)])
     ws = k3.make_workspace(dims, w.T, dev)
     y = torch.empty((w.T, w.d), dtype=torch.float32, device=dev)
@@ -168,13 +169,15 @@ def main() -> int:
 
     ids_np = ids.cpu().numpy()
     router_bytes = w.d * w.E * 2
-    per_set = [expert_bytes_per_step(w, ids_np[s]) + router_bytes for s in range(nsets)]
-    bytes_timed = sum(per_set[(args.warmup + i) % nsets] for i in range(args.steps))
-    value = bytes_timed / (t1 - t0) / 1e9
+    uniq = [len(np.unique(ids_np[s2])) for s2 in range(nsets)]
+    step_sets = [(args.warmup + i) % nsets for i in range(args.steps)]
+    bytes_timed = sum(uniq[s2] * w.expert_bytes + router_bytes for s2 in step_sets)
+    pairs = w.T * w.k
+    flops_step = 6.0 * w.d * w.f * pairs  # useful SwiGLU expert flops (router excluded)
 
-    # dominant kernel: MXFP4 gate/up GEMV, HIP events around its own launch
+    # dominant kernels timed live: HIP events around their own launches
     hip = Hip()
-    nprobe = min(args.steps, 100)
+    nprobe = min(args.steps, 100 if w.T <= 64 else 20)
     kern = {}
     for which, name in ((k3.KERNEL_GATE_UP, "gate_up"), (k3.KERNEL_DOWN, "down")):
         evs = [(hip.event(), hip.event()) for _ in range(nprobe)]
@@ -187,12 +190,11 @@ def main() -> int:
             hip.destroy(a)
             hip.destroy(b)
         kern[name] = sum(times) / len(times)
-    # algorithmic bytes per launch: gate+up rows of the distinct selected experts
-    sel = np.mean([len(np.unique(ids_np[(args.warmup + i) % nsets])) for i in range(nprobe)])
+    sel = float(np.mean([uniq[(args.warmup + i) % nsets] for i in range(nprobe)]))
     gu_bytes = sel * 2 * w.f * (w.d // 2 + w.d // 32)
     dn_bytes = sel * w.d * (w.f // 2 + w.f // 32)
-    gu_gbs = gu_bytes / (kern["gate_up"] * 1e-3) / 1e9
-    dn_gbs = dn_bytes / (kern["down"] * 1e-3) / 1e9
+    gu_s, dn_s = kern["gate_up"] * 1e-3, kern["down"] * 1e-3
+
     # HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE record, used only while
     # the kernel source it was measured on is unchanged
     traffic = None
@@ -207,10 +209,38 @@ def main() -> int:
         if tr.get("kernel_source_hash") == _kernel_hash():
             traffic = int(tr["bytes_per_launch"])
 
+    if w.T <= 64:  # decode-like: weight stream
+        value, unit = bytes_timed / (t1 - t0) / 1e9, "GB/s"
+        ach = gu_bytes / gu_s / 1e9
+        roof = {"bound": "hbm", "kernel": "gateup_decode_kernel (MXFP4 gate/up GEMV + SwiGLU)"
+                if w.T == 1 else "gateup_gemv_kernel (MXFP4 gate/up GEMV + SwiGLU)",
+                "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "bytes_per_launch": int(gu_bytes), "avg_launch_us": round(kern["gate_up"] * 1e3, 2)}
+        extra = {"down_us": round(kern["down"] * 1e3, 2),
+                 "down_GBps": round(dn_bytes / dn_s / 1e9, 1),
+                 "layer_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+                 "distinct_experts_per_step": round(float(np.mean(uniq)), 1)}
+    else:  # prefill: grouped GEMM
+        value, unit = flops_step * args.steps / (t1 - t0) / 1e12, "TFLOP/s"
+        gu_flops = 4.0 * w.d * w.f * pairs
+        ach = gu_flops / gu_s / 1e12
+        roof = {"bound": "mfma", "kernel": "mfma_ffn_kernel<gate/up> (bf16 MFMA grouped GEMM)",
+                "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                "flops_per_launch": gu_flops, "avg_launch_us": round(kern["gate_up"] * 1e3, 2)}
+        extra = {"down_us": round(kern["down"] * 1e3, 2),
+                 "down_TFLOPs": round(2.0 * w.d * w.f * pairs / dn_s / 1e12, 1),
+                 "layer_frac_of_mfma_peak": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
+                 "weight_GBps": round(bytes_timed / (t1 - t0) / 1e9, 1),
+                 "gateup_weight_GBps": round(gu_bytes / gu_s / 1e9, 1),
+                 "distinct_experts_per_step": round(float(np.mean(uniq)), 1),
+                 "hbm_floor_ms": round(float(np.mean(uniq)) * w.expert_bytes / (HBM_PEAK_GBS * 1e9) * 1e3, 3)}
+
     out = {
         "metric": "MoE layer MXFP4 weight-stream GB/s (decode) + TFLOP/s (prefill), % of peak",
         "value": round(value, 2),
-        "unit": "GB/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -223,14 +253,10 @@ def main() -> int:
         "config": {"workload": f"{w.name}: {workload_desc(w)}",
                    "bytes_per_step": int(round(bytes_timed / args.steps)),
                    "token_sets": nsets},
-        "roofline": {"bound": "hbm", "kernel": "gateup_decode_kernel (MXFP4 gate/up GEMV + SwiGLU)",
-                     "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "bytes_per_launch": int(gu_bytes), "avg_launch_us": round(kern["gate_up"] * 1e3, 2)},
-        "kernels": {"down_us": round(kern["down"] * 1e3, 2), "down_GBps": round(dn_gbs, 1),
-                    "layer_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": roof,
+        "kernels": extra,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and w.T == 1:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
     else:
         out["cpu_baseline"] = None
