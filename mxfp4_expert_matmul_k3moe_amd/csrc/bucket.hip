@@ -88,7 +88,7 @@ __device__ void active_and_tiles(int E, const int v[4], int32_t* act, int32_t* n
   const int e0 = threadIdx.x * 4;
   for (int i = 0; i < 4; ++i) {
     f[i] = (e0 + i < E && v[i] > 0) ? 1 : 0;
-    mt[i] = f[i] ? (v[i] + kMfmaTileM - 1) / kMfmaTileM : 0;
+    mt[i] = f[i] ? mfma_tiles_of(v[i]) : 0;
   }
   int nact, ntiles;
   block_scan4(f, fo, s_wave, &nact);

@@ -1,7 +1,7 @@
 // ffn_mfma.hip — grouped expert GEMMs on bf16 MFMA for many tokens per expert (prefill).
 //
-// Each tile is 64 tokens of one expert (its bucket rows) times a slice of that expert's
-// weight rows. The activation tile (bf16) is staged in LDS; each weight row's 32-element
+// Each tile is up to 64 tokens of one expert (its bucket rows; experts with at most 16 or
+// 32 tokens take a 16- or 32-row tile) times a slice of that expert's weight rows. The activation tile (bf16) is staged in LDS; each weight row's 32-element
 // MXFP4 block is loaded with one 16-byte load per lane and decoded in registers straight
 // into MFMA B operands, the E8M0 scale folded into the gfx950 scaled FP4->bf16
 // conversion (exact: E2M1 values times a power of two fit bf16 for normal scales).
@@ -23,17 +23,36 @@ namespace k3moe {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int BM = kMfmaTileM;  // 64 tokens per tile
-constexpr int BK = 128;         // K per step (4 MXFP4 blocks)
-constexpr int APITCH = BK + 8;  // bf16 per LDS row: 272 B, rows land on distinct banks
-constexpr int kWaves = 4;
+constexpr int BM = kMfmaTileM;     // 64 tokens per full tile
+constexpr int BK = 128;            // K per step (4 MXFP4 blocks per weight row)
+constexpr int kWaves = 8;          // 512 threads: two waves per SIMD, one block per CU
+constexpr int NT = 4;              // 16-wide N tiles per wave
+constexpr int kLdsBytes = 160 * 1024;
+constexpr int kBStage = kWaves * NT * 1024;  // weight blocks of one step: 16 B per lane per tile
+constexpr int kSStage = kWaves * 256;        // scale words of one step: 4 B per lane
 
-__device__ __forceinline__ int tile_expert(const int32_t* mtile_off, int n_act, int mt) {
+// One stage of the pipeline in LDS: [A: NA x MT x 4 KB-blocks][B: kBStage][scales: kSStage].
+// Every KB-block is written by one wave-wide 16-byte-per-lane DMA load (lane l lands at
+// byte 16 l) and read back by one wave-wide 16-byte LDS read at the same lane offsets.
+template <bool GATEUP, int MT>
+struct Pipe {
+  static constexpr int NA = GATEUP ? 1 : 2;       // x, or h_hi and h_lo
+  static constexpr int ABLK = NA * MT * 4;         // 1-KB A blocks per stage
+  static constexpr int ABYTES = ABLK * 1024;
+  static constexpr int BYTES = ABYTES + kBStage + kSStage;
+  static constexpr int S = (kLdsBytes / BYTES) < 4 ? (kLdsBytes / BYTES) : 4;  // stages
+  static_assert(S >= 2, "pipeline needs two stages");
+};
+
+// Active expert owning logical block L (blocks of expert a start at mtile_off[a] * nb).
+__device__ __forceinline__ int tile_expert_blocks(const int32_t* mtile_off, int n_act, int nb,
+                                                  int L) {
   int lo = 0, hi = n_act - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (mtile_off[mid] <= mt) lo = mid;
+    if (mtile_off[mid] * nb <= L) lo = mid;
     else hi = mid - 1;
   }
   return lo;
@@ -52,6 +71,34 @@ __device__ __forceinline__ void decode_b(const u32x4 q, float sc, bf16x8 out[4])
   }
 }
 
+// Asynchronous global -> LDS copies: 16 (or 4) bytes per lane, lane l writes dst + 16 l
+// (or dst + 4 l). dst must be the same for the whole wave.
+__device__ __forceinline__ void dma16(const void* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 4, 0, 0);
+}
+
+// Wait until at most N of this wave's vector-memory operations are outstanding. The
+// compiler does not order LDS reads after the DMA writes they depend on, so the pipeline
+// places these waits itself; the memory clobber keeps LDS reads below them.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier without the release fence of __syncthreads (which would wait for
+// every DMA in flight). Each wave first waits for its own DMA of the stage it is about to
+// read (wait_vm); LDS reads of the previous stage have all been consumed by MFMAs before a
+// wave reaches the barrier. The empty asm statements keep the compiler from moving memory
+// operations across it.
+__device__ __forceinline__ void barrier_no_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 struct MfmaArgs {
   int T, d, f, k;
   const uint16_t* a_src;  // gate/up: x [T][d]; down: h_hi [P][f]
@@ -64,129 +111,165 @@ struct MfmaArgs {
   float* z_out;     // down output
 };
 
-// GATEUP: N slice = 128 rows j (each wave 32 j, as 2 gate + 2 up 16-wide tiles).
-// DOWN:   N slice = 256 rows i (each wave 64 i, as 4 tiles).
+// GATEUP: N slice = 256 rows j (each wave 32 j, as 2 gate + 2 up 16-wide tiles).
+// DOWN:   N slice = 512 rows i (each wave 64 i, as 4 tiles).
+// MT = 16-row M subtiles in the tile (1, 2 or 4: tiles of 16, 32 or 64 tokens).
+template <bool GATEUP, int MT>
+__device__ __forceinline__ void mfma_tile(const MfmaArgs& a, uint8_t* lds, int e, int p0, int pn,
+                                          int nb);
+
+// Block -> work: blocks are spread over the 8 XCDs round-robin by the hardware; logical
+// work index L is laid out so that the blocks one XCD receives are consecutive in L,
+// and L runs expert-major, then N slice, then M tile, so the M tiles of one weight slice
+// run back to back on one XCD and find that slice in its L2.
 template <bool GATEUP>
-__global__ __launch_bounds__(256) void mfma_ffn_kernel(MfmaArgs a) {
-  constexpr int NA = GATEUP ? 1 : 2;  // activation tiles per stage: x, or h_hi and h_lo
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][NA][BM * APITCH];
+__global__ __launch_bounds__(512) void mfma_ffn_kernel(MfmaArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
   const int n_act = *a.n_act;
-  const int mt_glob = blockIdx.x / a.nblk_n;
-  const int nb = blockIdx.x - mt_glob * a.nblk_n;
-  if (n_act <= 0 || mt_glob >= a.mtile_off[n_act]) return;
-  const int ai = tile_expert(a.mtile_off, n_act, mt_glob);
+  if (n_act <= 0) return;
+  const int N = a.mtile_off[n_act] * a.nblk_n;  // blocks with work
+  const int b = blockIdx.x;
+  if (b >= N) return;
+  const int x = b & 7, slot = b >> 3;
+  int L = slot;
+  for (int x2 = 0; x2 < x; ++x2) L += (N - x2 + 7) >> 3;
+  const int ai = tile_expert_blocks(a.mtile_off, n_act, a.nblk_n, L);
   const int e = a.act[ai];
   const int P = a.T * a.k;
   const int pe0 = min(max(a.offsets[e], 0), P), pe1 = min(max(a.offsets[e + 1], pe0), P);
-  const int p0 = pe0 + (mt_glob - a.mtile_off[ai]) * BM;
+  const int cnt = pe1 - pe0;
+  const int mt_a = a.mtile_off[ai + 1] - a.mtile_off[ai];
+  const int Lr = L - a.mtile_off[ai] * a.nblk_n;
+  const int nb = Lr / mt_a, mloc = Lr - nb * mt_a;
+  const int p0 = pe0 + mloc * BM;
   const int pn = max(0, min(BM, pe1 - p0));
-  const int K = GATEUP ? a.d : a.f;     // contraction length
+  if (pn <= 0) return;
+  if (cnt <= 16) mfma_tile<GATEUP, 1>(a, lds, e, p0, pn, nb);
+  else if (cnt <= 32) mfma_tile<GATEUP, 2>(a, lds, e, p0, pn, nb);
+  else mfma_tile<GATEUP, 4>(a, lds, e, p0, pn, nb);
+}
+
+template <bool GATEUP, int MT>
+__device__ __forceinline__ void mfma_tile(const MfmaArgs& a, uint8_t* lds, int e, int p0, int pn,
+                                          int nb) {
+  using PP = Pipe<GATEUP, MT>;
+  constexpr int NA = PP::NA, S = PP::S, SB = PP::BYTES, AB = PP::ABYTES;
+  const int P = a.T * a.k;
+  const int K = GATEUP ? a.d : a.f;     // contraction length (multiple of BK)
   const int NR = GATEUP ? a.f : a.d;    // weight rows of one matrix
-  const int KB = K >> 5;                // scale blocks per weight row
-  const size_t rq = (size_t)(K >> 1);
+  const int KB = K >> 5;                // scale bytes per weight row
+  const size_t rq = (size_t)(K >> 1);   // nibble bytes per weight row
+  const int nk = K / BK;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 15, g = lane >> 4;
 
-  // staging assignment: 4 threads per tile row, 32 k (64 bytes) each
-  const int sr = tid >> 2, sq = tid & 3;
-  const uint16_t* srow[NA];
+  // A rows of this lane (row 16 m + ln of the tile), as element offsets into a_src / a_lo.
+  // Rows past the tile's end repeat its last row: their results are never stored.
+  size_t aoff[MT];
 #pragma unroll
-  for (int v = 0; v < NA; ++v) srow[v] = nullptr;
-  if (sr < pn) {
+  for (int m = 0; m < MT; ++m) {
+    const int r = min(16 * m + ln, pn - 1);
     if (GATEUP) {
-      const int pair = a.rows[p0 + sr];
-      if (pair >= 0 && pair < P) srow[0] = a.a_src + (size_t)(pair / a.k) * a.d;
+      const int pair = a.rows[p0 + r];
+      const int tok = (pair >= 0 && pair < P) ? pair / a.k : 0;
+      aoff[m] = (size_t)tok * a.d + 32 * g;
     } else {
-      srow[0] = a.a_src + (size_t)(p0 + sr) * a.f;
-      srow[NA - 1] = a.a_lo + (size_t)(p0 + sr) * a.f;
+      aoff[m] = (size_t)(p0 + r) * a.f + 32 * g;
     }
   }
 
-  // weight rows of this lane's N tiles
-  constexpr int NT = 4;
-  const uint8_t* wq[NT];
-  const uint8_t* wsc[NT];
-  bool wv[NT];
+  // weight rows: B lane (ln, g) of tile nt reads row rB[nt], block 4 ks + g; scale lanes
+  // l = 16 nt' + ln' read the scale word (4 blocks) of row rB[nt'] for lane ln'.
+  const uint8_t* bsrc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     int r;
-    const uint8_t *qb, *sb;
+    const uint8_t* qb;
     if (GATEUP) {
-      // tiles 0,1: gate rows; tiles 2,3: the same rows of up
-      r = nb * 128 + wave * 32 + (nt & 1) * 16 + ln;
+      r = nb * 256 + wave * 32 + (nt & 1) * 16 + ln;
       qb = (nt < 2) ? a.q0 : a.q1;
-      sb = (nt < 2) ? a.s0 : a.s1;
     } else {
-      r = nb * 256 + wave * 64 + nt * 16 + ln;
+      r = nb * 512 + wave * 64 + nt * 16 + ln;
       qb = a.q0;
+    }
+    r = min(r, NR - 1);  // rows past the matrix repeat its last row; never stored
+    bsrc[nt] = qb + ((size_t)e * NR + r) * rq + 16 * g;
+  }
+  const uint8_t* ssrc;
+  {
+    const int snt = lane >> 4, sln = lane & 15;
+    int r;
+    const uint8_t* sb;
+    if (GATEUP) {
+      r = nb * 256 + wave * 32 + (snt & 1) * 16 + sln;
+      sb = (snt < 2) ? a.s0 : a.s1;
+    } else {
+      r = nb * 512 + wave * 64 + snt * 16 + sln;
       sb = a.s0;
     }
-    wv[nt] = r < NR;
-    const size_t row = (size_t)e * NR + (wv[nt] ? r : 0);
-    wq[nt] = qb + row * rq;
-    wsc[nt] = sb + row * KB;
+    r = min(r, NR - 1);
+    ssrc = sb + ((size_t)e * NR + r) * KB;
   }
 
-  f32x4 acc[4][NT];
+  // this wave's share of the A blocks: ids wave, wave + 8, ...
+  constexpr int A_PER_WAVE = (PP::ABLK + kWaves - 1) / kWaves;
+  const int a_mine = (PP::ABLK >= kWaves) ? A_PER_WAVE : (wave < PP::ABLK ? 1 : 0);
+  auto issue = [&](int ks, int slotno) {
+    uint8_t* st = lds + slotno * SB;
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+    for (int j = 0; j < A_PER_WAVE; ++j) {
+      const int bi = wave + kWaves * j;
+      if (PP::ABLK >= kWaves || bi < PP::ABLK) {
+        const int v = bi / (MT * 4), m = (bi / 4) % MT, i = bi % 4;
+        const uint16_t* base = (NA == 2 && v == 1) ? a.a_lo : a.a_src;
+        dma16(base + aoff[m] + ks * BK + 8 * i, st + bi * 1024);
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      dma16(bsrc[nt] + (size_t)ks * 64, st + AB + (wave * NT + nt) * 1024);
+    dma4(ssrc + ks * 4, st + AB + kBStage + wave * 256);
+  };
+  // vector-memory operations one issue() puts in flight for this wave
+  const int ops = a_mine + NT + 1;
+
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = (K + BK - 1) / BK;
-  u32x4 stg[NA][4];
-  auto load_a = [&](int ks) {
-    const int k0 = ks * BK + sq * 32;
 #pragma unroll
-    for (int v = 0; v < NA; ++v)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bool ok = srow[v] != nullptr && (k0 + 8 * c) < K;
-        stg[v][c] = ok ? *reinterpret_cast<const u32x4*>(srow[v] + k0 + 8 * c)
-                       : u32x4{0u, 0u, 0u, 0u};
-      }
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int v = 0; v < NA; ++v) {
-      uint16_t* dst = &As[buf][v][sr * APITCH + sq * 32];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(dst + 8 * c) = stg[v][c];
-    }
-  };
-  u32x4 bq[NT];
-  uint32_t bs[NT];
-  auto load_b = [&](int ks) {
-    const int kb = ks * 4 + g;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const bool ok = wv[nt] && kb < KB;
-      bq[nt] = ok ? load_u32x4_nt(wq[nt] + (size_t)kb * 16) : u32x4{0u, 0u, 0u, 0u};
-      bs[nt] = ok ? (uint32_t)wsc[nt][kb] : 127u;
-    }
-  };
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) issue(s, s);
 
-  load_a(0);
-  load_b(0);
-  store_a(0);
-  __syncthreads();
   for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
+    // stage ks has landed once only the younger stages' operations are outstanding
+    if (ks + S - 2 < nk) {
+      if (ops == A_PER_WAVE + NT + 1) wait_vm<(S - 2) * (A_PER_WAVE + NT + 1)>();
+      else wait_vm<(S - 2) * (NT + 1)>();
+    } else {
+      wait_vm<0>();
+    }
+    barrier_no_fence();  // every wave's part of stage ks is in LDS; stage ks-1 is consumed
+    if (ks + S - 1 < nk) issue(ks + S - 1, (ks + S - 1) % S);
+
+    const uint8_t* st = lds + (ks % S) * SB;
     bf16x8 bop[NT][4];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) decode_b(bq[nt], e8m0_to_f32(bs[nt]), bop[nt]);
-    if (ks + 1 < nk) {
-      load_a(ks + 1);
-      load_b(ks + 1);
+    for (int nt = 0; nt < NT; ++nt) {
+      const u32x4 q = *reinterpret_cast<const u32x4*>(st + AB + (wave * NT + nt) * 1024 + lane * 16);
+      const uint32_t sc = st[AB + kBStage + wave * 256 + 4 * (nt * 16 + ln) + g];
+      decode_b(q, e8m0_to_f32(sc), bop[nt]);
     }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < MT; ++m) {
 #pragma unroll
       for (int v = 0; v < NA; ++v) {
-        const uint16_t* arow = &As[buf][v][(16 * m + ln) * APITCH + 32 * g];
         bf16x8 aop[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) aop[i] = *reinterpret_cast<const bf16x8*>(arow + 8 * i);
+        for (int i = 0; i < 4; ++i)
+          aop[i] = *reinterpret_cast<const bf16x8*>(st + ((v * MT + m) * 4 + i) * 1024 + lane * 16);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -195,15 +278,11 @@ __global__ __launch_bounds__(256) void mfma_ffn_kernel(MfmaArgs a) {
                 __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[i], bop[nt][i], acc[m][nt], 0, 0, 0);
       }
     }
-    if (ks + 1 < nk) {
-      store_a(buf ^ 1);
-      __syncthreads();
-    }
   }
 
   // epilogue: lane holds rows 4*g .. 4*g+3 of column ln of each 16x16 tile
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < MT; ++m) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * m + 4 * g + r;
@@ -211,7 +290,7 @@ __global__ __launch_bounds__(256) void mfma_ffn_kernel(MfmaArgs a) {
       if (GATEUP) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          const int j = nb * 128 + wave * 32 + nt * 16 + ln;
+          const int j = nb * 256 + wave * 32 + nt * 16 + ln;
           if (j < a.f) {
             const float hv = silu_f32(acc[m][nt][r]) * acc[m][nt + 2][r];
             const uint16_t hi = f32_to_bf16_rne(hv);
@@ -225,7 +304,7 @@ __global__ __launch_bounds__(256) void mfma_ffn_kernel(MfmaArgs a) {
         if (pair < 0 || pair >= P) continue;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const int i = nb * 256 + wave * 64 + nt * 16 + ln;
+          const int i = nb * 512 + wave * 64 + nt * 16 + ln;
           if (i < a.d) a.z_out[(size_t)pair * a.d + i] = acc[m][nt][r];
         }
       }
@@ -241,7 +320,7 @@ int mfma_mtiles_bound(int T, int E, int k) {
   return (int)(act + P / BM + 1);
 }
 
-bool mfma_shape_supported(int d, int f) { return d % 32 == 0 && f % 32 == 0; }
+bool mfma_shape_supported(int d, int f) { return d % BK == 0 && f % BK == 0; }
 
 hipError_t launch_gateup_mfma(int T, int d, int f, int E, int k, const uint16_t* x,
                               const MxPtrs& w, const int32_t* offsets, const int32_t* rows,
@@ -251,11 +330,11 @@ hipError_t launch_gateup_mfma(int T, int d, int f, int E, int k, const uint16_t*
   a.T = T; a.d = d; a.f = f; a.k = k; a.a_src = x;
   a.q0 = w.gate_q; a.s0 = w.gate_s; a.q1 = w.up_q; a.s1 = w.up_s;
   a.offsets = offsets; a.rows = rows; a.act = act; a.n_act = n_act; a.mtile_off = mtile_off;
-  a.nblk_n = (f + 127) / 128;
+  a.nblk_n = (f + 255) / 256;
   a.h_out = h;
   a.h_lo = h + (size_t)T * k * f;
   dim3 grid((unsigned)(mfma_mtiles_bound(T, E, k) * a.nblk_n));
-  mfma_ffn_kernel<true><<<grid, 256, 0, s>>>(a);
+  mfma_ffn_kernel<true><<<grid, 512, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -268,10 +347,10 @@ hipError_t launch_down_mfma(int T, int d, int f, int E, int k, const MxPtrs& w,
   a.a_lo = h + (size_t)T * k * f;
   a.q0 = w.down_q; a.s0 = w.down_s;
   a.offsets = offsets; a.rows = rows; a.act = act; a.n_act = n_act; a.mtile_off = mtile_off;
-  a.nblk_n = (d + 255) / 256;
+  a.nblk_n = (d + 511) / 512;
   a.z_out = z;
   dim3 grid((unsigned)(mfma_mtiles_bound(T, E, k) * a.nblk_n));
-  mfma_ffn_kernel<false><<<grid, 256, 0, s>>>(a);
+  mfma_ffn_kernel<false><<<grid, 512, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -234,8 +234,11 @@ int run_ffn(const k3moe_dims& dm, int32_t T, const void* x, int xf32,
   const int max_act = (int)(P < E ? P : E);
   float* h = ws.at<float>(R_H);
   int rc;
-  if (T > kGemvMaxTokens && !xf32) {
-    // many tokens per expert: grouped GEMMs on bf16 MFMA, h kept in bf16
+  const bool scales4 = ((reinterpret_cast<uintptr_t>(ex->gate_s) |
+                         reinterpret_cast<uintptr_t>(ex->up_s) |
+                         reinterpret_cast<uintptr_t>(ex->down_s)) & 3u) == 0;
+  if (T > kGemvMaxTokens && !xf32 && scales4 && k3moe::mfma_shape_supported(d, f)) {
+    // many tokens per expert: grouped GEMMs on bf16 MFMA, h kept as a bf16 hi/lo pair
     uint16_t* hb = ws.at<uint16_t>(R_H);
     float* z = ws.at<float>(R_Z);
     const int32_t* mt = ws.at<int32_t>(R_MTILE);

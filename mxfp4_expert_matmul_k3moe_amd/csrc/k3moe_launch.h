@@ -19,7 +19,12 @@ hipError_t launch_router_gemm(int T, int d, int E, const void* x, int xf32,
                               const uint16_t* w, double* logits, hipStream_t s);
 // ---- bucketing (bucket.hip) ----------------------------------------------------
 constexpr int kBucketTokens = 64;  // tokens per bucketing block
-constexpr int kMfmaTileM = 64;     // tokens per grouped-GEMM tile
+constexpr int kMfmaTileM = 64;     // tokens per full grouped-GEMM tile
+// Grouped-GEMM tiles of an expert with n tokens: one 16- or 32-row tile when n <= 32,
+// else ceil(n / 64) tiles of 64 rows (the MFMA work follows the real token count).
+__host__ __device__ inline int mfma_tiles_of(int n) {
+  return n <= 0 ? 0 : (n <= 32 ? 1 : (n + kMfmaTileM - 1) / kMfmaTileM);
+}
 struct BucketOut {
   int32_t* offsets;    // [E+1]
   int32_t* rows;       // [P] pair ids by bucket position
@@ -27,7 +32,7 @@ struct BucketOut {
   int32_t* n_act;      // [1]
   int32_t* pair_pos;   // [P] bucket position of pair id
   int32_t* pair_exp;   // [P] expert of pair id
-  int32_t* mtile_off;  // [E+1] prefix over active experts of ceil(count / kMfmaTileM)
+  int32_t* mtile_off;  // [E+1] prefix over active experts of mfma_tiles_of(count)
 };
 // nsum: number of fp64 partial arrays [nsum][T][E] to add (1 = plain logits).
 // bucket1 (T == 1 only, may be NULL): also write the single token's bucket.

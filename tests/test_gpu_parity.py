@@ -104,6 +104,11 @@ SHAPES = [
     Workload("k3_widths", 15, d=7168, f=1536, E=24, k=4, T=5),
     Workload("k3_widths_t1", 16, d=7168, f=1536, E=40, k=16, T=1),
     Workload("many_tokens", 17, d=256, f=128, E=16, k=2, T=130),
+    # grouped MFMA GEMMs with 16-, 32- and 64-row tiles, several M tiles per hot expert
+    # and partial N slices (f = 384 of 2 x 256 rows, d = 384 of 512)
+    Workload("mfma_mixed", 18, d=384, f=384, E=24, k=3, T=150, zipf_alpha=0.6),
+    # more than 64 tokens with d not a multiple of 128: per-expert GEMV path
+    Workload("gemv_many", 19, d=224, f=64, E=12, k=3, T=70),
 ]
 
 
