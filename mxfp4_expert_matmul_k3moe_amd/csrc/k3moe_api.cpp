@@ -70,7 +70,11 @@ Layout layout_for(const k3moe_dims& dm, int64_t T) {
   const int64_t NB = (T + k3moe::kBucketTokens - 1) / k3moe::kBucketTokens;
   const int64_t NC = k3moe::router_num_chunks((int)d);
   const int64_t tg = T < k3moe::kRouterGemvMaxT ? T : k3moe::kRouterGemvMaxT;
-  const size_t part_small = (size_t)(NC * tg * E * 8), part_big = (size_t)(T * E * 8);
+  // many-token router: up to 8 K-chunk partials, T * chunks bounded (monotone in T)
+  const int64_t budget = k3moe::router_split_budget((int)E);
+  const int64_t tk = T * 8 < budget ? T * 8 : budget;
+  const size_t part_small = (size_t)(NC * tg * E * 8),
+               part_big = (size_t)((tk > T ? tk : T) * E * 8);
   size_t sz[R_COUNT];
   sz[R_PART] = part_small > part_big ? part_small : part_big;
   sz[R_IDS] = (size_t)P * 4;
@@ -214,7 +218,7 @@ int run_router(const k3moe_dims& dm, int32_t T, const void* x, int xf32, const u
     e = k3moe::launch_router_gemv(T, dm.d_model, dm.n_experts, x, xf32, w, part, s);
     nsum = k3moe::router_num_chunks(dm.d_model);
   } else {
-    e = k3moe::launch_router_gemm(T, dm.d_model, dm.n_experts, x, xf32, w, part, s);
+    e = k3moe::launch_router_gemm(T, dm.d_model, dm.n_experts, x, xf32, w, part, &nsum, s);
   }
   int rc = hip_check(e, "router logits");
   if (rc) return rc;

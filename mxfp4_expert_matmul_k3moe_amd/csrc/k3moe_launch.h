@@ -15,8 +15,13 @@ constexpr int kRouterGemvMaxT = 64;   // above this the tiled fp64 GEMM is used
 
 hipError_t launch_router_gemv(int T, int d, int E, const void* x, int xf32,
                               const uint16_t* w, double* part, hipStream_t s);
+// K chunks of the many-token router (its partial-sum count; at most 8), and the bound
+// router_mfma_splits(T) * T <= max(T, min(8 T, router_split_budget(E))).
+int router_mfma_splits(int T, int d, int E);
+int router_split_budget(int E);
+// part[c][t][e] for c < *nsum (set on return), summed in order by route_topk.
 hipError_t launch_router_gemm(int T, int d, int E, const void* x, int xf32,
-                              const uint16_t* w, double* logits, hipStream_t s);
+                              const uint16_t* w, double* part, int* nsum, hipStream_t s);
 // ---- bucketing (bucket.hip) ----------------------------------------------------
 constexpr int kBucketTokens = 64;  // tokens per bucketing block
 constexpr int kMfmaTileM = 64;     // tokens per full grouped-GEMM tile

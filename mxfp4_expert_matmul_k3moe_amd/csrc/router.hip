@@ -168,60 +168,106 @@ __global__ __launch_bounds__(256) void router_gemv_vec_kernel(int T, int d, int 
   }
 }
 
-// Tiled fp64 GEMM for many tokens: logits[t][e] = sum_k x[t][k] W[k][e], k ascending
-// within each 16-row step, steps ascending. Tile 64 tokens x 64 experts; each thread
-// owns a 4x4 patch.
+// Many-token router on fp64 MFMA: part[c][t][e] = sum over the c-th K chunk of
+// x[t][k] * W[k][e], with v_mfma_f64_16x16x4_f64 (fp64 products and sums, like the
+// scalar paths). Block: 64 tokens x 64 experts x one K chunk, 4 waves of 32 x 32
+// (2 x 2 MFMA tiles). Operands are converted to fp64 once, when staged in LDS;
+// K advances 32 per stage, double-buffered, the next stage's global loads in flight
+// while the MFMAs of the current one run. Within a stage, lane group g = lane/16 feeds
+// k = 4 j + g to the j-th MFMA of every tile (A and B alike).
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+constexpr int kRmBK = 32;             // K per stage
+constexpr int kRmAP = kRmBK + 1;      // A row pitch in doubles (16 rows hit distinct banks)
+
 template <bool XF32>
-__global__ __launch_bounds__(256) void router_gemm_kernel(int T, int d, int E,
+__global__ __launch_bounds__(256) void router_mfma_kernel(int T, int d, int E, int kc,
                                                           const void* __restrict__ x,
                                                           const uint16_t* __restrict__ w,
-                                                          double* __restrict__ logits) {
-  constexpr int TM = 64, TN = 64, TK = 16;
-  __shared__ double xs[TK][TM + 1];
-  __shared__ double wsh[TK][TN + 1];
-  const int tid = threadIdx.x;
-  const int tm0 = blockIdx.x * TM, tn0 = blockIdx.y * TN;
-  const int ty = tid / 16, tx = tid % 16;  // 16 x 16 threads, 4x4 each
-  double acc[4][4];
+                                                          double* __restrict__ part) {
+  __shared__ double As[2][64 * kRmAP];
+  __shared__ double Bs[2][kRmBK * 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ln = lane & 15, g = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  const int c = blockIdx.z;
+  const int kbeg = c * kc, kend = min(d, kbeg + kc);
+  const int nst = (kend - kbeg + kRmBK - 1) / kRmBK;
+
+  // staging: thread -> (A row ar, 8 k at ak) and (B k-row bk, 8 experts at be)
+  const int ar = tid >> 2, ak = (tid & 3) * 8;
+  const int bk = tid >> 3, be = (tid & 7) * 8;
+  const bool arow_ok = t0 + ar < T;
+  double av[8], bv[8];
+  auto load = [&](int st) {
+    const int k = kbeg + st * kRmBK;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-  for (int k0 = 0; k0 < d; k0 += TK) {
-    __syncthreads();
-    for (int i = tid; i < TM * TK; i += 256) {
-      const int m = i / TK, kk = i % TK;
-      const int t = tm0 + m, k = k0 + kk;
-      xs[kk][m] = (t < T && k < d) ? load_x<XF32>(x, (size_t)t * d + k) : 0.0;
+    for (int u = 0; u < 8; ++u) {
+      const int ka = k + ak + u;
+      if (XF32) {
+        av[u] = (arow_ok && ka < kend)
+                    ? (double)static_cast<const float*>(x)[(size_t)(t0 + ar) * d + ka] : 0.0;
+      } else {
+        av[u] = (arow_ok && ka < kend)
+                    ? (double)bf16_bits_to_f32(static_cast<const uint16_t*>(x)[(size_t)(t0 + ar) * d + ka])
+                    : 0.0;
+      }
+      const int kb = k + bk, e = e0 + be + u;
+      bv[u] = (kb < kend && e < E) ? (double)bf16_bits_to_f32(w[(size_t)kb * E + e]) : 0.0;
     }
-    for (int i = tid; i < TN * TK; i += 256) {
-      const int kk = i / TN, n = i % TN;
-      const int e = tn0 + n, k = k0 + kk;
-      wsh[kk][n] = (e < E && k < d) ? (double)bf16_bits_to_f32(w[(size_t)k * E + e]) : 0.0;
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      As[buf][ar * kRmAP + ak + u] = av[u];
+      Bs[buf][bk * 64 + be + u] = bv[u];
     }
-    __syncthreads();
+  };
+
+  f64x4 acc[2][2];
 #pragma unroll
-    for (int kk = 0; kk < TK; ++kk) {
-      double a[4], b[4];
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = xs[kk][ty + 16 * i];
+    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nst) load(st + 1);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = wsh[kk][tx + 16 * j];
+    for (int j = 0; j < kRmBK / 4; ++j) {
+      const int kk = 4 * j + g;
+      double a[2], b[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i) a[i] = As[buf][(wm * 32 + i * 16 + ln) * kRmAP + kk];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+      for (int i = 0; i < 2; ++i) b[i] = Bs[buf][kk * 64 + wn * 32 + i * 16 + ln];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+    }
+    if (st + 1 < nst) {
+      __syncthreads();
+      store(buf ^ 1);
+      __syncthreads();
     }
   }
+  // fp64 16 x 16 result: value r of lane (ln, g) is row g + 4 r, column ln
+  double* out = part + (size_t)c * T * E;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = tm0 + ty + 16 * i;
+  for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = tn0 + tx + 16 * j;
-      if (t < T && e < E) logits[(size_t)t * E + e] = acc[i][j];
-    }
-  }
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + wm * 32 + mi * 16 + g + 4 * r;
+        const int e = e0 + wn * 32 + ni * 16 + ln;
+        if (t < T && e < E) out[(size_t)t * E + e] = acc[mi][ni][r];
+      }
 }
 
 // Total-order key of an fp64 logit: larger logit -> larger key; +0 and -0 share a
@@ -486,11 +532,28 @@ hipError_t launch_router_gemv(int T, int d, int E, const void* x, int xf32, cons
   return hipGetLastError();
 }
 
+// K chunks: about 2048 blocks of 64 x 64 over the chunks (a few waves of work on 256
+// CUs), at most 8, each chunk at least 512 deep. T * splits never exceeds
+// max(T, min(8 T, router_split_budget(E))), which sizes the partial-sum workspace.
+int router_split_budget(int E) { return 131072 / ((E + 63) / 64); }
+
+int router_mfma_splits(int T, int d, int E) {
+  long ks = (long)router_split_budget(E) / (T > 0 ? T : 1);
+  const long kmax = (d + 511) / 512;
+  if (ks > kmax) ks = kmax;
+  if (ks > 8) ks = 8;
+  return ks < 1 ? 1 : (int)ks;
+}
+
 hipError_t launch_router_gemm(int T, int d, int E, const void* x, int xf32, const uint16_t* w,
-                              double* logits, hipStream_t s) {
-  dim3 grid((T + 63) / 64, (E + 63) / 64);
-  if (xf32) router_gemm_kernel<true><<<grid, 256, 0, s>>>(T, d, E, x, w, logits);
-  else router_gemm_kernel<false><<<grid, 256, 0, s>>>(T, d, E, x, w, logits);
+                              double* part, int* nsum, hipStream_t s) {
+  const int ks = router_mfma_splits(T, d, E);
+  const int kc = ((d + ks - 1) / ks + kRmBK - 1) / kRmBK * kRmBK;
+  const int nch = (d + kc - 1) / kc;
+  *nsum = nch;
+  dim3 grid((T + 63) / 64, (E + 63) / 64, nch);
+  if (xf32) router_mfma_kernel<true><<<grid, 256, 0, s>>>(T, d, E, kc, x, w, part);
+  else router_mfma_kernel<false><<<grid, 256, 0, s>>>(T, d, E, kc, x, w, part);
   return hipGetLastError();
 }
 

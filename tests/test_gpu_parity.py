@@ -208,9 +208,11 @@ def test_repeat_runs_bit_identical(dev):
         assert np.array_equal(a["gates"], b["gates"])
 
 
-def test_fp32_activations(dev):
-    w = TOY.with_(T=3, name="toy_f32")
-    say("fp32 activations")
+@pytest.mark.parametrize("T", [3, 100])
+def test_fp32_activations(dev, T):
+    # T = 100: the many-token fp64 MFMA router reading fp32 activations
+    w = TOY.with_(T=T, name=f"toy_f32_t{T}")
+    say(f"fp32 activations T={T}")
     x = w.resid0()
     g = run_gpu_layer(w, x, dev, x_dtype="f32")
     ref = harness.run_layer(w, x)
