@@ -50,7 +50,10 @@ constexpr int kMaxK = 32;
 constexpr int kMaxT = 1 << 20;
 constexpr int kMaxWidth = 16384;
 // Above this many tokens, bf16 activations go through the MFMA grouped GEMMs.
-constexpr int kGemvMaxTokens = 64;
+// From this many tokens on (bf16 activations) the expert matmuls run as grouped MFMA GEMMs;
+// below, as per-expert GEMVs. At 32 tokens the MFMA path's down projection already streams
+// twice as fast as the GEMV one.
+constexpr int kMfmaMinTokens = 16;
 
 enum Region {
   R_PART, R_IDS, R_GATES, R_OFFS, R_ROWS, R_ACT, R_NACT, R_PPOS, R_PEXP, R_HIST, R_BASE,
@@ -241,7 +244,7 @@ int run_ffn(const k3moe_dims& dm, int32_t T, const void* x, int xf32,
   const bool scales4 = ((reinterpret_cast<uintptr_t>(ex->gate_s) |
                          reinterpret_cast<uintptr_t>(ex->up_s) |
                          reinterpret_cast<uintptr_t>(ex->down_s)) & 3u) == 0;
-  if (T > kGemvMaxTokens && !xf32 && scales4 && k3moe::mfma_shape_supported(d, f)) {
+  if (T >= kMfmaMinTokens && !xf32 && scales4 && k3moe::mfma_shape_supported(d, f)) {
     // many tokens per expert: grouped GEMMs on bf16 MFMA, h kept as a bf16 hi/lo pair
     uint16_t* hb = ws.at<uint16_t>(R_H);
     float* z = ws.at<float>(R_Z);

@@ -287,16 +287,17 @@ constexpr int kMaxSlots = 32;
 constexpr int kMaxChunks = 32;  // d <= 16384 in 512-row chunks
 constexpr int kMaxCand = 2048;  // candidate buffer; the exact ranking covers any count
 
-// One block (256 threads) per token; thread t holds the logits of experts t + 256*j
-// (j < KPT) in registers.
+// One block per token of NT = blockDim.x threads (a multiple of 64, at most 256): thread t
+// holds the logits of experts t + NT*j (j < KPT) in registers.
 //  1. logits = sum of the fp64 partials in chunk order (+ bias), as order keys;
-//  2. each wave ranks its 64 lane maxima (readlane broadcasts): the k-th best of them is
-//     at most the k-th best of all E, so the best such bound over the waves is a valid
-//     threshold, and every top-k element ranks at or above it;
+//  2. each wave sorts its 64 lane maxima (bitonic network over lanes): the k-th best of
+//     them is at most the k-th best of all E, so the best such bound over the waves is a
+//     valid threshold, and every top-k element ranks at or above it;
 //  3. candidates at or above the threshold are compacted into LDS (wave scans) and ranked
 //     exactly against each other; the softmax denominator is a per-thread ordered sum and
 //     a fixed reduction tree.
 // With `bk` (T == 1) the same block also writes the expert bucket of the single token.
+constexpr int kTopkMaxWaves = 4;
 struct Bucket1 {
   int32_t *offsets, *rows, *act, *n_act, *pair_pos, *pair_exp, *mtile_off;
 };
@@ -306,33 +307,28 @@ __device__ __forceinline__ double key_to_double(uint64_t kv) {
   return __longlong_as_double((long long)b);
 }
 
-__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
-  return ((uint64_t)hi << 32) | lo;
-}
-
 template <int KPT>
 __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
-                                                         const double* __restrict__ part,
-                                                         int nsum, const float* __restrict__ bias,
-                                                         int32_t* __restrict__ ids,
-                                                         float* __restrict__ gates, Bucket1 bk) {
+                                                          const double* __restrict__ part,
+                                                          int nsum, const float* __restrict__ bias,
+                                                          int32_t* __restrict__ ids,
+                                                          float* __restrict__ gates, Bucket1 bk) {
   __shared__ uint64_t keys[kMaxE];
   __shared__ uint64_t ckey[kMaxCand];
   __shared__ int cid[kMaxCand];
-  __shared__ uint64_t w_tk[4], w_mk[4];
-  __shared__ int w_ti[4], w_ok[4], w_cnt[4], w_nan[4];
-  __shared__ double w_sum[4];
+  __shared__ uint64_t w_tk[kTopkMaxWaves], w_mk[kTopkMaxWaves];
+  __shared__ int w_ti[kTopkMaxWaves], w_ok[kTopkMaxWaves], w_cnt[kTopkMaxWaves], w_nan[kTopkMaxWaves];
+  __shared__ double w_sum[kTopkMaxWaves];
   __shared__ int s_ids[kMaxSlots];
   const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int NT = blockDim.x, nw = NT >> 6;
 
   // 1. logits: all loads of a chunk issued before any add; chunks summed in order
   constexpr int CB = (64 / KPT) > 1 ? (64 / KPT) : 1;  // chunks whose loads go out together
   float bv[KPT];  // bias requested together with the first partials
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) bv[j] = bias ? bias[min(tid + 256 * j, E - 1)] : 0.0f;
+  for (int j = 0; j < KPT; ++j) bv[j] = bias ? bias[min(tid + NT * j, E - 1)] : 0.0f;
   double acc[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) acc[j] = 0.0;
@@ -342,7 +338,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
     for (int u = 0; u < CB; ++u)
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
-        const int e = min(tid + 256 * j, E - 1);
+        const int e = min(tid + NT * j, E - 1);
         const int c = min(c0 + u, nsum - 1);
         v[u][j] = part[((size_t)c * T + t) * E + e];  // clamped: always a valid address
       }
@@ -358,7 +354,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
   int bi = -1;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const int e = tid + 256 * j;
+    const int e = tid + NT * j;
     if (e < E) {
       const double l = bias ? acc[j] + (double)bv[j] : acc[j];
       nan_here |= (l != l);
@@ -370,26 +366,36 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
     }
   }
 
-  // 2. per-wave threshold from the 64 lane maxima
+  // 2. per-wave threshold: the 64 lane maxima sorted best-first by a bitonic network over
+  //    the lanes; lane 0 then holds the wave's best logit and lane k-1 the k-th best
   {
-    int rank = 0;
-    for (int l = 0; l < 64; ++l) {
-      const int oi = __builtin_amdgcn_readlane(bi, l);
-      const uint64_t ok = readlane64(bkey, l);
-      rank += (oi >= 0 && bi >= 0 && better(ok, oi, bkey, bi)) ? 1 : 0;
+    uint64_t sk = (bi >= 0) ? bkey : 0ull;
+    int si = (bi >= 0) ? bi : 0x7FFFFFFF;
+    for (int size = 2; size <= 64; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        const uint32_t plo = (uint32_t)__shfl_xor((int)(uint32_t)sk, stride, 64);
+        const uint32_t phi = (uint32_t)__shfl_xor((int)(uint32_t)(sk >> 32), stride, 64);
+        const int pi = __shfl_xor(si, stride, 64);
+        const uint64_t pk = ((uint64_t)phi << 32) | plo;
+        const bool desc = (lane & size) == 0;  // this run of `size` lanes sorts best-first
+        const bool low = (lane & stride) == 0;
+        if (better(pk, pi, sk, si) == (low == desc)) {
+          sk = pk;
+          si = pi;
+        }
+      }
     }
     const int nvalid = __popcll(__ballot(bi >= 0));
+    const bool anyn = __any(nan_here);
     if (lane == 0) {
       w_ok[wave] = nvalid >= k;
-      w_nan[wave] = 0;
+      w_nan[wave] = anyn ? 1 : 0;
+      w_mk[wave] = nvalid > 0 ? sk : 0ull;
     }
-    if (bi >= 0 && rank == 0) w_mk[wave] = bkey;
-    if (bi >= 0 && rank == k - 1) {
-      w_tk[wave] = bkey;
-      w_ti[wave] = bi;
+    if (lane == k - 1) {
+      w_tk[wave] = sk;
+      w_ti[wave] = si;
     }
-    if (__any(nan_here) && lane == 0) w_nan[wave] = 1;
-    if (nvalid == 0 && lane == 0) w_mk[wave] = 0;
   }
   __syncthreads();
   uint64_t tk = 0, mk = 0;
@@ -397,7 +403,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
   bool have = false;
   int anynan = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < nw; ++w) {
     if (w_ok[w] && (!have || better(w_tk[w], w_ti[w], tk, ti))) {
       tk = w_tk[w];
       ti = w_ti[w];
@@ -413,7 +419,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
   double se = 0.0;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const int e = tid + 256 * j;
+    const int e = tid + NT * j;
     if (e < E) {
       mine += better(tk, ti, key[j], e) ? 0 : 1;
       se += exp(key_to_double(key[j]) - m);
@@ -429,16 +435,17 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
   if (lane == 0) w_sum[wave] = se;
   __syncthreads();
   int base = 0, total = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  double wsum = 0.0;
+  for (int w = 0; w < nw; ++w) {
     base += (w < wave) ? w_cnt[w] : 0;
     total += w_cnt[w];
+    wsum += w_sum[w];
   }
-  const double sum = anynan ? __builtin_nan("") : ((w_sum[0] + w_sum[1]) + w_sum[2]) + w_sum[3];
+  const double sum = anynan ? __builtin_nan("") : wsum;
   pre = base + pre - mine;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const int e = tid + 256 * j;
+    const int e = tid + NT * j;
     if (e < E && !better(tk, ti, key[j], e)) {
       if (pre < kMaxCand) {
         cid[pre] = e;
@@ -451,7 +458,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
 
   // 4. exact ranks of the candidates
   if (total <= kMaxCand) {
-    for (int c = tid; c < total; c += 256) {
+    for (int c = tid; c < total; c += NT) {
       const int id = cid[c];
       const uint64_t kv = ckey[c];
       int r = 0;
@@ -465,7 +472,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
     }
   } else {
     // very many exact ties: rank every candidate against all logits
-    for (int e = tid; e < E; e += 256) {
+    for (int e = tid; e < E; e += NT) {
       const uint64_t kv = keys[e];
       if (better(tk, ti, kv, e)) continue;
       int r = 0;
@@ -566,12 +573,14 @@ hipError_t launch_route_topk(int T, int E, int k, const double* part, int nsum,
     b.n_act = bucket1->n_act; b.pair_pos = bucket1->pair_pos; b.pair_exp = bucket1->pair_exp;
     b.mtile_off = bucket1->mtile_off;
   }
+  // 256 threads (four waves) per token, up to 16 experts per thread
   const int kpt = (E + 255) / 256;
-  if (kpt <= 1) route_topk_kernel<1><<<T, 256, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
-  else if (kpt <= 2) route_topk_kernel<2><<<T, 256, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
-  else if (kpt <= 4) route_topk_kernel<4><<<T, 256, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
-  else if (kpt <= 8) route_topk_kernel<8><<<T, 256, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
-  else route_topk_kernel<16><<<T, 256, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
+  const int nt = 256;
+  if (kpt <= 1) route_topk_kernel<1><<<T, nt, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
+  else if (kpt <= 2) route_topk_kernel<2><<<T, nt, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
+  else if (kpt <= 4) route_topk_kernel<4><<<T, nt, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
+  else if (kpt <= 8) route_topk_kernel<8><<<T, nt, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
+  else route_topk_kernel<16><<<T, nt, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
   return hipGetLastError();
 }
 
