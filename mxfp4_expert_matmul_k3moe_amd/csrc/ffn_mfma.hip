@@ -31,18 +31,25 @@ constexpr int kWaves = 8;          // 512 threads: two waves per SIMD, one block
 constexpr int NT = 4;              // 16-wide N tiles per wave
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kBStage = kWaves * NT * 1024;  // weight blocks of one step: 16 B per lane per tile
-constexpr int kSStage = kWaves * 256;        // scale words of one step: 4 B per lane
+constexpr int kSStage = kWaves * 256;        // per-step scale words: 4 B per lane
+constexpr int kSGroup = kWaves * 1024;       // scale groups: 16 B per lane = 4 steps of scales
 
-// One stage of the pipeline in LDS: [A: NA x MT x 4 KB-blocks][B: kBStage][scales: kSStage].
+// One stage of the pipeline in LDS: [A: NA x MT x 4 KB-blocks][B: kBStage] plus, when the
+// scales come one step at a time (SG4 false), [scales: kSStage]. With SG4 (K a multiple of
+// 512) each lane fetches 16 scale bytes of its weight row (4 steps) every 4th step into
+// one of two scale-group slots after the stages: a quarter of the L1 requests of
+// per-step scale words, which otherwise cost as many requests as the nibbles.
 // Every KB-block is written by one wave-wide 16-byte-per-lane DMA load (lane l lands at
 // byte 16 l) and read back by one wave-wide 16-byte LDS read at the same lane offsets.
-template <bool GATEUP, int MT>
+template <bool GATEUP, int MT, bool SG4>
 struct Pipe {
   static constexpr int NA = GATEUP ? 1 : 2;       // x, or h_hi and h_lo
   static constexpr int ABLK = NA * MT * 4;         // 1-KB A blocks per stage
   static constexpr int ABYTES = ABLK * 1024;
-  static constexpr int BYTES = ABYTES + kBStage + kSStage;
-  static constexpr int S = (kLdsBytes / BYTES) < 4 ? (kLdsBytes / BYTES) : 4;  // stages
+  static constexpr int BYTES = ABYTES + kBStage + (SG4 ? 0 : kSStage);
+  static constexpr int RING = SG4 ? 2 * kSGroup : 0;  // scale-group slots
+  static constexpr int S0 = (kLdsBytes - RING) / BYTES;
+  static constexpr int S = S0 < 4 ? S0 : 4;        // stages
   static_assert(S >= 2, "pipeline needs two stages");
 };
 
@@ -114,7 +121,7 @@ struct MfmaArgs {
 // GATEUP: N slice = 256 rows j (each wave 32 j, as 2 gate + 2 up 16-wide tiles).
 // DOWN:   N slice = 512 rows i (each wave 64 i, as 4 tiles).
 // MT = 16-row M subtiles in the tile (1, 2 or 4: tiles of 16, 32 or 64 tokens).
-template <bool GATEUP, int MT>
+template <bool GATEUP, int MT, bool SG4>
 __device__ __forceinline__ void mfma_tile(const MfmaArgs& a, uint8_t* lds, int e, int p0, int pn,
                                           int nb);
 
@@ -144,15 +151,25 @@ __global__ __launch_bounds__(512) void mfma_ffn_kernel(MfmaArgs a) {
   const int p0 = pe0 + mloc * BM;
   const int pn = max(0, min(BM, pe1 - p0));
   if (pn <= 0) return;
-  if (cnt <= 16) mfma_tile<GATEUP, 1>(a, lds, e, p0, pn, nb);
-  else if (cnt <= 32) mfma_tile<GATEUP, 2>(a, lds, e, p0, pn, nb);
-  else mfma_tile<GATEUP, 4>(a, lds, e, p0, pn, nb);
+  // 16-byte scale groups need K a multiple of 512 and 16-byte aligned scale arrays
+  const bool sg4 = ((GATEUP ? a.d : a.f) % (4 * BK)) == 0 &&
+                   ((reinterpret_cast<uintptr_t>(a.s0) |
+                     reinterpret_cast<uintptr_t>(GATEUP ? a.s1 : a.s0)) & 15u) == 0;
+  if (sg4) {
+    if (cnt <= 16) mfma_tile<GATEUP, 1, true>(a, lds, e, p0, pn, nb);
+    else if (cnt <= 32) mfma_tile<GATEUP, 2, true>(a, lds, e, p0, pn, nb);
+    else mfma_tile<GATEUP, 4, true>(a, lds, e, p0, pn, nb);
+  } else {
+    if (cnt <= 16) mfma_tile<GATEUP, 1, false>(a, lds, e, p0, pn, nb);
+    else if (cnt <= 32) mfma_tile<GATEUP, 2, false>(a, lds, e, p0, pn, nb);
+    else mfma_tile<GATEUP, 4, false>(a, lds, e, p0, pn, nb);
+  }
 }
 
-template <bool GATEUP, int MT>
+template <bool GATEUP, int MT, bool SG4>
 __device__ __forceinline__ void mfma_tile(const MfmaArgs& a, uint8_t* lds, int e, int p0, int pn,
                                           int nb) {
-  using PP = Pipe<GATEUP, MT>;
+  using PP = Pipe<GATEUP, MT, SG4>;
   constexpr int NA = PP::NA, S = PP::S, SB = PP::BYTES, AB = PP::ABYTES;
   const int P = a.T * a.k;
   const int K = GATEUP ? a.d : a.f;     // contraction length (multiple of BK)
@@ -213,7 +230,8 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a, uint8_t* lds, int e
 
   // this wave's share of the A blocks: ids wave, wave + 8, ...
   constexpr int A_PER_WAVE = (PP::ABLK + kWaves - 1) / kWaves;
-  const int a_mine = (PP::ABLK >= kWaves) ? A_PER_WAVE : (wave < PP::ABLK ? 1 : 0);
+  const bool has_a = PP::ABLK >= kWaves || wave < PP::ABLK;
+  uint8_t* const sring = lds + S * SB;  // scale-group slots (SG4)
   auto issue = [&](int ks, int slotno) {
     uint8_t* st = lds + slotno * SB;
 #pragma unroll
@@ -228,10 +246,32 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a, uint8_t* lds, int e
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
       dma16(bsrc[nt] + (size_t)ks * 64, st + AB + (wave * NT + nt) * 1024);
-    dma4(ssrc + ks * 4, st + AB + kBStage + wave * 256);
+    if (SG4) {
+      if ((ks & 3) == 0) dma16(ssrc + ks * 4, sring + ((ks >> 2) & 1) * kSGroup + wave * 1024);
+    } else {
+      dma4(ssrc + ks * 4, st + AB + kBStage + wave * 256);
+    }
   };
-  // vector-memory operations one issue() puts in flight for this wave
-  const int ops = a_mine + NT + 1;
+  // Vector-memory operations of one stage for this wave: A blocks, NT weight blocks, and
+  // the per-step scale word (or, with SG4, one scale group on every 4th stage).
+  constexpr int OPS_A = A_PER_WAVE + NT + (SG4 ? 0 : 1);
+  constexpr int OPS_NOA = NT + (SG4 ? 0 : 1);
+  // wait until this wave's stage ks has landed: only stages ks+1 .. ks+S-2 may be pending
+  auto wait_stage = [&](int ks) {
+    if (ks + S - 2 >= nk) {
+      wait_vm<0>();
+      return;
+    }
+    // scale groups issued with the pending stages (multiples of 4 in ks+1 .. ks+S-2)
+    const int extra = SG4 ? ((ks + S - 2) >> 2) - (ks >> 2) : 0;
+    if (has_a) {
+      if (extra) wait_vm<(S - 2) * OPS_A + 1>();
+      else wait_vm<(S - 2) * OPS_A>();
+    } else {
+      if (extra) wait_vm<(S - 2) * OPS_NOA + 1>();
+      else wait_vm<(S - 2) * OPS_NOA>();
+    }
+  };
 
   f32x4 acc[MT][NT];
 #pragma unroll
@@ -244,13 +284,7 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a, uint8_t* lds, int e
     if (s < nk) issue(s, s);
 
   for (int ks = 0; ks < nk; ++ks) {
-    // stage ks has landed once only the younger stages' operations are outstanding
-    if (ks + S - 2 < nk) {
-      if (ops == A_PER_WAVE + NT + 1) wait_vm<(S - 2) * (A_PER_WAVE + NT + 1)>();
-      else wait_vm<(S - 2) * (NT + 1)>();
-    } else {
-      wait_vm<0>();
-    }
+    wait_stage(ks);
     barrier_no_fence();  // every wave's part of stage ks is in LDS; stage ks-1 is consumed
     if (ks + S - 1 < nk) issue(ks + S - 1, (ks + S - 1) % S);
 
@@ -259,7 +293,9 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a, uint8_t* lds, int e
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const u32x4 q = *reinterpret_cast<const u32x4*>(st + AB + (wave * NT + nt) * 1024 + lane * 16);
-      const uint32_t sc = st[AB + kBStage + wave * 256 + 4 * (nt * 16 + ln) + g];
+      const uint32_t sc =
+          SG4 ? sring[((ks >> 2) & 1) * kSGroup + wave * 1024 + 16 * (nt * 16 + ln) + 4 * (ks & 3) + g]
+              : st[AB + kBStage + wave * 256 + 4 * (nt * 16 + ln) + g];
       decode_b(q, e8m0_to_f32(sc), bop[nt]);
     }
 #pragma unroll

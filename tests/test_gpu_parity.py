@@ -109,8 +109,9 @@ SHAPES = [
     Workload("mfma_mixed", 18, d=384, f=384, E=24, k=3, T=150, zipf_alpha=0.6),
     # more than 64 tokens with d not a multiple of 128: per-expert GEMV path
     Workload("gemv_many", 19, d=224, f=64, E=12, k=3, T=70),
-    # the smallest token count that takes the grouped MFMA path
-    Workload("mfma_t16", 20, d=256, f=128, E=10, k=3, T=16),
+    # the smallest token count that takes the grouped MFMA path; d and f multiples of 512
+    # (scales fetched 4 steps at a time)
+    Workload("mfma_t16", 20, d=512, f=512, E=10, k=3, T=16),
 ]
 
 
