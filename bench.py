@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_MIN_TOKENS = 16  # the library's grouped-MFMA path starts at this many tokens
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
 
 
@@ -212,8 +213,13 @@ def main() -> int:
     if w.T <= 64:  # decode-like: weight stream
         value, unit = bytes_timed / (t1 - t0) / 1e9, "GB/s"
         ach = gu_bytes / gu_s / 1e9
-        roof = {"bound": "hbm", "kernel": "gateup_decode_kernel (MXFP4 gate/up GEMV + SwiGLU)"
-                if w.T == 1 else "gateup_gemv_kernel (MXFP4 gate/up GEMV + SwiGLU)",
+        if w.T == 1:
+            kname = "gateup_decode_kernel (MXFP4 gate/up GEMV + SwiGLU)"
+        elif w.T >= MFMA_MIN_TOKENS:
+            kname = "mfma_ffn_kernel<gate/up> (grouped MXFP4 x bf16 MFMA GEMM + SwiGLU)"
+        else:
+            kname = "gateup_gemv_kernel (MXFP4 gate/up GEMV + SwiGLU)"
+        roof = {"bound": "hbm", "kernel": kname,
                 "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "bytes_per_launch": int(gu_bytes), "avg_launch_us": round(kern["gate_up"] * 1e3, 2)}
