@@ -199,21 +199,47 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(int T, int d, int E, i
   const int bk = tid >> 3, be = (tid & 7) * 8;
   const bool arow_ok = t0 + ar < T;
   double av[8], bv[8];
+  // 16-byte loads where the 8 values are contiguous and aligned (k chunks are multiples
+  // of 32 and x rows are 16-byte aligned; W rows need E % 8 == 0 and an aligned base)
+  const bool wvec = (E % 8) == 0 && (reinterpret_cast<uintptr_t>(w) & 15u) == 0;
   auto load = [&](int st) {
     const int k = kbeg + st * kRmBK;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int ka = k + ak + u;
+    const int ka = k + ak;
+    if (arow_ok && ka < kend) {
       if (XF32) {
-        av[u] = (arow_ok && ka < kend)
-                    ? (double)static_cast<const float*>(x)[(size_t)(t0 + ar) * d + ka] : 0.0;
+        const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) +
+                                                          (size_t)(t0 + ar) * d + ka);
+        const f32x4 p0 = src[0], p1 = src[1];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          av[u] = (double)p0[u];
+          av[4 + u] = (double)p1[u];
+        }
       } else {
-        av[u] = (arow_ok && ka < kend)
-                    ? (double)bf16_bits_to_f32(static_cast<const uint16_t*>(x)[(size_t)(t0 + ar) * d + ka])
-                    : 0.0;
+        const u32x4 q = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) +
+                                                        (size_t)(t0 + ar) * d + ka);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          av[2 * u] = (double)__uint_as_float(q[u] << 16);
+          av[2 * u + 1] = (double)__uint_as_float(q[u] & 0xFFFF0000u);
+        }
       }
-      const int kb = k + bk, e = e0 + be + u;
-      bv[u] = (kb < kend && e < E) ? (double)bf16_bits_to_f32(w[(size_t)kb * E + e]) : 0.0;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) av[u] = 0.0;
+    }
+    const int kb = k + bk, eb = e0 + be;
+    if (kb < kend && wvec && eb + 8 <= E) {
+      const u32x4 q = *reinterpret_cast<const u32x4*>(w + (size_t)kb * E + eb);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        bv[2 * u] = (double)__uint_as_float(q[u] << 16);
+        bv[2 * u + 1] = (double)__uint_as_float(q[u] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        bv[u] = (kb < kend && eb + u < E) ? (double)bf16_bits_to_f32(w[(size_t)kb * E + eb + u]) : 0.0;
     }
   };
   auto store = [&](int buf) {
