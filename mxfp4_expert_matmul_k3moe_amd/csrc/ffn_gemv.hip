@@ -400,19 +400,54 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int d, int k, const
                                                       const float* __restrict__ resid,
                                                       const float* __restrict__ shared,
                                                       float* __restrict__ y,
-                                                      uint16_t* __restrict__ y_bf16) {
+                                                      uint16_t* __restrict__ y_bf16, int bf16_vec) {
+  // four consecutive outputs per thread (16-byte loads of z); the z rows of up to 8 slots
+  // are requested before any of them is added, and slots are added in slot order
   const int t = blockIdx.y;
-  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int i = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= d) return;
-  float acc = 0.0f;
-  for (int s = 0; s < k; ++s) {
-    const int pr = t * k + s;
-    if (pair_pos[pr] >= 0) acc = fmaf(gates[pr], z[(size_t)pr * d + i], acc);
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s0 = 0; s0 < k; s0 += 8) {
+    f32x4 v[8];
+    float g[8];
+    bool ok[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int pr = t * k + min(s0 + u, k - 1);  // clamped: always a valid row
+      ok[u] = (s0 + u < k) && pair_pos[pr] >= 0;
+      g[u] = gates[pr];
+      v[u] = *reinterpret_cast<const f32x4*>(z + (size_t)pr * d + i);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (ok[u]) {
+        acc[0] = fmaf(g[u], v[u][0], acc[0]);
+        acc[1] = fmaf(g[u], v[u][1], acc[1]);
+        acc[2] = fmaf(g[u], v[u][2], acc[2]);
+        acc[3] = fmaf(g[u], v[u][3], acc[3]);
+      }
   }
-  float out = acc;
-  if (resid) out = (resid[(size_t)t * d + i] + (shared ? shared[(size_t)t * d + i] : 0.0f)) + acc;
-  y[(size_t)t * d + i] = out;
-  if (y_bf16) y_bf16[(size_t)t * d + i] = f32_to_bf16_rne(out);
+  const size_t o = (size_t)t * d + i;
+  f32x4 out = acc;
+  if (resid) {
+    const f32x4 r = *reinterpret_cast<const f32x4*>(resid + o);
+    const f32x4 sh = shared ? *reinterpret_cast<const f32x4*>(shared + o) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) out[c] = (r[c] + sh[c]) + acc[c];
+  }
+  *reinterpret_cast<f32x4*>(y + o) = out;
+  if (y_bf16) {
+    const uint32_t lo = (uint32_t)f32_to_bf16_rne(out[0]) | ((uint32_t)f32_to_bf16_rne(out[1]) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16_rne(out[2]) | ((uint32_t)f32_to_bf16_rne(out[3]) << 16);
+    if (bf16_vec) {
+      *reinterpret_cast<uint2*>(y_bf16 + o) = make_uint2(lo, hi);
+    } else {
+      y_bf16[o] = (uint16_t)lo;
+      y_bf16[o + 1] = (uint16_t)(lo >> 16);
+      y_bf16[o + 2] = (uint16_t)hi;
+      y_bf16[o + 3] = (uint16_t)(hi >> 16);
+    }
+  }
 }
 
 int bpl_of(int nb) { return nb / lanes_per_row(nb); }
@@ -566,8 +601,11 @@ hipError_t launch_down_gemv(int T, int d, int f, int E, int k, const MxPtrs& w, 
 hipError_t launch_combine(int T, int d, int k, const float* z, const float* gates,
                           const int32_t* pair_pos, const float* resid, const float* shared,
                           float* y, uint16_t* y_bf16, hipStream_t s) {
-  dim3 grid((unsigned)((d + 255) / 256), (unsigned)T);
-  combine_kernel<<<grid, 256, 0, s>>>(T, d, k, z, gates, pair_pos, resid, shared, y, y_bf16);
+  // d is a multiple of 32; y and resid are 16-byte aligned (checked at the boundary)
+  dim3 grid((unsigned)((d / 4 + 255) / 256), (unsigned)T);
+  const int bf16_vec = (reinterpret_cast<uintptr_t>(y_bf16) & 7u) == 0;
+  combine_kernel<<<grid, 256, 0, s>>>(T, d, k, z, gates, pair_pos, resid, shared, y, y_bf16,
+                                      bf16_vec);
   return hipGetLastError();
 }
 
