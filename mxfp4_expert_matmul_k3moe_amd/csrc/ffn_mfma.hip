@@ -23,6 +23,7 @@ namespace k3moe {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BM = kMfmaTileM;     // 64 tokens per full tile
@@ -50,6 +51,23 @@ struct Pipe {
   static constexpr int RING = SG4 ? 2 * kSGroup : 0;  // scale-group slots
   static constexpr int S0 = (kLdsBytes - RING) / BYTES;
   static constexpr int S = S0 < 4 ? S0 : 4;        // stages
+  static_assert(S >= 2, "pipeline needs two stages");
+};
+
+// Gate/up on the gfx950 block-scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4): the MXFP4
+// weights are the FP4 operand as stored (a lane's 16 bytes = one 32-element block of its
+// row, with that block's E8M0 scale), the token is the FP8 operand as two E4M3 terms
+// x = hi * 2^s_hi + lo * 2^s_lo (scales per token row), multiplied in two MFMAs into one
+// fp32 accumulator. No weight decoding instructions at all. Per stage in LDS:
+// [A: MT x 2 terms x 2 halves of 1 KB][weights: kBStage] (+ per-step scale words).
+template <int MT, bool SG4>
+struct MxPipe {
+  static constexpr int ABLK = MT * 4;  // 1-KB token blocks: [m][term][half]
+  static constexpr int ABYTES = ABLK * 1024;
+  static constexpr int BYTES = ABYTES + kBStage + (SG4 ? 0 : kSStage);
+  static constexpr int RING = SG4 ? 2 * kSGroup : 0;
+  static constexpr int S0 = (kLdsBytes - RING) / BYTES;
+  static constexpr int S = S0 < 4 ? S0 : 4;
   static_assert(S >= 2, "pipeline needs two stages");
 };
 
@@ -110,6 +128,8 @@ struct MfmaArgs {
   int T, d, f, k;
   const uint16_t* a_src;  // gate/up: x [T][d]; down: h_hi [P][f]
   const uint16_t* a_lo;   // down: h_lo [P][f]
+  const uint8_t* x8;      // gate/up: x as fp8 E4M3 terms [T][2][d] (hi, lo)
+  const uint8_t* xs8;     // gate/up: E8M0 scale of each term row [T][2]
   const uint8_t *q0, *s0, *q1, *s1;  // gate/up: G and U; down: D (q1 unused)
   const int32_t *offsets, *rows, *act, *n_act, *mtile_off;
   int nblk_n;
@@ -129,6 +149,10 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a, uint8_t* lds, int e
 // work index L is laid out so that the blocks one XCD receives are consecutive in L,
 // and L runs expert-major, then N slice, then M tile, so the M tiles of one weight slice
 // run back to back on one XCD and find that slice in its L2.
+template <int MT, bool SG4>
+__device__ __forceinline__ void mx_gateup_tile(const MfmaArgs& a, uint8_t* lds, int e, int p0,
+                                               int pn, int nb);
+
 template <bool GATEUP>
 __global__ __launch_bounds__(512) void mfma_ffn_kernel(MfmaArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
@@ -155,6 +179,18 @@ __global__ __launch_bounds__(512) void mfma_ffn_kernel(MfmaArgs a) {
   const bool sg4 = ((GATEUP ? a.d : a.f) % (4 * BK)) == 0 &&
                    ((reinterpret_cast<uintptr_t>(a.s0) |
                      reinterpret_cast<uintptr_t>(GATEUP ? a.s1 : a.s0)) & 15u) == 0;
+  if (GATEUP) {
+    if (sg4) {
+      if (cnt <= 16) mx_gateup_tile<1, true>(a, lds, e, p0, pn, nb);
+      else if (cnt <= 32) mx_gateup_tile<2, true>(a, lds, e, p0, pn, nb);
+      else mx_gateup_tile<4, true>(a, lds, e, p0, pn, nb);
+    } else {
+      if (cnt <= 16) mx_gateup_tile<1, false>(a, lds, e, p0, pn, nb);
+      else if (cnt <= 32) mx_gateup_tile<2, false>(a, lds, e, p0, pn, nb);
+      else mx_gateup_tile<4, false>(a, lds, e, p0, pn, nb);
+    }
+    return;
+  }
   if (sg4) {
     if (cnt <= 16) mfma_tile<GATEUP, 1, true>(a, lds, e, p0, pn, nb);
     else if (cnt <= 32) mfma_tile<GATEUP, 2, true>(a, lds, e, p0, pn, nb);
@@ -348,6 +384,217 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a, uint8_t* lds, int e
   }
 }
 
+template <int MT, bool SG4>
+__device__ __forceinline__ void mx_gateup_tile(const MfmaArgs& a, uint8_t* lds, int e, int p0,
+                                               int pn, int nb) {
+  using PP = MxPipe<MT, SG4>;
+  constexpr int S = PP::S, SB = PP::BYTES, AB = PP::ABYTES;
+  const int P = a.T * a.k;
+  const int K = a.d, NR = a.f, KB = K >> 5;
+  const size_t rq = (size_t)(K >> 1);
+  const int nk = K / BK;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ln = lane & 15, g = lane >> 4;
+
+  // token of tile row 16 m + ln (rows past the tile's end repeat its last row)
+  auto tok_of = [&](int m) {
+    const int r = min(16 * m + ln, pn - 1);
+    const int pair = a.rows[p0 + r];
+    return (pair >= 0 && pair < P) ? pair / a.k : 0;
+  };
+  // A loads: wave w < 2 MT stages term (w & 1) of the tokens of M subtile w >> 1, in two
+  // halves; lane (ln, g) takes the 16 bytes the FP8 operand layout puts in its registers:
+  // k = 32 (g >> 1) + 16 (g & 1) (+ 64 for the second half) within the step
+  const bool has_a = wave < 2 * MT;
+  const int am = (wave >> 1) < MT ? (wave >> 1) : 0, at = wave & 1;
+  const uint8_t* asrc =
+      a.x8 + ((size_t)tok_of(am) * 2 + at) * K + 32 * (g >> 1) + 16 * (g & 1);
+  // per-lane E8M0 scales of the token terms of each M subtile (whole-row scales)
+  int sxh[MT], sxl[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int t = tok_of(m);
+    sxh[m] = a.xs8[2 * t];
+    sxl[m] = a.xs8[2 * t + 1];
+  }
+
+  // weight rows as in the bf16 path: lane (ln, g) of tile nt reads block 4 ks + g of row rB
+  const uint8_t* bsrc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    int r = nb * 256 + wave * 32 + (nt & 1) * 16 + ln;
+    const uint8_t* qb = (nt < 2) ? a.q0 : a.q1;
+    r = min(r, NR - 1);
+    bsrc[nt] = qb + ((size_t)e * NR + r) * rq + 16 * g;
+  }
+  const uint8_t* ssrc;
+  {
+    const int snt = lane >> 4, sln = lane & 15;
+    int r = nb * 256 + wave * 32 + (snt & 1) * 16 + sln;
+    const uint8_t* sb = (snt < 2) ? a.s0 : a.s1;
+    r = min(r, NR - 1);
+    ssrc = sb + ((size_t)e * NR + r) * KB;
+  }
+  uint8_t* const sring = lds + S * SB;
+  auto issue = [&](int ks, int slotno) {
+    uint8_t* st = lds + slotno * SB;
+    if (has_a) {
+      const int o = (am * 2 + at) * 2;
+      dma16(asrc + (size_t)ks * BK, st + o * 1024);
+      dma16(asrc + (size_t)ks * BK + 64, st + (o + 1) * 1024);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      dma16(bsrc[nt] + (size_t)ks * 64, st + AB + (wave * NT + nt) * 1024);
+    if (SG4) {
+      if ((ks & 3) == 0) dma16(ssrc + ks * 4, sring + ((ks >> 2) & 1) * kSGroup + wave * 1024);
+    } else {
+      dma4(ssrc + ks * 4, st + AB + kBStage + wave * 256);
+    }
+  };
+  constexpr int OPS_A = 2 + NT + (SG4 ? 0 : 1);
+  constexpr int OPS_NOA = NT + (SG4 ? 0 : 1);
+  auto wait_stage = [&](int ks) {
+    if (ks + S - 2 >= nk) {
+      wait_vm<0>();
+      return;
+    }
+    const int extra = SG4 ? ((ks + S - 2) >> 2) - (ks >> 2) : 0;
+    if (has_a) {
+      if (extra) wait_vm<(S - 2) * OPS_A + 1>();
+      else wait_vm<(S - 2) * OPS_A>();
+    } else {
+      if (extra) wait_vm<(S - 2) * OPS_NOA + 1>();
+      else wait_vm<(S - 2) * OPS_NOA>();
+    }
+  };
+
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) issue(s, s);
+
+  for (int ks = 0; ks < nk; ++ks) {
+    wait_stage(ks);
+    barrier_no_fence();
+    if (ks + S - 1 < nk) issue(ks + S - 1, (ks + S - 1) % S);
+
+    const uint8_t* st = lds + (ks % S) * SB;
+    i32x8 wop[NT];
+    int wsc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const u32x4 q = *reinterpret_cast<const u32x4*>(st + AB + (wave * NT + nt) * 1024 + lane * 16);
+      wop[nt] = i32x8{(int)q[0], (int)q[1], (int)q[2], (int)q[3], 0, 0, 0, 0};
+      wsc[nt] = SG4 ? sring[((ks >> 2) & 1) * kSGroup + wave * 1024 + 16 * (nt * 16 + ln) + 4 * (ks & 3) + g]
+                    : st[AB + kBStage + wave * 256 + 4 * (nt * 16 + ln) + g];
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const uint8_t* xh = st + ((m * 2 + 0) * 2) * 1024 + lane * 16;
+      const uint8_t* xl = st + ((m * 2 + 1) * 2) * 1024 + lane * 16;
+      const u32x4 h0 = *reinterpret_cast<const u32x4*>(xh), h1 = *reinterpret_cast<const u32x4*>(xh + 1024);
+      const u32x4 l0 = *reinterpret_cast<const u32x4*>(xl), l1 = *reinterpret_cast<const u32x4*>(xl + 1024);
+      const i32x8 xhi = {(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
+      const i32x8 xlo = {(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3], (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        acc[m][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wop[nt], xhi, acc[m][nt], 4, 0, 0,
+                                                                       wsc[nt], 0, sxh[m]);
+        acc[m][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wop[nt], xlo, acc[m][nt], 4, 0, 0,
+                                                                       wsc[nt], 0, sxl[m]);
+      }
+    }
+  }
+
+  // epilogue: lane (ln, g) holds weight rows 4 g .. 4 g + 3 of each 16-row tile, token ln
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int row = 16 * m + ln;
+    if (row >= pn) continue;
+    const size_t ob = (size_t)(p0 + row) * a.f;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int j0 = nb * 256 + wave * 32 + nt * 16 + 4 * g;  // f % 4 == 0: all four or none
+      if (j0 < a.f) {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float hv = silu_f32(acc[m][nt][r]) * acc[m][nt + 2][r];
+          hw[r] = f32_to_bf16_rne(hv);
+          lw[r] = f32_to_bf16_rne(hv - bf16_bits_to_f32(hw[r]));
+        }
+        *reinterpret_cast<uint2*>(a.h_out + ob + j0) = make_uint2(hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16));
+        *reinterpret_cast<uint2*>(a.h_lo + ob + j0) = make_uint2(lw[0] | (lw[1] << 16), lw[2] | (lw[3] << 16));
+      }
+    }
+  }
+}
+
+// Token rows -> two FP8 E4M3 terms with one E8M0 scale per term row. With e the exponent
+// that puts the row maximum in [128, 256): y = x 2^-e (exact), hi = RNE_e4m3(y), and the
+// remainder y - hi (exact in fp32) is coded the same way against its own maximum. For a
+// bf16 row every element is then carried to about 2^-22 of the row maximum. A non-finite
+// maximum gives scale byte 255 (NaN). One block per token.
+__global__ __launch_bounds__(256) void x8_prep_kernel(int d, const uint16_t* __restrict__ x,
+                                                      uint8_t* __restrict__ x8,
+                                                      uint8_t* __restrict__ xs8) {
+  __shared__ float red[4];
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint16_t* xr = x + (size_t)t * d;
+  auto block_max = [&](float v) {
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    __syncthreads();
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  };
+  // exponent putting m in [128, 256), or INT_MIN for m == 0, INT_MAX for non-finite m
+  auto top_exp = [](float m) -> int {
+    if (!(m <= 3.0e38f)) return 0x7fffffff;
+    if (m == 0.0f) return -0x7fffffff;
+    return ilogbf(m) - 7;
+  };
+  auto to_e4m3 = [](float v) { return __builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xFF; };
+  auto from_e4m3 = [](int q) { return __builtin_amdgcn_cvt_f32_fp8(q, 0); };
+
+  float mx = 0.0f;
+  for (int i = tid; i < d; i += 256) mx = fmaxf(mx, fabsf(bf16_bits_to_f32(xr[i])));
+  mx = block_max(mx);
+  const int eh0 = top_exp(mx);
+  const bool bad = eh0 == 0x7fffffff;
+  const int sh = bad ? 255 : min(max(eh0 + 127, 0), 254);
+  const int eh = sh - 127;  // exponent actually applied (row maximum may sit below 128)
+
+  float rm = 0.0f;
+  for (int i = tid; i < d; i += 256) {
+    const float y = ldexpf(bf16_bits_to_f32(xr[i]), -eh);
+    rm = fmaxf(rm, fabsf(y - from_e4m3(to_e4m3(y))));
+  }
+  rm = block_max(rm);
+  const int er0 = top_exp(rm);  // relative to the hi scale
+  const int sl = bad ? 255 : min(max(sh + max(er0, -300), 0), 254);
+  const int er = sl - sh;
+  uint8_t* hi = x8 + (size_t)t * 2 * d;
+  uint8_t* lo = hi + d;
+  for (int i = tid; i < d; i += 256) {
+    const float y = ldexpf(bf16_bits_to_f32(xr[i]), -eh);
+    const int q = to_e4m3(y);
+    const float r = y - from_e4m3(q);
+    hi[i] = (uint8_t)q;
+    lo[i] = (uint8_t)to_e4m3(ldexpf(r, -er));
+  }
+  if (tid == 0) {
+    xs8[2 * t] = (uint8_t)sh;
+    xs8[2 * t + 1] = (uint8_t)sl;
+  }
+}
+
 }  // namespace
 
 int mfma_mtiles_bound(int T, int E, int k) {
@@ -361,9 +608,11 @@ bool mfma_shape_supported(int d, int f) { return d % BK == 0 && f % BK == 0; }
 hipError_t launch_gateup_mfma(int T, int d, int f, int E, int k, const uint16_t* x,
                               const MxPtrs& w, const int32_t* offsets, const int32_t* rows,
                               const int32_t* act, const int32_t* n_act,
-                              const int32_t* mtile_off, uint16_t* h, hipStream_t s) {
+                              const int32_t* mtile_off, uint16_t* h, uint8_t* x8, uint8_t* xs8,
+                              hipStream_t s) {
+  x8_prep_kernel<<<T, 256, 0, s>>>(d, x, x8, xs8);
   MfmaArgs a{};
-  a.T = T; a.d = d; a.f = f; a.k = k; a.a_src = x;
+  a.T = T; a.d = d; a.f = f; a.k = k; a.a_src = x; a.x8 = x8; a.xs8 = xs8;
   a.q0 = w.gate_q; a.s0 = w.gate_s; a.q1 = w.up_q; a.s1 = w.up_s;
   a.offsets = offsets; a.rows = rows; a.act = act; a.n_act = n_act; a.mtile_off = mtile_off;
   a.nblk_n = (f + 255) / 256;

@@ -57,7 +57,7 @@ constexpr int kMfmaMinTokens = 16;
 
 enum Region {
   R_PART, R_IDS, R_GATES, R_OFFS, R_ROWS, R_ACT, R_NACT, R_PPOS, R_PEXP, R_HIST, R_BASE,
-  R_MASK, R_H, R_Z, R_XHAT, R_HSH, R_SSH, R_MTILE, R_COUNT
+  R_MASK, R_H, R_Z, R_XHAT, R_HSH, R_SSH, R_MTILE, R_X8, R_XS, R_COUNT
 };
 
 struct Layout {
@@ -97,6 +97,8 @@ Layout layout_for(const k3moe_dims& dm, int64_t T) {
   sz[R_HSH] = (size_t)(T * f * 4);
   sz[R_SSH] = (size_t)(T * d * 4);
   sz[R_MTILE] = (size_t)(E + 1) * 4;
+  sz[R_X8] = (size_t)(T * 2 * d);  // token rows as two FP8 terms
+  sz[R_XS] = (size_t)(T * 2);      // their E8M0 scales
   Layout L;
   size_t o = 0;
   for (int r = 0; r < R_COUNT; ++r) {
@@ -253,7 +255,8 @@ int run_ffn(const k3moe_dims& dm, int32_t T, const void* x, int xf32,
       Probe probe(K3MOE_KERNEL_GATE_UP, s);
       rc = hip_check(k3moe::launch_gateup_mfma(T, d, f, E, k, static_cast<const uint16_t*>(x), w,
                                                offsets, rows, ws.at<int32_t>(R_ACT),
-                                               ws.at<int32_t>(R_NACT), mt, hb, s),
+                                               ws.at<int32_t>(R_NACT), mt, hb,
+                                               ws.at<uint8_t>(R_X8), ws.at<uint8_t>(R_XS), s),
                      "gate/up (MFMA)");
     }
     if (rc) return rc;

@@ -90,7 +90,8 @@ bool mfma_shape_supported(int d, int f);
 hipError_t launch_gateup_mfma(int T, int d, int f, int E, int k, const uint16_t* x,
                               const MxPtrs& w, const int32_t* offsets, const int32_t* rows,
                               const int32_t* act, const int32_t* n_act,
-                              const int32_t* mtile_off, uint16_t* h, hipStream_t s);
+                              const int32_t* mtile_off, uint16_t* h, uint8_t* x8, uint8_t* xs8,
+                              hipStream_t s);
 // z (fp32 [P][d], pair-indexed) = D h, from both halves of h.
 hipError_t launch_down_mfma(int T, int d, int f, int E, int k, const MxPtrs& w,
                             const uint16_t* h, const int32_t* offsets, const int32_t* rows,
