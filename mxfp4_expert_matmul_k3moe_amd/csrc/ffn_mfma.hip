@@ -71,6 +71,18 @@ struct MxPipe {
   static_assert(S >= 2, "pipeline needs two stages");
 };
 
+// Same, with the weight scales held in registers; LDS keeps only a 2-KB staging slot per
+// wave through which the next scale chunk passes.
+constexpr int kScaleStage = 2048;
+template <int MT>
+struct MxPipeR {
+  static constexpr int ABYTES = MT * 4 * 1024;
+  static constexpr int BYTES = ABYTES + kBStage;
+  static constexpr int S0 = (kLdsBytes - kWaves * kScaleStage) / BYTES;
+  static constexpr int S = S0 < 4 ? S0 : 4;
+  static_assert(S >= 2, "pipeline needs two stages");
+};
+
 // Active expert owning logical block L (blocks of expert a start at mtile_off[a] * nb).
 __device__ __forceinline__ int tile_expert_blocks(const int32_t* mtile_off, int n_act, int nb,
                                                   int L) {
@@ -152,6 +164,9 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a, uint8_t* lds, int e
 template <int MT, bool SG4>
 __device__ __forceinline__ void mx_gateup_tile(const MfmaArgs& a, uint8_t* lds, int e, int p0,
                                                int pn, int nb);
+template <int MT>
+__device__ __forceinline__ void mx_gateup_tile_sr(const MfmaArgs& a, uint8_t* lds, int e, int p0,
+                                                  int pn, int nb);
 
 template <bool GATEUP>
 __global__ __launch_bounds__(512) void mfma_ffn_kernel(MfmaArgs a) {
@@ -181,9 +196,9 @@ __global__ __launch_bounds__(512) void mfma_ffn_kernel(MfmaArgs a) {
                      reinterpret_cast<uintptr_t>(GATEUP ? a.s1 : a.s0)) & 15u) == 0;
   if (GATEUP) {
     if (sg4) {
-      if (cnt <= 16) mx_gateup_tile<1, true>(a, lds, e, p0, pn, nb);
-      else if (cnt <= 32) mx_gateup_tile<2, true>(a, lds, e, p0, pn, nb);
-      else mx_gateup_tile<4, true>(a, lds, e, p0, pn, nb);
+      if (cnt <= 16) mx_gateup_tile_sr<1>(a, lds, e, p0, pn, nb);
+      else if (cnt <= 32) mx_gateup_tile_sr<2>(a, lds, e, p0, pn, nb);
+      else mx_gateup_tile_sr<4>(a, lds, e, p0, pn, nb);
     } else {
       if (cnt <= 16) mx_gateup_tile<1, false>(a, lds, e, p0, pn, nb);
       else if (cnt <= 32) mx_gateup_tile<2, false>(a, lds, e, p0, pn, nb);
@@ -521,6 +536,192 @@ __device__ __forceinline__ void mx_gateup_tile(const MfmaArgs& a, uint8_t* lds, 
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int j0 = nb * 256 + wave * 32 + nt * 16 + 4 * g;  // f % 4 == 0: all four or none
+      if (j0 < a.f) {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float hv = silu_f32(acc[m][nt][r]) * acc[m][nt + 2][r];
+          hw[r] = f32_to_bf16_rne(hv);
+          lw[r] = f32_to_bf16_rne(hv - bf16_bits_to_f32(hw[r]));
+        }
+        *reinterpret_cast<uint2*>(a.h_out + ob + j0) = make_uint2(hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16));
+        *reinterpret_cast<uint2*>(a.h_lo + ob + j0) = make_uint2(lw[0] | (lw[1] << 16), lw[2] | (lw[3] << 16));
+      }
+    }
+  }
+}
+
+// Gate/up tile for K % 512 == 0 with the weight scales kept in registers. Fetching a
+// 16-byte scale group every 4 K steps touches each 128-byte scale line eight times, far
+// enough apart that the line has left L2 in between; here the scales move 32 K steps
+// (128 blocks, 128 bytes per row) at a time, so each line is fetched once. Lane (ln, g) of
+// tile nt holds bytes [32 g, 32 g + 32) of its row's chunk; the 4 bytes of step j are
+// dword j & 7 of lane (ln, j >> 3), fetched with one ds_bpermute, and lane g keeps byte g.
+// The next chunk comes in during the current one, one tile per 8 K steps: a DMA into the
+// wave's staging slot, read into registers S steps later, once the pipeline's own wait has
+// covered it.
+template <int MT>
+__device__ __forceinline__ void mx_gateup_tile_sr(const MfmaArgs& a, uint8_t* lds, int e, int p0,
+                                                  int pn, int nb) {
+  using PP = MxPipeR<MT>;
+  constexpr int S = PP::S, SB = PP::BYTES, AB = PP::ABYTES;
+  static_assert(S <= 7, "scale read-back must land in the same 8-step group");
+  const int P = a.T * a.k;
+  const int K = a.d, NR = a.f, KB = K >> 5;
+  const size_t rq = (size_t)(K >> 1);
+  const int nk = K / BK;            // multiple of 4
+  const int nch = (KB + 127) >> 7;  // scale chunks of 32 K steps
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ln = lane & 15, g = lane >> 4;
+
+  auto tok_of = [&](int m) {
+    const int r = min(16 * m + ln, pn - 1);
+    const int pair = a.rows[p0 + r];
+    return (pair >= 0 && pair < P) ? pair / a.k : 0;
+  };
+  const bool has_a = wave < 2 * MT;
+  const int am = (wave >> 1) < MT ? (wave >> 1) : 0, at = wave & 1;
+  const uint8_t* asrc =
+      a.x8 + ((size_t)tok_of(am) * 2 + at) * K + 32 * (g >> 1) + 16 * (g & 1);
+  int sxh[MT], sxl[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int t = tok_of(m);
+    sxh[m] = a.xs8[2 * t];
+    sxl[m] = a.xs8[2 * t + 1];
+  }
+  auto row_of = [&](int nt) { return min(nb * 256 + wave * 32 + (nt & 1) * 16 + ln, NR - 1); };
+  const uint8_t* bsrc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+    bsrc[nt] = ((nt < 2) ? a.q0 : a.q1) + ((size_t)e * NR + row_of(nt)) * rq + 16 * g;
+  // this lane's 16-byte piece h of tile nt's scale chunk c (pieces past the row: offset 0)
+  auto spiece = [&](int nt, int c, int h) {
+    const int off = 128 * c + 32 * g + 16 * h;
+    return ((nt < 2) ? a.s0 : a.s1) + ((size_t)e * NR + row_of(nt)) * KB + (off < KB ? off : 0);
+  };
+  uint8_t* const stg = lds + S * SB + wave * kScaleStage;
+  auto issue = [&](int ks, int slotno) {
+    uint8_t* st = lds + slotno * SB;
+    if (has_a) {
+      const int o = (am * 2 + at) * 2;
+      dma16(asrc + (size_t)ks * BK, st + o * 1024);
+      dma16(asrc + (size_t)ks * BK + 64, st + (o + 1) * 1024);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      dma16(bsrc[nt] + (size_t)ks * 64, st + AB + (wave * NT + nt) * 1024);
+  };
+  constexpr int OPS_A = 2 + NT, OPS_NOA = NT, OPS_SC = 2;
+  // stage ks complete; `late`: a scale DMA was issued after stage ks (it is newer)
+  auto wait_stage = [&](int ks, bool late) {
+    if (ks + S - 2 >= nk) {
+      wait_vm<0>();
+      return;
+    }
+    if (has_a) {
+      if (late) wait_vm<(S - 2) * OPS_A + OPS_SC>();
+      else wait_vm<(S - 2) * OPS_A>();
+    } else {
+      if (late) wait_vm<(S - 2) * OPS_NOA + OPS_SC>();
+      else wait_vm<(S - 2) * OPS_NOA>();
+    }
+  };
+
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // chunk 0 straight into registers, issued ahead of the prologue; the asm below makes the
+  // compiler wait for it there (exact count) rather than inside the loop
+  u32x4 scur[NT][2], snxt[NT][2];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) scur[nt][h] = *reinterpret_cast<const u32x4*>(spiece(nt, 0, h));
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) issue(s, s);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(scur[nt][h]));
+
+  for (int ks0 = 0; ks0 < nk; ks0 += 8) {
+    const int q = (ks0 & 31) >> 3;  // group within the chunk = tile whose next chunk moves
+    const int c = ks0 >> 5;
+    if (q == 0 && c > 0) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        scur[nt][0] = snxt[nt][0];
+        scur[nt][1] = snxt[nt][1];
+      }
+    }
+    const bool pf = c + 1 < nch;  // whole chunk ahead of us: all 8 steps of the group exist
+    const int baddr = (ln + 16 * q) * 4;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int ks = ks0 + u;
+      if (ks < nk) {
+        wait_stage(ks, pf && u >= 1 && u <= S - 1);
+        barrier_no_fence();
+        if (ks + S - 1 < nk) issue(ks + S - 1, (ks + S - 1) % S);
+        if (pf && u == 0) {
+          // the previous tile's read-back (u == S of the last group) has returned
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          dma16(spiece(q, c + 1, 0), stg);
+          dma16(spiece(q, c + 1, 1), stg + 1024);
+        }
+        if (pf && u == S) {
+          const u32x4 v0 = *reinterpret_cast<const u32x4*>(stg + lane * 16);
+          const u32x4 v1 = *reinterpret_cast<const u32x4*>(stg + 1024 + lane * 16);
+          switch (q) {
+            case 0: snxt[0][0] = v0; snxt[0][1] = v1; break;
+            case 1: snxt[1][0] = v0; snxt[1][1] = v1; break;
+            case 2: snxt[2][0] = v0; snxt[2][1] = v1; break;
+            default: snxt[3][0] = v0; snxt[3][1] = v1; break;
+          }
+        }
+
+        const uint8_t* st = lds + (ks % S) * SB;
+        i32x8 wop[NT];
+        int wsc[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const u32x4 qv = *reinterpret_cast<const u32x4*>(st + AB + (wave * NT + nt) * 1024 + lane * 16);
+          wop[nt] = i32x8{(int)qv[0], (int)qv[1], (int)qv[2], (int)qv[3], 0, 0, 0, 0};
+          wsc[nt] = (int)((uint32_t)__builtin_amdgcn_ds_bpermute(baddr, (int)scur[nt][u >> 2][u & 3]) >> (8 * g));
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const uint8_t* xh = st + ((m * 2 + 0) * 2) * 1024 + lane * 16;
+          const uint8_t* xl = st + ((m * 2 + 1) * 2) * 1024 + lane * 16;
+          const u32x4 h0 = *reinterpret_cast<const u32x4*>(xh), h1 = *reinterpret_cast<const u32x4*>(xh + 1024);
+          const u32x4 l0 = *reinterpret_cast<const u32x4*>(xl), l1 = *reinterpret_cast<const u32x4*>(xl + 1024);
+          const i32x8 xhi = {(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
+          const i32x8 xlo = {(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3], (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            acc[m][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wop[nt], xhi, acc[m][nt], 4, 0, 0,
+                                                                           wsc[nt], 0, sxh[m]);
+            acc[m][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wop[nt], xlo, acc[m][nt], 4, 0, 0,
+                                                                           wsc[nt], 0, sxl[m]);
+          }
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int row = 16 * m + ln;
+    if (row >= pn) continue;
+    const size_t ob = (size_t)(p0 + row) * a.f;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int j0 = nb * 256 + wave * 32 + nt * 16 + 4 * g;
       if (j0 < a.f) {
         uint32_t hw[4], lw[4];
 #pragma unroll
