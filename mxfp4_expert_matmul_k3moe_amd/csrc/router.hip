@@ -314,7 +314,10 @@ constexpr int kMaxChunks = 32;  // d <= 16384 in 512-row chunks
 constexpr int kMaxCand = 2048;  // candidate buffer; the exact ranking covers any count
 
 // One block per token of NT = blockDim.x threads (a multiple of 64, at most 256): thread t
-// holds the logits of experts t + NT*j (j < KPT) in registers.
+// holds the logits of experts t + NT*j (j < KPT) in registers. WIDE: the block has 1024
+// threads, which form the logits one expert per thread into LDS (every partial in flight
+// at once); the first 256 threads then read their keys back and the rest only keep the
+// block's barrier count.
 //  1. logits = sum of the fp64 partials in chunk order (+ bias), as order keys;
 //  2. each wave sorts its 64 lane maxima (bitonic network over lanes): the k-th best of
 //     them is at most the k-th best of all E, so the best such bound over the waves is a
@@ -333,8 +336,8 @@ __device__ __forceinline__ double key_to_double(uint64_t kv) {
   return __longlong_as_double((long long)b);
 }
 
-template <int KPT>
-__global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
+template <int KPT, bool WIDE>
+__global__ __launch_bounds__(WIDE ? 1024 : 256) void route_topk_kernel(int T, int E, int k,
                                                           const double* __restrict__ part,
                                                           int nsum, const float* __restrict__ bias,
                                                           int32_t* __restrict__ ids,
@@ -348,47 +351,86 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int k,
   __shared__ int s_ids[kMaxSlots];
   const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int NT = blockDim.x, nw = NT >> 6;
+  const int NT = WIDE ? 256 : blockDim.x, nw = NT >> 6;
 
-  // 1. logits: all loads of a chunk issued before any add; chunks summed in order
-  constexpr int CB = (64 / KPT) > 1 ? (64 / KPT) : 1;  // chunks whose loads go out together
-  float bv[KPT];  // bias requested together with the first partials
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) bv[j] = bias ? bias[min(tid + NT * j, E - 1)] : 0.0f;
-  double acc[KPT];
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) acc[j] = 0.0;
-  for (int c0 = 0; c0 < nsum; c0 += CB) {
-    double v[CB][KPT];
-#pragma unroll
-    for (int u = 0; u < CB; ++u)
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        const int e = min(tid + NT * j, E - 1);
-        const int c = min(c0 + u, nsum - 1);
-        v[u][j] = part[((size_t)c * T + t) * E + e];  // clamped: always a valid address
-      }
-#pragma unroll
-    for (int u = 0; u < CB; ++u)
-#pragma unroll
-      for (int j = 0; j < KPT; ++j)
-        if (c0 + u < nsum) acc[j] = (c0 + u == 0) ? v[u][j] : acc[j] + v[u][j];
-  }
   uint64_t key[KPT];
   int nan_here = 0;
   uint64_t bkey = 0;
   int bi = -1;
+  if (WIDE) {
+    // 1. logits, one expert per thread of the whole block (every chunk's load in flight at
+    //    once), chunks summed in order; the first NT threads carry on from the LDS keys
+    for (int e = tid; e < E; e += blockDim.x) {
+      const float b = bias ? bias[e] : 0.0f;
+      double l = 0.0;
+      for (int c0 = 0; c0 < nsum; c0 += 16) {
+        double v[16];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const int e = tid + NT * j;
-    if (e < E) {
-      const double l = bias ? acc[j] + (double)bv[j] : acc[j];
-      nan_here |= (l != l);
-      key[j] = order_key(l);
-      keys[e] = key[j];
-      if (bi < 0 || better(key[j], e, bkey, bi)) { bkey = key[j]; bi = e; }
-    } else {
-      key[j] = 0;
+        for (int u = 0; u < 16; ++u) v[u] = part[((size_t)min(c0 + u, nsum - 1) * T + t) * E + e];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (c0 + u < nsum) l = (c0 + u == 0) ? v[u] : l + v[u];
+      }
+      if (bias) l += (double)b;
+      keys[e] = order_key(l);  // NaN -> key 0, which no number maps to
+    }
+    __syncthreads();
+    if (tid >= NT) {
+      // loader-only waves: match the three block barriers below (four with a bucket)
+      __syncthreads();
+      __syncthreads();
+      __syncthreads();
+      if (bk.offsets) __syncthreads();
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int e = tid + NT * j;
+      if (e < E) {
+        key[j] = keys[e];
+        nan_here |= (key[j] == 0ull);
+        if (bi < 0 || better(key[j], e, bkey, bi)) { bkey = key[j]; bi = e; }
+      } else {
+        key[j] = 0;
+      }
+    }
+  } else {
+    // 1. logits: all loads of a chunk issued before any add; chunks summed in order
+    constexpr int CB = (64 / KPT) > 1 ? (64 / KPT) : 1;  // chunks whose loads go out together
+    float bv[KPT];  // bias requested together with the first partials
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) bv[j] = bias ? bias[min(tid + NT * j, E - 1)] : 0.0f;
+    double acc[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) acc[j] = 0.0;
+    for (int c0 = 0; c0 < nsum; c0 += CB) {
+      double v[CB][KPT];
+#pragma unroll
+      for (int u = 0; u < CB; ++u)
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+          const int e = min(tid + NT * j, E - 1);
+          const int c = min(c0 + u, nsum - 1);
+          v[u][j] = part[((size_t)c * T + t) * E + e];  // clamped: always a valid address
+        }
+#pragma unroll
+      for (int u = 0; u < CB; ++u)
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+          if (c0 + u < nsum) acc[j] = (c0 + u == 0) ? v[u][j] : acc[j] + v[u][j];
+    }
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int e = tid + NT * j;
+      if (e < E) {
+        const double l = bias ? acc[j] + (double)bv[j] : acc[j];
+        nan_here |= (l != l);
+        key[j] = order_key(l);
+        keys[e] = key[j];
+        if (bi < 0 || better(key[j], e, bkey, bi)) { bkey = key[j]; bi = e; }
+      } else {
+        key[j] = 0;
+      }
     }
   }
 
@@ -599,14 +641,23 @@ hipError_t launch_route_topk(int T, int E, int k, const double* part, int nsum,
     b.n_act = bucket1->n_act; b.pair_pos = bucket1->pair_pos; b.pair_exp = bucket1->pair_exp;
     b.mtile_off = bucket1->mtile_off;
   }
-  // 256 threads (four waves) per token, up to 16 experts per thread
+  // four waves per token, up to 16 experts per thread; for few tokens (latency-bound) and
+  // more than 256 experts the logits are first formed by a 1024-thread block, one expert
+  // per thread
   const int kpt = (E + 255) / 256;
   const int nt = 256;
-  if (kpt <= 1) route_topk_kernel<1><<<T, nt, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
-  else if (kpt <= 2) route_topk_kernel<2><<<T, nt, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
-  else if (kpt <= 4) route_topk_kernel<4><<<T, nt, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
-  else if (kpt <= 8) route_topk_kernel<8><<<T, nt, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
-  else route_topk_kernel<16><<<T, nt, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
+  if (kpt > 1 && T <= kRouterGemvMaxT) {
+    if (kpt <= 2) route_topk_kernel<2, true><<<T, 1024, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
+    else if (kpt <= 4) route_topk_kernel<4, true><<<T, 1024, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
+    else if (kpt <= 8) route_topk_kernel<8, true><<<T, 1024, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
+    else route_topk_kernel<16, true><<<T, 1024, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
+    return hipGetLastError();
+  }
+  if (kpt <= 1) route_topk_kernel<1, false><<<T, nt, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
+  else if (kpt <= 2) route_topk_kernel<2, false><<<T, nt, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
+  else if (kpt <= 4) route_topk_kernel<4, false><<<T, nt, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
+  else if (kpt <= 8) route_topk_kernel<8, false><<<T, nt, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
+  else route_topk_kernel<16, false><<<T, nt, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
   return hipGetLastError();
 }
 
