@@ -741,13 +741,17 @@ __device__ __forceinline__ void mx_gateup_tile_sr(const MfmaArgs& a, uint8_t* ld
 // that puts the row maximum in [128, 256): y = x 2^-e (exact), hi = RNE_e4m3(y), and the
 // remainder y - hi (exact in fp32) is coded the same way against its own maximum. For a
 // bf16 row every element is then carried to about 2^-22 of the row maximum. A non-finite
-// maximum gives scale byte 255 (NaN). One block per token.
+// maximum gives scale byte 255 (NaN). One block per token; each thread holds up to
+// kPrepChunks 4-element pieces of the row in registers through the three sweeps (rows
+// longer than 256 * 4 * kPrepChunks are read again per sweep).
+constexpr int kPrepChunks = 8;
 __global__ __launch_bounds__(256) void x8_prep_kernel(int d, const uint16_t* __restrict__ x,
                                                       uint8_t* __restrict__ x8,
                                                       uint8_t* __restrict__ xs8) {
   __shared__ float red[4];
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint16_t* xr = x + (size_t)t * d;
+  const uint2* xr = reinterpret_cast<const uint2*>(x + (size_t)t * d);  // d % 4 == 0
+  const int nq = d >> 2;
   auto block_max = [&](float v) {
     for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
     __syncthreads();
@@ -763,9 +767,35 @@ __global__ __launch_bounds__(256) void x8_prep_kernel(int d, const uint16_t* __r
   };
   auto to_e4m3 = [](float v) { return __builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xFF; };
   auto from_e4m3 = [](int q) { return __builtin_amdgcn_cvt_f32_fp8(q, 0); };
+  auto unpack = [](uint2 v, float f[4]) {
+    f[0] = bf16_bits_to_f32(v.x & 0xFFFFu);
+    f[1] = bf16_bits_to_f32(v.x >> 16);
+    f[2] = bf16_bits_to_f32(v.y & 0xFFFFu);
+    f[3] = bf16_bits_to_f32(v.y >> 16);
+  };
+  const bool cached = nq <= 256 * kPrepChunks;
+  uint2 reg[kPrepChunks];
+  if (cached) {
+#pragma unroll
+    for (int c = 0; c < kPrepChunks; ++c) {
+      const int q = tid + 256 * c;
+      reg[c] = q < nq ? xr[q] : make_uint2(0u, 0u);
+    }
+  }
+  // piece c of this thread (c-th of the sweep), from registers or memory
+  auto piece = [&](int c, int q) { return cached ? reg[c] : xr[q]; };
 
   float mx = 0.0f;
-  for (int i = tid; i < d; i += 256) mx = fmaxf(mx, fabsf(bf16_bits_to_f32(xr[i])));
+  for (int q0 = 0; q0 < nq; q0 += 256 * kPrepChunks)
+#pragma unroll
+    for (int c = 0; c < kPrepChunks; ++c) {
+      const int q = q0 + tid + 256 * c;
+      if (q < nq) {
+        float f[4];
+        unpack(piece(c, q), f);
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(f[0]), fabsf(f[1])), fmaxf(fabsf(f[2]), fabsf(f[3]))));
+      }
+    }
   mx = block_max(mx);
   const int eh0 = top_exp(mx);
   const bool bad = eh0 == 0x7fffffff;
@@ -773,23 +803,45 @@ __global__ __launch_bounds__(256) void x8_prep_kernel(int d, const uint16_t* __r
   const int eh = sh - 127;  // exponent actually applied (row maximum may sit below 128)
 
   float rm = 0.0f;
-  for (int i = tid; i < d; i += 256) {
-    const float y = ldexpf(bf16_bits_to_f32(xr[i]), -eh);
-    rm = fmaxf(rm, fabsf(y - from_e4m3(to_e4m3(y))));
-  }
+  for (int q0 = 0; q0 < nq; q0 += 256 * kPrepChunks)
+#pragma unroll
+    for (int c = 0; c < kPrepChunks; ++c) {
+      const int q = q0 + tid + 256 * c;
+      if (q < nq) {
+        float f[4];
+        unpack(piece(c, q), f);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float y = ldexpf(f[i], -eh);
+          rm = fmaxf(rm, fabsf(y - from_e4m3(to_e4m3(y))));
+        }
+      }
+    }
   rm = block_max(rm);
   const int er0 = top_exp(rm);  // relative to the hi scale
   const int sl = bad ? 255 : min(max(sh + max(er0, -300), 0), 254);
   const int er = sl - sh;
-  uint8_t* hi = x8 + (size_t)t * 2 * d;
-  uint8_t* lo = hi + d;
-  for (int i = tid; i < d; i += 256) {
-    const float y = ldexpf(bf16_bits_to_f32(xr[i]), -eh);
-    const int q = to_e4m3(y);
-    const float r = y - from_e4m3(q);
-    hi[i] = (uint8_t)q;
-    lo[i] = (uint8_t)to_e4m3(ldexpf(r, -er));
-  }
+  uint32_t* hi = reinterpret_cast<uint32_t*>(x8 + (size_t)t * 2 * d);
+  uint32_t* lo = reinterpret_cast<uint32_t*>(x8 + (size_t)t * 2 * d + d);
+  for (int q0 = 0; q0 < nq; q0 += 256 * kPrepChunks)
+#pragma unroll
+    for (int c = 0; c < kPrepChunks; ++c) {
+      const int q = q0 + tid + 256 * c;
+      if (q < nq) {
+        float f[4];
+        unpack(piece(c, q), f);
+        uint32_t wh = 0, wl = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float y = ldexpf(f[i], -eh);
+          const int qh = to_e4m3(y);
+          wh |= (uint32_t)qh << (8 * i);
+          wl |= (uint32_t)to_e4m3(ldexpf(y - from_e4m3(qh), -er)) << (8 * i);
+        }
+        hi[q] = wh;
+        lo[q] = wl;
+      }
+    }
   if (tid == 0) {
     xs8[2 * t] = (uint8_t)sh;
     xs8[2 * t + 1] = (uint8_t)sl;
