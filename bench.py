@@ -106,7 +106,10 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode", choices=["decode", "batched", "prefill"])
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "batched", "prefill", "stack8"])
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="override the workload's token count (e.g. a prefill chunk sweep)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB megabytes 20 times (counter scale)")
     ap.add_argument("--token-sets", type=int, default=64)
@@ -139,6 +142,10 @@ def main() -> int:
     from k3gen.workloads import WORKLOADS
 
     w = WORKLOADS[args.workload]
+    if args.tokens:
+        w = w.with_(T=args.tokens)
+    if w.block:
+        return bench_stack(args, w)
     dev = torch.device("cuda:0")
     dims = k3.make_dims(w.d, w.f, w.E, w.k)
     ex = k3.MxExperts(**gdev.experts(w, 0, dev))
@@ -198,17 +205,7 @@ def main() -> int:
 
     # HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE record, used only while
     # the kernel source it was measured on is unchanged
-    traffic = None
-    prof_traffic = os.path.join(ROOT, "profiles", "gateup_decode_traffic.txt")
-    if args.workload == "decode" and os.path.exists(prof_traffic):
-        tr = {}
-        with open(prof_traffic) as fh:
-            for line in fh:
-                if ":" in line and not line.startswith("#"):
-                    key, val = line.split(":", 1)
-                    tr[key.strip()] = val.strip()
-        if tr.get("kernel_source_hash") == _kernel_hash():
-            traffic = int(tr["bytes_per_launch"])
+    traffic = decode_traffic() if args.workload == "decode" and not args.tokens else None
 
     if w.T <= 64:  # decode-like: weight stream
         value, unit = bytes_timed / (t1 - t0) / 1e9, "GB/s"
@@ -271,6 +268,120 @@ def main() -> int:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
     else:
         out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def decode_traffic():
+    """HBM bytes per launch of the T=1 gate/up kernel from the committed FETCH_SIZE /
+    WRITE_SIZE record, used only while the kernel source it was measured on is unchanged."""
+    prof_traffic = os.path.join(ROOT, "profiles", "gateup_decode_traffic.txt")
+    if not os.path.exists(prof_traffic):
+        return None
+    tr = {}
+    with open(prof_traffic) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                tr[key.strip()] = val.strip()
+    if tr.get("kernel_source_hash") != _kernel_hash():
+        return None
+    return int(tr["bytes_per_launch"])
+
+
+def bench_stack(args, w) -> int:
+    """Config 5: one token through `w.layers` resident blocks (RMSNorm -> routed MoE + bf16
+    shared SwiGLU -> residual), the fp32 residual chained from block to block. `value` =
+    per-token weight stream (per block: k selected experts + router + shared expert) / step
+    time."""
+    import numpy as np
+    import torch
+
+    import mxfp4_expert_matmul_k3moe_amd as k3
+    from k3gen import device as gdev
+
+    dev = torch.device("cuda:0")
+    dims = k3.make_dims(w.d, w.f, w.E, w.k)
+    layers = []
+    for l in range(w.layers):
+        ex = k3.MxExperts(**gdev.experts(w, l, dev))
+        b = gdev.block_extras(w, l, dev)
+        blk = k3.BlockWeights(b["rms_gamma"], b["sh_gate"], b["sh_up"], b["sh_down"], 1e-6)
+        layers.append((gdev.router_w(w, l, dev), gdev.bias(w, l, dev), ex, blk))
+    nsets = max(1, min(args.token_sets, 16))
+    h0 = torch.stack([torch.from_numpy(w.resid0(token_set=i)).to(dev) for i in range(nsets)])
+    ws = k3.make_workspace(dims, w.T, dev)
+    hb = [torch.empty((w.T, w.d), dtype=torch.float32, device=dev) for _ in range(2)]
+    ids = torch.empty((w.layers, w.T, w.k), dtype=torch.int32, device=dev)
+    gates = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+
+    def step(i):
+        h = h0[i % nsets]
+        for l, (wr, bias, ex, blk) in enumerate(layers):
+            y = hb[l % 2]
+            k3.layer_forward(dims, h, wr, bias, ex, blk, y=y, ids=ids[l], gates=gates, ws=ws)
+            h = y
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ids_np = ids.cpu().numpy()
+    distinct = [len(np.unique(ids_np[l])) for l in range(w.layers)]
+    router_bytes, shared_bytes = w.d * w.E * 2, 3 * w.d * w.f * 2
+    bytes_step = sum(n * w.expert_bytes + router_bytes + shared_bytes for n in distinct)
+
+    hip = Hip()
+    nprobe = min(args.steps, 50)
+    kern = {}
+    for which, name in ((k3.KERNEL_GATE_UP, "gate_up"), (k3.KERNEL_DOWN, "down")):
+        evs = [(hip.event(), hip.event()) for _ in range(nprobe)]
+        for i in range(nprobe):
+            k3.time_next_kernel(which, evs[i][0], evs[i][1])  # the first block's launch
+            step(args.warmup + i)
+        torch.cuda.synchronize()
+        times = [hip.elapsed_ms(a, b) for a, b in evs]
+        for a, b in evs:
+            hip.destroy(a)
+            hip.destroy(b)
+        kern[name] = sum(times) / len(times)
+    gu_bytes = w.k * 2 * w.f * (w.d // 2 + w.d // 32)
+    dn_bytes = w.k * w.d * (w.f // 2 + w.f // 32)
+    value = bytes_step * args.steps / (t1 - t0) / 1e9
+    ach = gu_bytes / (kern["gate_up"] * 1e-3) / 1e9
+    out = {
+        "metric": "MoE layer MXFP4 weight-stream GB/s (decode) + TFLOP/s (prefill), % of peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4*bf16->fp32 (router fp64; shared expert bf16)",
+        "data": "synthetic",
+        "config": {"workload": f"stack8: {workload_desc(w)} layers={w.layers}, block "
+                               "(RMSNorm, shared expert, residual)",
+                   "bytes_per_step": int(bytes_step), "token_sets": nsets},
+        "roofline": {"bound": "hbm",
+                     "kernel": "gateup_decode_kernel (MXFP4 gate/up GEMV + SwiGLU)",
+                     "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": decode_traffic(),
+                     "bytes_per_launch": int(gu_bytes),
+                     "avg_launch_us": round(kern["gate_up"] * 1e3, 2)},
+        "kernels": {"down_us": round(kern["down"] * 1e3, 2),
+                    "down_GBps": round(dn_bytes / (kern["down"] * 1e-3) / 1e9, 1),
+                    "layer_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+                    "us_per_block": round(ms_per_step * 1e3 / w.layers, 2)},
+        "cpu_baseline": None,
+    }
     print(json.dumps(out), flush=True)
     return 0
 

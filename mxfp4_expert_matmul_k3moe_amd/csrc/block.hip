@@ -14,27 +14,59 @@ namespace k3moe {
 namespace {
 
 // xhat = h / sqrt(mean(h^2) + eps) * gamma; the sum of squares runs in fp64 with a
-// fixed per-thread order and reduction tree.
+// fixed per-thread order and reduction tree. Each thread holds its 4-element pieces of
+// the row (16-byte loads, all in flight at once) through both passes.
+constexpr int kNormPieces = 8;  // rows up to 256 * 4 * 8 = 8192 elements stay in registers
 __global__ __launch_bounds__(256) void rmsnorm_kernel(int d, const float* __restrict__ h,
                                                       const uint16_t* __restrict__ gamma,
                                                       float eps, float* __restrict__ xhat) {
-  __shared__ double red[256];
-  const int t = blockIdx.x;
-  const float* ht = h + (size_t)t * d;
+  __shared__ double red[4];
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const f32x4* ht = reinterpret_cast<const f32x4*>(h + (size_t)t * d);  // d % 8 == 0
+  const int nq = d >> 2;
+  const bool cached = nq <= 256 * kNormPieces;
+  f32x4 v[kNormPieces];
+  uint32_t gm[kNormPieces][4];  // gamma of the same pieces, requested with them
+  if (cached) {
+#pragma unroll
+    for (int c = 0; c < kNormPieces; ++c) {
+      const int q = tid + 256 * c;
+      const int qc = q < nq ? q : 0;
+      v[c] = q < nq ? ht[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gm[c][i] = gamma[4 * qc + i];
+    }
+  }
   double ss = 0.0;
-  for (int i = threadIdx.x; i < d; i += 256) {
-    const double v = (double)ht[i];
-    ss += v * v;
-  }
-  red[threadIdx.x] = ss;
+  for (int q0 = 0; q0 < nq; q0 += 256 * kNormPieces)
+#pragma unroll
+    for (int c = 0; c < kNormPieces; ++c) {
+      const int q = q0 + tid + 256 * c;
+      if (q < nq) {
+        const f32x4 a = cached ? v[c] : ht[q];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ss += (double)a[i] * (double)a[i];
+      }
+    }
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  if (lane == 0) red[wave] = ss;
   __syncthreads();
-  for (int off = 128; off >= 1; off >>= 1) {
-    if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
-    __syncthreads();
-  }
-  const double r = sqrt(red[0] / (double)d + (double)eps);
-  for (int i = threadIdx.x; i < d; i += 256)
-    xhat[(size_t)t * d + i] = (float)((double)ht[i] / r * (double)bf16_bits_to_f32(gamma[i]));
+  const double inv = 1.0 / sqrt(((red[0] + red[1]) + (red[2] + red[3])) / (double)d + (double)eps);
+  f32x4* out = reinterpret_cast<f32x4*>(xhat + (size_t)t * d);
+  for (int q0 = 0; q0 < nq; q0 += 256 * kNormPieces)
+#pragma unroll
+    for (int c = 0; c < kNormPieces; ++c) {
+      const int q = q0 + tid + 256 * c;
+      if (q < nq) {
+        const f32x4 a = cached ? v[c] : ht[q];
+        f32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o[i] = (float)((double)a[i] * inv *
+                         (double)bf16_bits_to_f32(cached ? gm[c][i] : gamma[4 * q + i]));
+        out[q] = o;
+      }
+    }
 }
 
 // LDS layout of an fp32 activation row for 8-element chunks: chunk c = sub + lpr*i,
@@ -66,63 +98,69 @@ __device__ __forceinline__ void stage_row(const float* src, int n, int lpr, f32x
   }
 }
 
-// out[t][r] = sum_c W[r][c] * x[t][c] for a chunk of rows; two weight matrices at once
-// when W2 is given (gate and up share the activation). Epilogue: SWIGLU ? silu(a)*b : a.
+// Lane-group width for a row of nch 8-element chunks: the largest power of two <= 64
+// dividing nch that still leaves each lane at least 8 chunks (short rows get narrower
+// groups and more rows per wave).
+__host__ __device__ inline int gemv_lanes(int nch) {
+  int l = lanes_per_row(nch);
+  while (l > 1 && nch / l < 8) l >>= 1;
+  return l;
+}
+
+// out[t][r] = sum_c W[r][c] * x[t][c], one row group (rpw rows) per wave; two weight
+// matrices at once when W2 is given (gate and up share the activation). Epilogue:
+// SWIGLU ? silu(a)*b : a. A lane takes chunks sub, sub + lpr, ... in rounds of
+// kGemvChunks whose loads all go out before their math; the first round is requested
+// before the token is staged in LDS, since the weights do not depend on it.
+constexpr int kGemvChunks = 8;
 template <bool SWIGLU>
-__global__ __launch_bounds__(256) void bf16_gemv_kernel(int T, int nrows, int ncols,
-                                                        const float* __restrict__ x,
-                                                        const uint16_t* __restrict__ W1,
-                                                        const uint16_t* __restrict__ W2,
-                                                        int rc, float* __restrict__ out) {
+__global__ __launch_bounds__(256, 2) void bf16_gemv_kernel(int T, int nrows, int ncols,
+                                                           const float* __restrict__ x,
+                                                           const uint16_t* __restrict__ W1,
+                                                           const uint16_t* __restrict__ W2,
+                                                           float* __restrict__ out) {
   extern __shared__ __attribute__((aligned(16))) f32x4 xs[];
   const int nch = ncols >> 3;
-  const int lpr = lanes_per_row(nch), cpl = nch / lpr, rpw = 64 / lpr;
+  const int lpr = gemv_lanes(nch), cpl = nch / lpr, rpw = 64 / lpr;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane & (lpr - 1), rsel = lane / lpr;
-  const int r0 = blockIdx.x * rc, r1 = min(nrows, r0 + rc);
+  const int r = (blockIdx.x * 4 + wave) * rpw + rsel;
+  const bool rv = r < nrows;
+  const int rr = rv ? r : nrows - 1;  // loads stay in bounds; results of !rv are dropped
+  const uint16_t* w1 = W1 + (size_t)rr * ncols + (size_t)sub * 8;
+  const uint16_t* w2 = SWIGLU ? W2 + (size_t)rr * ncols + (size_t)sub * 8 : nullptr;
   for (int t = 0; t < T; ++t) {
-    __syncthreads();
-    stage_row(x + (size_t)t * ncols, ncols, lpr, xs);
-    __syncthreads();
-    for (int rb = r0 + wave * rpw; rb < r1; rb += 4 * rpw) {
-      const int r = rb + rsel;
-      const bool rv = r < r1;
-      float a1 = 0.0f, a2 = 0.0f;
-      if (rv) {
-        const uint16_t* w1 = W1 + (size_t)r * ncols;
-        const uint16_t* w2 = SWIGLU ? W2 + (size_t)r * ncols : nullptr;
-        int i = 0;
-        for (; i + 4 <= cpl; i += 4) {
-          u32x4 v1[4], v2[4];
+    u32x4 v1[kGemvChunks], v2[kGemvChunks];
+    auto load_round = [&](int i0) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int c = sub + lpr * (i + u);
-            v1[u] = load_u32x4_nt(reinterpret_cast<const uint8_t*>(w1 + (size_t)c * 8));
-            if (SWIGLU) v2[u] = load_u32x4_nt(reinterpret_cast<const uint8_t*>(w2 + (size_t)c * 8));
-          }
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int c = sub + lpr * (i + u);
-            const f32x4 xa = xs[xs_slot(c, 0, lpr)], xb = xs[xs_slot(c, 1, lpr)];
-            a1 = bf16x8_dot(v1[u], xa, xb, a1);
-            if (SWIGLU) a2 = bf16x8_dot(v2[u], xa, xb, a2);
-          }
-        }
-        for (; i < cpl; ++i) {
-          const int c = sub + lpr * i;
-          const u32x4 v1 = load_u32x4_nt(reinterpret_cast<const uint8_t*>(w1 + (size_t)c * 8));
-          const f32x4 xa = xs[xs_slot(c, 0, lpr)], xb = xs[xs_slot(c, 1, lpr)];
-          a1 = bf16x8_dot(v1, xa, xb, a1);
-          if (SWIGLU) {
-            const u32x4 v2 = load_u32x4_nt(reinterpret_cast<const uint8_t*>(w2 + (size_t)c * 8));
-            a2 = bf16x8_dot(v2, xa, xb, a2);
-          }
+      for (int i = 0; i < kGemvChunks; ++i) {
+        if (i0 + i < cpl) {
+          const size_t off = (size_t)lpr * (i0 + i) * 8;
+          v1[i] = load_u32x4_nt(reinterpret_cast<const uint8_t*>(w1 + off));
+          if (SWIGLU) v2[i] = load_u32x4_nt(reinterpret_cast<const uint8_t*>(w2 + off));
         }
       }
-      a1 = group_sum_rt(a1, lpr);
-      if (SWIGLU) a2 = group_sum_rt(a2, lpr);
-      if (rv && sub == 0) out[(size_t)t * nrows + r] = SWIGLU ? silu_f32(a1) * a2 : a1;
+    };
+    load_round(0);
+    __syncthreads();  // the previous token's LDS reads are done
+    stage_row(x + (size_t)t * ncols, ncols, lpr, xs);
+    __syncthreads();
+    float a1 = 0.0f, a2 = 0.0f;
+    for (int i0 = 0; i0 < cpl; i0 += kGemvChunks) {
+      if (i0 > 0) load_round(i0);
+#pragma unroll
+      for (int i = 0; i < kGemvChunks; ++i) {
+        if (i0 + i < cpl) {
+          const int c = sub + lpr * (i0 + i);
+          const f32x4 xa = xs[xs_slot(c, 0, lpr)], xb = xs[xs_slot(c, 1, lpr)];
+          a1 = bf16x8_dot(v1[i], xa, xb, a1);
+          if (SWIGLU) a2 = bf16x8_dot(v2[i], xa, xb, a2);
+        }
+      }
     }
+    a1 = group_sum_rt(a1, lpr);
+    if (SWIGLU) a2 = group_sum_rt(a2, lpr);
+    if (rv && sub == 0) out[(size_t)t * nrows + r] = SWIGLU ? silu_f32(a1) * a2 : a1;
   }
 }
 
@@ -137,17 +175,16 @@ hipError_t launch_rmsnorm(int T, int d, const float* h, const uint16_t* gamma, f
 hipError_t launch_dense_swiglu(int T, int d, int f, const float* x, const uint16_t* wg,
                                const uint16_t* wu, const uint16_t* wd, float* hbuf, float* out,
                                hipStream_t s) {
+  // one row group per wave: at d = 7168, f = 1536 that is 384 and 448 blocks
   {
-    const int lpr = lanes_per_row(d >> 3), rpw = 64 / lpr;
-    const int rc = 4 * rpw * 2;
-    dim3 grid((unsigned)((f + rc - 1) / rc));
-    bf16_gemv_kernel<true><<<grid, 256, (size_t)d * 4, s>>>(T, f, d, x, wg, wu, rc, hbuf);
+    const int rows = 4 * (64 / gemv_lanes(d >> 3));
+    dim3 grid((unsigned)((f + rows - 1) / rows));
+    bf16_gemv_kernel<true><<<grid, 256, (size_t)d * 4, s>>>(T, f, d, x, wg, wu, hbuf);
   }
   {
-    const int lpr = lanes_per_row(f >> 3), rpw = 64 / lpr;
-    const int rc = 4 * rpw * 2;
-    dim3 grid((unsigned)((d + rc - 1) / rc));
-    bf16_gemv_kernel<false><<<grid, 256, (size_t)f * 4, s>>>(T, d, f, hbuf, wd, nullptr, rc, out);
+    const int rows = 4 * (64 / gemv_lanes(f >> 3));
+    dim3 grid((unsigned)((d + rows - 1) / rows));
+    bf16_gemv_kernel<false><<<grid, 256, (size_t)f * 4, s>>>(T, d, f, hbuf, wd, nullptr, out);
   }
   return hipGetLastError();
 }

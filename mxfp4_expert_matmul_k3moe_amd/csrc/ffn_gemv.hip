@@ -118,6 +118,9 @@ __global__ __launch_bounds__(256) void gateup_gemv_kernel(GateUpArgs a) {
                   }
                   gacc[tk] = fmaf(e8m0_to_f32(gsc[ii]), block_dot_f32(gw[ii], xv), gacc[tk]);
                   uacc[tk] = fmaf(e8m0_to_f32(usc[ii]), block_dot_f32(uw[ii], xv), uacc[tk]);
+                  // keeps the next block's 32 activations from being read early: holding
+                  // every block's would cost 32 registers each
+                  asm volatile("" ::: "memory");
                 } else {
                   uint32_t xp[16];
 #pragma unroll
@@ -175,7 +178,7 @@ struct GateUpDecodeArgs {
 };
 
 template <bool XF32, int BPL>
-__global__ __launch_bounds__(256) void gateup_decode_kernel(GateUpDecodeArgs a) {
+__global__ __launch_bounds__(256, 2) void gateup_decode_kernel(GateUpDecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) u32x4 xs[];
   constexpr int Q = XF32 ? 8 : 4;
   const int d = a.d, f = a.f;
@@ -227,6 +230,10 @@ __global__ __launch_bounds__(256) void gateup_decode_kernel(GateUpDecodeArgs a) 
         }
         gacc = fmaf(e8m0_to_f32(gsc[i]), block_dot_f32(gw[i], xv), gacc);
         uacc = fmaf(e8m0_to_f32(usc[i]), block_dot_f32(uw[i], xv), uacc);
+        // one block at a time: the next block's weights are converted (and its 32
+        // activations read) only after this block's sums; converting every block first
+        // would hold 64 fp32 values per block and halve the occupancy
+        if (i + 1 < BPL) asm volatile("" : "+v"(gacc), "+v"(uacc), "+v"(gw[i + 1]), "+v"(uw[i + 1])::"memory");
       } else {
         uint32_t xp[16];
 #pragma unroll
