@@ -8,6 +8,7 @@
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "k3moe_launch.h"
@@ -212,6 +213,31 @@ k3moe::BucketOut bucket_out(const Ws& ws, int32_t* offsets, int32_t* rows) {
   return o;
 }
 
+// An event owned for the duration of one call (destroying a recorded event is allowed:
+// it is released once its pending work is done).
+struct EventGuard {
+  hipEvent_t e = nullptr;
+  EventGuard() = default;
+  EventGuard(const EventGuard&) = delete;
+  EventGuard& operator=(const EventGuard&) = delete;
+  ~EventGuard() {
+    if (e) hipEventDestroy(e);
+  }
+};
+
+// One non-blocking side stream per device (default priority), created on first use and
+// kept for the life of the process, for work that can overlap the routed path.
+hipStream_t side_stream() {
+  static std::mutex mu;
+  static hipStream_t streams[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!streams[dev] && hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking) != hipSuccess)
+    streams[dev] = nullptr;
+  return streams[dev];
+}
+
 int run_router(const k3moe_dims& dm, int32_t T, const void* x, int xf32, const uint16_t* w,
                const float* bias, int32_t* ids, float* gates, const Ws& ws, hipStream_t s,
                const k3moe::BucketOut* bucket1 = nullptr) {
@@ -233,10 +259,16 @@ int run_router(const k3moe_dims& dm, int32_t T, const void* x, int xf32, const u
 }
 
 
+// shared_ready (nullable): an event the stream waits on before the launch that reads
+// `shared` (the shared expert runs on a side stream).
 int run_ffn(const k3moe_dims& dm, int32_t T, const void* x, int xf32,
             const k3moe_mx_experts* ex, const int32_t* offsets, const int32_t* rows,
             const float* gates, const float* resid, const float* shared, float* y,
-            uint16_t* y_bf16, const Ws& ws, hipStream_t s) {
+            uint16_t* y_bf16, const Ws& ws, hipStream_t s, hipEvent_t shared_ready = nullptr) {
+  auto join = [&]() -> int {
+    return shared_ready ? hip_check(hipStreamWaitEvent(s, shared_ready, 0), "join shared expert")
+                        : 0;
+  };
   const int d = dm.d_model, f = dm.d_ff, E = dm.n_experts, k = dm.top_k;
   k3moe::MxPtrs w{ex->gate_q, ex->gate_s, ex->up_q, ex->up_s, ex->down_q, ex->down_s};
   const int64_t P = (int64_t)T * k;
@@ -267,7 +299,7 @@ int run_ffn(const k3moe_dims& dm, int32_t T, const void* x, int xf32,
                                              s),
                      "down (MFMA)");
     }
-    if (rc) return rc;
+    if (rc || (rc = join())) return rc;
     return hip_check(k3moe::launch_combine(T, d, k, z, gates, ws.at<int32_t>(R_PPOS), resid,
                                            shared, y, y_bf16, s),
                      "combine");
@@ -281,7 +313,7 @@ int run_ffn(const k3moe_dims& dm, int32_t T, const void* x, int xf32,
                                                  h, cu_count(), s),
                      "gate/up (decode)");
     }
-    if (rc) return rc;
+    if (rc || (rc = join())) return rc;
     Probe probe(K3MOE_KERNEL_DOWN, s);
     return hip_check(k3moe::launch_down_decode(d, f, k, w, h, ws.at<int32_t>(R_PPOS),
                                                ws.at<int32_t>(R_PEXP), gates, resid, shared, y,
@@ -304,7 +336,7 @@ int run_ffn(const k3moe_dims& dm, int32_t T, const void* x, int xf32,
                                            max_act, z, s),
                    "down");
   }
-  if (rc) return rc;
+  if (rc || (rc = join())) return rc;
   return hip_check(k3moe::launch_combine(T, d, k, z, gates, ws.at<int32_t>(R_PPOS), resid,
                                          shared, y, y_bf16, s),
                    "combine");
@@ -433,6 +465,35 @@ int k3moe_layer_forward(const k3moe_dims* dims, int32_t T, const void* x, int x_
     xin = xhat;
     xf32 = 1;
   }
+  // The shared expert needs only xhat: it runs on a side stream, overlapping the router,
+  // top-k and gate/up, and the launch that adds it into y waits for it (per-call events).
+  const float* resid = nullptr;
+  const float* shared = nullptr;
+  EventGuard fork, joined;
+  if (blk) {
+    float* ssh = w.at<float>(R_SSH);
+    hipStream_t s2 = side_stream();
+    if (s2 && (hipEventCreateWithFlags(&fork.e, hipEventDisableTiming) != hipSuccess ||
+               hipEventCreateWithFlags(&joined.e, hipEventDisableTiming) != hipSuccess))
+      s2 = nullptr;  // no side stream: the shared expert runs in order on `s`
+    if (s2) {
+      if ((rc = hip_check(hipEventRecord(fork.e, s), "fork shared expert")) ||
+          (rc = hip_check(hipStreamWaitEvent(s2, fork.e, 0), "fork shared expert")))
+        return rc;
+    }
+    rc = hip_check(k3moe::launch_dense_swiglu(T, d, dims->d_ff, static_cast<const float*>(xin),
+                                              blk->sh_gate, blk->sh_up, blk->sh_down,
+                                              w.at<float>(R_HSH), ssh, s2 ? s2 : s),
+                   "shared expert");
+    if (rc) return rc;
+    if (s2 && (rc = hip_check(hipEventRecord(joined.e, s2), "join shared expert"))) return rc;
+    if (!s2 && joined.e) {
+      hipEventDestroy(joined.e);
+      joined.e = nullptr;
+    }
+    resid = static_cast<const float*>(x);
+    shared = ssh;
+  }
   int32_t* offs = w.at<int32_t>(R_OFFS);
   int32_t* rows = w.at<int32_t>(R_ROWS);
   const k3moe::BucketOut bo = bucket_out(w, offs, rows);
@@ -447,19 +508,8 @@ int k3moe_layer_forward(const k3moe_dims* dims, int32_t T, const void* x, int x_
                    "bucket");
     if (rc) return rc;
   }
-  const float* resid = nullptr;
-  const float* shared = nullptr;
-  if (blk) {
-    float* ssh = w.at<float>(R_SSH);
-    rc = hip_check(k3moe::launch_dense_swiglu(T, d, dims->d_ff, static_cast<const float*>(xin),
-                                              blk->sh_gate, blk->sh_up, blk->sh_down,
-                                              w.at<float>(R_HSH), ssh, s),
-                   "shared expert");
-    if (rc) return rc;
-    resid = static_cast<const float*>(x);
-    shared = ssh;
-  }
-  return run_ffn(*dims, T, xin, xf32, experts, offs, rows, gates, resid, shared, y, y_bf16, w, s);
+  return run_ffn(*dims, T, xin, xf32, experts, offs, rows, gates, resid, shared, y, y_bf16, w, s,
+                 joined.e);
 }
 
 }  // extern "C"
