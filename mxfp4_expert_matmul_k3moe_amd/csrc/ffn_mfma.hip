@@ -1,28 +1,26 @@
-// ffn_mfma.hip — grouped expert GEMMs on bf16 MFMA for many tokens per expert (prefill).
+// ffn_mfma.hip — grouped expert GEMMs on the gfx950 block-scaled MFMA for many tokens per
+// expert (prefill, batched decode).
 //
 // Each tile is up to 64 tokens of one expert (its bucket rows; experts with at most 16 or
-// 32 tokens take a 16- or 32-row tile) times a slice of that expert's weight rows. The activation tile (bf16) is staged in LDS; each weight row's 32-element
-// MXFP4 block is loaded with one 16-byte load per lane and decoded in registers straight
-// into MFMA B operands, the E8M0 scale folded into the gfx950 scaled FP4->bf16
-// conversion (exact: E2M1 values times a power of two fit bf16 for normal scales).
-// v_mfma_f32_16x16x32_bf16 accumulates in fp32.
-//
-// K is walked in steps of 128 = 4 scale blocks. Within a step, lane group g = lane/16
-// owns block g and feeds its 32 elements to four MFMAs, 8 per MFMA; the activation
-// operand uses the same permutation of k, which leaves every dot product unchanged.
-//
-// Gate/up: h = silu(G x) * (U x), written as a pair of bf16 arrays h_hi = bf16(h),
-// h_lo = bf16(h - h_hi), which together carry h to about 2^-16 relative.
-// Down: z = D h_hi + D h_lo (two MFMAs per step on the same decoded B operand), fp32,
-// one row per (token, slot) pair, combined later in slot order.
-// Source of the form: "Kimi K3 纯 C 语言 CPU 推理实战" (chenxutan.com/d/5901.html) §1.2, §2.3.
+// 32 tokens take a 16- or 32-row tile) times a slice of that expert's weight rows. Both
+// GEMMs run on v_mfma_scale_f32_16x16x128_f8f6f4 with the MXFP4 weights as its FP4
+// operand exactly as stored (a lane's 16 bytes are one 32-element block of its row, the
+// block's E8M0 byte is that lane's scale) and the activations as its FP8 operand, split
+// exactly enough into E4M3 terms that each carry their own E8M0 scales:
+//  - gate/up: the token as two terms with one scale per term row (exact for bf16 x to
+//    about 2^-22 of the row maximum); h = silu(G x) * (U x) leaves the epilogue as three
+//    terms with one scale per term and 32-element block of h;
+//  - down: z = D h from the three terms, fp32, one row per (token, slot) pair, combined
+//    later in slot order.
+// Every term is one more MFMA into the same fp32 accumulator; no instruction decodes a
+// weight. K is walked in steps of 128 (4 scale blocks). Source of the form: "Kimi K3 纯
+// C 语言 CPU 推理实战" (chenxutan.com/d/5901.html) §1.2, §2.3.
 #include "k3moe_device.h"
 #include "k3moe_launch.h"
 
 namespace k3moe {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -34,25 +32,6 @@ constexpr int kLdsBytes = 160 * 1024;
 constexpr int kBStage = kWaves * NT * 1024;  // weight blocks of one step: 16 B per lane per tile
 constexpr int kSStage = kWaves * 256;        // per-step scale words: 4 B per lane
 constexpr int kSGroup = kWaves * 1024;       // scale groups: 16 B per lane = 4 steps of scales
-
-// One stage of the pipeline in LDS: [A: NA x MT x 4 KB-blocks][B: kBStage] plus, when the
-// scales come one step at a time (SG4 false), [scales: kSStage]. With SG4 (K a multiple of
-// 512) each lane fetches 16 scale bytes of its weight row (4 steps) every 4th step into
-// one of two scale-group slots after the stages: a quarter of the L1 requests of
-// per-step scale words, which otherwise cost as many requests as the nibbles.
-// Every KB-block is written by one wave-wide 16-byte-per-lane DMA load (lane l lands at
-// byte 16 l) and read back by one wave-wide 16-byte LDS read at the same lane offsets.
-template <bool GATEUP, int MT, bool SG4>
-struct Pipe {
-  static constexpr int NA = GATEUP ? 1 : 2;       // x, or h_hi and h_lo
-  static constexpr int ABLK = NA * MT * 4;         // 1-KB A blocks per stage
-  static constexpr int ABYTES = ABLK * 1024;
-  static constexpr int BYTES = ABYTES + kBStage + (SG4 ? 0 : kSStage);
-  static constexpr int RING = SG4 ? 2 * kSGroup : 0;  // scale-group slots
-  static constexpr int S0 = (kLdsBytes - RING) / BYTES;
-  static constexpr int S = S0 < 4 ? S0 : 4;        // stages
-  static_assert(S >= 2, "pipeline needs two stages");
-};
 
 // Gate/up on the gfx950 block-scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4): the MXFP4
 // weights are the FP4 operand as stored (a lane's 16 bytes = one 32-element block of its
@@ -95,19 +74,6 @@ __device__ __forceinline__ int tile_expert_blocks(const int32_t* mtile_off, int 
   return lo;
 }
 
-// One MXFP4 block (16 bytes, 32 elements) with its scale -> 4 MFMA B operands of 8 bf16.
-__device__ __forceinline__ void decode_b(const u32x4 q, float sc, bf16x8 out[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    u32x4 v;
-    v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[i], sc, 0));
-    v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[i], sc, 1));
-    v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[i], sc, 2));
-    v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[i], sc, 3));
-    out[i] = __builtin_bit_cast(bf16x8, v);
-  }
-}
-
 // Asynchronous global -> LDS copies: 16 (or 4) bytes per lane, lane l writes dst + 16 l
 // (or dst + 4 l). dst must be the same for the whole wave.
 __device__ __forceinline__ void dma16(const void* src, uint8_t* dst) {
@@ -130,6 +96,23 @@ __device__ __forceinline__ void wait_vm() {
 // read (wait_vm); LDS reads of the previous stage have all been consumed by MFMAs before a
 // wave reaches the barrier. The empty asm statements keep the compiler from moving memory
 // operations across it.
+// Same with a wave-uniform count n < 32 (one scalar branch to the matching immediate).
+__device__ __forceinline__ void wait_vm_n(int n) {
+  switch (n) {
+#define K3_W(N) \
+  case N:       \
+    wait_vm<N>(); \
+    break;
+    K3_W(0) K3_W(1) K3_W(2) K3_W(3) K3_W(4) K3_W(5) K3_W(6) K3_W(7) K3_W(8) K3_W(9) K3_W(10)
+    K3_W(11) K3_W(12) K3_W(13) K3_W(14) K3_W(15) K3_W(16) K3_W(17) K3_W(18) K3_W(19) K3_W(20)
+    K3_W(21) K3_W(22) K3_W(23) K3_W(24) K3_W(25) K3_W(26) K3_W(27) K3_W(28) K3_W(29) K3_W(30)
+#undef K3_W
+    default:
+      wait_vm<0>();
+      break;
+  }
+}
+
 __device__ __forceinline__ void barrier_no_fence() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -138,24 +121,101 @@ __device__ __forceinline__ void barrier_no_fence() {
 
 struct MfmaArgs {
   int T, d, f, k;
-  const uint16_t* a_src;  // gate/up: x [T][d]; down: h_hi [P][f]
-  const uint16_t* a_lo;   // down: h_lo [P][f]
   const uint8_t* x8;      // gate/up: x as fp8 E4M3 terms [T][2][d] (hi, lo)
   const uint8_t* xs8;     // gate/up: E8M0 scale of each term row [T][2]
   const uint8_t *q0, *s0, *q1, *s1;  // gate/up: G and U; down: D (q1 unused)
   const int32_t *offsets, *rows, *act, *n_act, *mtile_off;
   int nblk_n;
-  uint16_t* h_out;  // gate/up output: h_hi
-  uint16_t* h_lo;   // gate/up output: h_lo
-  float* z_out;     // down output
+  uint8_t* h8;   // h as three E4M3 terms [P][3][f], bucket order (gate/up out, down in)
+  uint8_t* hs8;  // their E8M0 scales [P][3][f/32], one per term and 32-element block
+  float* z_out;  // down output
 };
 
-// GATEUP: N slice = 256 rows j (each wave 32 j, as 2 gate + 2 up 16-wide tiles).
-// DOWN:   N slice = 512 rows i (each wave 64 i, as 4 tiles).
-// MT = 16-row M subtiles in the tile (1, 2 or 4: tiles of 16, 32 or 64 tokens).
-template <bool GATEUP, int MT, bool SG4>
-__device__ __forceinline__ void mfma_tile(const MfmaArgs& a, uint8_t* lds, int e, int p0, int pn,
-                                          int nb);
+
+// OCP E4M3 code of v (round to nearest even) and the value of a code.
+__device__ __forceinline__ int e4m3_code(float v) {
+  return __builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xFF;
+}
+__device__ __forceinline__ float e4m3_value(int q) { return __builtin_amdgcn_cvt_f32_fp8(q, 0); }
+// Exponent e putting m in [128, 256); kExpZero for m == 0, kExpBad for a non-finite m.
+constexpr int kExpZero = -0x7fffffff, kExpBad = 0x7fffffff;
+__device__ __forceinline__ int top_exp(float m) {
+  if (!__builtin_isfinite(m)) return kExpBad;
+  if (m == 0.0f) return kExpZero;
+  return ilogbf(m) - 7;
+}
+
+// Gate/up epilogue: h = silu(gate) * up of a lane's 8 values, stored as three E4M3 terms
+// with one E8M0 scale per term and 32-element block of h. A wave's block of j holds the
+// values of the 4 lanes ln + 16 g' (2 tiles x 4 rows each), so each block maximum is two
+// lane exchanges. Term t: 2^s_t puts the block maximum of what is left in [128, 256), the
+// values are rounded to E4M3 and the exact remainder goes to the next term (arithmetic in
+// the domain scaled by the first term). Three terms carry h to about 2^-13 of the block
+// maximum (rel. L2 error of D h about 2e-5 on SwiGLU-like h, against 2e-3 for one bf16
+// rounding). A non-finite block maximum gives scale bytes 255 (NaN).
+template <int MT>
+__device__ __forceinline__ void store_h_terms(const MfmaArgs& a, const f32x4 (&acc)[MT][NT], int p0,
+                                              int pn, int nb, int wave, int ln, int g) {
+  const int F = a.f, FB = F >> 5;
+  const int jb = nb * 256 + wave * 32;  // first j of this wave's block (f % 32 == 0)
+  if (jb >= F) return;                 // wave-uniform
+  auto bmax = [](float v) {
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    return fmaxf(v, __shfl_xor(v, 32, 64));
+  };
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    float y[8];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[4 * nt + r] = silu_f32(acc[m][nt][r]) * acc[m][nt + 2][r];
+    float mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(y[i]));
+    mx = bmax(mx);
+    const int e0 = top_exp(mx);
+    const bool bad = e0 == kExpBad;
+    const int s0 = bad ? 255 : min(max(e0 + 127, 0), 254);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = ldexpf(y[i], 127 - s0);  // exact: maximum below 256
+    uint32_t w[3][2];
+    int sc[3];
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      int er = 0;  // exponent of term t relative to term 0
+      if (t == 0) {
+        sc[0] = s0;
+      } else {
+        float rm = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rm = fmaxf(rm, fabsf(y[i]));
+        rm = bmax(rm);
+        const int ex = top_exp(rm);
+        sc[t] = bad ? 255 : min(max(s0 + max(ex, -300), 0), 254);
+        er = sc[t] - s0;
+      }
+      w[t][0] = w[t][1] = 0u;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int q = e4m3_code(ldexpf(y[i], -er));
+        y[i] -= ldexpf(e4m3_value(q), er);
+        w[t][i >> 2] |= (uint32_t)q << (8 * (i & 3));
+      }
+    }
+    const int row = 16 * m + ln;
+    if (row < pn) {
+      const size_t base = (size_t)(p0 + row) * 3;
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        uint8_t* dst = a.h8 + (base + t) * F + jb + 4 * g;
+        *reinterpret_cast<uint32_t*>(dst) = w[t][0];
+        *reinterpret_cast<uint32_t*>(dst + 16) = w[t][1];
+        if (g == 0) a.hs8[(base + t) * FB + (jb >> 5)] = (uint8_t)sc[t];
+      }
+    }
+  }
+}
 
 // Block -> work: blocks are spread over the 8 XCDs round-robin by the hardware; logical
 // work index L is laid out so that the blocks one XCD receives are consecutive in L,
@@ -167,6 +227,9 @@ __device__ __forceinline__ void mx_gateup_tile(const MfmaArgs& a, uint8_t* lds, 
 template <int MT>
 __device__ __forceinline__ void mx_gateup_tile_sr(const MfmaArgs& a, uint8_t* lds, int e, int p0,
                                                   int pn, int nb);
+template <int MT, bool SG4>
+__device__ __forceinline__ void mx_down_tile(const MfmaArgs& a, uint8_t* lds, int e, int p0, int pn,
+                                             int nb);
 
 template <bool GATEUP>
 __global__ __launch_bounds__(512) void mfma_ffn_kernel(MfmaArgs a) {
@@ -207,195 +270,13 @@ __global__ __launch_bounds__(512) void mfma_ffn_kernel(MfmaArgs a) {
     return;
   }
   if (sg4) {
-    if (cnt <= 16) mfma_tile<GATEUP, 1, true>(a, lds, e, p0, pn, nb);
-    else if (cnt <= 32) mfma_tile<GATEUP, 2, true>(a, lds, e, p0, pn, nb);
-    else mfma_tile<GATEUP, 4, true>(a, lds, e, p0, pn, nb);
+    if (cnt <= 16) mx_down_tile<1, true>(a, lds, e, p0, pn, nb);
+    else if (cnt <= 32) mx_down_tile<2, true>(a, lds, e, p0, pn, nb);
+    else mx_down_tile<4, true>(a, lds, e, p0, pn, nb);
   } else {
-    if (cnt <= 16) mfma_tile<GATEUP, 1, false>(a, lds, e, p0, pn, nb);
-    else if (cnt <= 32) mfma_tile<GATEUP, 2, false>(a, lds, e, p0, pn, nb);
-    else mfma_tile<GATEUP, 4, false>(a, lds, e, p0, pn, nb);
-  }
-}
-
-template <bool GATEUP, int MT, bool SG4>
-__device__ __forceinline__ void mfma_tile(const MfmaArgs& a, uint8_t* lds, int e, int p0, int pn,
-                                          int nb) {
-  using PP = Pipe<GATEUP, MT, SG4>;
-  constexpr int NA = PP::NA, S = PP::S, SB = PP::BYTES, AB = PP::ABYTES;
-  const int P = a.T * a.k;
-  const int K = GATEUP ? a.d : a.f;     // contraction length (multiple of BK)
-  const int NR = GATEUP ? a.f : a.d;    // weight rows of one matrix
-  const int KB = K >> 5;                // scale bytes per weight row
-  const size_t rq = (size_t)(K >> 1);   // nibble bytes per weight row
-  const int nk = K / BK;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ln = lane & 15, g = lane >> 4;
-
-  // A rows of this lane (row 16 m + ln of the tile), as element offsets into a_src / a_lo.
-  // Rows past the tile's end repeat its last row: their results are never stored.
-  size_t aoff[MT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    const int r = min(16 * m + ln, pn - 1);
-    if (GATEUP) {
-      const int pair = a.rows[p0 + r];
-      const int tok = (pair >= 0 && pair < P) ? pair / a.k : 0;
-      aoff[m] = (size_t)tok * a.d + 32 * g;
-    } else {
-      aoff[m] = (size_t)(p0 + r) * a.f + 32 * g;
-    }
-  }
-
-  // weight rows: B lane (ln, g) of tile nt reads row rB[nt], block 4 ks + g; scale lanes
-  // l = 16 nt' + ln' read the scale word (4 blocks) of row rB[nt'] for lane ln'.
-  const uint8_t* bsrc[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    int r;
-    const uint8_t* qb;
-    if (GATEUP) {
-      r = nb * 256 + wave * 32 + (nt & 1) * 16 + ln;
-      qb = (nt < 2) ? a.q0 : a.q1;
-    } else {
-      r = nb * 512 + wave * 64 + nt * 16 + ln;
-      qb = a.q0;
-    }
-    r = min(r, NR - 1);  // rows past the matrix repeat its last row; never stored
-    bsrc[nt] = qb + ((size_t)e * NR + r) * rq + 16 * g;
-  }
-  const uint8_t* ssrc;
-  {
-    const int snt = lane >> 4, sln = lane & 15;
-    int r;
-    const uint8_t* sb;
-    if (GATEUP) {
-      r = nb * 256 + wave * 32 + (snt & 1) * 16 + sln;
-      sb = (snt < 2) ? a.s0 : a.s1;
-    } else {
-      r = nb * 512 + wave * 64 + snt * 16 + sln;
-      sb = a.s0;
-    }
-    r = min(r, NR - 1);
-    ssrc = sb + ((size_t)e * NR + r) * KB;
-  }
-
-  // this wave's share of the A blocks: ids wave, wave + 8, ...
-  constexpr int A_PER_WAVE = (PP::ABLK + kWaves - 1) / kWaves;
-  const bool has_a = PP::ABLK >= kWaves || wave < PP::ABLK;
-  uint8_t* const sring = lds + S * SB;  // scale-group slots (SG4)
-  auto issue = [&](int ks, int slotno) {
-    uint8_t* st = lds + slotno * SB;
-#pragma unroll
-    for (int j = 0; j < A_PER_WAVE; ++j) {
-      const int bi = wave + kWaves * j;
-      if (PP::ABLK >= kWaves || bi < PP::ABLK) {
-        const int v = bi / (MT * 4), m = (bi / 4) % MT, i = bi % 4;
-        const uint16_t* base = (NA == 2 && v == 1) ? a.a_lo : a.a_src;
-        dma16(base + aoff[m] + ks * BK + 8 * i, st + bi * 1024);
-      }
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      dma16(bsrc[nt] + (size_t)ks * 64, st + AB + (wave * NT + nt) * 1024);
-    if (SG4) {
-      if ((ks & 3) == 0) dma16(ssrc + ks * 4, sring + ((ks >> 2) & 1) * kSGroup + wave * 1024);
-    } else {
-      dma4(ssrc + ks * 4, st + AB + kBStage + wave * 256);
-    }
-  };
-  // Vector-memory operations of one stage for this wave: A blocks, NT weight blocks, and
-  // the per-step scale word (or, with SG4, one scale group on every 4th stage).
-  constexpr int OPS_A = A_PER_WAVE + NT + (SG4 ? 0 : 1);
-  constexpr int OPS_NOA = NT + (SG4 ? 0 : 1);
-  // wait until this wave's stage ks has landed: only stages ks+1 .. ks+S-2 may be pending
-  auto wait_stage = [&](int ks) {
-    if (ks + S - 2 >= nk) {
-      wait_vm<0>();
-      return;
-    }
-    // scale groups issued with the pending stages (multiples of 4 in ks+1 .. ks+S-2)
-    const int extra = SG4 ? ((ks + S - 2) >> 2) - (ks >> 2) : 0;
-    if (has_a) {
-      if (extra) wait_vm<(S - 2) * OPS_A + 1>();
-      else wait_vm<(S - 2) * OPS_A>();
-    } else {
-      if (extra) wait_vm<(S - 2) * OPS_NOA + 1>();
-      else wait_vm<(S - 2) * OPS_NOA>();
-    }
-  };
-
-  f32x4 acc[MT][NT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-  for (int s = 0; s < S - 1; ++s)
-    if (s < nk) issue(s, s);
-
-  for (int ks = 0; ks < nk; ++ks) {
-    wait_stage(ks);
-    barrier_no_fence();  // every wave's part of stage ks is in LDS; stage ks-1 is consumed
-    if (ks + S - 1 < nk) issue(ks + S - 1, (ks + S - 1) % S);
-
-    const uint8_t* st = lds + (ks % S) * SB;
-    bf16x8 bop[NT][4];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const u32x4 q = *reinterpret_cast<const u32x4*>(st + AB + (wave * NT + nt) * 1024 + lane * 16);
-      const uint32_t sc =
-          SG4 ? sring[((ks >> 2) & 1) * kSGroup + wave * 1024 + 16 * (nt * 16 + ln) + 4 * (ks & 3) + g]
-              : st[AB + kBStage + wave * 256 + 4 * (nt * 16 + ln) + g];
-      decode_b(q, e8m0_to_f32(sc), bop[nt]);
-    }
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-#pragma unroll
-      for (int v = 0; v < NA; ++v) {
-        bf16x8 aop[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          aop[i] = *reinterpret_cast<const bf16x8*>(st + ((v * MT + m) * 4 + i) * 1024 + lane * 16);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[m][nt] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[i], bop[nt][i], acc[m][nt], 0, 0, 0);
-      }
-    }
-  }
-
-  // epilogue: lane holds rows 4*g .. 4*g+3 of column ln of each 16x16 tile
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 16 * m + 4 * g + r;
-      if (row >= pn) continue;
-      if (GATEUP) {
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const int j = nb * 256 + wave * 32 + nt * 16 + ln;
-          if (j < a.f) {
-            const float hv = silu_f32(acc[m][nt][r]) * acc[m][nt + 2][r];
-            const uint16_t hi = f32_to_bf16_rne(hv);
-            const size_t o = (size_t)(p0 + row) * a.f + j;
-            a.h_out[o] = hi;
-            a.h_lo[o] = f32_to_bf16_rne(hv - bf16_bits_to_f32(hi));
-          }
-        }
-      } else {
-        const int pair = a.rows[p0 + row];
-        if (pair < 0 || pair >= P) continue;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const int i = nb * 512 + wave * 64 + nt * 16 + ln;
-          if (i < a.d) a.z_out[(size_t)pair * a.d + i] = acc[m][nt][r];
-        }
-      }
-    }
+    if (cnt <= 16) mx_down_tile<1, false>(a, lds, e, p0, pn, nb);
+    else if (cnt <= 32) mx_down_tile<2, false>(a, lds, e, p0, pn, nb);
+    else mx_down_tile<4, false>(a, lds, e, p0, pn, nb);
   }
 }
 
@@ -528,27 +409,7 @@ __device__ __forceinline__ void mx_gateup_tile(const MfmaArgs& a, uint8_t* lds, 
   }
 
   // epilogue: lane (ln, g) holds weight rows 4 g .. 4 g + 3 of each 16-row tile, token ln
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    const int row = 16 * m + ln;
-    if (row >= pn) continue;
-    const size_t ob = (size_t)(p0 + row) * a.f;
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int j0 = nb * 256 + wave * 32 + nt * 16 + 4 * g;  // f % 4 == 0: all four or none
-      if (j0 < a.f) {
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float hv = silu_f32(acc[m][nt][r]) * acc[m][nt + 2][r];
-          hw[r] = f32_to_bf16_rne(hv);
-          lw[r] = f32_to_bf16_rne(hv - bf16_bits_to_f32(hw[r]));
-        }
-        *reinterpret_cast<uint2*>(a.h_out + ob + j0) = make_uint2(hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16));
-        *reinterpret_cast<uint2*>(a.h_lo + ob + j0) = make_uint2(lw[0] | (lw[1] << 16), lw[2] | (lw[3] << 16));
-      }
-    }
-  }
+  store_h_terms<MT>(a, acc, p0, pn, nb, wave, ln, g);
 }
 
 // Gate/up tile for K % 512 == 0 with the weight scales kept in registers. Fetching a
@@ -714,25 +575,148 @@ __device__ __forceinline__ void mx_gateup_tile_sr(const MfmaArgs& a, uint8_t* ld
     }
   }
 
+  store_h_terms<MT>(a, acc, p0, pn, nb, wave, ln, g);
+}
+
+// Down on the block-scaled MFMA: D (FP4, as stored) against h as three E4M3 terms with
+// their per-32-block scales (B operand; the scale of block g of pair column x comes from
+// lane (x, g)). Per stage a wave DMAs its share of the h tile (a term's 128 bytes per pair
+// in the FP8 operand lane order, and each pair's 4 scale bytes of every term), its 4
+// weight tiles and their scales; each wave waits on its own DMA count. 3 MFMAs per
+// (M subtile, N tile, step).
+template <int MT, bool SG4>
+struct MxDownPipe {
+  static constexpr int ADATA = MT * 6 * 1024;      // [m][term][half] 1-KB blocks
+  static constexpr int ABYTES = ADATA + MT * 256;  // + scale words [m][term x 16 pairs]
+  static constexpr int BYTES = ABYTES + kBStage + (SG4 ? 0 : kSStage);
+  static constexpr int RING = SG4 ? 2 * kSGroup : 0;
+  static constexpr int S0 = (kLdsBytes - RING) / BYTES;
+  static constexpr int S = S0 < 4 ? S0 : 4;
+  static_assert(S >= 2, "pipeline needs two stages");
+  static constexpr int A_PER_WAVE = (6 * MT + kWaves - 1) / kWaves;
+};
+
+template <int MT, bool SG4>
+__device__ __forceinline__ void mx_down_tile(const MfmaArgs& a, uint8_t* lds, int e, int p0, int pn,
+                                             int nb) {
+  using PP = MxDownPipe<MT, SG4>;
+  constexpr int S = PP::S, SB = PP::BYTES, AB = PP::ABYTES, AW = PP::A_PER_WAVE;
+  const int P = a.T * a.k;
+  const int K = a.f, NR = a.d, KB = K >> 5;
+  const size_t F = (size_t)K, rq = (size_t)(K >> 1);
+  const int nk = K / BK;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ln = lane & 15, g = lane >> 4;
+  uint8_t* const sring = lds + S * SB;
+
+  // term rows (x3) of this lane's pair in each M subtile; rows past the tile's end repeat
+  // its last row (their results are never stored)
+  size_t hrow[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) hrow[m] = (size_t)(p0 + min(16 * m + ln, pn - 1)) * 3;
+  const uint8_t* hlane = a.h8 + 32 * (g >> 1) + 16 * (g & 1);
+  // scale-word lanes: pair ln, term lane >> 4 (the fourth group repeats term 2)
+  const int sw_t = min(lane >> 4, 2);
+  const uint8_t* bsrc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = min(nb * 512 + wave * 64 + nt * 16 + ln, NR - 1);
+    bsrc[nt] = a.q0 + ((size_t)e * NR + r) * rq + 16 * g;
+  }
+  const uint8_t* ssrc;
+  {
+    const int r = min(nb * 512 + wave * 64 + (lane >> 4) * 16 + (lane & 15), NR - 1);
+    ssrc = a.s0 + ((size_t)e * NR + r) * KB;
+  }
+  auto issue = [&](int ks, int slotno) {
+    uint8_t* st = lds + slotno * SB;
+#pragma unroll
+    for (int j = 0; j < AW; ++j) {
+      const int b = wave + kWaves * j;
+      if (b < 6 * MT) {
+        const int m = b / 6, t = (b % 6) >> 1, hh = b & 1;
+        dma16(hlane + (hrow[m] + t) * F + (size_t)ks * BK + 64 * hh, st + b * 1024);
+      }
+    }
+    if (wave < MT) {
+      const size_t row = (size_t)(p0 + min(16 * wave + ln, pn - 1)) * 3 + sw_t;
+      dma4(a.hs8 + row * KB + 4 * ks, st + PP::ADATA + wave * 256);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      dma16(bsrc[nt] + (size_t)ks * 64, st + AB + (wave * NT + nt) * 1024);
+    if (SG4) {
+      if ((ks & 3) == 0) dma16(ssrc + ks * 4, sring + ((ks >> 2) & 1) * kSGroup + wave * 1024);
+    } else {
+      dma4(ssrc + ks * 4, st + AB + kBStage + wave * 256);
+    }
+  };
+  // this wave's DMAs per stage: its h blocks, the scale words of subtile `wave`, weights
+  int na = 0;
+#pragma unroll
+  for (int j = 0; j < AW; ++j) na += (wave + kWaves * j < 6 * MT) ? 1 : 0;
+  const int ops = na + (wave < MT ? 1 : 0) + NT + (SG4 ? 0 : 1);
+  auto wait_stage = [&](int ks) {
+    if (ks + S - 2 >= nk) {
+      wait_vm<0>();
+      return;
+    }
+    const int extra = SG4 ? ((ks + S - 2) >> 2) - (ks >> 2) : 0;
+    wait_vm_n((S - 2) * ops + extra);
+  };
+
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) issue(s, s);
+
+  for (int ks = 0; ks < nk; ++ks) {
+    wait_stage(ks);
+    barrier_no_fence();
+    if (ks + S - 1 < nk) issue(ks + S - 1, (ks + S - 1) % S);
+
+    const uint8_t* st = lds + (ks % S) * SB;
+    i32x8 wop[NT];
+    int wsc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const u32x4 q = *reinterpret_cast<const u32x4*>(st + AB + (wave * NT + nt) * 1024 + lane * 16);
+      wop[nt] = i32x8{(int)q[0], (int)q[1], (int)q[2], (int)q[3], 0, 0, 0, 0};
+      wsc[nt] = SG4 ? sring[((ks >> 2) & 1) * kSGroup + wave * 1024 + 16 * (nt * 16 + ln) + 4 * (ks & 3) + g]
+                    : st[AB + kBStage + wave * 256 + 4 * (nt * 16 + ln) + g];
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        const uint8_t* xb = st + ((m * 3 + t) * 2) * 1024 + lane * 16;
+        const u32x4 h0 = *reinterpret_cast<const u32x4*>(xb), h1 = *reinterpret_cast<const u32x4*>(xb + 1024);
+        const i32x8 xop = {(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
+        const int xsc = st[PP::ADATA + m * 256 + (ln + 16 * t) * 4 + g];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[m][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wop[nt], xop, acc[m][nt], 4, 0, 0,
+                                                                         wsc[nt], 0, xsc);
+      }
+    }
+  }
+
+  // epilogue: lane (ln, g) holds output rows 4 g .. 4 g + 3 of each tile for pair row ln
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     const int row = 16 * m + ln;
     if (row >= pn) continue;
-    const size_t ob = (size_t)(p0 + row) * a.f;
+    const int pair = a.rows[p0 + row];
+    if (pair < 0 || pair >= P) continue;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int j0 = nb * 256 + wave * 32 + nt * 16 + 4 * g;
-      if (j0 < a.f) {
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float hv = silu_f32(acc[m][nt][r]) * acc[m][nt + 2][r];
-          hw[r] = f32_to_bf16_rne(hv);
-          lw[r] = f32_to_bf16_rne(hv - bf16_bits_to_f32(hw[r]));
-        }
-        *reinterpret_cast<uint2*>(a.h_out + ob + j0) = make_uint2(hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16));
-        *reinterpret_cast<uint2*>(a.h_lo + ob + j0) = make_uint2(lw[0] | (lw[1] << 16), lw[2] | (lw[3] << 16));
-      }
+    for (int nt = 0; nt < NT; ++nt) {
+      const int i0 = nb * 512 + wave * 64 + nt * 16 + 4 * g;  // d % 4 == 0: all four or none
+      if (i0 < a.d) *reinterpret_cast<f32x4*>(a.z_out + (size_t)pair * a.d + i0) = acc[m][nt];
     }
   }
 }
@@ -761,7 +745,7 @@ __global__ __launch_bounds__(256) void x8_prep_kernel(int d, const uint16_t* __r
   };
   // exponent putting m in [128, 256), or INT_MIN for m == 0, INT_MAX for non-finite m
   auto top_exp = [](float m) -> int {
-    if (!(m <= 3.0e38f)) return 0x7fffffff;
+    if (!__builtin_isfinite(m)) return 0x7fffffff;
     if (m == 0.0f) return -0x7fffffff;
     return ilogbf(m) - 7;
   };
@@ -861,28 +845,29 @@ bool mfma_shape_supported(int d, int f) { return d % BK == 0 && f % BK == 0; }
 hipError_t launch_gateup_mfma(int T, int d, int f, int E, int k, const uint16_t* x,
                               const MxPtrs& w, const int32_t* offsets, const int32_t* rows,
                               const int32_t* act, const int32_t* n_act,
-                              const int32_t* mtile_off, uint16_t* h, uint8_t* x8, uint8_t* xs8,
-                              hipStream_t s) {
+                              const int32_t* mtile_off, uint8_t* h8, uint8_t* hs8, uint8_t* x8,
+                              uint8_t* xs8, hipStream_t s) {
   x8_prep_kernel<<<T, 256, 0, s>>>(d, x, x8, xs8);
   MfmaArgs a{};
-  a.T = T; a.d = d; a.f = f; a.k = k; a.a_src = x; a.x8 = x8; a.xs8 = xs8;
+  a.T = T; a.d = d; a.f = f; a.k = k; a.x8 = x8; a.xs8 = xs8;
   a.q0 = w.gate_q; a.s0 = w.gate_s; a.q1 = w.up_q; a.s1 = w.up_s;
   a.offsets = offsets; a.rows = rows; a.act = act; a.n_act = n_act; a.mtile_off = mtile_off;
   a.nblk_n = (f + 255) / 256;
-  a.h_out = h;
-  a.h_lo = h + (size_t)T * k * f;
+  a.h8 = h8;
+  a.hs8 = hs8;
   dim3 grid((unsigned)(mfma_mtiles_bound(T, E, k) * a.nblk_n));
   mfma_ffn_kernel<true><<<grid, 512, 0, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_down_mfma(int T, int d, int f, int E, int k, const MxPtrs& w,
-                            const uint16_t* h, const int32_t* offsets, const int32_t* rows,
-                            const int32_t* act, const int32_t* n_act, const int32_t* mtile_off,
-                            float* z, hipStream_t s) {
+                            const uint8_t* h8, const uint8_t* hs8, const int32_t* offsets,
+                            const int32_t* rows, const int32_t* act, const int32_t* n_act,
+                            const int32_t* mtile_off, float* z, hipStream_t s) {
   MfmaArgs a{};
-  a.T = T; a.d = d; a.f = f; a.k = k; a.a_src = h;
-  a.a_lo = h + (size_t)T * k * f;
+  a.T = T; a.d = d; a.f = f; a.k = k;
+  a.h8 = const_cast<uint8_t*>(h8);
+  a.hs8 = const_cast<uint8_t*>(hs8);
   a.q0 = w.down_q; a.s0 = w.down_s;
   a.offsets = offsets; a.rows = rows; a.act = act; a.n_act = n_act; a.mtile_off = mtile_off;
   a.nblk_n = (d + 511) / 512;

@@ -92,7 +92,7 @@ Layout layout_for(const k3moe_dims& dm, int64_t T) {
   sz[R_HIST] = (size_t)(NB * E * 4);
   sz[R_BASE] = (size_t)(NB * E * 4);
   sz[R_MASK] = (size_t)(NB * E * 8);
-  sz[R_H] = (size_t)(P * f * 4);
+  sz[R_H] = (size_t)(P * f * 4);  // fp32 h, or three FP8 terms + their block scales
   sz[R_Z] = (size_t)(P * d * 4);
   sz[R_XHAT] = (size_t)(T * d * 4);
   sz[R_HSH] = (size_t)(T * f * 4);
@@ -279,22 +279,24 @@ int run_ffn(const k3moe_dims& dm, int32_t T, const void* x, int xf32,
                          reinterpret_cast<uintptr_t>(ex->up_s) |
                          reinterpret_cast<uintptr_t>(ex->down_s)) & 3u) == 0;
   if (T >= kMfmaMinTokens && !xf32 && scales4 && k3moe::mfma_shape_supported(d, f)) {
-    // many tokens per expert: grouped GEMMs on bf16 MFMA, h kept as a bf16 hi/lo pair
-    uint16_t* hb = ws.at<uint16_t>(R_H);
+    // many tokens per expert: grouped GEMMs on the block-scaled FP4 x FP8 MFMA, h kept as
+    // three E4M3 terms [P][3][f] with per-32-block scales [P][3][f/32] (in the h region)
+    uint8_t* h8 = ws.at<uint8_t>(R_H);
+    uint8_t* hs8 = h8 + (size_t)P * 3 * f;
     float* z = ws.at<float>(R_Z);
     const int32_t* mt = ws.at<int32_t>(R_MTILE);
     {
       Probe probe(K3MOE_KERNEL_GATE_UP, s);
       rc = hip_check(k3moe::launch_gateup_mfma(T, d, f, E, k, static_cast<const uint16_t*>(x), w,
                                                offsets, rows, ws.at<int32_t>(R_ACT),
-                                               ws.at<int32_t>(R_NACT), mt, hb,
+                                               ws.at<int32_t>(R_NACT), mt, h8, hs8,
                                                ws.at<uint8_t>(R_X8), ws.at<uint8_t>(R_XS), s),
                      "gate/up (MFMA)");
     }
     if (rc) return rc;
     {
       Probe probe(K3MOE_KERNEL_DOWN, s);
-      rc = hip_check(k3moe::launch_down_mfma(T, d, f, E, k, w, hb, offsets, rows,
+      rc = hip_check(k3moe::launch_down_mfma(T, d, f, E, k, w, h8, hs8, offsets, rows,
                                              ws.at<int32_t>(R_ACT), ws.at<int32_t>(R_NACT), mt, z,
                                              s),
                      "down (MFMA)");

@@ -85,18 +85,19 @@ hipError_t launch_combine(int T, int d, int k, const float* z, const float* gate
 // Upper bound on the number of M tiles over all active experts.
 int mfma_mtiles_bound(int T, int E, int k);
 bool mfma_shape_supported(int d, int f);
-// h = silu(G x) * (U x) for every (expert, token) pair, bucket order, as two bf16 arrays
-// h[0 .. P*f) = bf16(h) and h[P*f .. 2*P*f) = bf16(h - bf16(h)).
+// h = silu(G x) * (U x) for every (expert, token) pair, bucket order, as three E4M3 terms
+// h8 [P][3][f] with their E8M0 scales hs8 [P][3][f/32] (one per term and 32-block); x8
+// [T][2][d] and xs8 [T][2] receive the tokens' own FP8 terms on the way.
 hipError_t launch_gateup_mfma(int T, int d, int f, int E, int k, const uint16_t* x,
                               const MxPtrs& w, const int32_t* offsets, const int32_t* rows,
                               const int32_t* act, const int32_t* n_act,
-                              const int32_t* mtile_off, uint16_t* h, uint8_t* x8, uint8_t* xs8,
-                              hipStream_t s);
-// z (fp32 [P][d], pair-indexed) = D h, from both halves of h.
+                              const int32_t* mtile_off, uint8_t* h8, uint8_t* hs8, uint8_t* x8,
+                              uint8_t* xs8, hipStream_t s);
+// z (fp32 [P][d], pair-indexed) = D h from the three terms of h.
 hipError_t launch_down_mfma(int T, int d, int f, int E, int k, const MxPtrs& w,
-                            const uint16_t* h, const int32_t* offsets, const int32_t* rows,
-                            const int32_t* act, const int32_t* n_act, const int32_t* mtile_off,
-                            float* z, hipStream_t s);
+                            const uint8_t* h8, const uint8_t* hs8, const int32_t* offsets,
+                            const int32_t* rows, const int32_t* act, const int32_t* n_act,
+                            const int32_t* mtile_off, float* z, hipStream_t s);
 
 // ---- block extras (block.hip) ---------------------------------------------------------
 hipError_t launch_rmsnorm(int T, int d, const float* h, const uint16_t* gamma, float eps,
