@@ -56,10 +56,10 @@
  *   - Input values are not scanned: NaN inputs and E8M0 255 propagate as NaN.
  *   - Alignment: x, y and the MXFP4 nibble arrays must be 16-byte aligned (EINVAL).
  *     With 16 or more tokens, bf16 activations, d_model and d_ff multiples of 128 and
- *     4-byte aligned scale arrays, the expert matmuls run as grouped MFMA GEMMs (gate/up
- *     on the block-scaled FP4 x FP8 MFMA with the token split exactly into two FP8
- *     terms, down on bf16 MFMA with h as a bf16 pair); otherwise as per-expert GEMVs.
- *     All accumulate in fp32 (results agree to rounding).
+ *     4-byte aligned scale arrays, the expert matmuls run as grouped GEMMs on the
+ *     block-scaled FP4 x FP8 MFMA (the token split exactly into two FP8 terms, h into
+ *     three FP8 terms with per-32-block scales); otherwise as per-expert GEMVs. All
+ *     accumulate in fp32 (results agree to rounding).
  *   - Limits (EUNSUPPORTED beyond): n_experts <= 4096, T <= 1048576, d_model <= 16384,
  *     d_ff <= 16384; the expert kernels also need (d_ff/32)/p <= 4, with p the largest
  *     power of two <= 64 dividing d_ff/32 (true for d_ff = 1536, 256, 32, any multiple
