@@ -189,6 +189,30 @@ def test_nan_scale_propagates(dev):
     assert np.isnan(yg[5]) and np.isfinite(np.delete(yg, 5)).all()
 
 
+def test_nan_scales_propagate_grouped_gemm(dev):
+    """E8M0 255 on the grouped-GEMM path: a gate scale makes h NaN for the expert's pairs
+    (NaN through the FP8 terms of h into down: every output of those tokens), a down scale
+    makes one output row NaN. The NaN pattern must be the oracle's."""
+    w = next(s for s in SHAPES if s.name == "mfma_t16")
+    x = w.x_bf16()
+    ref0 = harness.run_layer(w, x)
+    e = int(ref0["ids"][0, 0])
+    for name, row, blk in (("gate_s", 7, 0), ("down_s", 5, 1)):
+        say(f"E8M0 255 in {name}[{e}, {row}, {blk}] ({w.name}, T={w.T})")
+        ex = gdev.experts(w, 0, dev)
+        ex[name][e, row, blk] = 255
+        g = run_gpu_layer(w, x, dev, experts=ex)
+        over = w.expert_host(0, e)
+        over[name][row, blk] = 255
+        ref = harness.run_layer(w, x, expert_override={e: over})
+        yg = g["y"].cpu().numpy()
+        nan_ref = np.isnan(ref["y"])
+        assert nan_ref.any() and not nan_ref.all()
+        assert np.array_equal(np.isnan(yg), nan_ref)
+        ok = ~nan_ref.any(axis=1)  # tokens that did not pick e stay within tolerance
+        assert rel_l2(yg[ok].astype(np.float64), ref["y"][ok]).max() <= TOL
+
+
 def test_down_scale_plus_one_doubles_exactly(dev):
     for w in (TOY, TINY):
         say(f"down scales +1 doubles y exactly ({w.name})")
