@@ -319,9 +319,10 @@ constexpr int kMaxCand = 2048;  // candidate buffer; the exact ranking covers an
 // at once); the first 256 threads then read their keys back and the rest only keep the
 // block's barrier count.
 //  1. logits = sum of the fp64 partials in chunk order (+ bias), as order keys;
-//  2. each wave sorts its 64 lane maxima (bitonic network over lanes): the k-th best of
-//     them is at most the k-th best of all E, so the best such bound over the waves is a
-//     valid threshold, and every top-k element ranks at or above it;
+//  2. each wave sorts the upper 32 bits of its 64 lane maxima (bitonic network over
+//     lanes): the k-th best of them is at most the upper bits of the k-th best of all E,
+//     so the best such bound over the waves is a valid threshold, and every top-k element
+//     has its upper bits at or above it;
 //  3. candidates at or above the threshold are compacted into LDS (wave scans) and ranked
 //     exactly against each other; the softmax denominator is a per-thread ordered sum and
 //     a fixed reduction tree.
@@ -345,8 +346,8 @@ __global__ __launch_bounds__(WIDE ? 1024 : 256) void route_topk_kernel(int T, in
   __shared__ uint64_t keys[kMaxE];
   __shared__ uint64_t ckey[kMaxCand];
   __shared__ int cid[kMaxCand];
-  __shared__ uint64_t w_tk[kTopkMaxWaves], w_mk[kTopkMaxWaves];
-  __shared__ int w_ti[kTopkMaxWaves], w_ok[kTopkMaxWaves], w_cnt[kTopkMaxWaves], w_nan[kTopkMaxWaves];
+  __shared__ uint32_t w_tk[kTopkMaxWaves], w_mk[kTopkMaxWaves];
+  __shared__ int w_ok[kTopkMaxWaves], w_cnt[kTopkMaxWaves], w_nan[kTopkMaxWaves];
   __shared__ double w_sum[kTopkMaxWaves];
   __shared__ int s_ids[kMaxSlots];
   const int t = blockIdx.x;
@@ -434,23 +435,18 @@ __global__ __launch_bounds__(WIDE ? 1024 : 256) void route_topk_kernel(int T, in
     }
   }
 
-  // 2. per-wave threshold: the 64 lane maxima sorted best-first by a bitonic network over
-  //    the lanes; lane 0 then holds the wave's best logit and lane k-1 the k-th best
+  // 2. per-wave threshold on the upper 32 bits of the keys (a monotone map, so the bound
+  //    below stays valid and candidates are ranked on the full keys): the 64 lane maxima
+  //    sorted best-first by a bitonic network over the lanes; lane 0 then holds the wave's
+  //    best and lane k-1 its k-th best
   {
-    uint64_t sk = (bi >= 0) ? bkey : 0ull;
-    int si = (bi >= 0) ? bi : 0x7FFFFFFF;
+    uint32_t sk = (bi >= 0) ? (uint32_t)(bkey >> 32) : 0u;
     for (int size = 2; size <= 64; size <<= 1) {
       for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        const uint32_t plo = (uint32_t)__shfl_xor((int)(uint32_t)sk, stride, 64);
-        const uint32_t phi = (uint32_t)__shfl_xor((int)(uint32_t)(sk >> 32), stride, 64);
-        const int pi = __shfl_xor(si, stride, 64);
-        const uint64_t pk = ((uint64_t)phi << 32) | plo;
+        const uint32_t pk = (uint32_t)__shfl_xor((int)sk, stride, 64);
         const bool desc = (lane & size) == 0;  // this run of `size` lanes sorts best-first
         const bool low = (lane & stride) == 0;
-        if (better(pk, pi, sk, si) == (low == desc)) {
-          sk = pk;
-          si = pi;
-        }
+        sk = (low == desc) ? (pk > sk ? pk : sk) : (pk < sk ? pk : sk);
       }
     }
     const int nvalid = __popcll(__ballot(bi >= 0));
@@ -458,29 +454,23 @@ __global__ __launch_bounds__(WIDE ? 1024 : 256) void route_topk_kernel(int T, in
     if (lane == 0) {
       w_ok[wave] = nvalid >= k;
       w_nan[wave] = anyn ? 1 : 0;
-      w_mk[wave] = nvalid > 0 ? sk : 0ull;
+      w_mk[wave] = nvalid > 0 ? sk : 0u;
     }
-    if (lane == k - 1) {
-      w_tk[wave] = sk;
-      w_ti[wave] = si;
-    }
+    if (lane == k - 1) w_tk[wave] = sk;
   }
   __syncthreads();
-  uint64_t tk = 0, mk = 0;
-  int ti = 0x7FFFFFFF;
-  bool have = false;
+  // threshold: the best wave bound (0 admits every expert when no wave has k valid lanes)
+  uint32_t tk = 0, mk = 0;
   int anynan = 0;
 #pragma unroll
   for (int w = 0; w < nw; ++w) {
-    if (w_ok[w] && (!have || better(w_tk[w], w_ti[w], tk, ti))) {
-      tk = w_tk[w];
-      ti = w_ti[w];
-      have = true;
-    }
+    if (w_ok[w] && w_tk[w] > tk) tk = w_tk[w];
     mk = (w_mk[w] > mk) ? w_mk[w] : mk;
     anynan |= w_nan[w];
   }
-  const double m = key_to_double(mk);
+  // softmax shift: the largest logit with the low 32 key bits cleared, at most 2^-20 of its
+  // magnitude below it (any shift near the maximum gives the same quotients)
+  const double m = key_to_double((uint64_t)mk << 32);
 
   // 3. candidates (wave scan) and softmax denominator
   int mine = 0;
@@ -489,7 +479,7 @@ __global__ __launch_bounds__(WIDE ? 1024 : 256) void route_topk_kernel(int T, in
   for (int j = 0; j < KPT; ++j) {
     const int e = tid + NT * j;
     if (e < E) {
-      mine += better(tk, ti, key[j], e) ? 0 : 1;
+      mine += ((uint32_t)(key[j] >> 32) >= tk) ? 1 : 0;
       se += exp(key_to_double(key[j]) - m);
     }
   }
@@ -514,7 +504,7 @@ __global__ __launch_bounds__(WIDE ? 1024 : 256) void route_topk_kernel(int T, in
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int e = tid + NT * j;
-    if (e < E && !better(tk, ti, key[j], e)) {
+    if (e < E && (uint32_t)(key[j] >> 32) >= tk) {
       if (pre < kMaxCand) {
         cid[pre] = e;
         ckey[pre] = key[j];
@@ -524,8 +514,26 @@ __global__ __launch_bounds__(WIDE ? 1024 : 256) void route_topk_kernel(int T, in
   }
   __syncthreads();
 
-  // 4. exact ranks of the candidates
-  if (total <= kMaxCand) {
+  // 4. exact ranks of the candidates: with at most NT/4 of them, four threads share a
+  //    candidate, each comparing it with every fourth other one, and add their counts
+  if (4 * total <= NT) {
+    const int c = tid >> 2, part = tid & 3;
+    const bool has = c < total;
+    const uint64_t kv = has ? ckey[c] : 0ull;
+    const int id = has ? cid[c] : 0;
+    int r = 0;
+    if (has) {
+#pragma unroll 4
+      for (int j = part; j < total; j += 4) r += better(ckey[j], cid[j], kv, id) ? 1 : 0;
+    }
+    r += __shfl_xor(r, 1, 64);
+    r += __shfl_xor(r, 2, 64);
+    if (has && part == 0 && r < k) {
+      ids[(size_t)t * k + r] = id;
+      gates[(size_t)t * k + r] = (float)(exp(key_to_double(kv) - m) / sum);
+      if (bk.offsets) s_ids[r] = id;
+    }
+  } else if (total <= kMaxCand) {
     for (int c = tid; c < total; c += NT) {
       const int id = cid[c];
       const uint64_t kv = ckey[c];
@@ -542,7 +550,7 @@ __global__ __launch_bounds__(WIDE ? 1024 : 256) void route_topk_kernel(int T, in
     // very many exact ties: rank every candidate against all logits
     for (int e = tid; e < E; e += NT) {
       const uint64_t kv = keys[e];
-      if (better(tk, ti, kv, e)) continue;
+      if ((uint32_t)(kv >> 32) < tk) continue;
       int r = 0;
       for (int j = 0; j < E; ++j) r += better(keys[j], j, kv, e) ? 1 : 0;
       if (r < k) {
