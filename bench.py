@@ -71,6 +71,45 @@ def expert_bytes_per_step(w, ids_np) -> int:
     return int(len(np.unique(ids_np))) * w.expert_bytes
 
 
+def capture_graph(fn):
+    """One HIP graph of fn(), captured on a torch stream after an eager run of fn()."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def timed_loop(args, step, nsets):
+    """Warm-up, then exactly args.steps timed steps (eager, or graph replays with --graph);
+    returns (t0, t1)."""
+    import torch
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if args.graph:
+        graphs = [capture_graph(lambda s=s: step(s)) for s in range(nsets)]
+        for i in range(args.warmup):
+            graphs[i % nsets].replay()
+        torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if args.graph:
+            graphs[(args.warmup + i) % nsets].replay()
+        else:
+            step(args.warmup + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return t0, t1
+
+
 def cpu_baseline(w, n_tokens: int, budget_s: float = 20.0):
     """Time the fp64 oracle on single-token layers of the same workload.
 
@@ -115,6 +154,9 @@ def main() -> int:
     ap.add_argument("--token-sets", type=int, default=64)
     ap.add_argument("--cpu-tokens", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one HIP graph per token set (captured on the "
+                         "caller's stream) instead of eager calls")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -165,14 +207,7 @@ def main() -> int:
         k3.layer_forward(dims, xs[s], wr, bias, ex, y=y, y_bf16=ybf, ids=ids[s], gates=gates,
                          ws=ws)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    t0, t1 = timed_loop(args, step, nsets)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
     ids_np = ids.cpu().numpy()
@@ -260,7 +295,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {workload_desc(w)}",
                    "bytes_per_step": int(round(bytes_timed / args.steps)),
-                   "token_sets": nsets},
+                   "token_sets": nsets, "hip_graph": bool(args.graph)},
         "roofline": roof,
         "kernels": extra,
     }
@@ -322,14 +357,7 @@ def bench_stack(args, w) -> int:
             k3.layer_forward(dims, h, wr, bias, ex, blk, y=y, ids=ids[l], gates=gates, ws=ws)
             h = y
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    t0, t1 = timed_loop(args, step, nsets)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     ids_np = ids.cpu().numpy()
     distinct = [len(np.unique(ids_np[l])) for l in range(w.layers)]
@@ -369,7 +397,8 @@ def bench_stack(args, w) -> int:
         "data": "synthetic",
         "config": {"workload": f"stack8: {workload_desc(w)} layers={w.layers}, block "
                                "(RMSNorm, shared expert, residual)",
-                   "bytes_per_step": int(bytes_step), "token_sets": nsets},
+                   "bytes_per_step": int(bytes_step), "token_sets": nsets,
+                   "hip_graph": bool(args.graph)},
         "roofline": {"bound": "hbm",
                      "kernel": "gateup_decode_kernel (MXFP4 gate/up GEMV + SwiGLU)",
                      "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -37,14 +37,16 @@
  *   - Every pointer argument except `stream` and the structs' host copies is DEVICE
  *     memory owned by the caller. The library never allocates device memory; its only
  *     state is cached device properties and, once block mode has run on a device, one
- *     non-blocking side stream of default priority for that device. Calls with distinct
- *     workspaces may run concurrently on distinct streams.
+ *     non-blocking side stream of default priority for that device and, per host thread
+ *     that ran block mode there, one pair of fork/join events (all kept until the process
+ *     ends). Calls with distinct workspaces may run concurrently on distinct streams.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = default
  *     stream). The caller synchronises. In block mode the shared expert runs on the
  *     side stream, forked from `stream` after the RMSNorm and joined back into it (by
- *     events created per call) before the launch that adds it into y, so all of a
- *     call's work is complete once `stream` is. Results are bit-identical from run to
- *     run.
+ *     the calling thread's events) before the launch that adds it into y, so all of a
+ *     call's work is complete once `stream` is; the same calls can be captured into a
+ *     HIP graph on `stream` (the side stream joins the capture through the fork event).
+ *     Results are bit-identical from run to run.
  *   - Arguments are validated on the host before anything is enqueued; nothing is
  *     defaulted. Errors: K3MOE_EINVAL (null required pointer, negative T, d_model or
  *     d_ff not a positive multiple of 32, n_experts < 1, top_k outside

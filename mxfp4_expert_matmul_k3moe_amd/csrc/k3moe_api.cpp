@@ -213,17 +213,25 @@ k3moe::BucketOut bucket_out(const Ws& ws, int32_t* offsets, int32_t* rows) {
   return o;
 }
 
-// An event owned for the duration of one call (destroying a recorded event is allowed:
-// it is released once its pending work is done).
-struct EventGuard {
-  hipEvent_t e = nullptr;
-  EventGuard() = default;
-  EventGuard(const EventGuard&) = delete;
-  EventGuard& operator=(const EventGuard&) = delete;
-  ~EventGuard() {
-    if (e) hipEventDestroy(e);
+// Fork and join events of block mode: one pair per host thread and device, created on
+// first use and kept. Each call records them again; a stream wait takes the event's record
+// at the time of the wait, calls from one thread are ordered on the host, and other
+// threads have their own pair. (Creating and destroying them per call cost more host
+// time than a decoder block's kernels take on the GPU.)
+bool fork_join_events(hipEvent_t& fork, hipEvent_t& joined) {
+  thread_local hipEvent_t ev[64][2] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  for (int i = 0; i < 2; ++i) {
+    if (!ev[dev][i] && hipEventCreateWithFlags(&ev[dev][i], hipEventDisableTiming) != hipSuccess) {
+      ev[dev][i] = nullptr;
+      return false;
+    }
   }
-};
+  fork = ev[dev][0];
+  joined = ev[dev][1];
+  return true;
+}
 
 // One non-blocking side stream per device (default priority), created on first use and
 // kept for the life of the process, for work that can overlap the routed path.
@@ -471,16 +479,15 @@ int k3moe_layer_forward(const k3moe_dims* dims, int32_t T, const void* x, int x_
   // top-k and gate/up, and the launch that adds it into y waits for it (per-call events).
   const float* resid = nullptr;
   const float* shared = nullptr;
-  EventGuard fork, joined;
+  hipEvent_t fork = nullptr, joined = nullptr;
   if (blk) {
     float* ssh = w.at<float>(R_SSH);
     hipStream_t s2 = side_stream();
-    if (s2 && (hipEventCreateWithFlags(&fork.e, hipEventDisableTiming) != hipSuccess ||
-               hipEventCreateWithFlags(&joined.e, hipEventDisableTiming) != hipSuccess))
+    if (s2 && !fork_join_events(fork, joined))
       s2 = nullptr;  // no side stream: the shared expert runs in order on `s`
     if (s2) {
-      if ((rc = hip_check(hipEventRecord(fork.e, s), "fork shared expert")) ||
-          (rc = hip_check(hipStreamWaitEvent(s2, fork.e, 0), "fork shared expert")))
+      if ((rc = hip_check(hipEventRecord(fork, s), "fork shared expert")) ||
+          (rc = hip_check(hipStreamWaitEvent(s2, fork, 0), "fork shared expert")))
         return rc;
     }
     rc = hip_check(k3moe::launch_dense_swiglu(T, d, dims->d_ff, static_cast<const float*>(xin),
@@ -488,11 +495,8 @@ int k3moe_layer_forward(const k3moe_dims* dims, int32_t T, const void* x, int x_
                                               w.at<float>(R_HSH), ssh, s2 ? s2 : s),
                    "shared expert");
     if (rc) return rc;
-    if (s2 && (rc = hip_check(hipEventRecord(joined.e, s2), "join shared expert"))) return rc;
-    if (!s2 && joined.e) {
-      hipEventDestroy(joined.e);
-      joined.e = nullptr;
-    }
+    if (s2 && (rc = hip_check(hipEventRecord(joined, s2), "join shared expert"))) return rc;
+    if (!s2) joined = nullptr;
     resid = static_cast<const float*>(x);
     shared = ssh;
   }
@@ -511,7 +515,7 @@ int k3moe_layer_forward(const k3moe_dims* dims, int32_t T, const void* x, int x_
     if (rc) return rc;
   }
   return run_ffn(*dims, T, xin, xf32, experts, offs, rows, gates, resid, shared, y, y_bf16, w, s,
-                 joined.e);
+                 joined);
 }
 
 }  // extern "C"
