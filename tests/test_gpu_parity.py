@@ -172,6 +172,29 @@ def test_zero_input_routes_first_k(dev):
     assert_layer(w, g, ref)
 
 
+@pytest.mark.parametrize("E,k,T", [(32, 4, 1), (896, 16, 1), (896, 16, 80)])
+def test_router_near_ties_below_upper_key_bits(dev, E, k, T):
+    # x = 0, so every logit is exactly its fp32 bias. Clusters of biases that differ only
+    # in the last fp32 mantissa bits share the upper 32 bits of their fp64 order keys, so
+    # the threshold cannot separate them and the exact ranking on full keys must.
+    say(f"router near-ties in the low key bits: E={E} k={k} T={T}")
+    rng = np.random.default_rng(E + k + T)
+    perm = rng.permutation(E)
+    bias = rng.uniform(-2.0, -1.0, E).astype(np.float32)
+    for c, base in enumerate((1.0, 0.5, 0.25)):
+        idx = perm[8 * c:8 * c + 8]
+        bias[idx] = (np.float32(base) + rng.permutation(8).astype(np.float32) *
+                     np.float32(base * 2.0 ** -23)).astype(np.float32)
+    d = 512
+    dims = k3.make_dims(d, 256, E, k)
+    x = torch.zeros((T, d), dtype=torch.bfloat16, device=dev)
+    wr = torch.zeros((d, E), dtype=torch.bfloat16, device=dev)
+    ids, gates = k3.router(dims, x, wr, torch.from_numpy(bias).to(dev))
+    torch.cuda.synchronize()
+    ids_r, gates_r = oracle.route(np.tile(bias.astype(np.float64), (T, 1)), k)
+    check_routing(ids.cpu().numpy(), gates.cpu().numpy(), ids_r, gates_r)
+
+
 def test_nan_scale_propagates(dev):
     w = TOY
     say("E8M0 255 in one down row of a selected expert")
