@@ -832,6 +832,195 @@ __global__ __launch_bounds__(256) void x8_prep_kernel(int d, const uint16_t* __r
   }
 }
 
+
+// ---- down projection of one token on the block-scaled MFMA (decode) -----------------------
+// Persistent: one block per CU, one wave per slot (k <= 16); the block walks 16-row tiles of
+// the output (tile = block, block + grid, ...). Wave q:
+//  1. loads its expert's 16 rows of the tile as the MFMA's FP4 operand straight into
+//     registers: for K step s (128 elements), lane (r, g) = (lane & 15, lane >> 4) takes
+//     MXFP4 block 4s + g of row r (the four lanes of a row read 64 contiguous bytes) and the
+//     dword with the step's four scale bytes of its row (its own is byte g);
+//  2. once per block, while the first tile's loads are in flight, splits the slot's fp32 h
+//     into three E4M3 terms with one E8M0 scale per term (for the whole slot, steps of 2^4
+//     apart) into its own LDS area (natural order);
+//  3. runs one MFMA per step with the three terms as B columns 0..2 (other columns zero), so
+//     column c of the result is term c's share of z; z = (C0 + C1) + C2. The next tile's
+//     weight loads are issued as soon as the last MFMA has its operands.
+// After a barrier the block adds the k slot results of each row in slot order, so y is
+// bit-identical from run to run. Weights are multiplied as stored; nothing is decoded.
+constexpr int kDecMfmaSlots = 16;
+constexpr int kDecMfmaMaxF = 1536;  // K steps <= 12
+constexpr int kDecTermBytes = 3 * kDecMfmaMaxF;
+
+struct DownDecMArgs {
+  int d, f, k;
+  const uint8_t *dq, *ds;
+  const float* h;
+  const int32_t *pair_pos, *pair_exp;
+  const float* gates;
+  const float *resid, *shared;
+  float* y;
+  uint16_t* y_bf16;
+};
+
+template <int NK>
+__global__ __launch_bounds__(1024) void down_decode_mfma_kernel(DownDecMArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t tb[kDecMfmaSlots][kDecTermBytes];
+  __shared__ float zs[2][kDecMfmaSlots][16];
+  __shared__ float gsh[kDecMfmaSlots];
+  const int F = NK * BK, FB = F >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, q = tid >> 6;  // wave = slot
+  const int ln = lane & 15, g = lane >> 4;
+  const int ntiles = a.d >> 4;  // d % 16 == 0
+  int tile = blockIdx.x;
+  if (tid < a.k) gsh[tid] = a.gates[tid];
+  const int pos = a.pair_pos[q];
+  const int e = a.pair_exp[q];
+  const bool sv = pos >= 0 && e >= 0;
+
+  // h of the slot first (four values per lane and round), so that waiting for it later
+  // leaves the weight loads behind it in flight
+  constexpr int NR = (NK * BK / 4 + 63) / 64;
+  const float* hr = a.h + (size_t)(sv ? pos : 0) * F;
+  f32x4 hv[NR];
+#pragma unroll
+  for (int v0 = 0; v0 < NR; ++v0) {
+    const int c = v0 * 64 + lane;
+    hv[v0] = c < (F >> 2) ? reinterpret_cast<const f32x4*>(hr)[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // 1. weights of one tile's 16 rows (every row exists)
+  const uint8_t* wq0 = a.dq + ((size_t)(sv ? e : 0) * a.d + ln) * (size_t)(F >> 1) + 16 * g;
+  const uint8_t* ws0 = a.ds + ((size_t)(sv ? e : 0) * a.d + ln) * (size_t)FB;
+  u32x4 w[NK];
+  uint32_t sw[NK];
+  auto load_tile = [&](int t) {
+    const uint8_t* wq = wq0 + (size_t)t * 16 * (size_t)(F >> 1);
+    const uint32_t* wsc = reinterpret_cast<const uint32_t*>(ws0 + (size_t)t * 16 * (size_t)FB);
+#pragma unroll
+    for (int s = 0; s < NK; ++s) sw[s] = wsc[s];  // scales first: step s waits for block s only
+#pragma unroll
+    for (int s = 0; s < NK; ++s) w[s] = load_u32x4_nt(wq + 64 * s);
+  };
+  load_tile(tile);  // the grid has at most one block per tile, so this tile exists
+
+  // 2. three E4M3 terms of h with one E8M0 scale per term for the whole slot: 2^(s0-127)
+  //    puts the slot maximum in [128, 256), term t has scale s0 - 4t. RNE to E4M3 leaves a
+  //    remainder of at most 2^-4 of each value, so 16 x the remainder fits the next term,
+  //    and every value is carried to about 2^-12 of itself (subnormal floor 2^-18 of the
+  //    slot maximum). A non-finite maximum gives scale bytes 255 (NaN), as does the oracle's
+  //    sum over every h value for each output row.
+  uint8_t* tq = tb[q];
+  float mx = 0.0f;
+#pragma unroll
+  for (int v0 = 0; v0 < NR; ++v0)
+    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(hv[v0][0]), fabsf(hv[v0][1])),
+                         fmaxf(fabsf(hv[v0][2]), fabsf(hv[v0][3]))));
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  const int e0 = top_exp(mx);
+  const bool bad = e0 == kExpBad;
+  const int s0 = bad ? 255 : min(max(e0 + 127, 0), 254);
+  int tsc[3], ter[3];  // term scale byte and its exponent relative to term 0
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    tsc[t] = bad ? 255 : max(s0 - 4 * t, 0);
+    ter[t] = tsc[t] - s0;
+  }
+#pragma unroll
+  for (int v0 = 0; v0 < NR; ++v0) {
+    const int c = v0 * 64 + lane;
+    float y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = ldexpf(hv[v0][i], 127 - s0);  // exact: maximum < 256
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      float ys[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ys[i] = t == 0 ? y[i] : ldexpf(y[i], -ter[t]);
+      // two E4M3 codes (RNE) per conversion, written into the term's dword in place
+      int wd = __builtin_amdgcn_cvt_pk_fp8_f32(ys[0], ys[1], 0, false);
+      wd = __builtin_amdgcn_cvt_pk_fp8_f32(ys[2], ys[3], wd, true);
+      if (t < 2) {
+        y[0] -= ldexpf(__builtin_amdgcn_cvt_f32_fp8(wd, 0), ter[t]);
+        y[1] -= ldexpf(__builtin_amdgcn_cvt_f32_fp8(wd, 1), ter[t]);
+        y[2] -= ldexpf(__builtin_amdgcn_cvt_f32_fp8(wd, 2), ter[t]);
+        y[3] -= ldexpf(__builtin_amdgcn_cvt_f32_fp8(wd, 3), ter[t]);
+      }
+      if (c < (F >> 2)) *reinterpret_cast<int*>(tq + t * F + 4 * c) = wd;
+    }
+  }
+  // the wave reads back what its own lanes wrote (LDS operations of a wave are in order)
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+
+  // 3. one MFMA per K step; B column ln < 3 is term ln, the rest zero with scale 1
+  const bool bl = ln < 3;
+  const uint8_t* tb_ln = tq + (bl ? ln : 0) * F + 16 * g;
+  const int bsc = bl ? tsc[ln == 0 ? 0 : (ln == 1 ? 1 : 2)] : 127;
+  for (int it = 0; tile < ntiles; ++it) {
+    // the B operands are the same for every tile; they are read again per tile from LDS, one
+    // step ahead of the MFMA that takes them (the asm statements keep the compiler from
+    // gathering all of them into the registers the weights need)
+    asm volatile("" ::: "memory");
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    u32x4 b0 = {0u, 0u, 0u, 0u}, b1 = {0u, 0u, 0u, 0u};
+    if (bl) {
+      b0 = *reinterpret_cast<const u32x4*>(tb_ln);
+      b1 = *reinterpret_cast<const u32x4*>(tb_ln + 64);
+    }
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      u32x4 n0 = {0u, 0u, 0u, 0u}, n1 = {0u, 0u, 0u, 0u};
+      if (s + 1 < NK && bl) {
+        n0 = *reinterpret_cast<const u32x4*>(tb_ln + BK * (s + 1));
+        n1 = *reinterpret_cast<const u32x4*>(tb_ln + BK * (s + 1) + 64);
+      }
+      // an FP4 operand occupies the low four registers of the tuple; the upper four are
+      // left undefined so that no zero registers are kept per step
+      typedef int i32x4v __attribute__((ext_vector_type(4)));
+      const i32x4v wi = __builtin_bit_cast(i32x4v, w[s]);
+      const i32x8 aop = __builtin_shufflevector(wi, wi, 0, 1, 2, 3, -1, -1, -1, -1);
+      const i32x8 bop = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                         (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+      const int asc = (int)((sw[s] >> (8 * g)) & 0xFFu);
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop, acc, 4, 0, 0, asc, 0, bsc);
+      b0 = n0;
+      b1 = n1;
+      // ties the MFMA to this point: the next step's LDS reads (and, after the last step,
+      // the next tile's weight loads) stay below it
+      asm volatile("" : "+v"(acc)::"memory");
+    }
+    const int r0 = tile * 16;
+    const int next = tile + (int)gridDim.x;
+    const bool more = next < ntiles;  // on the only path that goes on, w is reloaded
+    if (more) load_tile(next);
+    // lane (c, g) holds column c of rows 4 g .. 4 g + 3
+    float (*zb)[16] = zs[it & 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float c1 = __shfl_down(acc[i], 1, 64);
+      const float c2 = __shfl_down(acc[i], 2, 64);
+      if (ln == 0) zb[q][4 * g + i] = sv ? (acc[i] + c1) + c2 : 0.0f;
+    }
+    // barrier without draining the next tile's loads: only LDS writes must be complete
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (tid < 16) {
+      const int r = r0 + tid;
+      float s2 = 0.0f;
+      for (int j = 0; j < a.k; ++j) s2 = fmaf(gsh[j], zb[j][tid], s2);
+      float out = s2;
+      if (a.resid) out = (a.resid[r] + (a.shared ? a.shared[r] : 0.0f)) + s2;
+      a.y[r] = out;
+      if (a.y_bf16) a.y_bf16[r] = f32_to_bf16_rne(out);
+    }
+    if (!more) break;
+    tile = next;
+  }
+}
+
 }  // namespace
 
 int mfma_mtiles_bound(int T, int E, int k) {
@@ -874,6 +1063,35 @@ hipError_t launch_down_mfma(int T, int d, int f, int E, int k, const MxPtrs& w,
   a.z_out = z;
   dim3 grid((unsigned)(mfma_mtiles_bound(T, E, k) * a.nblk_n));
   mfma_ffn_kernel<false><<<grid, 512, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+
+bool down_decode_mfma_supported(int d, int f, int k) {
+  return d % 16 == 0 && f % BK == 0 && f <= kDecMfmaMaxF && k >= 1 && k <= kDecMfmaSlots;
+}
+
+hipError_t launch_down_decode_mfma(int d, int f, int k, const MxPtrs& w, const float* h,
+                                   const int32_t* pair_pos, const int32_t* pair_exp,
+                                   const float* gates, const float* resid, const float* shared,
+                                   float* y, uint16_t* y_bf16, int n_cu, hipStream_t s) {
+  DownDecMArgs a;
+  a.d = d; a.f = f; a.k = k; a.dq = w.down_q; a.ds = w.down_s; a.h = h;
+  a.pair_pos = pair_pos; a.pair_exp = pair_exp; a.gates = gates;
+  a.resid = resid; a.shared = shared; a.y = y; a.y_bf16 = y_bf16;
+  const int ntiles = d / 16;
+  const dim3 grid((unsigned)(ntiles < n_cu ? ntiles : (n_cu > 0 ? n_cu : 1))), block((unsigned)(64 * k));
+  switch (f / BK) {
+#define K3_DM(N)                                               \
+  case N:                                                      \
+    down_decode_mfma_kernel<N><<<grid, block, 0, s>>>(a);      \
+    break;
+    K3_DM(1) K3_DM(2) K3_DM(3) K3_DM(4) K3_DM(5) K3_DM(6)
+    K3_DM(7) K3_DM(8) K3_DM(9) K3_DM(10) K3_DM(11) K3_DM(12)
+#undef K3_DM
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -71,6 +71,14 @@ hipError_t launch_down_decode(int d, int f, int k, const MxPtrs& w, const float*
                               const float* gates, const float* resid, const float* shared,
                               float* y, uint16_t* y_bf16, int n_cu, hipStream_t s,
                               int rows_per_block = 0, int rows_per_step = 4);
+// T == 1 down projection + ordered combine on the block-scaled MFMA (ffn_mfma.hip): one
+// persistent block per CU walking 16-row output tiles, one wave per slot; needs d % 16 == 0,
+// f % 128 == 0, f <= 1536 and k <= 16. launch_down_decode takes it whenever the shape allows.
+bool down_decode_mfma_supported(int d, int f, int k);
+hipError_t launch_down_decode_mfma(int d, int f, int k, const MxPtrs& w, const float* h,
+                                   const int32_t* pair_pos, const int32_t* pair_exp,
+                                   const float* gates, const float* resid, const float* shared,
+                                   float* y, uint16_t* y_bf16, int n_cu, hipStream_t s);
 // Any T: per-expert down projection into z [P][d] (pair-indexed).
 hipError_t launch_down_gemv(int T, int d, int f, int E, int k, const MxPtrs& w,
                             const float* h, const int32_t* offsets, const int32_t* rows,
