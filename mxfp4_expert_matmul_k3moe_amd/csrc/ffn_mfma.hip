@@ -834,8 +834,8 @@ __global__ __launch_bounds__(256) void x8_prep_kernel(int d, const uint16_t* __r
 
 
 // ---- down projection of one token on the block-scaled MFMA (decode) -----------------------
-// Persistent: one block per CU, one wave per slot (k <= 16); the block walks 16-row tiles of
-// the output (tile = block, block + grid, ...). Wave q:
+// Persistent: one block per CU, one wave per slot (k <= 16); the block owns an equal range of
+// output rows (28 of 7168 on 256 CUs) and walks it in tiles of 16 rows. Wave q:
 //  1. loads its expert's 16 rows of the tile as the MFMA's FP4 operand straight into
 //     registers: for K step s (128 elements), lane (r, g) = (lane & 15, lane >> 4) takes
 //     MXFP4 block 4s + g of row r (the four lanes of a row read 64 contiguous bytes) and the
@@ -861,6 +861,7 @@ struct DownDecMArgs {
   const float *resid, *shared;
   float* y;
   uint16_t* y_bf16;
+  int rpb;  // output rows per block
 };
 
 template <int NK>
@@ -871,8 +872,9 @@ __global__ __launch_bounds__(1024) void down_decode_mfma_kernel(DownDecMArgs a) 
   const int F = NK * BK, FB = F >> 5;
   const int tid = threadIdx.x, lane = tid & 63, q = tid >> 6;  // wave = slot
   const int ln = lane & 15, g = lane >> 4;
-  const int ntiles = a.d >> 4;  // d % 16 == 0
-  int tile = blockIdx.x;
+  // rows [rb0, rb1) of this block, walked in tiles of 16 (the last may be partial)
+  const int rb0 = blockIdx.x * a.rpb, rb1 = min(a.d, rb0 + a.rpb);
+  int r0 = rb0;
   if (tid < a.k) gsh[tid] = a.gates[tid];
   const int pos = a.pair_pos[q];
   const int e = a.pair_exp[q];
@@ -889,20 +891,23 @@ __global__ __launch_bounds__(1024) void down_decode_mfma_kernel(DownDecMArgs a) 
     hv[v0] = c < (F >> 2) ? reinterpret_cast<const f32x4*>(hr)[c] : f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // 1. weights of one tile's 16 rows (every row exists)
-  const uint8_t* wq0 = a.dq + ((size_t)(sv ? e : 0) * a.d + ln) * (size_t)(F >> 1) + 16 * g;
-  const uint8_t* ws0 = a.ds + ((size_t)(sv ? e : 0) * a.d + ln) * (size_t)FB;
+  // 1. weights of one tile's 16 rows; lanes of rows past the block's range read the last row
+  //    of the range again (same addresses as a lane in the same load, so no extra traffic;
+  //    their results are never combined). Unconditional loads keep the wait counts exact.
+  const uint8_t* wq0 = a.dq + (size_t)(sv ? e : 0) * a.d * (size_t)(F >> 1) + 16 * g;
+  const uint8_t* ws0 = a.ds + (size_t)(sv ? e : 0) * a.d * (size_t)FB;
   u32x4 w[NK];
   uint32_t sw[NK];
-  auto load_tile = [&](int t) {
-    const uint8_t* wq = wq0 + (size_t)t * 16 * (size_t)(F >> 1);
-    const uint32_t* wsc = reinterpret_cast<const uint32_t*>(ws0 + (size_t)t * 16 * (size_t)FB);
+  auto load_tile = [&](int rt) {
+    const int row = min(rt + ln, rb1 - 1);
+    const uint8_t* wq = wq0 + (size_t)row * (size_t)(F >> 1);
+    const uint32_t* wsc = reinterpret_cast<const uint32_t*>(ws0 + (size_t)row * (size_t)FB);
 #pragma unroll
     for (int s = 0; s < NK; ++s) sw[s] = wsc[s];  // scales first: step s waits for block s only
 #pragma unroll
     for (int s = 0; s < NK; ++s) w[s] = load_u32x4_nt(wq + 64 * s);
   };
-  load_tile(tile);  // the grid has at most one block per tile, so this tile exists
+  load_tile(r0);  // every block has at least one row
 
   // 2. three E4M3 terms of h with one E8M0 scale per term for the whole slot: 2^(s0-127)
   //    puts the slot maximum in [128, 256), term t has scale s0 - 4t. RNE to E4M3 leaves a
@@ -958,7 +963,7 @@ __global__ __launch_bounds__(1024) void down_decode_mfma_kernel(DownDecMArgs a) 
   const bool bl = ln < 3;
   const uint8_t* tb_ln = tq + (bl ? ln : 0) * F + 16 * g;
   const int bsc = bl ? tsc[ln == 0 ? 0 : (ln == 1 ? 1 : 2)] : 127;
-  for (int it = 0; tile < ntiles; ++it) {
+  for (int it = 0;; ++it) {
     // the B operands are the same for every tile; they are read again per tile from LDS, one
     // step ahead of the MFMA that takes them (the asm statements keep the compiler from
     // gathering all of them into the registers the weights need)
@@ -991,9 +996,8 @@ __global__ __launch_bounds__(1024) void down_decode_mfma_kernel(DownDecMArgs a) 
       // the next tile's weight loads) stay below it
       asm volatile("" : "+v"(acc)::"memory");
     }
-    const int r0 = tile * 16;
-    const int next = tile + (int)gridDim.x;
-    const bool more = next < ntiles;  // on the only path that goes on, w is reloaded
+    const int next = r0 + 16;
+    const bool more = next < rb1;  // on the only path that goes on, w is reloaded
     if (more) load_tile(next);
     // lane (c, g) holds column c of rows 4 g .. 4 g + 3
     float (*zb)[16] = zs[it & 1];
@@ -1007,7 +1011,7 @@ __global__ __launch_bounds__(1024) void down_decode_mfma_kernel(DownDecMArgs a) 
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (tid < 16) {
+    if (tid < min(16, rb1 - r0)) {
       const int r = r0 + tid;
       float s2 = 0.0f;
       for (int j = 0; j < a.k; ++j) s2 = fmaf(gsh[j], zb[j][tid], s2);
@@ -1017,7 +1021,7 @@ __global__ __launch_bounds__(1024) void down_decode_mfma_kernel(DownDecMArgs a) 
       if (a.y_bf16) a.y_bf16[r] = f32_to_bf16_rne(out);
     }
     if (!more) break;
-    tile = next;
+    r0 = next;
   }
 }
 
@@ -1079,8 +1083,11 @@ hipError_t launch_down_decode_mfma(int d, int f, int k, const MxPtrs& w, const f
   a.d = d; a.f = f; a.k = k; a.dq = w.down_q; a.ds = w.down_s; a.h = h;
   a.pair_pos = pair_pos; a.pair_exp = pair_exp; a.gates = gates;
   a.resid = resid; a.shared = shared; a.y = y; a.y_bf16 = y_bf16;
-  const int ntiles = d / 16;
-  const dim3 grid((unsigned)(ntiles < n_cu ? ntiles : (n_cu > 0 ? n_cu : 1))), block((unsigned)(64 * k));
+  // equal row ranges for one block per CU (16 rows at least)
+  const int nb = n_cu > 0 ? n_cu : 1;
+  a.rpb = (d + nb - 1) / nb;
+  if (a.rpb < 16) a.rpb = 16;
+  const dim3 grid((unsigned)((d + a.rpb - 1) / a.rpb)), block((unsigned)(64 * k));
   switch (f / BK) {
 #define K3_DM(N)                                               \
   case N:                                                      \

@@ -72,8 +72,9 @@ hipError_t launch_down_decode(int d, int f, int k, const MxPtrs& w, const float*
                               float* y, uint16_t* y_bf16, int n_cu, hipStream_t s,
                               int rows_per_block = 0, int rows_per_step = 4);
 // T == 1 down projection + ordered combine on the block-scaled MFMA (ffn_mfma.hip): one
-// persistent block per CU walking 16-row output tiles, one wave per slot; needs d % 16 == 0,
-// f % 128 == 0, f <= 1536 and k <= 16. launch_down_decode takes it whenever the shape allows.
+// persistent block per CU walking its equal share of output rows in 16-row tiles, one wave
+// per slot; needs d % 16 == 0, f % 128 == 0, f <= 1536 and k <= 16. launch_down_decode takes
+// it whenever the shape allows.
 bool down_decode_mfma_supported(int d, int f, int k);
 hipError_t launch_down_decode_mfma(int d, int f, int k, const MxPtrs& w, const float* h,
                                    const int32_t* pair_pos, const int32_t* pair_exp,
