@@ -551,7 +551,9 @@ hipError_t launch_down_decode(int d, int f, int k, const MxPtrs& w, const float*
                               const float* gates, const float* resid, const float* shared,
                               float* y, uint16_t* y_bf16, int n_cu, hipStream_t s,
                               int rows_per_block, int rows_per_step) {
-  if (rows_per_block == 0 && down_decode_mfma_supported(d, f, k))
+  // the MFMA kernel reads the scales as dwords: it needs them 4-byte aligned
+  if (rows_per_block == 0 && (reinterpret_cast<uintptr_t>(w.down_s) & 3u) == 0 &&
+      down_decode_mfma_supported(d, f, k))
     return launch_down_decode_mfma(d, f, k, w, h, pair_pos, pair_exp, gates, resid, shared, y,
                                    y_bf16, n_cu, s);
   DownT1Args a;

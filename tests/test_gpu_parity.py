@@ -112,6 +112,10 @@ SHAPES = [
     # the smallest token count that takes the grouped MFMA path; d and f multiples of 512
     # (scales fetched 4 steps at a time)
     Workload("mfma_t16", 20, d=512, f=512, E=10, k=3, T=16),
+    # one token with more than 16 slots: the fp32-FMA down kernel instead of the MFMA one
+    Workload("k20_t1", 21, d=512, f=256, E=40, k=20, T=1),
+    # one token on the MFMA down kernel with 6 K steps (f = 768)
+    Workload("mfma_t1_f768", 22, d=384, f=768, E=12, k=5, T=1),
 ]
 
 
@@ -234,6 +238,27 @@ def test_nan_scales_propagate_grouped_gemm(dev):
         assert np.array_equal(np.isnan(yg), nan_ref)
         ok = ~nan_ref.any(axis=1)  # tokens that did not pick e stay within tolerance
         assert rel_l2(yg[ok].astype(np.float64), ref["y"][ok]).max() <= TOL
+
+
+def test_unaligned_scales_take_the_gemv_kernels(dev):
+    """Scale arrays starting at an odd address: the MFMA kernels read scales as dwords, so
+    one token (down) and 20 tokens (grouped GEMMs) must fall back to the byte-reading GEMV
+    kernels and still match the oracle."""
+    for w in (TOY, TOY.with_(T=20, name="toy20")):
+        say(f"odd-address scale arrays ({w.name}, T={w.T})")
+        x = w.x_bf16()
+        ex = gdev.experts(w, 0, dev)
+        for name in ("gate_s", "up_s", "down_s"):
+            t = ex[name]
+            buf = torch.empty(t.numel() + 1, dtype=torch.uint8, device=dev)
+            v = buf[1:].view(t.shape)
+            v.copy_(t)
+            assert v.data_ptr() % 2 == 1
+            ex[name] = v
+        g = run_gpu_layer(w, x, dev, experts=ex)
+        ref = harness.run_layer(w, x)
+        err = assert_layer(w, g, ref)
+        assert err.max() < 1e-4
 
 
 def test_down_scale_plus_one_doubles_exactly(dev):
