@@ -161,6 +161,65 @@ K3MOE_API int k3moe_layer_forward(const k3moe_dims* dims, int32_t T, const void*
                         uint16_t* y_bf16, int32_t* topk_ids, float* topk_gates, void* ws,
                         size_t ws_bytes, void* stream);
 
+/* ---- Routed experts beyond HBM: an HBM slot cache over host-resident experts ----------
+ * The routed experts are never all kept in fast memory: those a token selects are read on
+ * demand from slower storage and multiplied in their packed form, and recently used ones
+ * stay cached, least recently used evicted first ("用纯C语言把1.56TB的Kimi K3模型塞进8GB内存
+ * 运行", kongchang.com, section 专家权重永不常驻内存; project card "P053
+ * FareedKhan-dev/kimi-k3-in-c", core features, expert streaming; "Kimi K3 纯 C 语言 CPU 推理
+ * 实战" §3.3, the LRU expert cache). Here a layer's E experts stay in HOST memory and
+ * n_slots of them at a time in HBM:
+ *   host_experts: the k3moe_mx_experts layout with HOST pointers, all E experts (pinned
+ *     memory, e.g. hipHostMalloc, lets the copies run asynchronously; pageable memory works
+ *     but each copy then blocks the host);
+ *   slot_experts: the same layout with DEVICE pointers and n_slots in place of E;
+ *   state: a caller-owned HOST buffer of k3moe_cache_state_bytes() bytes, 8-byte aligned,
+ *     set up by k3moe_cache_init(); it maps experts to slots and keeps the host copies of
+ *     the routed ids. One state belongs to one (host_experts, slot_experts) pair; calls
+ *     that share a state must not overlap.
+ * Policy (k3moe_cache_plan): an expert already in a slot keeps it (hit); each missing expert,
+ * in order of first appearance among the ids, takes the least recently used slot that the
+ * same call does not use (lowest slot index among equals; empty slots first) (miss). */
+typedef struct {
+  int64_t hits;          /* distinct routed experts found in a slot       */
+  int64_t misses;        /* distinct routed experts copied into a slot    */
+  int64_t bytes_copied;  /* host -> HBM bytes enqueued for the misses     */
+  int32_t distinct;      /* distinct experts of the last call (0 if none) */
+} k3moe_cache_stats;
+
+/* Bytes of a state for n_experts experts, n_slots slots (1 <= n_slots <= n_experts) and up
+ * to max_ids routed ids (T * top_k) per call; 0 if the arguments are invalid. */
+K3MOE_API size_t k3moe_cache_state_bytes(int32_t n_experts, int32_t n_slots, int32_t max_ids);
+/* Empty cache (no expert resident). EINVAL: invalid arguments or state not 8-byte aligned;
+ * EWORKSPACE: state_bytes too small. */
+K3MOE_API int k3moe_cache_init(void* state, size_t state_bytes, int32_t n_experts,
+                               int32_t n_slots, int32_t max_ids);
+/* Host-side plan for n_ids routed ids (HOST array, each in [0, E)): updates the state and
+ * writes slot_ids[n_ids] (the slot of each id) and, per miss, fetch[2 i] = expert and
+ * fetch[2 i + 1] = slot (room for 2 * n_slots ints), *n_fetch = misses. EINVAL: an id out of
+ * range or a bad state; EUNSUPPORTED: more distinct experts than slots (nothing assigned).
+ * No GPU work. */
+K3MOE_API int k3moe_cache_plan(void* state, int32_t n_ids, const int32_t* ids,
+                               int32_t* slot_ids, int32_t* fetch, int32_t* n_fetch);
+/* Cumulative hits, misses and bytes of the state (distinct: that of the last call). */
+K3MOE_API int k3moe_cache_stats_get(const void* state, k3moe_cache_stats* out);
+/* One MoE layer (no block extras) with the experts in the slot cache: router on `stream`,
+ * routed ids copied to the host (this SYNCHRONISES `stream`), plan, host -> HBM copies of
+ * the missing experts enqueued on `stream`, slot ids to the device, bucketing by slot, and
+ * the routed experts run from the slots. y, y_bf16, topk_ids and topk_gates are those of
+ * k3moe_layer_forward with all E experts resident, bit for bit. call_stats (nullable, host)
+ * receives this call's hits, misses, bytes and distinct count. EUNSUPPORTED: T * top_k
+ * above the state's max_ids, top_k above n_slots, or more distinct experts in the batch
+ * than slots. ws: k3moe_workspace_bytes(dims, T). */
+K3MOE_API int k3moe_layer_forward_cached(const k3moe_dims* dims, int32_t T, const void* x,
+                                         int x_dtype, const uint16_t* w_router,
+                                         const float* logit_bias,
+                                         const k3moe_mx_experts* host_experts,
+                                         const k3moe_mx_experts* slot_experts, void* state,
+                                         float* y, uint16_t* y_bf16, int32_t* topk_ids,
+                                         float* topk_gates, k3moe_cache_stats* call_stats,
+                                         void* ws, size_t ws_bytes, void* stream);
+
 /* Diagnostics for live per-kernel timing. Arms a one-shot probe on the calling thread:
  * the next entry-point call that launches kernel `which` records hipEvent_t ev_start on
  * its stream right before that launch and ev_stop right after it, then disarms. The

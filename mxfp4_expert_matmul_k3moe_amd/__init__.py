@@ -45,6 +45,11 @@ class _Block(ctypes.Structure):
                 ("sh_down", ctypes.c_void_p)]
 
 
+class CacheStats(ctypes.Structure):
+    _fields_ = [("hits", ctypes.c_int64), ("misses", ctypes.c_int64),
+                ("bytes_copied", ctypes.c_int64), ("distinct", ctypes.c_int32)]
+
+
 @dataclasses.dataclass
 class MxExperts:
     """One layer of routed experts: uint8 device tensors, stacked over experts.
@@ -98,6 +103,19 @@ def lib() -> ctypes.CDLL:
         L.k3moe_layer_forward.argtypes = [D, i32, vp, ctypes.c_int, vp, vp,
                                           ctypes.POINTER(_MxExperts), ctypes.POINTER(_Block),
                                           vp, vp, vp, vp, vp, sz, vp]
+        L.k3moe_cache_state_bytes.restype = sz
+        L.k3moe_cache_state_bytes.argtypes = [i32, i32, i32]
+        L.k3moe_cache_init.restype = ctypes.c_int
+        L.k3moe_cache_init.argtypes = [vp, sz, i32, i32, i32]
+        L.k3moe_cache_plan.restype = ctypes.c_int
+        L.k3moe_cache_plan.argtypes = [vp, i32, vp, vp, vp, ctypes.POINTER(i32)]
+        L.k3moe_cache_stats_get.restype = ctypes.c_int
+        L.k3moe_cache_stats_get.argtypes = [vp, ctypes.POINTER(CacheStats)]
+        L.k3moe_layer_forward_cached.restype = ctypes.c_int
+        L.k3moe_layer_forward_cached.argtypes = [D, i32, vp, ctypes.c_int, vp, vp,
+                                                 ctypes.POINTER(_MxExperts),
+                                                 ctypes.POINTER(_MxExperts), vp, vp, vp, vp, vp,
+                                                 ctypes.POINTER(CacheStats), vp, sz, vp]
         _lib = L
     return _lib
 
@@ -271,3 +289,92 @@ def layer_forward(dims: Dims, x: torch.Tensor, w_router: torch.Tensor,
                                      _ptr(y_bf16), _ptr(ids), _ptr(gates), _ptr(w), w.numel(),
                                      _stream(stream)))
     return y
+
+
+# ---- routed experts beyond HBM: the slot cache -------------------------------------------
+class ExpertCache:
+    """Host state of an HBM slot cache over host-resident experts (k3moe_cache_*): which
+    expert sits in which of `n_slots` slots, least recently used evicted first. Held in a
+    host buffer owned here; `max_ids` bounds T * top_k per call."""
+
+    def __init__(self, n_experts: int, n_slots: int, max_ids: int):
+        import numpy as np
+        n = int(lib().k3moe_cache_state_bytes(n_experts, n_slots, max_ids))
+        if n == 0:
+            raise ValueError(f"invalid cache shape E={n_experts} slots={n_slots} "
+                             f"max_ids={max_ids}")
+        self._buf = np.zeros((n + 7) // 8, dtype=np.uint64)  # 8-byte aligned
+        self.n_experts, self.n_slots, self.max_ids = n_experts, n_slots, max_ids
+        _check(lib().k3moe_cache_init(self.ptr, self._buf.nbytes, n_experts, n_slots, max_ids))
+
+    @property
+    def ptr(self) -> ctypes.c_void_p:
+        return ctypes.c_void_p(self._buf.ctypes.data)
+
+    def plan(self, ids):
+        """Host-side plan for routed ids: returns (slot of each id, [(expert, slot) per miss])."""
+        import numpy as np
+        a = np.ascontiguousarray(np.asarray(ids, dtype=np.int32).reshape(-1))
+        slots = np.empty_like(a)
+        fetch = np.empty(2 * self.n_slots, dtype=np.int32)
+        nf = ctypes.c_int32(0)
+        _check(lib().k3moe_cache_plan(self.ptr, a.size, ctypes.c_void_p(a.ctypes.data),
+                                      ctypes.c_void_p(slots.ctypes.data),
+                                      ctypes.c_void_p(fetch.ctypes.data), ctypes.byref(nf)))
+        return slots, [(int(fetch[2 * i]), int(fetch[2 * i + 1])) for i in range(nf.value)]
+
+    def stats(self) -> CacheStats:
+        st = CacheStats()
+        _check(lib().k3moe_cache_stats_get(self.ptr, ctypes.byref(st)))
+        return st
+
+
+def _host_experts_struct(dims: Dims, ex: MxExperts) -> _MxExperts:
+    E, d, f = dims.n_experts, dims.d_model, dims.d_ff
+    shapes = {"gate_q": f * d // 2, "gate_s": f * d // 32, "up_q": f * d // 2,
+              "up_s": f * d // 32, "down_q": d * f // 2, "down_s": d * f // 32}
+    s = _MxExperts()
+    for n, per in shapes.items():
+        t = getattr(ex, n)
+        if t.is_cuda or not t.is_contiguous() or t.dtype != torch.uint8:
+            raise ValueError(f"host experts.{n} must be a contiguous uint8 host tensor")
+        if t.numel() != E * per:
+            raise ValueError(f"host experts.{n} has {t.numel()} bytes, expected {E * per}")
+        setattr(s, n, t.data_ptr())
+    return s
+
+
+def layer_forward_cached(dims: Dims, x: torch.Tensor, w_router: torch.Tensor,
+                         logit_bias: Optional[torch.Tensor], host_experts: MxExperts,
+                         slot_experts: MxExperts, cache: ExpertCache, *,
+                         y: Optional[torch.Tensor] = None, y_bf16: Optional[torch.Tensor] = None,
+                         ids: Optional[torch.Tensor] = None, gates: Optional[torch.Tensor] = None,
+                         ws: Optional[torch.Tensor] = None, stream=None):
+    """y = MoE(x) with the experts in host memory and `cache.n_slots` of them in HBM
+    (k3moe_layer_forward_cached; synchronises the stream once to read the routed ids).
+    Returns (y, this call's CacheStats)."""
+    T = x.shape[0]
+    d, E, k = dims.d_model, dims.n_experts, dims.top_k
+    _dev(x, "x", (torch.bfloat16, torch.float32), (T, d))
+    _dev(w_router, "w_router", (torch.bfloat16, torch.int16), (d, E))
+    if logit_bias is not None:
+        _dev(logit_bias, "logit_bias", torch.float32, (E,))
+    y = torch.empty((T, d), dtype=torch.float32, device=x.device) if y is None else \
+        _dev(y, "y", torch.float32, (T, d))
+    if y_bf16 is not None:
+        _dev(y_bf16, "y_bf16", (torch.bfloat16, torch.int16), (T, d))
+    if ids is not None:
+        _dev(ids, "ids", torch.int32, (T, k))
+    if gates is not None:
+        _dev(gates, "gates", torch.float32, (T, k))
+    hs = _host_experts_struct(dims, host_experts)
+    sdims = Dims(dims.d_model, dims.d_ff, cache.n_slots, dims.top_k)
+    ss = _experts_struct(sdims, slot_experts)
+    w = _ws(dims, T, ws, x.device)
+    st = CacheStats()
+    _check(lib().k3moe_layer_forward_cached(ctypes.byref(dims), T, _ptr(x), _x_dtype(x),
+                                            _ptr(w_router), _ptr(logit_bias), ctypes.byref(hs),
+                                            ctypes.byref(ss), cache.ptr, _ptr(y), _ptr(y_bf16),
+                                            _ptr(ids), _ptr(gates), ctypes.byref(st), _ptr(w),
+                                            w.numel(), _stream(stream)))
+    return y, st

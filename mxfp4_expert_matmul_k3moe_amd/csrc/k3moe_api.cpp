@@ -11,6 +11,7 @@
 #include <mutex>
 #include <string>
 
+#include "k3moe_cache.h"
 #include "k3moe_launch.h"
 
 namespace {
@@ -58,7 +59,7 @@ constexpr int kMfmaMinTokens = 16;
 
 enum Region {
   R_PART, R_IDS, R_GATES, R_OFFS, R_ROWS, R_ACT, R_NACT, R_PPOS, R_PEXP, R_HIST, R_BASE,
-  R_MASK, R_H, R_Z, R_XHAT, R_HSH, R_SSH, R_MTILE, R_X8, R_XS, R_COUNT
+  R_MASK, R_H, R_Z, R_XHAT, R_HSH, R_SSH, R_MTILE, R_X8, R_XS, R_SIDS, R_COUNT
 };
 
 struct Layout {
@@ -100,6 +101,7 @@ Layout layout_for(const k3moe_dims& dm, int64_t T) {
   sz[R_MTILE] = (size_t)(E + 1) * 4;
   sz[R_X8] = (size_t)(T * 2 * d);  // token rows as two FP8 terms
   sz[R_XS] = (size_t)(T * 2);      // their E8M0 scales
+  sz[R_SIDS] = (size_t)P * 4;      // slot ids of the cached layer
   Layout L;
   size_t o = 0;
   for (int r = 0; r < R_COUNT; ++r) {
@@ -435,6 +437,133 @@ int k3moe_expert_ffn(const k3moe_dims* dims, int32_t T, const void* x, int x_dty
   if (rc) return rc;
   return run_ffn(*dims, T, x, x_dtype == K3MOE_F32, experts, expert_offsets, bucket_rows,
                  topk_gates, nullptr, nullptr, y, nullptr, w, s);
+}
+
+size_t k3moe_cache_state_bytes(int32_t n_experts, int32_t n_slots, int32_t max_ids) {
+  return k3moe::cache_state_bytes(n_experts, n_slots, max_ids);
+}
+
+int k3moe_cache_init(void* state, size_t state_bytes, int32_t n_experts, int32_t n_slots,
+                     int32_t max_ids) {
+  const int r = k3moe::cache_init(state, state_bytes, n_experts, n_slots, max_ids);
+  if (r == -3)
+    return fail(K3MOE_EWORKSPACE, "cache state of %zu bytes < %zu needed", state_bytes,
+                k3moe::cache_state_bytes(n_experts, n_slots, max_ids));
+  if (r)
+    return fail(K3MOE_EINVAL,
+                "cache init: need 1 <= n_slots=%d <= n_experts=%d, max_ids=%d >= 1 and an "
+                "8-byte aligned state",
+                n_slots, n_experts, max_ids);
+  return K3MOE_OK;
+}
+
+int k3moe_cache_plan(void* state, int32_t n_ids, const int32_t* ids, int32_t* slot_ids,
+                     int32_t* fetch, int32_t* n_fetch) {
+  k3moe::CacheView v = k3moe::cache_view(state);
+  if (!v.h) return fail(K3MOE_EINVAL, "state is not an initialised cache state");
+  if (n_ids < 0) return fail(K3MOE_EINVAL, "n_ids=%d is negative", n_ids);
+  if (n_ids > 0 && (!ids || !slot_ids || !fetch)) return fail(K3MOE_EINVAL, "NULL array");
+  if (!n_fetch) return fail(K3MOE_EINVAL, "n_fetch is NULL");
+  int32_t nd = 0;
+  const int r = k3moe::cache_plan(v, n_ids, ids, slot_ids, fetch, n_fetch, &nd);
+  if (r == -1) return fail(K3MOE_EINVAL, "an id is outside [0, %d)", v.h->n_experts);
+  if (r == -2)
+    return fail(K3MOE_EUNSUPPORTED, "%d distinct experts in one call, more than the %d slots", nd,
+                v.h->n_slots);
+  return K3MOE_OK;
+}
+
+int k3moe_cache_stats_get(const void* state, k3moe_cache_stats* out) {
+  k3moe::CacheView v = k3moe::cache_view(const_cast<void*>(state));
+  if (!v.h) return fail(K3MOE_EINVAL, "state is not an initialised cache state");
+  if (!out) return fail(K3MOE_EINVAL, "out is NULL");
+  out->hits = v.h->hits;
+  out->misses = v.h->misses;
+  out->bytes_copied = v.h->bytes;
+  out->distinct = 0;
+  return K3MOE_OK;
+}
+
+int k3moe_layer_forward_cached(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
+                               const uint16_t* w_router, const float* logit_bias,
+                               const k3moe_mx_experts* host_experts,
+                               const k3moe_mx_experts* slot_experts, void* state, float* y,
+                               uint16_t* y_bf16, int32_t* topk_ids, float* topk_gates,
+                               k3moe_cache_stats* call_stats, void* ws, size_t ws_bytes,
+                               void* stream) {
+  int rc;
+  if (call_stats) *call_stats = k3moe_cache_stats{0, 0, 0, 0};
+  if ((rc = check_dims(dims)) || (rc = check_T(T)) || (rc = check_dtype(x_dtype))) return rc;
+  if (T == 0) return K3MOE_OK;
+  if ((rc = check_expert_shape(*dims))) return rc;
+  if ((rc = need_ptr(x, "x", true)) || (rc = need_ptr(w_router, "w_router")) ||
+      (rc = check_experts(host_experts)) || (rc = check_experts(slot_experts)) ||
+      (rc = need_ptr(y, "y", true)))
+    return rc;
+  k3moe::CacheView cv = k3moe::cache_view(state);
+  if (!cv.h) return fail(K3MOE_EINVAL, "state is not an initialised cache state");
+  if (cv.h->n_experts != dims->n_experts)
+    return fail(K3MOE_EINVAL, "cache state has %d experts, dims %d", cv.h->n_experts,
+                dims->n_experts);
+  const int k = dims->top_k, C = cv.h->n_slots;
+  const int64_t P = (int64_t)T * k;
+  if (P > cv.h->max_ids)
+    return fail(K3MOE_EUNSUPPORTED, "T*top_k=%lld above the state's max_ids=%d", (long long)P,
+                cv.h->max_ids);
+  if (k > C) return fail(K3MOE_EUNSUPPORTED, "top_k=%d above n_slots=%d", k, C);
+  Ws w;
+  if ((rc = get_ws(*dims, T, ws, ws_bytes, &w))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* ids = topk_ids ? topk_ids : w.at<int32_t>(R_IDS);
+  float* gates = topk_gates ? topk_gates : w.at<float>(R_GATES);
+  const int xf32 = x_dtype == K3MOE_F32;
+  if ((rc = run_router(*dims, T, x, xf32, w_router, logit_bias, ids, gates, w, s))) return rc;
+  // the plan needs the routed ids on the host
+  if ((rc = hip_check(hipMemcpyAsync(cv.ids, ids, (size_t)P * 4, hipMemcpyDeviceToHost, s),
+                      "routed ids to host")) ||
+      (rc = hip_check(hipStreamSynchronize(s), "routed ids to host")))
+    return rc;
+  int32_t nf = 0, nd = 0;
+  const int pr = k3moe::cache_plan(cv, (int32_t)P, cv.ids, cv.slots, cv.fetch, &nf, &nd);
+  if (pr == -1) return fail(K3MOE_EINVAL, "a routed id is outside [0, %d)", dims->n_experts);
+  if (pr == -2)
+    return fail(K3MOE_EUNSUPPORTED, "%d distinct experts in one call, more than the %d slots", nd,
+                C);
+  const size_t d = (size_t)dims->d_model, f = (size_t)dims->d_ff;
+  const size_t nq_gu = f * d / 2, ns_gu = f * d / 32, nq_d = d * f / 2, ns_d = d * f / 32;
+  const size_t sizes[6] = {nq_gu, ns_gu, nq_gu, ns_gu, nq_d, ns_d};
+  const uint8_t* src[6] = {host_experts->gate_q, host_experts->gate_s, host_experts->up_q,
+                           host_experts->up_s, host_experts->down_q, host_experts->down_s};
+  const uint8_t* dst[6] = {slot_experts->gate_q, slot_experts->gate_s, slot_experts->up_q,
+                           slot_experts->up_s, slot_experts->down_q, slot_experts->down_s};
+  size_t bytes = 0;
+  for (int32_t i = 0; i < nf; ++i) {
+    const size_t e = (size_t)cv.fetch[2 * i], sl = (size_t)cv.fetch[2 * i + 1];
+    for (int a = 0; a < 6; ++a) {
+      rc = hip_check(hipMemcpyAsync(const_cast<uint8_t*>(dst[a]) + sl * sizes[a],
+                                    src[a] + e * sizes[a], sizes[a], hipMemcpyHostToDevice, s),
+                     "expert to its slot");
+      if (rc) return rc;
+      bytes += sizes[a];
+    }
+  }
+  cv.h->bytes += (int64_t)bytes;
+  int32_t* sids = w.at<int32_t>(R_SIDS);
+  if ((rc = hip_check(hipMemcpyAsync(sids, cv.slots, (size_t)P * 4, hipMemcpyHostToDevice, s),
+                      "slot ids to device")))
+    return rc;
+  k3moe_dims dc = *dims;
+  dc.n_experts = C;
+  int32_t* offs = w.at<int32_t>(R_OFFS);
+  int32_t* rows = w.at<int32_t>(R_ROWS);
+  const k3moe::BucketOut bo = bucket_out(w, offs, rows);
+  rc = hip_check(k3moe::launch_bucket(T, C, k, sids, bo, w.at<uint32_t>(R_HIST),
+                                      w.at<uint32_t>(R_BASE), w.at<uint64_t>(R_MASK), s),
+                 "bucket by slot");
+  if (rc) return rc;
+  if (call_stats) *call_stats = k3moe_cache_stats{nd - nf, nf, (int64_t)bytes, nd};
+  return run_ffn(dc, T, x, xf32, slot_experts, offs, rows, gates, nullptr, nullptr, y, y_bf16, w,
+                 s);
 }
 
 int k3moe_layer_forward(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,

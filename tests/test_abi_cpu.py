@@ -7,6 +7,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import mxfp4_expert_matmul_k3moe_amd as k3
@@ -27,7 +28,9 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"k3moe_version", "k3moe_workspace_bytes", "k3moe_router",
                           "k3moe_route_bucket", "k3moe_expert_ffn", "k3moe_layer_forward",
-                          "k3moe_last_error", "k3moe_time_next_kernel"}
+                          "k3moe_last_error", "k3moe_time_next_kernel",
+                          "k3moe_cache_state_bytes", "k3moe_cache_init", "k3moe_cache_plan",
+                          "k3moe_cache_stats_get", "k3moe_layer_forward_cached"}
     L = k3.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -127,3 +130,29 @@ def test_binding_refuses_host_tensors():
     x = torch.zeros(1, 7168, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         k3.router(K3, x, torch.zeros(7168, 896, dtype=torch.bfloat16))
+
+
+def test_layer_forward_cached_validation():
+    """Everything the cached layer rejects is rejected on the host, before any GPU work."""
+    L = k3.lib()
+    ex = k3._MxExperts(*(0x100000 for _ in range(6)))
+    cache = k3.ExpertCache(896, 32, 16)  # room for one token of top-16
+
+    def call(dims=K3, T=1, state=cache.ptr, host=ex, slots=ex, nbytes=1 << 40):
+        return L.k3moe_layer_forward_cached(ctypes.byref(dims), T, FAKE, 0, FAKE, None,
+                                            ctypes.byref(host) if host is not None else None,
+                                            ctypes.byref(slots) if slots is not None else None,
+                                            state, FAKE, None, None, None, None, FAKE, nbytes,
+                                            None)
+
+    assert call(T=0) == k3.OK  # no-op
+    assert call(state=None) == k3.EINVAL
+    junk = np.zeros(64, dtype=np.uint64)
+    assert call(state=ctypes.c_void_p(junk.ctypes.data)) == k3.EINVAL  # not a cache state
+    assert call(host=None) == k3.EINVAL
+    assert call(slots=None) == k3.EINVAL
+    assert call(dims=k3.make_dims(7168, 1536, 895, 16)) == k3.EINVAL  # E differs from the state
+    assert call(T=2) == k3.EUNSUPPORTED  # T * top_k above max_ids
+    small = k3.ExpertCache(896, 8, 16)
+    assert call(state=small.ptr) == k3.EUNSUPPORTED  # top_k above n_slots
+    assert call(nbytes=100) == k3.EWORKSPACE
