@@ -206,7 +206,11 @@ K3MOE_API int k3moe_cache_stats_get(const void* state, k3moe_cache_stats* out);
 /* One MoE layer (no block extras) with the experts in the slot cache: router on `stream`,
  * routed ids copied to the host (this SYNCHRONISES `stream`), plan, host -> HBM copies of
  * the missing experts enqueued on `stream`, slot ids to the device, bucketing by slot, and
- * the routed experts run from the slots. y, y_bf16, topk_ids and topk_gates are those of
+ * the routed experts run from the slots. The copies of several missing experts are spread
+ * over 4 copy streams per device (non-blocking, default priority, created on first use and
+ * kept until the process ends), forked from `stream` and joined back into it by the calling
+ * thread's events before the bucketing, so the call's work is complete once `stream` is.
+ * y, y_bf16, topk_ids and topk_gates are those of
  * k3moe_layer_forward with all E experts resident, bit for bit. call_stats (nullable, host)
  * receives this call's hits, misses, bytes and distinct count. EUNSUPPORTED: T * top_k
  * above the state's max_ids, top_k above n_slots, or more distinct experts in the batch

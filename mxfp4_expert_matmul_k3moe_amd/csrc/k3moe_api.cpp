@@ -248,6 +248,40 @@ hipStream_t side_stream() {
   return streams[dev];
 }
 
+// Copy streams of the expert slot cache: kCopyStreams non-blocking streams per device
+// (default priority), created on first use and kept, so the host -> HBM copies of several
+// missing experts run on several DMA engines at once; plus, per host thread and device,
+// one fork event and one join event per copy stream.
+constexpr int kCopyStreams = 4;
+bool copy_streams(hipStream_t (&cs)[kCopyStreams], hipEvent_t& fork,
+                  hipEvent_t (&join)[kCopyStreams]) {
+  static std::mutex mu;
+  static hipStream_t streams[64][kCopyStreams] = {};
+  thread_local hipEvent_t ev[64][kCopyStreams + 1] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < kCopyStreams; ++i)
+      if (!streams[dev][i] &&
+          hipStreamCreateWithFlags(&streams[dev][i], hipStreamNonBlocking) != hipSuccess) {
+        streams[dev][i] = nullptr;
+        return false;
+      }
+  }
+  for (int i = 0; i <= kCopyStreams; ++i)
+    if (!ev[dev][i] && hipEventCreateWithFlags(&ev[dev][i], hipEventDisableTiming) != hipSuccess) {
+      ev[dev][i] = nullptr;
+      return false;
+    }
+  for (int i = 0; i < kCopyStreams; ++i) {
+    cs[i] = streams[dev][i];
+    join[i] = ev[dev][i + 1];
+  }
+  fork = ev[dev][0];
+  return true;
+}
+
 int run_router(const k3moe_dims& dm, int32_t T, const void* x, int xf32, const uint16_t* w,
                const float* bias, int32_t* ids, float* gates, const Ws& ws, hipStream_t s,
                const k3moe::BucketOut* bucket1 = nullptr) {
@@ -536,17 +570,33 @@ int k3moe_layer_forward_cached(const k3moe_dims* dims, int32_t T, const void* x,
                            host_experts->up_s, host_experts->down_q, host_experts->down_s};
   const uint8_t* dst[6] = {slot_experts->gate_q, slot_experts->gate_s, slot_experts->up_q,
                            slot_experts->up_s, slot_experts->down_q, slot_experts->down_s};
+  // missing experts round-robin over the copy streams (forked from and joined back into
+  // `s` by events; in order on `s` if they cannot be set up)
+  hipStream_t cs[kCopyStreams];
+  hipEvent_t fork = nullptr, join[kCopyStreams];
+  const int ncs = nf > 1 && copy_streams(cs, fork, join) ? (nf < kCopyStreams ? nf : kCopyStreams)
+                                                          : 0;
+  if (ncs) {
+    if ((rc = hip_check(hipEventRecord(fork, s), "fork expert copies"))) return rc;
+    for (int j = 0; j < ncs; ++j)
+      if ((rc = hip_check(hipStreamWaitEvent(cs[j], fork, 0), "fork expert copies"))) return rc;
+  }
   size_t bytes = 0;
   for (int32_t i = 0; i < nf; ++i) {
     const size_t e = (size_t)cv.fetch[2 * i], sl = (size_t)cv.fetch[2 * i + 1];
+    hipStream_t cps = ncs ? cs[i % ncs] : s;
     for (int a = 0; a < 6; ++a) {
       rc = hip_check(hipMemcpyAsync(const_cast<uint8_t*>(dst[a]) + sl * sizes[a],
-                                    src[a] + e * sizes[a], sizes[a], hipMemcpyHostToDevice, s),
+                                    src[a] + e * sizes[a], sizes[a], hipMemcpyHostToDevice, cps),
                      "expert to its slot");
       if (rc) return rc;
       bytes += sizes[a];
     }
   }
+  for (int j = 0; j < ncs; ++j)
+    if ((rc = hip_check(hipEventRecord(join[j], cs[j]), "join expert copies")) ||
+        (rc = hip_check(hipStreamWaitEvent(s, join[j], 0), "join expert copies")))
+      return rc;
   cv.h->bytes += (int64_t)bytes;
   int32_t* sids = w.at<int32_t>(R_SIDS);
   if ((rc = hip_check(hipMemcpyAsync(sids, cv.slots, (size_t)P * 4, hipMemcpyHostToDevice, s),
