@@ -526,12 +526,30 @@ def bench_cached(args, w) -> int:
     return 0
 
 
+def _function_text(src: str, marker: str) -> str:
+    """Source of the top-level function whose signature contains `marker`: from the
+    template line above it (if any) to its closing brace at column 0."""
+    i = src.index(marker)
+    start = src.rfind("\n", 0, i) + 1
+    prev = src.rfind("\n", 0, start - 1) + 1
+    if src[prev:start].startswith("template"):
+        start = prev
+    end = src.index("\n}\n", i) + 3
+    return src[start:end]
+
+
 def _kernel_hash() -> str:
+    """Hash of the T=1 gate/up kernel's own source: its template, its launcher and the
+    device helpers it uses (the traffic record holds while these are unchanged)."""
     import hashlib
+    csrc = os.path.join(ROOT, "mxfp4_expert_matmul_k3moe_amd", "csrc")
+    with open(os.path.join(csrc, "ffn_gemv.hip")) as fh:
+        src = fh.read()
     h = hashlib.sha256()
-    for n in ("ffn_gemv.hip", "k3moe_device.h"):
-        with open(os.path.join(ROOT, "mxfp4_expert_matmul_k3moe_amd", "csrc", n), "rb") as fh:
-            h.update(fh.read())
+    h.update(_function_text(src, "void gateup_decode_kernel(").encode())
+    h.update(_function_text(src, "hipError_t launch_gateup_decode(").encode())
+    with open(os.path.join(csrc, "k3moe_device.h"), "rb") as fh:
+        h.update(fh.read())
     return h.hexdigest()[:16]
 
 

@@ -104,19 +104,41 @@ __global__ __launch_bounds__(256) void router_gemv_vec_kernel(int T, int d, int 
   const bool cv = col0 < E;
   for (int t0 = 0; t0 < T; t0 += NT) {
     const int nt = min(NT, T - t0);
-    // weight loads first (clamped to valid rows/columns, masked below), then the activations
     u32x4 wv[RPL];
+    if constexpr (NT == 1) {
+      // one token: the chunk's activations first (rows tid and tid + 256, loads clamped and
+      // masked), then every weight load; the activations go to LDS as soon as their own
+      // loads land and the barrier waits only for LDS, so all weight loads stay in flight
+      if (t0 > 0) __syncthreads();
+      const int ra = threadIdx.x, rb = threadIdx.x + 256;
+      const double xa = load_x<XF32>(x, (size_t)t0 * d + k0 + min(ra, nrows - 1));
+      const double xb = load_x<XF32>(x, (size_t)t0 * d + k0 + min(rb, nrows - 1));
+      asm volatile("" ::: "memory");
 #pragma unroll
-    for (int u = 0; u < RPL; ++u) {
-      const int r = min(wave * (kRouterRows / 4) + rl + 8 * u, nrows - 1);
-      wv[u] = *reinterpret_cast<const u32x4*>(w + (size_t)(k0 + r) * E + (cv ? col0 : 0));
+      for (int u = 0; u < RPL; ++u) {
+        const int r = min(wave * (kRouterRows / 4) + rl + 8 * u, nrows - 1);
+        wv[u] = *reinterpret_cast<const u32x4*>(w + (size_t)(k0 + r) * E + (cv ? col0 : 0));
+      }
+      xs[ra][0] = ra < nrows ? xa : 0.0;
+      xs[rb][0] = rb < nrows ? xb : 0.0;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    } else {
+      // weight loads first (clamped to valid rows/columns, masked below), then the
+      // activations
+#pragma unroll
+      for (int u = 0; u < RPL; ++u) {
+        const int r = min(wave * (kRouterRows / 4) + rl + 8 * u, nrows - 1);
+        wv[u] = *reinterpret_cast<const u32x4*>(w + (size_t)(k0 + r) * E + (cv ? col0 : 0));
+      }
+      __syncthreads();
+      for (int i = threadIdx.x; i < nrows * NT; i += 256) {
+        const int r = i / NT, tt = i % NT;
+        xs[r][tt] = (tt < nt) ? load_x<XF32>(x, (size_t)(t0 + tt) * d + k0 + r) : 0.0;
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    for (int i = threadIdx.x; i < nrows * NT; i += 256) {
-      const int r = i / NT, tt = i % NT;
-      xs[r][tt] = (tt < nt) ? load_x<XF32>(x, (size_t)(t0 + tt) * d + k0 + r) : 0.0;
-    }
-    __syncthreads();
     double acc[NT][8];
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt)
