@@ -141,7 +141,10 @@ K3MOE_API int k3moe_route_bucket(const k3moe_dims* dims, int32_t T, const int32_
 /* Routed experts + gate-weighted combine for already-routed tokens:
  * y_t = sum_slot topk_gates[t][slot] * E_e(x_t), e the expert whose bucket holds pair
  * t*k+slot. Each expert's MXFP4 weights are read once per call for all of its tokens and
- * decoded in registers; nothing dequantised is written to memory. Slots are summed in slot
+ * either converted in registers (GEMV kernels) or fed as stored to the block-scaled FP4 x
+ * FP8 MFMA (one token's down projection with d_ff a multiple of 128 up to 1536 and top_k
+ * <= 16; grouped GEMMs from 16 tokens); nothing dequantised is written to memory. In the
+ * MFMA paths h enters as three FP8 (E4M3) terms with E8M0 scales. Slots are summed in slot
  * order. x: [T][d_model] of x_dtype. y: fp32 [T][d_model], overwritten. */
 K3MOE_API int k3moe_expert_ffn(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
                      const k3moe_mx_experts* experts, const int32_t* expert_offsets,
