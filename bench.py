@@ -140,6 +140,35 @@ def cpu_baseline(w, n_tokens: int, budget_s: float = 20.0):
                       f"{sec:.1f} s of oracle time"}
 
 
+def cpu_tuned_baseline(w, n_tokens: int, budget_s: float = 10.0):
+    """Time the tuned CPU comparator (cpu_tuned/: AVX2 across outputs, OpenMP, equal to the
+    oracle bit for bit) on single-token layers of the same workload, like cpu_baseline."""
+    import numpy as np
+
+    import cpu_tuned
+    import oracle
+    wr = w.router_w(0)
+    bias = w.bias(0)
+    sec, done = 0.0, 0
+    for i in range(n_tokens):
+        x = w.x_bf16(token_set=1000 + i, T=1)
+        ids, _, _, _ = oracle.layer_route(x, wr, bias, w.k)  # untimed: which experts to draw
+        experts = {int(e): w.expert_host(0, int(e)) for e in np.unique(ids)}
+        t0 = time.perf_counter()
+        cpu_tuned.layer_forward(x, wr, bias, experts, w.d, w.f, w.E, w.k)
+        sec += time.perf_counter() - t0
+        done += 1
+        if sec >= budget_s:
+            break
+    bytes_total = done * (w.k * w.expert_bytes + w.d * w.E * 2)
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(bytes_total / sec / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "tuned CPU (AVX2 across outputs, OpenMP), equal to the oracle bit for bit"
+                    if cpu_tuned.simd() else "tuned CPU (scalar host), equal to the oracle",
+            "sample": f"{done} single-token decode layers ({workload_desc(w)}), "
+                      f"{sec:.2f} s"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -306,6 +335,7 @@ def main() -> int:
     }
     if not args.no_cpu_baseline and w.T == 1:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
+        out["cpu_tuned"] = cpu_tuned_baseline(w, args.cpu_tokens)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
