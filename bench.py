@@ -146,13 +146,12 @@ def cpu_tuned_baseline(w, n_tokens: int, budget_s: float = 10.0):
     import numpy as np
 
     import cpu_tuned
-    import oracle
     wr = w.router_w(0)
     bias = w.bias(0)
     sec, done = 0.0, 0
     for i in range(n_tokens):
         x = w.x_bf16(token_set=1000 + i, T=1)
-        ids, _, _, _ = oracle.layer_route(x, wr, bias, w.k)  # untimed: which experts to draw
+        ids, _ = cpu_tuned.layer_route(x, wr, bias, w.k)  # untimed: which experts to draw
         experts = {int(e): w.expert_host(0, int(e)) for e in np.unique(ids)}
         t0 = time.perf_counter()
         cpu_tuned.layer_forward(x, wr, bias, experts, w.d, w.f, w.E, w.k)

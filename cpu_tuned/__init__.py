@@ -25,6 +25,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB)
         L.k3cpu_layer_forward.restype = ctypes.c_int
         L.k3cpu_layer_forward.argtypes = [ctypes.c_int32] * 5 + [ctypes.c_void_p] * 7
+        L.k3cpu_layer_route.restype = ctypes.c_int
+        L.k3cpu_layer_route.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 5
         L.k3cpu_simd.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -59,3 +61,20 @@ def layer_forward(x, w_router, bias, experts, d, f, E, k):
     if rc != 0:
         raise RuntimeError(f"k3cpu_layer_forward failed ({rc})")
     return y, ids, gates
+
+
+def layer_route(x, w_router, bias, k):
+    """Routing only: (ids int32 [T][k], gates fp64 [T][k])."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    w = np.ascontiguousarray(w_router, dtype=np.uint16)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    T, d = x.shape
+    E = w.shape[1]
+    ids = np.empty((T, k), dtype=np.int32)
+    gates = np.empty((T, k), dtype=np.float64)
+    rc = lib().k3cpu_layer_route(T, d, E, k, x.ctypes.data, w.ctypes.data,
+                                 None if b is None else b.ctypes.data, ids.ctypes.data,
+                                 gates.ctypes.data)
+    if rc != 0:
+        raise RuntimeError(f"k3cpu_layer_route failed ({rc})")
+    return ids, gates

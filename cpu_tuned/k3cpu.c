@@ -218,4 +218,23 @@ int k3cpu_layer_forward(int32_t T, int32_t d, int32_t f, int32_t E, int32_t k,
   return rc;
 }
 
+int k3cpu_layer_route(int32_t T, int32_t d, int32_t E, int32_t k, const uint16_t* x,
+                      const uint16_t* w_router, const float* bias, int32_t* ids,
+                      double* gates) {
+  if (T < 0 || d <= 0 || E <= 0 || k < 1 || k > E) return -1;
+  tables();
+  double* xd = (double*)malloc((size_t)d * sizeof(double));
+  double* l = (double*)malloc((size_t)E * sizeof(double));
+  double* p = (double*)malloc((size_t)E * sizeof(double));
+  unsigned char* taken = (unsigned char*)malloc((size_t)E);
+  const int rc = (xd && l && p && taken) ? 0 : -2;
+  for (int32_t t = 0; t < T && rc == 0; ++t) {
+    for (int32_t i = 0; i < d; ++i) xd[i] = bf16d(x[(int64_t)t * d + i]);
+    router_logits(xd, w_router, bias, d, E, l);
+    route(l, E, k, ids + (int64_t)t * k, gates + (int64_t)t * k, p, taken);
+  }
+  free(xd); free(l); free(p); free(taken);
+  return rc;
+}
+
 int k3cpu_simd(void) { return have_avx2(); }

@@ -20,6 +20,10 @@ typedef struct { /* one expert, host pointers (layouts as in include/k3moe.h) */
 int k3cpu_layer_forward(int32_t T, int32_t d, int32_t f, int32_t E, int32_t k,
                         const uint16_t* x, const uint16_t* w_router, const float* bias,
                         const k3cpu_expert* experts, double* y, int32_t* ids, double* gates);
+/* Routing only (router GEMV, softmax, top-k) of the same layer: ids [T][k], gates [T][k]. */
+int k3cpu_layer_route(int32_t T, int32_t d, int32_t E, int32_t k, const uint16_t* x,
+                      const uint16_t* w_router, const float* bias, int32_t* ids,
+                      double* gates);
 /* 1 when the AVX2 paths run on this host, else 0 (scalar loops, same results). */
 int k3cpu_simd(void);
 

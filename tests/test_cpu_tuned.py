@@ -20,6 +20,8 @@ def _check(w: Workload, token_sets=(0,)):
         y_c, ids_c, g_c = cpu_tuned.layer_forward(x, wr, bias, experts, w.d, w.f, w.E, w.k)
         assert np.array_equal(ids_c, ids_o)
         assert np.array_equal(g_c, g_o)
+        ids_r, g_r = cpu_tuned.layer_route(x, wr, bias, w.k)
+        assert np.array_equal(ids_r, ids_o) and np.array_equal(g_r, g_o)
         assert np.array_equal(y_c, y_o), f"{w.name} set {ts}: max diff {np.abs(y_c - y_o).max()}"
 
 
