@@ -371,6 +371,26 @@ def test_prefill_k3(dev):
     torch.cuda.empty_cache()
 
 
+def test_prefill_k3_t8192(dev):
+    """The largest chunk of the prefill sweep that the oracle routes in seconds: 8192 tokens,
+    the hottest experts spread over a hundred and more 64-row tiles."""
+    w = PREFILL.with_(T=8192, name="prefill_t8192")
+    say("prefill: T=8192 with Zipf(1.1) logit bias")
+    x = w.x_bf16()
+    ex = gdev.experts(w, 0, dev)
+    g = run_gpu_layer(w, x, dev, experts=ex)
+    ids_all, gates_all, _, _ = oracle.layer_route(x, w.router_w(0), w.bias(0), w.k)
+    check_routing(g["ids"], g["gates"], ids_all, gates_all)
+    counts = np.bincount(ids_all.ravel(), minlength=w.E)
+    print(f"    touched experts {int((counts > 0).sum())}, max load {counts.max()}", flush=True)
+    assert counts.max() > 64 * 64  # some expert spans more than 64 full tiles
+    rows = [0, 4095, 8191]
+    ref = harness.run_layer(w, x, tokens=rows)
+    assert_layer(w, g, ref, rows=rows)
+    del ex
+    torch.cuda.empty_cache()
+
+
 def test_stack8_k3(dev):
     w = STACK8
     say("8 stacked blocks, T=1, ~126 GB of MXFP4 experts resident")
