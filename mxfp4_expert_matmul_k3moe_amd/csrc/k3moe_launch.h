@@ -61,11 +61,14 @@ hipError_t launch_gateup_gemv(int T, int d, int f, int E, int k, const void* x, 
                               const MxPtrs& w, const int32_t* offsets, const int32_t* rows,
                               const int32_t* act, const int32_t* n_act, int max_act,
                               float* h, hipStream_t s);
-// T == 1, persistent decode kernels (grid sized from the CU count).
+// T == 1, persistent decode kernels (grid sized from the CU count); blocks_per_cu <= 0
+// picks 4 resident blocks per CU.
 hipError_t launch_gateup_decode(int d, int f, int k, const void* x, int xf32, const MxPtrs& w,
                                 const int32_t* offsets, const int32_t* act, const int32_t* n_act,
                                 float* h, int n_cu, hipStream_t s, int blocks_per_cu = 0);
-// rows_per_block <= 0 picks about two blocks per CU; rows_per_step in {2, 4, 8}.
+// rows_per_block == 0: the MFMA kernel below when the shape and a 4-byte aligned down_s
+// allow it, else the fp32-FMA kernel with about two blocks per CU; rows_per_block > 0
+// forces the fp32-FMA kernel with that many rows per block; rows_per_step in {2, 4, 8}.
 hipError_t launch_down_decode(int d, int f, int k, const MxPtrs& w, const float* h,
                               const int32_t* pair_pos, const int32_t* pair_exp,
                               const float* gates, const float* resid, const float* shared,
