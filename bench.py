@@ -191,7 +191,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one MI355X: this build runs the layer on a single GPU "
+        print("bench.py measures one MI355X: the library runs the layer on a single GPU "
               "(expert-parallel sharding across GPUs is not implemented); use --gpus 1.",
               file=sys.stderr)
         return 2
