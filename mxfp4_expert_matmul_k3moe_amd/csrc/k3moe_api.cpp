@@ -420,7 +420,7 @@ int k3moe_router(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
   int rc;
   if ((rc = check_dims(dims)) || (rc = check_T(T)) || (rc = check_dtype(x_dtype))) return rc;
   if (T == 0) return K3MOE_OK;
-  if ((rc = need_ptr(x, "x")) || (rc = need_ptr(w_router, "w_router")) ||
+  if ((rc = need_ptr(x, "x", true)) || (rc = need_ptr(w_router, "w_router")) ||
       (rc = need_ptr(topk_ids, "topk_ids")) || (rc = need_ptr(topk_gates, "topk_gates")))
     return rc;
   Ws w;

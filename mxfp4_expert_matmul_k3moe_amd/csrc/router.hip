@@ -102,9 +102,18 @@ __global__ __launch_bounds__(256) void router_gemv_vec_kernel(int T, int d, int 
   const int cg = lane & 7, rl = lane >> 3;
   const int col0 = blockIdx.y * kRouterCols + cg * 8;
   const bool cv = col0 < E;
+  u32x4 wv[RPL];
+  if constexpr (NT > 1) {
+    // several tokens: the block's weights are loaded once (clamped to valid rows/columns,
+    // masked below) and stay in registers for every token group
+#pragma unroll
+    for (int u = 0; u < RPL; ++u) {
+      const int r = min(wave * (kRouterRows / 4) + rl + 8 * u, nrows - 1);
+      wv[u] = *reinterpret_cast<const u32x4*>(w + (size_t)(k0 + r) * E + (cv ? col0 : 0));
+    }
+  }
   for (int t0 = 0; t0 < T; t0 += NT) {
     const int nt = min(NT, T - t0);
-    u32x4 wv[RPL];
     if constexpr (NT == 1) {
       // one token: the chunk's activations first (rows tid and tid + 256, loads clamped and
       // masked), then every weight load; the activations go to LDS as soon as their own
@@ -125,17 +134,44 @@ __global__ __launch_bounds__(256) void router_gemv_vec_kernel(int T, int d, int 
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     } else {
-      // weight loads first (clamped to valid rows/columns, masked below), then the
-      // activations
+      // no barrier before refilling xs: every wave finished reading it before the barrier
+      // that publishes the previous group's wave sums.
+      // Activations of the group: one 16-byte load (8 bf16 or 4 fp32 values) per thread and
+      // step, all issued before any is used (one element per load made every element its
+      // own round trip to L2); x rows and the chunk start are 16-byte aligned and nrows is
+      // a multiple of 32
+      constexpr int VPL = XF32 ? 4 : 8;
+      constexpr int LPT = kRouterRows / VPL;              // loads per token
+      constexpr int ITER = (NT * LPT + 255) / 256;        // loads per thread
+      u32x4 xq[ITER];
 #pragma unroll
-      for (int u = 0; u < RPL; ++u) {
-        const int r = min(wave * (kRouterRows / 4) + rl + 8 * u, nrows - 1);
-        wv[u] = *reinterpret_cast<const u32x4*>(w + (size_t)(k0 + r) * E + (cv ? col0 : 0));
+      for (int it = 0; it < ITER; ++it) {
+        const int i = threadIdx.x + 256 * it;
+        const int tt = i / LPT, r0 = (i - tt * LPT) * VPL;
+        const bool ok = i < NT * LPT && tt < nt && r0 < nrows;
+        const size_t el = (size_t)(t0 + (ok ? tt : 0)) * d + k0 + (ok ? r0 : 0);
+        xq[it] = XF32 ? *reinterpret_cast<const u32x4*>(static_cast<const float*>(x) + el)
+                      : *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + el);
       }
-      __syncthreads();
-      for (int i = threadIdx.x; i < nrows * NT; i += 256) {
-        const int r = i / NT, tt = i % NT;
-        xs[r][tt] = (tt < nt) ? load_x<XF32>(x, (size_t)(t0 + tt) * d + k0 + r) : 0.0;
+#pragma unroll
+      for (int it = 0; it < ITER; ++it) {
+        const int i = threadIdx.x + 256 * it;
+        if (i >= NT * LPT) continue;
+        const int tt = i / LPT, r0 = (i - tt * LPT) * VPL;
+        const bool ok = tt < nt && r0 < nrows;
+        double v[VPL];
+        if (XF32) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] = (double)__uint_as_float(xq[it][u]);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            v[2 * u] = (double)__uint_as_float(xq[it][u] << 16);
+            v[2 * u + 1] = (double)__uint_as_float(xq[it][u] & 0xFFFF0000u);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < VPL; ++u) xs[r0 + u][tt] = ok ? v[u] : 0.0;
       }
       __syncthreads();
     }
@@ -617,7 +653,10 @@ int router_num_chunks(int d) { return (d + kRouterRows - 1) / kRouterRows; }
 hipError_t launch_router_gemv(int T, int d, int E, const void* x, int xf32, const uint16_t* w,
                               double* part, hipStream_t s) {
   dim3 grid(router_num_chunks(d), (E + kRouterCols - 1) / kRouterCols);
-  if (E % 8 == 0) {
+  // 16-byte loads: W rows (and, for several tokens, x rows) must start on 16 bytes
+  const bool a16w = (reinterpret_cast<uintptr_t>(w) & 15u) == 0;
+  const bool a16x = (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
+  if (E % 8 == 0 && a16w && (T == 1 || a16x)) {
     if (T == 1) {
       if (xf32) router_gemv_vec_kernel<true, 1><<<grid, 256, 0, s>>>(T, d, E, x, w, part);
       else router_gemv_vec_kernel<false, 1><<<grid, 256, 0, s>>>(T, d, E, x, w, part);

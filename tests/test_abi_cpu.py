@@ -79,6 +79,7 @@ def test_bad_scalars_and_pointers_rejected():
     assert _router(K3, T=(1 << 20) + 1) == k3.EUNSUPPORTED
     assert _router(K3, dt=7) == k3.EINVAL
     assert _router(K3, x=None) == k3.EINVAL
+    assert _router(K3, x=ctypes.c_void_p(0x100008)) == k3.EINVAL  # x rows need 16 bytes
     assert _router(K3, w=None) == k3.EINVAL
     assert _router(K3, ids=None) == k3.EINVAL
     assert _router(K3, nbytes=16) == k3.EWORKSPACE
