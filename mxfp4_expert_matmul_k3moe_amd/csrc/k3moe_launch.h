@@ -13,6 +13,10 @@ int router_chunk_rows(int d);
 int router_num_chunks(int d);
 constexpr int kRouterGemvMaxT = 64;   // above this the tiled fp64 GEMM is used
 
+// part[c][t][e] over 512-row chunks c. With E % 8 == 0 and 16-byte aligned operands: one
+// token on the all-loads-in-flight GEMV, 2..9 tokens in groups of 4 sharing the block's
+// weights, 10..64 tokens on work items (chunk, 512 columns, 4 tokens) that sum over K inside
+// each lane; otherwise the scalar kernel.
 hipError_t launch_router_gemv(int T, int d, int E, const void* x, int xf32,
                               const uint16_t* w, double* part, hipStream_t s);
 // K chunks of the many-token router (its partial-sum count; at most 8), and the bound

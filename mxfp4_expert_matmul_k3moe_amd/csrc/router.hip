@@ -16,6 +16,8 @@ namespace {
 constexpr int kRouterRows = 512;  // W rows per partial chunk (4 waves x 128)
 constexpr int kRouterCols = 64;   // W columns per block (one lane each)
 constexpr int kTokGroup = 4;      // tokens per pass over a chunk
+constexpr int kRouterTokMinT = 10;  // from here on the in-lane-reduction kernel
+constexpr int kRouterTokWaves = 4;  // its waves per block
 
 template <bool XF32>
 __device__ __forceinline__ double load_x(const void* x, size_t i) {
@@ -221,6 +223,161 @@ __global__ __launch_bounds__(256) void router_gemv_vec_kernel(int T, int d, int 
       if (col < E) {
         const double s = ((wsum[0][tt][c] + wsum[1][tt][c]) + wsum[2][tt][c]) + wsum[3][tt][c];
         part[((size_t)chunk * T + t0 + tt) * E + col] = s;
+      }
+    }
+  }
+}
+
+// Several tokens: the K reduction stays inside each lane (no cross-lane sums). A work item
+// is (512-row chunk, 512-column slab, group of 4 tokens); its block of NW waves gives wave w
+// the chunk's rows [w R, w R + R), R = 512 / NW, and lane l the columns slab * 512 + 8 l .. + 7.
+// A lane accumulates its 4 x 8 outputs over its rows in row order, reading rows in batches
+// of 8 with the next batch in flight; the wave sums are then added by a fixed pairwise tree
+// (wave w + wave w + NW/2, then halves again). Consecutive work items (the token groups of
+// one weight tile first) are given to blocks on the same XCD (blocks are dealt to the 8
+// XCDs round robin), so a weight tile is read from HBM once and then from that XCD's L2.
+// Needs E % 8 == 0, 16-byte aligned W and x.
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+constexpr int kRtSlab = 512;   // columns per work item (64 lanes x 8)
+constexpr int kRtTok = 4;      // tokens per work item
+constexpr int kRtBatch = 8;    // W rows per load batch
+// x of a work item in LDS: row r, token t at r * 4 + t + 2 * (r / 8) doubles (the pad keeps
+// the staging writes of neighbouring lanes on different banks, and rows 16-byte aligned)
+__device__ __forceinline__ int rt_xs_at(int r) { return r * kRtTok + 2 * (r >> 3); }
+constexpr int kRtXsLen = kRouterRows * kRtTok + 2 * (kRouterRows / 8);
+constexpr int kRtAcc = kRtTok * 8;  // outputs per lane
+
+__host__ __device__ inline int rt_slabs(int E) { return (E + kRtSlab - 1) / kRtSlab; }
+
+template <bool XF32, int NW>
+__global__ __launch_bounds__(64 * NW) void router_tok_kernel(int T, int d, int E, int n_tg,
+                                                             int n_items,
+                                                             const void* __restrict__ x,
+                                                             const uint16_t* __restrict__ w,
+                                                             double* __restrict__ part) {
+  constexpr int NTH = 64 * NW, WROWS = kRouterRows / NW;
+  constexpr int RED = (NW / 2) * kRtAcc * 64;  // first reduction stage
+  // the activations while the waves accumulate, then the reduction stages (after a barrier
+  // that every read of the activations precedes)
+  __shared__ __align__(16) double lds[RED > kRtXsLen ? RED : kRtXsLen];
+  double* xs = lds;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = blockIdx.x, n8 = n_items / 8, rem = n_items % 8, xcd = b % 8;
+  const int item = xcd * n8 + min(xcd, rem) + b / 8;
+  const int n_slab = rt_slabs(E);
+  const int tg = item % n_tg, slab = (item / n_tg) % n_slab, chunk = item / (n_tg * n_slab);
+  const int t0 = tg * kRtTok, nt = min(kRtTok, T - t0);
+  const int k0 = chunk * kRouterRows, nrows = min(kRouterRows, d - k0);
+  const int col0 = slab * kRtSlab + lane * 8;
+  const bool cv = col0 < E;  // E % 8 == 0: a lane's 8 columns are all valid or none
+  const int rw0 = wave * WROWS;
+  const uint16_t* wcol = w + (cv ? col0 : 0);
+
+  u32x4 wa[kRtBatch], wb[kRtBatch];
+  // rows clamped to the chunk's last valid row; batches past it are skipped below
+  auto load = [&](u32x4 (&dst)[kRtBatch], int bi) {
+#pragma unroll
+    for (int i = 0; i < kRtBatch; ++i) {
+      const int r = min(rw0 + kRtBatch * bi + i, nrows - 1);
+      dst[i] = *reinterpret_cast<const u32x4*>(wcol + (size_t)(k0 + r) * E);
+    }
+  };
+  load(wa, 0);
+
+  // the work item's activations: one 16-byte load (8 bf16 or 4 fp32 values) per thread
+  {
+    constexpr int VPL = XF32 ? 4 : 8;
+    constexpr int LPT = kRouterRows / VPL;  // loads per token
+    constexpr int NLD = kRtTok * LPT;
+    constexpr int ITER = (NLD + NTH - 1) / NTH;
+    u32x4 xq[ITER];
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int i = min((int)threadIdx.x + NTH * it, NLD - 1);
+      const int tt = i / LPT, r0 = (i - tt * LPT) * VPL;
+      const bool ok = tt < nt && r0 < nrows;
+      const size_t el = (size_t)(t0 + (ok ? tt : 0)) * d + k0 + (ok ? r0 : 0);
+      xq[it] = XF32 ? *reinterpret_cast<const u32x4*>(static_cast<const float*>(x) + el)
+                    : *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + el);
+    }
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int i = threadIdx.x + NTH * it;
+      if (i >= NLD) break;
+      const int tt = i / LPT, r0 = (i - tt * LPT) * VPL;
+      const bool ok = tt < nt && r0 < nrows;
+      double v[VPL];
+      if (XF32) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = (double)__uint_as_float(xq[it][u]);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          v[2 * u] = (double)__uint_as_float(xq[it][u] << 16);
+          v[2 * u + 1] = (double)__uint_as_float(xq[it][u] & 0xFFFF0000u);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < VPL; ++u) xs[rt_xs_at(r0 + u) + tt] = ok ? v[u] : 0.0;
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  double acc[kRtAcc];
+#pragma unroll
+  for (int i = 0; i < kRtAcc; ++i) acc[i] = 0.0;
+  auto fma_batch = [&](const u32x4 (&src)[kRtBatch], int bi) {
+    const int rb = rw0 + kRtBatch * bi;
+    if (rb >= nrows) return;  // wave-uniform: nrows is a multiple of 32
+#pragma unroll
+    for (int i = 0; i < kRtBatch; ++i) {
+      const f64x2* xr = reinterpret_cast<const f64x2*>(&xs[rt_xs_at(rb + i)]);
+      const f64x2 x01 = xr[0], x23 = xr[1];
+      const double xv[kRtTok] = {x01[0], x01[1], x23[0], x23[1]};
+      double wd[8];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        wd[2 * c] = (double)__uint_as_float(src[i][c] << 16);
+        wd[2 * c + 1] = (double)__uint_as_float(src[i][c] & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int tt = 0; tt < kRtTok; ++tt)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[tt * 8 + c] = fma(xv[tt], wd[c], acc[tt * 8 + c]);
+    }
+  };
+  constexpr int NB = WROWS / kRtBatch;
+  static_assert(NB % 2 == 0, "batches are taken in pairs");
+  for (int bi = 0; bi < NB; bi += 2) {
+    load(wb, bi + 1);
+    fma_batch(wa, bi);
+    load(wa, min(bi + 2, NB - 1));  // the last pair reloads a batch it does not use
+    fma_batch(wb, bi + 1);
+  }
+
+  // wave sums: wave w takes wave w + half, for half = NW/2, NW/4, ..., 1
+#pragma unroll
+  for (int half = NW / 2; half >= 1; half /= 2) {
+    __syncthreads();  // the previous stage's (or the activations') readers are done
+    if (wave >= half && wave < 2 * half) {
+#pragma unroll
+      for (int i = 0; i < kRtAcc; ++i) lds[((wave - half) * kRtAcc + i) * 64 + lane] = acc[i];
+    }
+    __syncthreads();
+    if (wave < half) {
+#pragma unroll
+      for (int i = 0; i < kRtAcc; ++i) acc[i] += lds[(wave * kRtAcc + i) * 64 + lane];
+    }
+  }
+  if (wave == 0 && cv) {
+#pragma unroll
+    for (int tt = 0; tt < kRtTok; ++tt) {
+      if (tt < nt) {
+        f64x2* dst = reinterpret_cast<f64x2*>(part + ((size_t)chunk * T + t0 + tt) * E + col0);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dst[c] = f64x2{acc[tt * 8 + 2 * c], acc[tt * 8 + 2 * c + 1]};
       }
     }
   }
@@ -656,6 +813,16 @@ hipError_t launch_router_gemv(int T, int d, int E, const void* x, int xf32, cons
   // 16-byte loads: W rows (and, for several tokens, x rows) must start on 16 bytes
   const bool a16w = (reinterpret_cast<uintptr_t>(w) & 15u) == 0;
   const bool a16x = (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
+  if (E % 8 == 0 && a16w && T >= kRouterTokMinT && a16x) {
+    const int n_tg = (T + kRtTok - 1) / kRtTok;
+    const int n_items = router_num_chunks(d) * rt_slabs(E) * n_tg;
+    constexpr int NW = kRouterTokWaves;
+    if (xf32)
+      router_tok_kernel<true, NW><<<n_items, 64 * NW, 0, s>>>(T, d, E, n_tg, n_items, x, w, part);
+    else
+      router_tok_kernel<false, NW><<<n_items, 64 * NW, 0, s>>>(T, d, E, n_tg, n_items, x, w, part);
+    return hipGetLastError();
+  }
   if (E % 8 == 0 && a16w && (T == 1 || a16x)) {
     if (T == 1) {
       if (xf32) router_gemv_vec_kernel<true, 1><<<grid, 256, 0, s>>>(T, d, E, x, w, part);

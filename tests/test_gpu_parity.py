@@ -283,6 +283,29 @@ def test_repeat_runs_bit_identical(dev):
         assert np.array_equal(a["gates"], b["gates"])
 
 
+@pytest.mark.parametrize("d,E,k,T,xdt", [
+    (7168, 896, 16, 9, "bf16"),    # last token count on the 4-token-group GEMV
+    (7168, 896, 16, 10, "bf16"),   # first one on the in-lane-reduction kernel
+    (7008, 896, 16, 33, "bf16"),   # last 512-row chunk ragged (352 rows), ragged token group
+    (1024, 40, 8, 13, "bf16"),     # one column slab with 5 of 64 lanes in use
+    (2080, 520, 16, 64, "f32"),    # last chunk 32 rows (one wave), second slab one lane wide
+    (7168, 896, 16, 64, "f32"),
+])
+def test_router_multi_token_shapes(dev, d, E, k, T, xdt):
+    say(f"router, several tokens: d={d} E={E} k={k} T={T} x={xdt}")
+    from k3gen import host_normal_bf16, host_normal_f32
+    key = d * 7919 + E * 31 + T
+    xh = (host_normal_bf16(key, T * d, 0.0, 1.0) if xdt == "bf16"
+          else host_normal_f32(key, T * d, 0.0, 1.0)).reshape(T, d)
+    wh = host_normal_bf16(key + 1, d * E, 0.0, 0.02).reshape(d, E)
+    dims = k3.make_dims(d, 256, E, k)
+    x = gdev.bf16_tensor(xh, dev) if xdt == "bf16" else torch.from_numpy(xh).to(dev)
+    ids, gates = k3.router(dims, x, gdev.bf16_tensor(wh, dev))
+    torch.cuda.synchronize()
+    ids_r, gates_r = oracle.route(oracle.router_logits(oracle.load_x(xh), wh, None), k)
+    check_routing(ids.cpu().numpy(), gates.cpu().numpy(), ids_r, gates_r)
+
+
 @pytest.mark.parametrize("T", [3, 100])
 def test_fp32_activations(dev, T):
     # T = 100: the many-token fp64 MFMA router reading fp32 activations
