@@ -110,6 +110,22 @@ def timed_loop(args, step, nsets):
     return t0, t1
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def omp_threads() -> int:
+    """Threads the OpenMP host code (oracle, tuned comparator) runs with."""
+    return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
 def cpu_baseline(w, n_tokens: int, budget_s: float = 20.0):
     """Time the fp64 oracle on single-token layers of the same workload.
 
@@ -133,11 +149,41 @@ def cpu_baseline(w, n_tokens: int, budget_s: float = 20.0):
         if sec >= budget_s:
             break
     bytes_total = done * (w.k * w.expert_bytes + w.d * w.E * 2)
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(bytes_total / sec / 1e9, 4), "unit": "GB/s", "cores": cores,
-            "kind": "oracle",
+    return {"value": round(bytes_total / sec / 1e9, 4), "unit": "GB/s", "cores": omp_threads(),
+            "cpu": cpu_model(), "kind": "oracle",
             "sample": f"{done} single-token decode layers ({workload_desc(w)}), fp64 oracle, "
                       f"{sec:.1f} s of oracle time"}
+
+
+def cpu_baseline_prefill(w, n_tokens: int = 16, budget_s: float = 15.0):
+    """The fp64 oracle on a bounded sample of the prefill chunk: `n_tokens` rows of the
+    chunk's first token set, evenly spaced, each run as a one-token layer (router with the
+    chunk's Zipf bias, its 16 experts drawn untimed before it). Useful SwiGLU flops
+    (6 d f per routed pair) per second of oracle time."""
+    import numpy as np
+
+    import oracle
+    wr = w.router_w(0)
+    bias = w.bias(0)
+    xall = w.x_bf16(token_set=0)
+    rows = np.unique(np.linspace(0, w.T - 1, n_tokens).round().astype(int))
+    sec, done = 0.0, 0
+    for t in rows:
+        x = np.ascontiguousarray(xall[t:t + 1])
+        ids, _, _, _ = oracle.layer_route(x, wr, bias, w.k)
+        experts = {int(e): w.expert_host(0, int(e)) for e in np.unique(ids)}
+        t0 = time.perf_counter()
+        oracle.layer_route(x, wr, bias, w.k)
+        oracle.layer_forward(x, wr, bias, experts, w.d, w.f, w.E, w.k)
+        sec += time.perf_counter() - t0
+        done += 1
+        if sec >= budget_s:
+            break
+    flops = done * 6.0 * w.d * w.f * w.k
+    return {"value": round(flops / sec / 1e9, 3), "unit": "GFLOP/s", "cores": omp_threads(),
+            "cpu": cpu_model(), "kind": "oracle",
+            "sample": f"{done} of the {w.T} tokens of the prefill chunk ({workload_desc(w)}), "
+                      f"evenly spaced, each as a one-token layer, fp64 oracle, {sec:.1f} s"}
 
 
 def cpu_tuned_baseline(w, n_tokens: int, budget_s: float = 10.0):
@@ -160,12 +206,163 @@ def cpu_tuned_baseline(w, n_tokens: int, budget_s: float = 10.0):
         if sec >= budget_s:
             break
     bytes_total = done * (w.k * w.expert_bytes + w.d * w.E * 2)
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(bytes_total / sec / 1e9, 4), "unit": "GB/s", "cores": cores,
+    return {"value": round(bytes_total / sec / 1e9, 4), "unit": "GB/s", "cores": omp_threads(),
+            "cpu": cpu_model(),
             "kind": "tuned CPU (AVX2 across outputs, OpenMP), equal to the oracle bit for bit"
                     if cpu_tuned.simd() else "tuned CPU (scalar host), equal to the oracle",
             "sample": f"{done} single-token decode layers ({workload_desc(w)}), "
                       f"{sec:.2f} s"}
+
+
+DTYPE_DECODE = ("mxfp4 weights: gate/up bf16 x fp4->bf16 dot2 (fp32 acc), down block-scaled "
+                "MFMA fp4 x 3 fp8(e4m3) terms of h (fp32 acc); router fp64")
+DTYPE_GROUPED = ("mxfp4 weights on block-scaled MFMA: fp4 x 2 fp8(e4m3) terms of x (gate/up), "
+                 "fp4 x 3 fp8(e4m3) terms of h (down), fp32 acc; router fp64")
+DTYPE_GEMV = "mxfp4 weights: fp4->bf16/fp32 conversions, fp32 FMA/dot2 (fp32 acc); router fp64"
+
+
+def dtype_of(w) -> str:
+    if w.T == 1:
+        return DTYPE_DECODE
+    return DTYPE_GROUPED if w.T >= MFMA_MIN_TOKENS else DTYPE_GEMV
+
+
+def spread(vals):
+    import numpy as np
+    v = np.asarray(vals, dtype=float)
+    med = float(np.median(v))
+    return {"ms_per_step": [round(float(a), 5) for a in v], "median": round(med, 5),
+            "spread_pct": round(float((v.max() - v.min()) / med * 100.0), 2)}
+
+
+class LayerLeg:
+    """One bare MoE layer workload (decode, batched or prefill) resident on the GPU: its
+    experts, router, bias, token sets, workspace and outputs, and one step =
+    k3moe_layer_forward over the next token set."""
+
+    def __init__(self, args, w, dev):
+        import torch
+
+        import mxfp4_expert_matmul_k3moe_amd as k3
+        from k3gen import device as gdev
+        self.args, self.w, self.k3 = args, w, k3
+        self.dims = k3.make_dims(w.d, w.f, w.E, w.k)
+        self.ex = k3.MxExperts(**gdev.experts(w, 0, dev))
+        self.wr = gdev.router_w(w, 0, dev)
+        self.bias = gdev.bias(w, 0, dev)
+        # fresh tokens every step; prefill steps read most experts anyway, so fewer sets
+        self.nsets = max(1, args.token_sets if w.T <= 64 else min(args.token_sets, 4))
+        self.xs = torch.stack([gdev.x_bf16(w, token_set=i, device=dev)
+                               for i in range(self.nsets)])
+        self.ws = k3.make_workspace(self.dims, w.T, dev)
+        self.y = torch.empty((w.T, w.d), dtype=torch.float32, device=dev)
+        self.ybf = torch.empty((w.T, w.d), dtype=torch.bfloat16, device=dev)
+        self.ids = torch.empty((self.nsets, w.T, w.k), dtype=torch.int32, device=dev)
+        self.gates = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+
+    def step(self, i):
+        s = i % self.nsets
+        self.k3.layer_forward(self.dims, self.xs[s], self.wr, self.bias, self.ex, y=self.y,
+                              y_bf16=self.ybf, ids=self.ids[s], gates=self.gates, ws=self.ws)
+
+    def measure(self, repeats: int) -> dict:
+        """W warm-up steps, exactly K timed steps, then `repeats` more timed runs of K steps
+        (for median and spread), then the dominant kernels timed live by HIP events."""
+        import numpy as np
+        import torch
+        args, w, k3 = self.args, self.w, self.k3
+        t0, t1 = timed_loop(args, self.step, self.nsets)
+        runs = [(t1 - t0) * 1e3 / args.steps]
+        for r in range(repeats):
+            torch.cuda.synchronize()
+            a = time.perf_counter()
+            for i in range(args.steps):
+                self.step(args.warmup + i)
+            torch.cuda.synchronize()
+            runs.append((time.perf_counter() - a) * 1e3 / args.steps)
+        ids_np = self.ids.cpu().numpy()
+        uniq = [len(np.unique(ids_np[s2])) for s2 in range(self.nsets)]
+        step_sets = [(args.warmup + i) % self.nsets for i in range(args.steps)]
+        hip = Hip()
+        nprobe = min(args.steps, 100 if w.T <= 64 else 20)
+        kern = {}
+        for which, name in ((k3.KERNEL_GATE_UP, "gate_up"), (k3.KERNEL_DOWN, "down")):
+            evs = [(hip.event(), hip.event()) for _ in range(nprobe)]
+            for i in range(nprobe):
+                k3.time_next_kernel(which, evs[i][0], evs[i][1])
+                self.step(args.warmup + i)
+            torch.cuda.synchronize()
+            times = [hip.elapsed_ms(a, b) for a, b in evs]
+            for a, b in evs:
+                hip.destroy(a)
+                hip.destroy(b)
+            kern[name] = sum(times) / len(times)
+        sel = float(np.mean([uniq[(args.warmup + i) % self.nsets] for i in range(nprobe)]))
+        return {"sec": t1 - t0, "ms_per_step": runs[0], "runs": runs, "uniq": uniq,
+                "bytes_timed": sum(uniq[s2] * w.expert_bytes + w.d * w.E * 2
+                                   for s2 in step_sets),
+                "gate_up_ms": kern["gate_up"], "down_ms": kern["down"], "sel": sel}
+
+
+def decode_like_fields(w, m, traffic):
+    """value / roofline / kernels of a weight-stream (T <= 64) workload."""
+    import numpy as np
+    value = m["bytes_timed"] / m["sec"] / 1e9
+    gu_bytes = m["sel"] * 2 * w.f * (w.d // 2 + w.d // 32)
+    dn_bytes = m["sel"] * w.d * (w.f // 2 + w.f // 32)
+    ach = gu_bytes / (m["gate_up_ms"] * 1e-3) / 1e9
+    if w.T == 1:
+        kname = "gateup_decode_kernel (MXFP4 gate/up GEMV + SwiGLU)"
+    elif w.T >= MFMA_MIN_TOKENS:
+        kname = ("mfma_ffn_kernel<gate/up> (grouped GEMM on the block-scaled FP4 x FP8 MFMA, "
+                 "token as two FP8 terms, + SwiGLU)")
+    else:
+        kname = "gateup_gemv_kernel (MXFP4 gate/up GEMV + SwiGLU)"
+    roof = {"bound": "hbm", "kernel": kname, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "bytes_per_launch": int(gu_bytes), "avg_launch_us": round(m["gate_up_ms"] * 1e3, 2)}
+    extra = {"down_us": round(m["down_ms"] * 1e3, 2),
+             "down_GBps": round(dn_bytes / (m["down_ms"] * 1e-3) / 1e9, 1),
+             "experts_GBps": round((gu_bytes + dn_bytes) /
+                                   ((m["gate_up_ms"] + m["down_ms"]) * 1e-3) / 1e9, 1),
+             "layer_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+             "distinct_experts_per_step": round(float(np.mean(m["uniq"])), 1)}
+    return value, "GB/s", roof, extra
+
+
+def prefill_fields(w, m, traffic):
+    """value / roofline / kernels of a grouped-GEMM (prefill) workload."""
+    import numpy as np
+    pairs = w.T * w.k
+    value = 6.0 * w.d * w.f * pairs / (m["ms_per_step"] * 1e-3) / 1e12
+    gu_flops = 4.0 * w.d * w.f * pairs
+    dn_flops = 2.0 * w.d * w.f * pairs
+    gu_s, dn_s = m["gate_up_ms"] * 1e-3, m["down_ms"] * 1e-3
+    gu_bytes = m["sel"] * 2 * w.f * (w.d // 2 + w.d // 32)
+    dn_bytes = m["sel"] * w.d * (w.f // 2 + w.f // 32)
+    ach = gu_flops / gu_s / 1e12
+    floor_ms = float(np.mean(m["uniq"])) * w.expert_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
+    # two FP8-rate MFMAs (5.0 PFLOP/s) per useful product: 2.5 PFLOP/s of useful flops,
+    # the same ceiling as bf16 MFMA
+    roof = {"bound": "mfma",
+            "kernel": "mfma_ffn_kernel<gate/up> (grouped GEMM, block-scaled FP4 x FP8 MFMA, "
+                      "two FP8 token terms)",
+            "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+            "flops_per_launch": gu_flops, "avg_launch_us": round(m["gate_up_ms"] * 1e3, 2),
+            "weight_bytes_per_launch": int(gu_bytes),
+            "hbm_GBps": round(gu_bytes / gu_s / 1e9, 1),
+            "hbm_frac": round(gu_bytes / gu_s / 1e9 / HBM_PEAK_GBS, 4)}
+    extra = {"down_us": round(m["down_ms"] * 1e3, 2),
+             "down_TFLOPs": round(dn_flops / dn_s / 1e12, 1),
+             "down_frac_of_mfma_peak": round(dn_flops / dn_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+             "down_hbm_GBps": round(dn_bytes / dn_s / 1e9, 1),
+             "layer_frac_of_mfma_peak": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
+             "weight_GBps": round(m["bytes_timed"] / m["sec"] / 1e9, 1),
+             "distinct_experts_per_step": round(float(np.mean(m["uniq"])), 1),
+             "hbm_floor_ms": round(floor_ms, 3),
+             "frac_of_hbm_floor": round(floor_ms / m["ms_per_step"], 4)}
+    return value, "TFLOP/s", roof, extra
 
 
 def main() -> int:
@@ -184,7 +381,12 @@ def main() -> int:
                     help="only run a plain device copy of MB megabytes 20 times (counter scale)")
     ap.add_argument("--token-sets", type=int, default=64)
     ap.add_argument("--cpu-tokens", type=int, default=32)
+    ap.add_argument("--repeats", type=int, default=3,
+                    help="extra timed runs of --steps steps after the first, for the median "
+                         "and spread")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="decode: leave out the prefill leg of the default line")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one HIP graph per token set (captured on the "
                          "caller's stream) instead of eager calls")
@@ -196,7 +398,6 @@ def main() -> int:
               file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     if args.calibrate_copy:
@@ -210,8 +411,6 @@ def main() -> int:
         print(json.dumps({"calibrate_copy_bytes": n, "launches": 20}), flush=True)
         return 0
 
-    import mxfp4_expert_matmul_k3moe_amd as k3
-    from k3gen import device as gdev
     from k3gen.workloads import WORKLOADS
 
     w = WORKLOADS["decode" if args.workload == "cached" else args.workload]
@@ -222,140 +421,115 @@ def main() -> int:
     if w.block:
         return bench_stack(args, w)
     dev = torch.device("cuda:0")
-    dims = k3.make_dims(w.d, w.f, w.E, w.k)
-    ex = k3.MxExperts(**gdev.experts(w, 0, dev))
-    wr = gdev.router_w(w, 0, dev)
-    bias = gdev.bias(w, 0, dev)
-    # fresh tokens every step; prefill steps read most experts anyway, so fewer sets suffice
-    nsets = max(1, args.token_sets if w.T <= 64 else min(args.token_sets, 4))
-    xs = torch.stack([gdev.x_bf16(w, token_set=i, device=dev) for i in range(nsets)])
-    ws = k3.make_workspace(dims, w.T, dev)
-    y = torch.empty((w.T, w.d), dtype=torch.float32, device=dev)
-    ybf = torch.empty((w.T, w.d), dtype=torch.bfloat16, device=dev)
-    ids = torch.empty((nsets, w.T, w.k), dtype=torch.int32, device=dev)
-    gates = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
-
-    def step(i):
-        s = i % nsets
-        k3.layer_forward(dims, xs[s], wr, bias, ex, y=y, y_bf16=ybf, ids=ids[s], gates=gates,
-                         ws=ws)
-
-    t0, t1 = timed_loop(args, step, nsets)
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-
-    ids_np = ids.cpu().numpy()
-    router_bytes = w.d * w.E * 2
-    uniq = [len(np.unique(ids_np[s2])) for s2 in range(nsets)]
-    step_sets = [(args.warmup + i) % nsets for i in range(args.steps)]
-    bytes_timed = sum(uniq[s2] * w.expert_bytes + router_bytes for s2 in step_sets)
-    pairs = w.T * w.k
-    flops_step = 6.0 * w.d * w.f * pairs  # useful SwiGLU expert flops (router excluded)
-
-    # dominant kernels timed live: HIP events around their own launches
-    hip = Hip()
-    nprobe = min(args.steps, 100 if w.T <= 64 else 20)
-    kern = {}
-    for which, name in ((k3.KERNEL_GATE_UP, "gate_up"), (k3.KERNEL_DOWN, "down")):
-        evs = [(hip.event(), hip.event()) for _ in range(nprobe)]
-        for i in range(nprobe):
-            k3.time_next_kernel(which, evs[i][0], evs[i][1])
-            step(args.warmup + i)
-        torch.cuda.synchronize()
-        times = [hip.elapsed_ms(a, b) for a, b in evs]
-        for a, b in evs:
-            hip.destroy(a)
-            hip.destroy(b)
-        kern[name] = sum(times) / len(times)
-    sel = float(np.mean([uniq[(args.warmup + i) % nsets] for i in range(nprobe)]))
-    gu_bytes = sel * 2 * w.f * (w.d // 2 + w.d // 32)
-    dn_bytes = sel * w.d * (w.f // 2 + w.f // 32)
-    gu_s, dn_s = kern["gate_up"] * 1e-3, kern["down"] * 1e-3
-
-    # HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE record, used only while
-    # the kernel source it was measured on is unchanged
-    traffic = decode_traffic() if args.workload == "decode" and not args.tokens else None
-
-    if w.T <= 64:  # decode-like: weight stream
-        value, unit = bytes_timed / (t1 - t0) / 1e9, "GB/s"
-        ach = gu_bytes / gu_s / 1e9
+    metric = "MoE layer MXFP4 weight-stream GB/s (decode) + TFLOP/s (prefill), % of peak"
+    # the default line carries both halves of the metric: the prefill chunk (config 4) runs
+    # first, then the decode headline; CPU baselines run before any GPU work
+    with_prefill = (args.workload == "decode" and not args.tokens and not args.no_prefill
+                    and not args.graph)
+    cpu = {}
+    if not args.no_cpu_baseline:
         if w.T == 1:
-            kname = "gateup_decode_kernel (MXFP4 gate/up GEMV + SwiGLU)"
-        elif w.T >= MFMA_MIN_TOKENS:
-            kname = ("mfma_ffn_kernel<gate/up> (grouped GEMM on the block-scaled FP4 x FP8 MFMA, "
-                     "token as two FP8 terms, + SwiGLU)")
-        else:
-            kname = "gateup_gemv_kernel (MXFP4 gate/up GEMV + SwiGLU)"
-        roof = {"bound": "hbm", "kernel": kname,
-                "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "bytes_per_launch": int(gu_bytes), "avg_launch_us": round(kern["gate_up"] * 1e3, 2)}
-        extra = {"down_us": round(kern["down"] * 1e3, 2),
-                 "down_GBps": round(dn_bytes / dn_s / 1e9, 1),
-                 "layer_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
-                 "distinct_experts_per_step": round(float(np.mean(uniq)), 1)}
-    else:  # prefill: grouped GEMM
-        value, unit = flops_step * args.steps / (t1 - t0) / 1e12, "TFLOP/s"
-        gu_flops = 4.0 * w.d * w.f * pairs
-        ach = gu_flops / gu_s / 1e12
-        # two FP8-rate MFMAs (5.0 PFLOP/s) per useful product: 2.5 PFLOP/s of useful flops,
-        # the same ceiling as bf16 MFMA
-        roof = {"bound": "mfma",
-                "kernel": "mfma_ffn_kernel<gate/up> (grouped GEMM, block-scaled FP4 x FP8 MFMA, "
-                          "two FP8 token terms)",
-                "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
-                "flops_per_launch": gu_flops, "avg_launch_us": round(kern["gate_up"] * 1e3, 2)}
-        extra = {"down_us": round(kern["down"] * 1e3, 2),
-                 "down_TFLOPs": round(2.0 * w.d * w.f * pairs / dn_s / 1e12, 1),
-                 "layer_frac_of_mfma_peak": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
-                 "weight_GBps": round(bytes_timed / (t1 - t0) / 1e9, 1),
-                 "gateup_weight_GBps": round(gu_bytes / gu_s / 1e9, 1),
-                 "distinct_experts_per_step": round(float(np.mean(uniq)), 1),
-                 "hbm_floor_ms": round(float(np.mean(uniq)) * w.expert_bytes / (HBM_PEAK_GBS * 1e9) * 1e3, 3)}
+            cpu["base"] = cpu_baseline(w, args.cpu_tokens)
+            cpu["tuned"] = cpu_tuned_baseline(w, args.cpu_tokens)
+        if with_prefill or (w.T > 64 and not args.tokens):
+            cpu["prefill"] = cpu_baseline_prefill(WORKLOADS["prefill"])
+
+    prefill_obj = None
+    if with_prefill:
+        wp = WORKLOADS["prefill"]
+        leg = LayerLeg(args, wp, dev)
+        mp = leg.measure(args.repeats)
+        del leg
+        torch.cuda.empty_cache()
+        v, unit, roof, extra = prefill_fields(wp, mp, grouped_traffic(wp))
+        prefill_obj = {"value": round(v, 2), "unit": unit, "steps": args.steps,
+                       "warmup": args.warmup, "ms_per_step": round(mp["ms_per_step"], 5),
+                       "repeats": spread(mp["runs"]), "dtype": dtype_of(wp),
+                       "config": {"workload": f"{wp.name}: {workload_desc(wp)}",
+                                  "token_sets": min(args.token_sets, 4)},
+                       "roofline": roof, "kernels": extra,
+                       "cpu_baseline": cpu.get("prefill")}
+
+    leg = LayerLeg(args, w, dev)
+    m = leg.measure(args.repeats)
+    if w.T <= 64:
+        traffic = decode_traffic() if args.workload == "decode" and not args.tokens else None
+        value, unit, roof, extra = decode_like_fields(w, m, traffic)
+    else:
+        value, unit, roof, extra = prefill_fields(w, m, grouped_traffic(w))
 
     out = {
-        "metric": "MoE layer MXFP4 weight-stream GB/s (decode) + TFLOP/s (prefill), % of peak",
+        "metric": metric,
         "value": round(value, 2),
         "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(m["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4*bf16->fp32 (router fp64)",
+        "dtype": dtype_of(w),
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {workload_desc(w)}",
-                   "bytes_per_step": int(round(bytes_timed / args.steps)),
-                   "token_sets": nsets, "hip_graph": bool(args.graph)},
+                   "bytes_per_step": int(round(m["bytes_timed"] / args.steps)),
+                   "token_sets": leg.nsets, "hip_graph": bool(args.graph),
+                   "preceded_by": "the prefill leg below, on the same GPU" if prefill_obj
+                   else None},
+        "repeats": spread(m["runs"]),
         "roofline": roof,
         "kernels": extra,
+        "cpu_baseline": cpu.get("base") if w.T == 1 else cpu.get("prefill"),
     }
-    if not args.no_cpu_baseline and w.T == 1:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
-        out["cpu_tuned"] = cpu_tuned_baseline(w, args.cpu_tokens)
-    else:
-        out["cpu_baseline"] = None
+    if "tuned" in cpu:
+        out["cpu_tuned"] = cpu["tuned"]
+    if prefill_obj is not None:
+        out["prefill"] = prefill_obj
     print(json.dumps(out), flush=True)
     return 0
+
+
+def _read_record(name: str) -> dict:
+    path = os.path.join(ROOT, "profiles", name)
+    tr = {}
+    if os.path.exists(path):
+        with open(path) as fh:
+            for line in fh:
+                if ":" in line and not line.startswith("#"):
+                    key, val = line.split(":", 1)
+                    tr[key.strip()] = val.strip()
+    return tr
 
 
 def decode_traffic():
     """HBM bytes per launch of the T=1 gate/up kernel from the committed FETCH_SIZE /
     WRITE_SIZE record, used only while the kernel source it was measured on is unchanged."""
-    prof_traffic = os.path.join(ROOT, "profiles", "gateup_decode_traffic.txt")
-    if not os.path.exists(prof_traffic):
-        return None
-    tr = {}
-    with open(prof_traffic) as fh:
-        for line in fh:
-            if ":" in line and not line.startswith("#"):
-                key, val = line.split(":", 1)
-                tr[key.strip()] = val.strip()
-    if tr.get("kernel_source_hash") != _kernel_hash():
+    tr = _read_record("gateup_decode_traffic.txt")
+    if not tr or tr.get("kernel_source_hash") != _kernel_hash():
         return None
     return int(tr["bytes_per_launch"])
+
+
+def grouped_traffic(w):
+    """HBM bytes per launch of the grouped gate/up GEMM on the prefill chunk (T=2048, Zipf
+    bias) from the committed counter record, while the grouped-GEMM source is unchanged."""
+    if w.name != "prefill" or w.T != 2048:
+        return None
+    tr = _read_record("gateup_grouped_traffic.txt")
+    if not tr or tr.get("kernel_source_hash") != _grouped_hash():
+        return None
+    return int(tr["bytes_per_launch"])
+
+
+def _grouped_hash() -> str:
+    """Hash of the grouped-GEMM source (ffn_mfma.hip and k3moe_device.h)."""
+    import hashlib
+    csrc = os.path.join(ROOT, "mxfp4_expert_matmul_k3moe_amd", "csrc")
+    h = hashlib.sha256()
+    for n in ("ffn_mfma.hip", "k3moe_device.h"):
+        with open(os.path.join(csrc, n), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def bench_stack(args, w) -> int:
@@ -427,7 +601,8 @@ def bench_stack(args, w) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4*bf16->fp32 (router fp64; shared expert bf16)",
+        "dtype": DTYPE_DECODE.replace("gate/up bf16", "gate/up fp32 x") +
+                 "; shared expert bf16 weights x fp32 (fp32 acc)",
         "data": "synthetic",
         "config": {"workload": f"stack8: {workload_desc(w)} layers={w.layers}, block "
                                "(RMSNorm, shared expert, residual)",
@@ -535,7 +710,7 @@ def bench_cached(args, w) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4*bf16->fp32 (router fp64)",
+        "dtype": DTYPE_DECODE,
         "data": "synthetic",
         "config": {"workload": f"cached decode: {workload_desc(w)}, {w.E} experts in pinned "
                                f"host memory, {C} HBM slots, LRU",
@@ -552,6 +727,12 @@ def bench_cached(args, w) -> int:
         "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
+    # hand the pinned host memory (all E experts, ~15.7 GB at K3 size) back to the HIP
+    # runtime before the interpreter exits, rather than from torch's allocator finalisers
+    torch.cuda.synchronize()
+    del host_ex, src
+    host.clear()
+    torch._C._host_emptyCache()
     return 0
 
 

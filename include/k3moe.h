@@ -38,8 +38,9 @@
  *     memory owned by the caller. The library never allocates device memory; its only
  *     state is cached device properties and, once block mode has run on a device, one
  *     non-blocking side stream of default priority for that device and, per host thread
- *     that ran block mode there, one pair of fork/join events (all kept until the process
- *     ends). Calls with distinct workspaces may run concurrently on distinct streams.
+ *     that ran block mode there, one pair of fork/join events (kept until k3moe_release()
+ *     or the process end; the slot cache below keeps copy streams the same way). Calls
+ *     with distinct workspaces may run concurrently on distinct streams.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = default
  *     stream). The caller synchronises. In block mode the shared expert runs on the
  *     side stream, forked from `stream` after the RMSNorm and joined back into it (by
@@ -59,13 +60,18 @@
  *   - Alignment: x, y and the MXFP4 nibble arrays must be 16-byte aligned (EINVAL).
  *     With 16 or more tokens, bf16 activations, d_model and d_ff multiples of 128 and
  *     4-byte aligned scale arrays, the expert matmuls run as grouped GEMMs on the
- *     block-scaled FP4 x FP8 MFMA (the token split exactly into two FP8 terms, h into
- *     three FP8 terms with per-32-block scales); otherwise as per-expert GEMVs. All
- *     accumulate in fp32 (results agree to rounding).
+ *     block-scaled FP4 x FP8 MFMA: the token enters as two FP8 (E4M3) terms with one
+ *     E8M0 scale per term row, which carry every bf16 element to about 2^-22 of the row's
+ *     largest magnitude (smaller elements lose low bits); h enters as three FP8 terms
+ *     with one scale per term and 32-element block (to about 2^-13 of the block's
+ *     largest magnitude). Otherwise the matmuls run as per-expert GEMVs on fp32
+ *     conversions of the packed weights. All accumulate in fp32.
  *   - Limits (EUNSUPPORTED beyond): n_experts <= 4096, T <= 1048576, d_model <= 16384,
  *     d_ff <= 16384; the expert kernels also need (d_ff/32)/p <= 4, with p the largest
  *     power of two <= 64 dividing d_ff/32 (true for d_ff = 1536, 256, 32, any multiple
- *     of 2048, ...).
+ *     of 2048, ...). The workspace grows about as T * top_k * 4 * (d_model + d_ff) bytes
+ *     (1.27 GB at T = 2048 on the K3 layer), so in practice HBM bounds T well below the
+ *     nominal limit: split longer prefills into chunks.
  */
 #ifndef K3MOE_H
 #define K3MOE_H
@@ -130,15 +136,23 @@ K3MOE_API int k3moe_router(const k3moe_dims* dims, int32_t T, const void* x, int
                  const uint16_t* w_router, const float* logit_bias, int32_t* topk_ids,
                  float* topk_gates, void* ws, size_t ws_bytes, void* stream);
 
-/* Stable counting sort of the T*k (token, slot) pairs by expert (the token lists the
- * grouped expert matmuls consume). topk_ids: [T][k], each in [0, E) and distinct within a
- * token (ids outside [0, E) are a caller error; the kernels ignore such pairs).
+/* Stable counting sort of the T*k (token, slot) pairs by expert: the per-expert token lists
+ * that let each selected expert's weights be read once for all tokens routed to it, and
+ * experts routed no token be skipped ("用纯C语言把1.56TB的Kimi K3模型塞进8GB内存运行",
+ * kongchang.com, section 专家权重永不常驻内存: the router decides which experts are read;
+ * "Kimi K3 纯 C 语言 CPU 推理实战" §2.4, moe_forward's loop over the selected experts of each
+ * token). topk_ids: [T][k], each in [0, E) and distinct within a token (ids outside [0, E)
+ * are a caller error; the kernels ignore such pairs).
  * Writes expert_offsets [E+1] and bucket_rows [T*k]. */
 K3MOE_API int k3moe_route_bucket(const k3moe_dims* dims, int32_t T, const int32_t* topk_ids,
                        int32_t* expert_offsets, int32_t* bucket_rows, void* ws,
                        size_t ws_bytes, void* stream);
 
-/* Routed experts + gate-weighted combine for already-routed tokens:
+/* Routed experts + gate-weighted combine for already-routed tokens ("Kimi K3 纯 C 语言 CPU
+ * 推理实战" §1.2, y = sum_i g_i(x) E_i(x); §2.4, moe_forward's expert evaluation and
+ * gate-weighted accumulation; §2.3, the [N][K] weight layout with 32-element scale groups;
+ * project card "P053 FareedKhan-dev/kimi-k3-in-c", core features: the MXFP4 weights are
+ * multiplied in packed form):
  * y_t = sum_slot topk_gates[t][slot] * E_e(x_t), e the expert whose bucket holds pair
  * t*k+slot. Each expert's MXFP4 weights are read once per call for all of its tokens and
  * either converted in registers (GEMV kernels) or fed as stored to the block-scaled FP4 x
@@ -151,7 +165,11 @@ K3MOE_API int k3moe_expert_ffn(const k3moe_dims* dims, int32_t T, const void* x,
                      const int32_t* bucket_rows, const float* topk_gates, float* y,
                      void* ws, size_t ws_bytes, void* stream);
 
-/* One whole layer: router -> top-k -> bucket -> experts -> combine.
+/* One whole layer: router -> top-k -> bucket -> experts -> combine ("Kimi K3 纯 C 语言 CPU
+ * 推理实战" §1.2 and §2.4, moe_forward). Block mode adds the parts of a decoder block
+ * around it: RMSNorm ("用纯C语言把1.56TB的Kimi K3模型塞进8GB内存运行", kongchang.com, the
+ * model's layer structure) and the always-active shared expert kept at high precision
+ * ("Kimi K3 纯 C 语言 CPU 推理实战" §1.2, 16 routed experts plus one shared expert).
  * blk == NULL: y = MoE(x).
  * blk != NULL (block mode): x must be fp32 (x_dtype K3MOE_F32), the residual h;
  *   xhat = h / sqrt(mean(h^2) + rms_eps) * rms_gamma feeds the router, the routed experts
@@ -237,6 +255,16 @@ K3MOE_API int k3moe_time_next_kernel(int which, void* ev_start, void* ev_stop);
 
 /* Message describing the calling thread's last non-OK status ("" if none). */
 K3MOE_API const char* k3moe_last_error(void);
+
+/* Teardown of what the library keeps between calls: synchronises and destroys, on every
+ * device where they exist, the block-mode side stream and the slot cache's copy streams,
+ * and destroys the CALLING thread's fork/join events (other threads' events stay until the
+ * process ends). Call it when no call into the library is in flight on any thread, before
+ * the HIP runtime is torn down (e.g. from an exit handler; the Python binding registers
+ * one). Returns K3MOE_OK, or K3MOE_EHIP if a HIP call failed (the rest is still released).
+ * Touches no HIP state if the library never created any of these. A later call that needs
+ * them creates them again. */
+K3MOE_API int k3moe_release(void);
 
 #ifdef __cplusplus
 }

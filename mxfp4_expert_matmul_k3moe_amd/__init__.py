@@ -8,6 +8,7 @@ missing, every call raises.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import dataclasses
 import os
@@ -116,7 +117,12 @@ def lib() -> ctypes.CDLL:
                                                  ctypes.POINTER(_MxExperts),
                                                  ctypes.POINTER(_MxExperts), vp, vp, vp, vp, vp,
                                                  ctypes.POINTER(CacheStats), vp, sz, vp]
+        L.k3moe_release.restype = ctypes.c_int
+        L.k3moe_release.argtypes = []
         _lib = L
+        # streams and events the library keeps are released while the HIP runtime is
+        # still up (Python's exit handlers run before the runtime's own finalisers)
+        atexit.register(L.k3moe_release)
     return _lib
 
 

@@ -461,9 +461,16 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int d, int k, const
 
 int bpl_of(int nb) { return nb / lanes_per_row(nb); }
 
+constexpr int kMaxDecodeBpl = 8;
+
 }  // namespace
 
 bool down_fused_supported(int f, int k) { return k * lanes_per_row(f >> 5) <= 512; }
+
+// The T == 1 gate/up kernel holds all of a lane's blocks of one row at once (one pass, at
+// most 8 per lane); wider rows (e.g. d_model = 288, 2304, 4608: 9 blocks per lane) take the
+// per-expert GEMV kernel, which walks the row in groups of 8.
+bool gateup_decode_supported(int d) { return bpl_of(d >> 5) <= kMaxDecodeBpl; }
 
 bool gemv_shape_supported(int d, int f) {
   // down projections keep a row slice of h in registers: at most 4 blocks per lane
@@ -533,6 +540,7 @@ hipError_t launch_gateup_decode(int d, int f, int k, const void* x, int xf32, co
   if (blocks_per_cu <= 0) blocks_per_cu = xf32 ? 2 : 4;
   const int cap = blocks_per_cu * n_cu;
   if (grid > cap) grid = cap;
+  if (bpl > kMaxDecodeBpl) return hipErrorInvalidValue;  // see gateup_decode_supported
   const size_t lds = (size_t)d * (xf32 ? 4 : 2);
 #define K3_GD(XF, B) gateup_decode_kernel<XF, B><<<grid, 256, lds, s>>>(a)
 #define K3_GD_B(XF)                   \

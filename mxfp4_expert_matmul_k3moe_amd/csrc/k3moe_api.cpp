@@ -215,70 +215,81 @@ k3moe::BucketOut bucket_out(const Ws& ws, int32_t* offsets, int32_t* rows) {
   return o;
 }
 
+// HIP objects the library keeps between calls: per device, one side stream (block mode)
+// and kCopyStreams copy streams (slot cache), created on first use; per host thread and
+// device, the fork/join events of block mode and of the copy streams. They live until
+// k3moe_release() or the process ends. g_created tells k3moe_release whether anything was
+// ever made (so it touches no HIP state in a process that never ran a kernel).
+constexpr int kMaxDev = 64;
+constexpr int kCopyStreams = 4;
+std::mutex g_obj_mu;
+hipStream_t g_side[kMaxDev] = {};
+hipStream_t g_copy[kMaxDev][kCopyStreams] = {};
+std::atomic<bool> g_created{false};
+thread_local hipEvent_t t_fj[kMaxDev][2] = {};
+thread_local hipEvent_t t_cp[kMaxDev][kCopyStreams + 1] = {};
+
+bool make_event(hipEvent_t& ev) {
+  if (ev) return true;
+  if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) {
+    ev = nullptr;
+    return false;
+  }
+  g_created.store(true);
+  return true;
+}
+
+bool make_stream(hipStream_t& st) {  // caller holds g_obj_mu
+  if (st) return true;
+  if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) {
+    st = nullptr;
+    return false;
+  }
+  g_created.store(true);
+  return true;
+}
+
 // Fork and join events of block mode: one pair per host thread and device, created on
 // first use and kept. Each call records them again; a stream wait takes the event's record
 // at the time of the wait, calls from one thread are ordered on the host, and other
 // threads have their own pair. (Creating and destroying them per call cost more host
 // time than a decoder block's kernels take on the GPU.)
 bool fork_join_events(hipEvent_t& fork, hipEvent_t& joined) {
-  thread_local hipEvent_t ev[64][2] = {};
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
-  for (int i = 0; i < 2; ++i) {
-    if (!ev[dev][i] && hipEventCreateWithFlags(&ev[dev][i], hipEventDisableTiming) != hipSuccess) {
-      ev[dev][i] = nullptr;
-      return false;
-    }
-  }
-  fork = ev[dev][0];
-  joined = ev[dev][1];
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return false;
+  if (!make_event(t_fj[dev][0]) || !make_event(t_fj[dev][1])) return false;
+  fork = t_fj[dev][0];
+  joined = t_fj[dev][1];
   return true;
 }
 
-// One non-blocking side stream per device (default priority), created on first use and
-// kept for the life of the process, for work that can overlap the routed path.
+// One non-blocking side stream per device (default priority) for work that can overlap
+// the routed path.
 hipStream_t side_stream() {
-  static std::mutex mu;
-  static hipStream_t streams[64] = {};
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  std::lock_guard<std::mutex> lock(mu);
-  if (!streams[dev] && hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking) != hipSuccess)
-    streams[dev] = nullptr;
-  return streams[dev];
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
+  std::lock_guard<std::mutex> lock(g_obj_mu);
+  return make_stream(g_side[dev]) ? g_side[dev] : nullptr;
 }
 
 // Copy streams of the expert slot cache: kCopyStreams non-blocking streams per device
-// (default priority), created on first use and kept, so the host -> HBM copies of several
-// missing experts run on several DMA engines at once; plus, per host thread and device,
-// one fork event and one join event per copy stream.
-constexpr int kCopyStreams = 4;
+// (default priority), so the host -> HBM copies of several missing experts run on several
+// DMA engines at once; plus, per host thread and device, one fork event and one join event
+// per copy stream.
 bool copy_streams(hipStream_t (&cs)[kCopyStreams], hipEvent_t& fork,
                   hipEvent_t (&join)[kCopyStreams]) {
-  static std::mutex mu;
-  static hipStream_t streams[64][kCopyStreams] = {};
-  thread_local hipEvent_t ev[64][kCopyStreams + 1] = {};
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return false;
   {
-    std::lock_guard<std::mutex> lock(mu);
+    std::lock_guard<std::mutex> lock(g_obj_mu);
     for (int i = 0; i < kCopyStreams; ++i)
-      if (!streams[dev][i] &&
-          hipStreamCreateWithFlags(&streams[dev][i], hipStreamNonBlocking) != hipSuccess) {
-        streams[dev][i] = nullptr;
-        return false;
-      }
+      if (!make_stream(g_copy[dev][i])) return false;
+    for (int i = 0; i < kCopyStreams; ++i) cs[i] = g_copy[dev][i];
   }
   for (int i = 0; i <= kCopyStreams; ++i)
-    if (!ev[dev][i] && hipEventCreateWithFlags(&ev[dev][i], hipEventDisableTiming) != hipSuccess) {
-      ev[dev][i] = nullptr;
-      return false;
-    }
-  for (int i = 0; i < kCopyStreams; ++i) {
-    cs[i] = streams[dev][i];
-    join[i] = ev[dev][i + 1];
-  }
-  fork = ev[dev][0];
+    if (!make_event(t_cp[dev][i])) return false;
+  for (int i = 0; i < kCopyStreams; ++i) join[i] = t_cp[dev][i + 1];
+  fork = t_cp[dev][0];
   return true;
 }
 
@@ -350,7 +361,7 @@ int run_ffn(const k3moe_dims& dm, int32_t T, const void* x, int xf32,
                                            shared, y, y_bf16, s),
                      "combine");
   }
-  if (T == 1 && k3moe::down_fused_supported(f, k)) {
+  if (T == 1 && k3moe::down_fused_supported(f, k) && k3moe::gateup_decode_supported(d)) {
     // single token: persistent decode kernels
     {
       Probe probe(K3MOE_KERNEL_GATE_UP, s);
@@ -408,6 +419,47 @@ int k3moe_time_next_kernel(int which, void* ev_start, void* ev_stop) {
 }
 
 const char* k3moe_last_error(void) { return g_err.c_str(); }
+
+int k3moe_release(void) {
+  if (!g_created.load()) return K3MOE_OK;
+  int cur = 0;
+  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  int rc = K3MOE_OK;
+  auto note = [&](hipError_t e, const char* what) {
+    if (e != hipSuccess && rc == K3MOE_OK) rc = hip_check(e, what);
+  };
+  {
+    std::lock_guard<std::mutex> lock(g_obj_mu);
+    for (int dev = 0; dev < kMaxDev; ++dev) {
+      hipStream_t* own[1 + kCopyStreams] = {&g_side[dev]};
+      for (int i = 0; i < kCopyStreams; ++i) own[1 + i] = &g_copy[dev][i];
+      bool any = false;
+      for (hipStream_t* p : own) any = any || *p;
+      for (hipEvent_t ev : t_fj[dev]) any = any || ev;
+      for (hipEvent_t ev : t_cp[dev]) any = any || ev;
+      if (!any) continue;
+      note(hipSetDevice(dev), "release: set device");
+      for (hipStream_t* p : own)
+        if (*p) {
+          note(hipStreamSynchronize(*p), "release: synchronize stream");
+          note(hipStreamDestroy(*p), "release: destroy stream");
+          *p = nullptr;
+        }
+      for (hipEvent_t& ev : t_fj[dev])
+        if (ev) {
+          note(hipEventDestroy(ev), "release: destroy event");
+          ev = nullptr;
+        }
+      for (hipEvent_t& ev : t_cp[dev])
+        if (ev) {
+          note(hipEventDestroy(ev), "release: destroy event");
+          ev = nullptr;
+        }
+    }
+  }
+  if (have_cur) note(hipSetDevice(cur), "release: restore device");
+  return rc;
+}
 
 size_t k3moe_workspace_bytes(const k3moe_dims* dims, int32_t max_tokens) {
   if (check_dims(dims) || max_tokens < 0 || max_tokens > kMaxT) return 0;

@@ -66,7 +66,9 @@ hipError_t launch_gateup_gemv(int T, int d, int f, int E, int k, const void* x, 
                               const int32_t* act, const int32_t* n_act, int max_act,
                               float* h, hipStream_t s);
 // T == 1, persistent decode kernels (grid sized from the CU count); blocks_per_cu <= 0
-// picks 4 resident blocks per CU.
+// picks 4 resident blocks per CU. Needs gateup_decode_supported(d): at most 8 MXFP4 blocks
+// of a row per lane (else hipErrorInvalidValue; the GEMV kernel above takes such rows).
+bool gateup_decode_supported(int d);
 hipError_t launch_gateup_decode(int d, int f, int k, const void* x, int xf32, const MxPtrs& w,
                                 const int32_t* offsets, const int32_t* act, const int32_t* n_act,
                                 float* h, int n_cu, hipStream_t s, int blocks_per_cu = 0);

@@ -30,13 +30,16 @@ def test_exports_every_declared_symbol():
                           "k3moe_route_bucket", "k3moe_expert_ffn", "k3moe_layer_forward",
                           "k3moe_last_error", "k3moe_time_next_kernel",
                           "k3moe_cache_state_bytes", "k3moe_cache_init", "k3moe_cache_plan",
-                          "k3moe_cache_stats_get", "k3moe_layer_forward_cached"}
+                          "k3moe_cache_stats_get", "k3moe_layer_forward_cached",
+                          "k3moe_release"}
     L = k3.lib()
     for n in names:
         assert hasattr(L, n), n
     assert L.k3moe_version() == 1
     assert L.k3moe_time_next_kernel(99, None, None) == k3.EINVAL
     assert L.k3moe_time_next_kernel(k3.KERNEL_GATE_UP, None, None) == k3.OK  # disarm
+    # nothing created yet: release touches no HIP state and succeeds
+    assert L.k3moe_release() == k3.OK
 
 
 def test_workspace_bytes_monotone_and_zero_for_bad_dims():

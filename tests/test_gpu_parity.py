@@ -4,7 +4,12 @@ Bars (the oracle is the reference):
   - routing: expert ids and their order bit-exact; gates within 2 fp32 ulps;
   - bucketing: offsets and rows bit-exact;
   - layer output: max over tokens of ||y_gpu - y_ref||_2 / ||y_ref||_2 <= 2e-3 on the
-    fp32 output (the 2e-3 relative bound, read per token in the L2 norm);
+    fp32 output (the 2e-3 relative bound, read per token in the L2 norm), and per element
+    max_i |y_gpu[t,i] - y_ref[t,i]| / rms(y_ref[t]) <= 5 x the L2 bar (the largest of d
+    roughly normal errors stays within about 5 of their standard deviations; relative to
+    the row rms, since single outputs can sit arbitrarily close to zero);
+  - K3-width layers are also held to 5e-4 in L2 (about 10 x the 2e-5 .. 6e-5 the FP8-term
+    MFMA paths measure), so a single wrong tile row or N slice cannot hide under 2e-3;
   - the bf16 copy equals round-to-nearest-even of the fp32 output;
   - repeated runs are bit-identical.
 Every case prints its name before touching the GPU.
@@ -21,6 +26,8 @@ from oracle import harness
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
+K3_TOL = 5e-4
+ELEM_FACTOR = 5.0
 
 
 @pytest.fixture(scope="module")
@@ -69,17 +76,67 @@ def run_gpu_layer(w: Workload, x_np, dev, layer=0, experts=None, block=False, x_
     return {"y": y, "ybf": ybf, "ids": ids.cpu().numpy(), "gates": gates.cpu().numpy()}
 
 
+def rel_elem(yg: np.ndarray, yr: np.ndarray) -> np.ndarray:
+    """Per token: the largest element error relative to the reference row's rms."""
+    rms = np.sqrt(np.mean(yr * yr, axis=1))
+    return np.max(np.abs(yg - yr), axis=1) / np.maximum(rms, 1e-300)
+
+
 def assert_layer(w: Workload, g, ref, rows=None, tol=TOL):
     ids_g, gates_g = g["ids"], g["gates"]
     yg = g["y"].cpu().double().numpy()
     if rows is not None:
         ids_g, gates_g, yg = ids_g[rows], gates_g[rows], yg[rows]
     check_routing(ids_g, gates_g, ref["ids"], ref["gates"])
+    assert np.isfinite(yg).all() and np.isfinite(ref["y"]).all()
     err = rel_l2(yg, ref["y"])
-    print(f"    max rel L2 err {err.max():.3e}  (tokens {len(err)})", flush=True)
+    el = rel_elem(yg, ref["y"])
+    print(f"    max rel L2 err {err.max():.3e}, max elem err / row rms {el.max():.3e}  "
+          f"(tokens {len(err)})", flush=True)
     assert err.max() <= tol
+    assert el.max() <= ELEM_FACTOR * tol, f"element error {el.max():.3e} of the row rms"
     assert torch.equal(g["ybf"], g["y"].to(torch.bfloat16)), "bf16 copy is not RNE(fp32)"
     return err
+
+
+def tile_probe_tokens(ids: np.ndarray, E: int, want: int = 40, seed: int = 0) -> list:
+    """Tokens whose (token, expert) pairs sit where the grouped GEMM's tiling has edges.
+
+    Bucket rows of an expert run in ascending token order; an expert with n tokens takes one
+    16-row tile (n <= 16), one 32-row tile (n <= 32) or ceil(n / 64) tiles of 64 rows. Taken:
+    the first and last row of several 64-row tiles of the two hottest experts and of their
+    final partial tiles, the first and last row of experts on 16-, 32- and single partial
+    64-row tiles, tokens 0 and T-1, then random tokens up to `want`."""
+    T, k = ids.shape
+    members = [[] for _ in range(E)]
+    for t in range(T):
+        for e in ids[t]:
+            members[int(e)].append(t)
+    counts = np.array([len(m) for m in members])
+    pick = {0, T - 1}
+
+    def rows_of(e, rows):
+        for r in rows:
+            if 0 <= r < counts[e]:
+                pick.add(members[e][r])
+
+    for e in np.argsort(-counts, kind="stable")[:2]:
+        n = int(counts[e])
+        nt = (n + 63) // 64
+        tiles = sorted({0, 1, nt // 2, nt - 2, nt - 1} & set(range(nt)))
+        for m in tiles:
+            rows_of(e, [64 * m, 64 * m + 63, min(64 * m + 63, n - 1)])
+    for lo, hi in ((1, 16), (17, 32), (33, 64), (65, 128)):
+        cand = [e for e in range(E) if lo <= counts[e] <= hi]
+        # the fullest and the emptiest tile of each kind
+        cand.sort(key=lambda e: (-counts[e], e))
+        for e in cand[:1] + cand[-1:]:
+            rows_of(e, [0, counts[e] - 1, counts[e] // 2])
+    rng = np.random.default_rng(seed)
+    rest = [t for t in rng.permutation(T) if t not in pick]
+    while len(pick) < want and rest:
+        pick.add(int(rest.pop()))
+    return sorted(int(t) for t in pick)
 
 
 # ---- generator ----------------------------------------------------------------------------
@@ -116,6 +173,11 @@ SHAPES = [
     Workload("k20_t1", 21, d=512, f=256, E=40, k=20, T=1),
     # one token on the MFMA down kernel with 6 K steps (f = 768)
     Workload("mfma_t1_f768", 22, d=384, f=768, E=12, k=5, T=1),
+    # one token with 9 MXFP4 blocks of a row per lane (d = 288: 1 lane x 9 blocks;
+    # d = 2304: 8 lanes x 9 blocks): the GEMV gate/up, which walks rows in groups of 8
+    Workload("d288_t1", 23, d=288, f=64, E=12, k=3, T=1),
+    Workload("d2304_t1", 24, d=2304, f=256, E=16, k=4, T=1),
+    Workload("d4608_t1", 25, d=4608, f=128, E=9, k=2, T=1),
 ]
 
 
@@ -357,22 +419,21 @@ def test_decode_k3(dev, k3_decode_layer):
         x = w.x_bf16(token_set=ts)
         g = run_gpu_layer(w, x, dev, experts=k3_decode_layer)
         ref = harness.run_layer(w, x)
-        assert_layer(w, g, ref)
+        assert_layer(w, g, ref, tol=K3_TOL)
         g2 = run_gpu_layer(w, x, dev, experts=k3_decode_layer)
         assert torch.equal(g["y"], g2["y"])
 
 
 def test_batched_k3(dev):
+    """All 32 tokens of the batched-decode workload against the oracle (grouped GEMMs with
+    16- and 32-row tiles at K3 widths)."""
     w = BATCHED
-    say("batched decode: T=32")
+    say("batched decode: T=32, every token")
     x = w.x_bf16()
     ex = gdev.experts(w, 0, dev)
     g = run_gpu_layer(w, x, dev, experts=ex)
-    rows = [0, 11, 31]
-    ref = harness.run_layer(w, x, tokens=rows)
-    assert_layer(w, g, ref, rows=rows)
-    ids_all, _, _, _ = oracle.layer_route(x, w.router_w(0), None, w.k)
-    assert np.array_equal(g["ids"], ids_all)
+    ref = harness.run_layer(w, x)
+    assert_layer(w, g, ref, tol=K3_TOL)
     del ex
     torch.cuda.empty_cache()
 
@@ -387,9 +448,10 @@ def test_prefill_k3(dev):
     check_routing(g["ids"], g["gates"], ids_all, gates_all)
     counts = np.bincount(ids_all.ravel(), minlength=w.E)
     print(f"    touched experts {int((counts > 0).sum())}, max load {counts.max()}", flush=True)
-    rows = [0, 1023, 2047]
+    rows = tile_probe_tokens(ids_all, w.E)
+    assert len(rows) >= 32
     ref = harness.run_layer(w, x, tokens=rows)
-    assert_layer(w, g, ref, rows=rows)
+    assert_layer(w, g, ref, rows=rows, tol=K3_TOL)
     del ex
     torch.cuda.empty_cache()
 
@@ -407,9 +469,10 @@ def test_prefill_k3_t8192(dev):
     counts = np.bincount(ids_all.ravel(), minlength=w.E)
     print(f"    touched experts {int((counts > 0).sum())}, max load {counts.max()}", flush=True)
     assert counts.max() > 64 * 64  # some expert spans more than 64 full tiles
-    rows = [0, 4095, 8191]
+    rows = tile_probe_tokens(ids_all, w.E, seed=1)
+    assert len(rows) >= 32
     ref = harness.run_layer(w, x, tokens=rows)
-    assert_layer(w, g, ref, rows=rows)
+    assert_layer(w, g, ref, rows=rows, tol=K3_TOL)
     del ex
     torch.cuda.empty_cache()
 
@@ -426,7 +489,10 @@ def test_stack8_k3(dev):
         assert np.array_equal(g["ids"], ref["ids"][l]), f"routing differs at layer {l}"
         h = g["y"].cpu().numpy()
     err = rel_l2(h.astype(np.float64), ref["y"])
-    print(f"    max rel L2 err after 8 blocks {err.max():.3e}", flush=True)
+    el = rel_elem(h.astype(np.float64), ref["y"])
+    print(f"    max rel L2 err after 8 blocks {err.max():.3e}, max elem err / rms {el.max():.3e}",
+          flush=True)
     assert err.max() <= TOL
+    assert el.max() <= ELEM_FACTOR * TOL
     del layers
     torch.cuda.empty_cache()
