@@ -182,6 +182,29 @@ K3MOE_API int k3moe_layer_forward(const k3moe_dims* dims, int32_t T, const void*
                         uint16_t* y_bf16, int32_t* topk_ids, float* topk_gates, void* ws,
                         size_t ws_bytes, void* stream);
 
+/* Bytes of the static device scratch behind k3moe_layer_forward_noalloc (one copy per GPU
+ * the library runs on). 64 MiB: T <= 64 tokens on the K3 layer (d_model 7168, d_ff 1536,
+ * 896 experts, top-16) need at most 45 MiB. */
+#define K3MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* k3moe_layer_forward for callers that cannot allocate device memory or pass a workspace
+ * (code being captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc): same arguments without ws / ws_bytes, same kernels and the same results bit
+ * for bit. Its scratch is a static device array of K3MOE_NOALLOC_SCRATCH_BYTES per GPU, whose
+ * address is looked up (hipGetSymbolAddress) by the first call on each device; the call
+ * itself allocates nothing (no hipMalloc / hipFree, and in block mode the shared expert runs
+ * in order on `stream` rather than on the library's side stream). K3MOE_EUNSUPPORTED if
+ * k3moe_workspace_bytes(dims, T) exceeds the scratch; K3MOE_EHIP if the lookup fails. Every
+ * call on a GPU shares that GPU's scratch and nothing in it needs to start zeroed: calls that
+ * overlap on one GPU (on different streams or host threads) race, so serialise them, e.g. on
+ * one stream. */
+K3MOE_API int k3moe_layer_forward_noalloc(const k3moe_dims* dims, int32_t T, const void* x,
+                                          int x_dtype, const uint16_t* w_router,
+                                          const float* logit_bias,
+                                          const k3moe_mx_experts* experts,
+                                          const k3moe_block* blk, float* y, uint16_t* y_bf16,
+                                          int32_t* topk_ids, float* topk_gates, void* stream);
+
 /* ---- Routed experts beyond HBM: an HBM slot cache over host-resident experts ----------
  * The routed experts are never all kept in fast memory: those a token selects are read on
  * demand from slower storage and multiplied in their packed form, and recently used ones

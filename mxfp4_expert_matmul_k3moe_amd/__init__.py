@@ -117,6 +117,10 @@ def lib() -> ctypes.CDLL:
                                                  ctypes.POINTER(_MxExperts),
                                                  ctypes.POINTER(_MxExperts), vp, vp, vp, vp, vp,
                                                  ctypes.POINTER(CacheStats), vp, sz, vp]
+        L.k3moe_layer_forward_noalloc.restype = ctypes.c_int
+        L.k3moe_layer_forward_noalloc.argtypes = [D, i32, vp, ctypes.c_int, vp, vp,
+                                                  ctypes.POINTER(_MxExperts),
+                                                  ctypes.POINTER(_Block), vp, vp, vp, vp, vp]
         L.k3moe_release.restype = ctypes.c_int
         L.k3moe_release.argtypes = []
         _lib = L
@@ -260,11 +264,13 @@ def layer_forward(dims: Dims, x: torch.Tensor, w_router: torch.Tensor,
                   logit_bias: Optional[torch.Tensor], experts: MxExperts,
                   block: Optional[BlockWeights] = None, *, y: Optional[torch.Tensor] = None,
                   y_bf16: Optional[torch.Tensor] = None, ids: Optional[torch.Tensor] = None,
-                  gates: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                  gates: Optional[torch.Tensor] = None, ws=None,
                   stream=None) -> torch.Tensor:
     """y = MoE(x) (or, with ``block``, h + S(RMSNorm(h)) + MoE(RMSNorm(h)) for fp32 h).
 
-    ``y_bf16``/``ids``/``gates``, when given, are filled in as well."""
+    ``y_bf16``/``ids``/``gates``, when given, are filled in as well. ``ws``: a device
+    workspace of at least workspace_bytes(dims, T) bytes, None to allocate one, or False for
+    the allocation-free entry point (see layer_forward_noalloc)."""
     T = x.shape[0]
     d, E, k, f = dims.d_model, dims.n_experts, dims.top_k, dims.d_ff
     _dev(x, "x", (torch.bfloat16, torch.float32), (T, d))
@@ -289,12 +295,34 @@ def layer_forward(dims: Dims, x: torch.Tensor, w_router: torch.Tensor,
                    block.sh_up.data_ptr(), block.sh_down.data_ptr())
         blk_ref = ctypes.byref(b)
     es = _experts_struct(dims, experts)
+    if ws is False:  # the allocation-free entry point: static device scratch
+        _check(lib().k3moe_layer_forward_noalloc(ctypes.byref(dims), T, _ptr(x), _x_dtype(x),
+                                                 _ptr(w_router), _ptr(logit_bias),
+                                                 ctypes.byref(es), blk_ref, _ptr(y),
+                                                 _ptr(y_bf16), _ptr(ids), _ptr(gates),
+                                                 _stream(stream)))
+        return y
     w = _ws(dims, T, ws, x.device)
     _check(lib().k3moe_layer_forward(ctypes.byref(dims), T, _ptr(x), _x_dtype(x), _ptr(w_router),
                                      _ptr(logit_bias), ctypes.byref(es), blk_ref, _ptr(y),
                                      _ptr(y_bf16), _ptr(ids), _ptr(gates), _ptr(w), w.numel(),
                                      _stream(stream)))
     return y
+
+
+def layer_forward_noalloc(dims: Dims, x: torch.Tensor, w_router: torch.Tensor,
+                          logit_bias: Optional[torch.Tensor], experts: MxExperts,
+                          block: Optional[BlockWeights] = None, *, y: torch.Tensor,
+                          y_bf16: Optional[torch.Tensor] = None,
+                          ids: Optional[torch.Tensor] = None,
+                          gates: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """layer_forward through k3moe_layer_forward_noalloc: no workspace, nothing allocated
+    (y must be given); the library's static per-GPU scratch is used instead, so calls on one
+    GPU must not overlap."""
+    if y is None:
+        raise ValueError("layer_forward_noalloc needs y (it allocates nothing)")
+    return layer_forward(dims, x, w_router, logit_bias, experts, block, y=y, y_bf16=y_bf16,
+                         ids=ids, gates=gates, ws=False, stream=stream)
 
 
 # ---- routed experts beyond HBM: the slot cache -------------------------------------------

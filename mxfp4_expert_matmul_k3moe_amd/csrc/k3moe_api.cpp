@@ -668,11 +668,14 @@ int k3moe_layer_forward_cached(const k3moe_dims* dims, int32_t T, const void* x,
                  s);
 }
 
-int k3moe_layer_forward(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
-                        const uint16_t* w_router, const float* logit_bias,
-                        const k3moe_mx_experts* experts, const k3moe_block* blk, float* y,
-                        uint16_t* y_bf16, int32_t* topk_ids, float* topk_gates, void* ws,
-                        size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Host-side checks of a whole-layer call (everything but the workspace).
+int check_layer(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
+                const uint16_t* w_router, const k3moe_mx_experts* experts, const k3moe_block* blk,
+                const float* y) {
   int rc;
   if ((rc = check_dims(dims)) || (rc = check_T(T)) || (rc = check_dtype(x_dtype))) return rc;
   if (T == 0) return K3MOE_OK;
@@ -689,9 +692,17 @@ int k3moe_layer_forward(const k3moe_dims* dims, int32_t T, const void* x, int x_
       return rc;
     if (!(blk->rms_eps >= 0.0f)) return fail(K3MOE_EINVAL, "rms_eps must be >= 0");
   }
-  Ws w;
-  if ((rc = get_ws(*dims, T, ws, ws_bytes, &w))) return rc;
-  hipStream_t s = (hipStream_t)stream;
+  return K3MOE_OK;
+}
+
+// The layer on a carved workspace. side_ok: block mode's shared expert may run on the
+// library's side stream (created on first use); otherwise it runs in order on `s` (same
+// kernels, same buffers, so the same results bit for bit).
+int run_layer(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
+              const uint16_t* w_router, const float* logit_bias, const k3moe_mx_experts* experts,
+              const k3moe_block* blk, float* y, uint16_t* y_bf16, int32_t* topk_ids,
+              float* topk_gates, const Ws& w, hipStream_t s, bool side_ok) {
+  int rc;
   const int d = dims->d_model;
   int32_t* ids = topk_ids ? topk_ids : w.at<int32_t>(R_IDS);
   float* gates = topk_gates ? topk_gates : w.at<float>(R_GATES);
@@ -713,7 +724,7 @@ int k3moe_layer_forward(const k3moe_dims* dims, int32_t T, const void* x, int x_
   hipEvent_t fork = nullptr, joined = nullptr;
   if (blk) {
     float* ssh = w.at<float>(R_SSH);
-    hipStream_t s2 = side_stream();
+    hipStream_t s2 = side_ok ? side_stream() : nullptr;
     if (s2 && !fork_join_events(fork, joined))
       s2 = nullptr;  // no side stream: the shared expert runs in order on `s`
     if (s2) {
@@ -747,6 +758,79 @@ int k3moe_layer_forward(const k3moe_dims* dims, int32_t T, const void* x, int x_
   }
   return run_ffn(*dims, T, xin, xf32, experts, offs, rows, gates, resid, shared, y, y_bf16, w, s,
                  joined);
+}
+
+
+}  // namespace
+
+// Scratch of the allocation-free entry point, one copy per device (each GPU the library runs
+// on holds it until the process ends). In host code this name is not a device address: the
+// address comes from hipGetSymbolAddress, once per device (scratch_on_device).
+static __device__ __align__(256) uint8_t scratch[K3MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up by the first call made with
+// that device current and kept; nullptr (message set) if the lookup fails.
+void* scratch_on_device() {
+  static std::mutex mu;
+  static void* addr[kMaxDev] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
+    fail(K3MOE_EHIP, "no current HIP device");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      fail(K3MOE_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+      return nullptr;
+    }
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int k3moe_layer_forward(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
+                        const uint16_t* w_router, const float* logit_bias,
+                        const k3moe_mx_experts* experts, const k3moe_block* blk, float* y,
+                        uint16_t* y_bf16, int32_t* topk_ids, float* topk_gates, void* ws,
+                        size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_layer(dims, T, x, x_dtype, w_router, experts, blk, y))) return rc;
+  if (T == 0) return K3MOE_OK;
+  Ws w;
+  if ((rc = get_ws(*dims, T, ws, ws_bytes, &w))) return rc;
+  return run_layer(dims, T, x, x_dtype, w_router, logit_bias, experts, blk, y, y_bf16, topk_ids,
+                   topk_gates, w, (hipStream_t)stream, true);
+}
+
+int k3moe_layer_forward_noalloc(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
+                                const uint16_t* w_router, const float* logit_bias,
+                                const k3moe_mx_experts* experts, const k3moe_block* blk,
+                                float* y, uint16_t* y_bf16, int32_t* topk_ids,
+                                float* topk_gates, void* stream) {
+  int rc;
+  if ((rc = check_layer(dims, T, x, x_dtype, w_router, experts, blk, y))) return rc;
+  if (T == 0) return K3MOE_OK;
+  Ws w;
+  w.L = layout_for(*dims, T);
+  if (w.L.total > (size_t)K3MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(K3MOE_EUNSUPPORTED,
+                "T=%d needs %zu bytes of scratch, above the %zu bytes of the allocation-free "
+                "entry point's static scratch (k3moe_layer_forward takes a workspace instead)",
+                T, w.L.total, (size_t)K3MOE_NOALLOC_SCRATCH_BYTES);
+  void* base = scratch_on_device();
+  if (!base) return K3MOE_EHIP;
+  w.base = static_cast<char*>(base);  // 256-byte aligned
+  return run_layer(dims, T, x, x_dtype, w_router, logit_bias, experts, blk, y, y_bf16, topk_ids,
+                   topk_gates, w, (hipStream_t)stream, false);
 }
 
 }  // extern "C"

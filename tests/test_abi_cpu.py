@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
                           "k3moe_last_error", "k3moe_time_next_kernel",
                           "k3moe_cache_state_bytes", "k3moe_cache_init", "k3moe_cache_plan",
                           "k3moe_cache_stats_get", "k3moe_layer_forward_cached",
-                          "k3moe_release"}
+                          "k3moe_release", "k3moe_layer_forward_noalloc"}
     L = k3.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -160,3 +160,21 @@ def test_layer_forward_cached_validation():
     small = k3.ExpertCache(896, 8, 16)
     assert call(state=small.ptr) == k3.EUNSUPPORTED  # top_k above n_slots
     assert call(nbytes=100) == k3.EWORKSPACE
+
+
+def test_noalloc_rejects_beyond_its_scratch():
+    """T whose workspace exceeds the static scratch: EUNSUPPORTED on the host, before any
+    HIP call (the K3 layer needs more than 64 MiB from about 96 tokens on)."""
+    L = k3.lib()
+    assert k3.workspace_bytes(K3, 64) <= 64 << 20 < k3.workspace_bytes(K3, 128)
+    es = k3._MxExperts(*([FAKE.value] * 6))
+    rc = L.k3moe_layer_forward_noalloc(ctypes.byref(K3), 128, FAKE, 0, FAKE, None,
+                                       ctypes.byref(es), None, FAKE, None, None, None, None)
+    assert rc == k3.EUNSUPPORTED
+    assert b"static scratch" in L.k3moe_last_error()
+    # invalid arguments are still rejected first, and T = 0 is a no-op
+    assert L.k3moe_layer_forward_noalloc(ctypes.byref(K3), -1, FAKE, 0, FAKE, None,
+                                         ctypes.byref(es), None, FAKE, None, None, None,
+                                         None) == k3.EINVAL
+    assert L.k3moe_layer_forward_noalloc(ctypes.byref(K3), 0, None, 0, None, None, None, None,
+                                         None, None, None, None, None) == k3.OK
