@@ -15,6 +15,8 @@
 // Every term is one more MFMA into the same fp32 accumulator; no instruction decodes a
 // weight. K is walked in steps of 128 (4 scale blocks). Source of the form: "Kimi K3 纯
 // C 语言 CPU 推理实战" (chenxutan.com/d/5901.html) §1.2, §2.3.
+#include <type_traits>
+
 #include "k3moe_device.h"
 #include "k3moe_launch.h"
 
@@ -32,6 +34,11 @@ constexpr int kLdsBytes = 160 * 1024;
 constexpr int kBStage = kWaves * NT * 1024;  // weight blocks of one step: 16 B per lane per tile
 constexpr int kSStage = kWaves * 256;        // per-step scale words: 4 B per lane
 constexpr int kSGroup = kWaves * 1024;       // scale groups: 16 B per lane = 4 steps of scales
+// register-fed gate/up tiles (mx_gateup_tile_rw)
+constexpr int kWRing = 4;       // weight steps held per wave: the current one and 3 ahead
+constexpr int kTokStages = 4;   // token stages in LDS
+constexpr int kScaleSteps = 8;  // K steps per scale chunk (32 bytes of a row)
+static_assert(kTokStages - 1 == 3, "the last scale chunk of the K loop peels three steps");
 
 // Gate/up on the gfx950 block-scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4): the MXFP4
 // weights are the FP4 operand as stored (a lane's 16 bytes = one 32-element block of its
@@ -111,6 +118,14 @@ __device__ __forceinline__ void wait_vm_n(int n) {
       wait_vm<0>();
       break;
   }
+}
+
+// s_waitcnt vmcnt(N) (other counters left alone) as the builtin, so the compiler's own wait
+// insertion knows which vector-memory results it guarantees.
+template <int N>
+__device__ __forceinline__ void wait_vm_known() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 __device__ __forceinline__ void barrier_no_fence() {
@@ -227,6 +242,9 @@ __device__ __forceinline__ void mx_gateup_tile(const MfmaArgs& a, uint8_t* lds, 
 template <int MT>
 __device__ __forceinline__ void mx_gateup_tile_sr(const MfmaArgs& a, uint8_t* lds, int e, int p0,
                                                   int pn, int nb);
+template <int MT>
+__device__ __forceinline__ void mx_gateup_tile_rw(const MfmaArgs& a, uint8_t* lds, int e, int p0,
+                                                  int pn, int nb);
 template <int MT, bool SG4>
 __device__ __forceinline__ void mx_down_tile(const MfmaArgs& a, uint8_t* lds, int e, int p0, int pn,
                                              int nb);
@@ -258,7 +276,11 @@ __global__ __launch_bounds__(512) void mfma_ffn_kernel(MfmaArgs a) {
                    ((reinterpret_cast<uintptr_t>(a.s0) |
                      reinterpret_cast<uintptr_t>(GATEUP ? a.s1 : a.s0)) & 15u) == 0;
   if (GATEUP) {
-    if (sg4) {
+    if (sg4 && a.d % (kScaleSteps * BK) == 0) {
+      if (cnt <= 16) mx_gateup_tile_rw<1>(a, lds, e, p0, pn, nb);
+      else if (cnt <= 32) mx_gateup_tile_rw<2>(a, lds, e, p0, pn, nb);
+      else mx_gateup_tile_rw<4>(a, lds, e, p0, pn, nb);
+    } else if (sg4) {
       if (cnt <= 16) mx_gateup_tile_sr<1>(a, lds, e, p0, pn, nb);
       else if (cnt <= 32) mx_gateup_tile_sr<2>(a, lds, e, p0, pn, nb);
       else mx_gateup_tile_sr<4>(a, lds, e, p0, pn, nb);
@@ -574,6 +596,192 @@ __device__ __forceinline__ void mx_gateup_tile_sr(const MfmaArgs& a, uint8_t* ld
       }
     }
   }
+
+  store_h_terms<MT>(a, acc, p0, pn, nb, wave, ln, g);
+}
+
+// Gate/up tile for K % 512 == 0 with the weights loaded straight into the MFMA's FP4
+// operand registers: lane (ln, g) of tile nt loads the 16 bytes of MXFP4 block 4 ks + g of
+// its row (the four lanes of a row read 64 contiguous bytes per step), kWRing - 1 steps ahead
+// of the step that uses them, into a register ring. Only the tokens' FP8 terms pass through
+// LDS (a kTokStages-stage DMA pipeline shared by the block's waves), so the weights cost no
+// LDS bandwidth. The weight scales come into registers 8 steps (32 bytes of a row) at a
+// time, one chunk ahead: lane (ln, g) holds bytes [8 g, 8 g + 8) of its row's chunk, and
+// the byte of block g of step j is byte g of dword j & 1 of lane (ln, j >> 1), fetched with
+// one ds_bpermute. Every byte of weights and scales leaves HBM once per tile.
+
+// Buffer resource over `bytes` bytes at `base` (raw loads; out-of-range lanes read 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+template <int MT>
+__device__ __forceinline__ void mx_gateup_tile_rw(const MfmaArgs& a, uint8_t* lds, int e, int p0,
+                                                  int pn, int nb) {
+  constexpr int S = kTokStages, AB = MT * 4 * 1024;
+  static_assert(S * AB <= kLdsBytes, "token stages exceed LDS");
+  static_assert(kWRing == S, "the wait counts below assume as many weight steps as stages");
+  const int P = a.T * a.k;
+  const int K = a.d, NR = a.f, KB = K >> 5;
+  const uint32_t rq = (uint32_t)(K >> 1);
+  const int nk = K / BK;  // multiple of kScaleSteps (K % 1024 == 0)
+  const int nch = nk / kScaleSteps;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
+  const int ln = lane & 15, g = lane >> 4;
+
+  auto tok_of = [&](int m) {
+    const int r = min(16 * m + ln, pn - 1);
+    const int pair = a.rows[p0 + r];
+    return (pair >= 0 && pair < P) ? pair / a.k : 0;
+  };
+  // token DMA: waves w < 2 MT stage term (w & 1) of M subtile w >> 1 (as in the LDS-fed tiles)
+  const int am = (wave >> 1) < MT ? (wave >> 1) : 0, at = wave & 1;
+  const uint8_t* asrc =
+      a.x8 + ((size_t)tok_of(am) * 2 + at) * K + 32 * (g >> 1) + 16 * (g & 1);
+  int sxh[MT], sxl[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int t = tok_of(m);
+    sxh[m] = a.xs8[2 * t];
+    sxl[m] = a.xs8[2 * t + 1];
+  }
+  // expert e's G and U (weights, scales) as buffer resources; tiles 0, 1: rows +0..15,
+  // +16..31 of G; tiles 2, 3: the same rows of U (rows past the end read the last row again;
+  // their results are never stored)
+  const size_t eoff = (size_t)e * NR;
+  const __amdgpu_buffer_rsrc_t rq_g = buf_rsrc(a.q0 + eoff * rq, (uint32_t)NR * rq);
+  const __amdgpu_buffer_rsrc_t rq_u = buf_rsrc(a.q1 + eoff * rq, (uint32_t)NR * rq);
+  const __amdgpu_buffer_rsrc_t rs_g = buf_rsrc(a.s0 + eoff * KB, (uint32_t)(NR * KB));
+  const __amdgpu_buffer_rsrc_t rs_u = buf_rsrc(a.s1 + eoff * KB, (uint32_t)(NR * KB));
+  uint32_t vq[NT], vs[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const uint32_t r = (uint32_t)min(nb * 256 + wave * 32 + (nt & 1) * 16 + ln, NR - 1);
+    vq[nt] = r * rq + 16u * g;
+    vs[nt] = r * (uint32_t)KB + 8u * g;
+  }
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  auto sload = [&](int nt, int c) {  // this lane's 8 bytes of scale chunk c of its row
+    return __builtin_amdgcn_raw_buffer_load_b64(nt < 2 ? rs_g : rs_u, vs[nt], 32 * c, 0);
+  };
+
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // The K loop, compiled once for the waves that stage tokens (HA) and once for the others,
+  // so that each copy issues a fixed number of loads per step and every wait is exact.
+  auto kloop = [&](auto ha_c) {
+    constexpr bool HA = decltype(ha_c)::value;
+    constexpr int OPS = NT + (HA ? 2 : 0);  // loads per step: weights, then the token stage
+    u32x4 wr[kWRing][NT];
+    u32x2 scur[NT], snxt[NT];
+    auto issue = [&](int ks, u32x4 (&dst)[NT]) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        dst[nt] = __builtin_amdgcn_raw_buffer_load_b128(nt < 2 ? rq_g : rq_u, vq[nt], ks * 64, 0);
+      asm volatile("" ::: "memory");
+      if constexpr (HA) {
+        uint8_t* st = lds + (ks % S) * AB;
+        const int o = (am * 2 + at) * 2;
+        dma16(asrc + (size_t)ks * BK, st + o * 1024);
+        dma16(asrc + (size_t)ks * BK + 64, st + (o + 1) * 1024);
+      }
+      asm volatile("" ::: "memory");
+    };
+    // Step ks = 8 c + u of chunk c. AHEAD: steps still to be issued after this one (S - 1 in
+    // steady state). SL: this chunk loads the next scale chunk (at u = 0, before the step's
+    // own loads); SWAP: this chunk takes over the scale chunk loaded 8 steps ago.
+    auto step = [&](int ks, int c, auto u_c, auto ahead_c, auto sl_c, auto swap_c) {
+      constexpr int u = decltype(u_c)::value;
+      constexpr int AHEAD = decltype(ahead_c)::value;
+      constexpr bool SL = decltype(sl_c)::value, SWAP = decltype(swap_c)::value;
+      // the weights of step ks and its token stage (issued in that order) have landed once at
+      // most the loads issued after them are in flight: those of steps ks + 1 and ks + 2
+      // (when issued) and, at u = 1 and 2, the scale loads made at u = 0
+      constexpr int LATER = AHEAD >= 2 ? 2 : AHEAD;
+      constexpr int EXTRA = (SL && (u == 1 || u == 2)) ? NT : 0;
+      wait_vm_known<LATER * OPS + EXTRA>();
+      if constexpr (u == 0 && SWAP) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) scur[nt] = snxt[nt];  // complete: loaded 8 steps ago
+      }
+      barrier_no_fence();
+      if constexpr (u == 0 && SL) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) snxt[nt] = sload(nt, c + 1);
+        asm volatile("" ::: "memory");
+      }
+      if constexpr (AHEAD >= S - 1) issue(ks + S - 1, wr[(u + S - 1) % kWRing]);
+      const uint8_t* st = lds + (ks % S) * AB;
+      const int baddr = (ln + 16 * (u >> 1)) * 4;
+      i32x8 wop[NT];
+      int wsc[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        // an FP4 operand takes the low four registers of the tuple; the upper four are left
+        // undefined so that no zero registers are kept per tile
+        typedef int i32x4v __attribute__((ext_vector_type(4)));
+        const i32x4v wi = __builtin_bit_cast(i32x4v, wr[u % kWRing][nt]);
+        wop[nt] = __builtin_shufflevector(wi, wi, 0, 1, 2, 3, -1, -1, -1, -1);
+        wsc[nt] = (int)(((uint32_t)__builtin_amdgcn_ds_bpermute(baddr, (int)scur[nt][u & 1]) >>
+                         (8 * g)) & 0xFFu);
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const uint8_t* xh = st + ((m * 2 + 0) * 2) * 1024 + lane * 16;
+        const uint8_t* xl = st + ((m * 2 + 1) * 2) * 1024 + lane * 16;
+        const u32x4 h0 = *reinterpret_cast<const u32x4*>(xh), h1 = *reinterpret_cast<const u32x4*>(xh + 1024);
+        const u32x4 l0 = *reinterpret_cast<const u32x4*>(xl), l1 = *reinterpret_cast<const u32x4*>(xl + 1024);
+        const i32x8 xhi = {(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
+        const i32x8 xlo = {(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3], (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          acc[m][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wop[nt], xhi, acc[m][nt], 4, 0, 0,
+                                                                         wsc[nt], 0, sxh[m]);
+          acc[m][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wop[nt], xlo, acc[m][nt], 4, 0, 0,
+                                                                         wsc[nt], 0, sxl[m]);
+        }
+      }
+    };
+    using T0 = std::false_type;
+    using T1 = std::true_type;
+    (void)T0{};
+    // chunk c with `ahead` steps to issue in steady state; the last chunk's last S - 1 steps
+    // issue nothing
+    auto chunk = [&](int c, auto sl_c, auto swap_c, auto last_c) {
+      constexpr bool LAST = decltype(last_c)::value;
+      using A = std::integral_constant<int, S - 1>;
+      const int ks0 = c * kScaleSteps;
+      step(ks0 + 0, c, std::integral_constant<int, 0>{}, A{}, sl_c, swap_c);
+      step(ks0 + 1, c, std::integral_constant<int, 1>{}, A{}, sl_c, swap_c);
+      step(ks0 + 2, c, std::integral_constant<int, 2>{}, A{}, sl_c, swap_c);
+      step(ks0 + 3, c, std::integral_constant<int, 3>{}, A{}, sl_c, swap_c);
+      step(ks0 + 4, c, std::integral_constant<int, 4>{}, A{}, sl_c, swap_c);
+      step(ks0 + 5, c, std::integral_constant<int, 5>{},
+           std::integral_constant<int, LAST ? 2 : S - 1>{}, sl_c, swap_c);
+      step(ks0 + 6, c, std::integral_constant<int, 6>{},
+           std::integral_constant<int, LAST ? 1 : S - 1>{}, sl_c, swap_c);
+      step(ks0 + 7, c, std::integral_constant<int, 7>{},
+           std::integral_constant<int, LAST ? 0 : S - 1>{}, sl_c, swap_c);
+    };
+
+    // prologue: scale chunk 0 (taken over at step 0), then steps 0 .. S - 2 (nk >= 8 > S - 1)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) snxt[nt] = sload(nt, 0);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int s2 = 0; s2 < S - 1; ++s2) issue(s2, wr[s2]);
+    int c = 0;
+    for (; c + 1 < nch; ++c) chunk(c, T1{}, T1{}, T0{});
+    chunk(c, T0{}, T1{}, T1{});
+  };
+  if (wave < 2 * MT) kloop(std::true_type{});
+  else kloop(std::false_type{});
 
   store_h_terms<MT>(a, acc, p0, pn, nb, wave, ln, g);
 }

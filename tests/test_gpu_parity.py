@@ -178,6 +178,11 @@ SHAPES = [
     Workload("d288_t1", 23, d=288, f=64, E=12, k=3, T=1),
     Workload("d2304_t1", 24, d=2304, f=256, E=16, k=4, T=1),
     Workload("d4608_t1", 25, d=4608, f=128, E=9, k=2, T=1),
+    # the register-fed grouped gate/up (d a multiple of 1024): one scale chunk of 8 K steps
+    # (d = 1024), and three chunks with 16-, 32- and 64-row tiles, several M tiles per hot
+    # expert and a half-full second N slice (d = 3072, f = 384)
+    Workload("mfma_rw_d1024", 26, d=1024, f=256, E=12, k=3, T=40, zipf_alpha=0.6),
+    Workload("mfma_rw_mixed", 27, d=3072, f=384, E=24, k=3, T=150, zipf_alpha=0.6),
 ]
 
 
