@@ -227,6 +227,15 @@ def dtype_of(w) -> str:
     return DTYPE_GROUPED if w.T >= MFMA_MIN_TOKENS else DTYPE_GEMV
 
 
+def use_packed(args, w) -> bool:
+    """Expert layout of a layer leg: --layout if given (the default line's prefill leg
+    follows it too), else the packed tile layout wherever its grouped GEMMs run (more than
+    one token) and the row-major layout for one token."""
+    if args.layout:
+        return args.layout == "packed"
+    return w.T > 1 and w.d % 1024 == 0 and w.f % 512 == 0
+
+
 def spread(vals):
     import numpy as np
     v = np.asarray(vals, dtype=float)
@@ -260,14 +269,20 @@ class LayerLeg:
     experts, router, bias, token sets, workspace and outputs, and one step =
     k3moe_layer_forward over the next token set."""
 
-    def __init__(self, args, w, dev):
+    def __init__(self, args, w, dev, packed=False):
         import torch
 
         import mxfp4_expert_matmul_k3moe_amd as k3
         from k3gen import device as gdev
-        self.args, self.w, self.k3 = args, w, k3
+        self.args, self.w, self.k3, self.packed = args, w, k3, packed
         self.dims = k3.make_dims(w.d, w.f, w.E, w.k)
         self.ex = k3.MxExperts(**gdev.experts(w, 0, dev))
+        if packed:  # the packed tile layout, made once (weight preparation, not timed)
+            rm = self.ex
+            self.ex = k3.pack_experts(self.dims, rm)
+            torch.cuda.synchronize()
+            del rm
+            torch.cuda.empty_cache()
         self.wr = gdev.router_w(w, 0, dev)
         self.bias = gdev.bias(w, 0, dev)
         # fresh tokens every step; prefill steps read most experts anyway, so fewer sets
@@ -282,8 +297,9 @@ class LayerLeg:
 
     def step(self, i):
         s = i % self.nsets
-        self.k3.layer_forward(self.dims, self.xs[s], self.wr, self.bias, self.ex, y=self.y,
-                              y_bf16=self.ybf, ids=self.ids[s], gates=self.gates, ws=self.ws)
+        fwd = self.k3.layer_forward_packed if self.packed else self.k3.layer_forward
+        fwd(self.dims, self.xs[s], self.wr, self.bias, self.ex, y=self.y, y_bf16=self.ybf,
+            ids=self.ids[s], gates=self.gates, ws=self.ws)
 
     def measure(self, repeats: int) -> dict:
         """A read-only sweep (see clean_sweep), W warm-up steps, exactly K timed steps, then
@@ -326,7 +342,13 @@ class LayerLeg:
                 "gate_up_ms": kern["gate_up"], "down_ms": kern["down"], "sel": sel}
 
 
-def decode_like_fields(w, m, traffic):
+def grouped_label(packed: bool) -> str:
+    return ("mfma_ffn_kernel<gate/up> (grouped GEMM, block-scaled FP4 x FP8 MFMA, two FP8 "
+            "token terms, + SwiGLU; " + ("packed tile layout, 1 KB per weight tile step)"
+                                        if packed else "row-major weights)"))
+
+
+def decode_like_fields(w, m, traffic, packed=False):
     """value / roofline / kernels of a weight-stream (T <= 64) workload."""
     import numpy as np
     value = m["bytes_timed"] / m["sec"] / 1e9
@@ -335,9 +357,8 @@ def decode_like_fields(w, m, traffic):
     ach = gu_bytes / (m["gate_up_ms"] * 1e-3) / 1e9
     if w.T == 1:
         kname = "gateup_decode_kernel (MXFP4 gate/up GEMV + SwiGLU)"
-    elif w.T >= MFMA_MIN_TOKENS:
-        kname = ("mfma_ffn_kernel<gate/up> (grouped GEMM on the block-scaled FP4 x FP8 MFMA, "
-                 "token as two FP8 terms, + SwiGLU)")
+    elif w.T >= MFMA_MIN_TOKENS or packed:
+        kname = grouped_label(packed)
     else:
         kname = "gateup_gemv_kernel (MXFP4 gate/up GEMV + SwiGLU)"
     roof = {"bound": "hbm", "kernel": kname, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
@@ -352,7 +373,7 @@ def decode_like_fields(w, m, traffic):
     return value, "GB/s", roof, extra
 
 
-def prefill_fields(w, m, traffic):
+def prefill_fields(w, m, traffic, packed=False):
     """value / roofline / kernels of a grouped-GEMM (prefill) workload."""
     import numpy as np
     pairs = w.T * w.k
@@ -367,8 +388,7 @@ def prefill_fields(w, m, traffic):
     # two FP8-rate MFMAs (5.0 PFLOP/s) per useful product: 2.5 PFLOP/s of useful flops,
     # the same ceiling as bf16 MFMA
     roof = {"bound": "mfma",
-            "kernel": "mfma_ffn_kernel<gate/up> (grouped GEMM, block-scaled FP4 x FP8 MFMA, "
-                      "two FP8 token terms)",
+            "kernel": grouped_label(packed),
             "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
             "flops_per_launch": gu_flops, "avg_launch_us": round(m["gate_up_ms"] * 1e3, 2),
@@ -409,6 +429,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="decode: leave out the prefill leg of the default line")
+    ap.add_argument("--layout", choices=["rowmajor", "packed"], default=None,
+                    help="expert weight layout of a single-workload run (default: packed "
+                         "for the grouped-GEMM workloads, row-major for one token)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one HIP graph per token set (captured on the "
                          "caller's stream) instead of eager calls")
@@ -459,26 +482,30 @@ def main() -> int:
     prefill_obj = None
     if with_prefill:
         wp = WORKLOADS["prefill"]
-        leg = LayerLeg(args, wp, dev)
+        leg = LayerLeg(args, wp, dev, packed=use_packed(args, wp))
         mp = leg.measure(args.repeats)
         del leg
         torch.cuda.empty_cache()
-        v, unit, roof, extra = prefill_fields(wp, mp, grouped_traffic(wp))
+        pk = use_packed(args, wp)
+        v, unit, roof, extra = prefill_fields(wp, mp, grouped_traffic(wp, pk), pk)
         prefill_obj = {"value": round(v, 2), "unit": unit, "steps": args.steps,
                        "warmup": args.warmup, "ms_per_step": round(mp["ms_per_step"], 5),
                        "repeats": spread(mp["runs"]), "dtype": dtype_of(wp),
                        "config": {"workload": f"{wp.name}: {workload_desc(wp)}",
-                                  "token_sets": min(args.token_sets, 4)},
+                                  "token_sets": min(args.token_sets, 4),
+                                  "expert_layout": "packed" if use_packed(args, wp)
+                                  else "row-major"},
                        "roofline": roof, "kernels": extra,
                        "cpu_baseline": cpu.get("prefill")}
 
-    leg = LayerLeg(args, w, dev)
+    leg = LayerLeg(args, w, dev, packed=use_packed(args, w))
     m = leg.measure(args.repeats)
     if w.T <= 64:
         traffic = decode_traffic() if args.workload == "decode" and not args.tokens else None
-        value, unit, roof, extra = decode_like_fields(w, m, traffic)
+        value, unit, roof, extra = decode_like_fields(w, m, traffic, leg.packed)
     else:
-        value, unit, roof, extra = prefill_fields(w, m, grouped_traffic(w))
+        value, unit, roof, extra = prefill_fields(w, m, grouped_traffic(w, leg.packed),
+                                                  leg.packed)
 
     out = {
         "metric": metric,
@@ -496,6 +523,7 @@ def main() -> int:
         "config": {"workload": f"{w.name}: {workload_desc(w)}",
                    "bytes_per_step": int(round(m["bytes_timed"] / args.steps)),
                    "token_sets": leg.nsets, "hip_graph": bool(args.graph),
+                   "expert_layout": "packed" if leg.packed else "row-major",
                    "preceded_by": ("the prefill leg below, then " if prefill_obj else "") +
                    "a 6 GB read-only sweep (no dirty lines from input generation in the "
                    "caches; none of the layer's weights in them)"},
@@ -533,12 +561,14 @@ def decode_traffic():
     return int(tr["bytes_per_launch"])
 
 
-def grouped_traffic(w):
+def grouped_traffic(w, packed):
     """HBM bytes per launch of the grouped gate/up GEMM on the prefill chunk (T=2048, Zipf
-    bias) from the committed counter record, while the grouped-GEMM source is unchanged."""
+    bias) from the committed counter record of that layout, while the grouped-GEMM source is
+    unchanged."""
     if w.name != "prefill" or w.T != 2048:
         return None
-    tr = _read_record("gateup_grouped_traffic.txt")
+    tr = _read_record("gateup_grouped_packed_traffic.txt" if packed
+                      else "gateup_grouped_traffic.txt")
     if not tr or tr.get("kernel_source_hash") != _grouped_hash():
         return None
     return int(tr["bytes_per_launch"])

@@ -182,6 +182,51 @@ K3MOE_API int k3moe_layer_forward(const k3moe_dims* dims, int32_t T, const void*
                         uint16_t* y_bf16, int32_t* topk_ids, float* topk_gates, void* ws,
                         size_t ws_bytes, void* stream);
 
+/* ---- Packed tile layout of the expert weights ------------------------------------------
+ * The row-major layout above lets one load of a block-scaled MFMA operand (16 rows x 128
+ * elements) read only 64 contiguous bytes per row. The packed layout stores each such tile
+ * contiguously, in the order the MFMA's 64 lanes hold it, so one 16-byte-per-lane load reads
+ * 1 KB in one piece; it holds the same E2M1 codes and E8M0 scales, permuted (nothing is
+ * decoded). For an MXFP4 matrix [R][K] of one expert (R % 16 == 0, K % 128 == 0), with
+ * nk = K/128 steps, nch = ceil(nk/8) chunks of 8 steps, tile t = rows 16t .. 16t+15 and lane
+ * L = i + 16 g (i < 16, g < 4):
+ *   codes  [R/16][nk][64][16 B]: entry (t, s, L) = bytes [64 s + 16 g, 64 s + 16 g + 16) of
+ *          row 16 t + i (elements 128 s + 32 g .. 128 s + 32 g + 31), R K / 2 bytes in all;
+ *   scales [R/16][nch][64][8 B]: byte j of entry (t, c, L) = the E8M0 scale of block
+ *          4 (8 c + j) + g of row 16 t + i; 0 where 8 c + j >= nk.
+ * Experts are stacked as in k3moe_mx_experts. The layout follows the MFMA's operand order on
+ * gfx950; the formats themselves are those of "Kimi K3 纯 C 语言 CPU 推理实战" §2.3 ([N][K]
+ * weights, one scale per 32 consecutive K elements) and the project card "P053
+ * FareedKhan-dev/kimi-k3-in-c", core features (MXFP4, multiplied in packed form). Packed
+ * experts need d_model % 1024 == 0 and d_ff % 512 == 0 (K3: 7168, 1536). */
+typedef struct {
+  size_t gate_q, gate_s, up_q, up_s, down_q, down_s; /* bytes per expert of each tensor */
+} k3moe_packed_bytes;
+
+/* Per-expert sizes of the packed tensors (codes keep their size; scales are padded to whole
+ * chunks of 8 steps). Pure host function; K3MOE_EUNSUPPORTED for shapes the layout excludes. */
+K3MOE_API int k3moe_packed_expert_bytes(const k3moe_dims* dims, k3moe_packed_bytes* per_expert);
+
+/* Writes the packed copy of all dims->n_experts experts of `src` (row-major, device) into
+ * `dst` (device buffers of k3moe_packed_expert_bytes per expert, scales 8-byte aligned;
+ * must not overlap src). Asynchronous on `stream`. Meant to run once when weights are
+ * loaded. */
+K3MOE_API int k3moe_pack_experts(const k3moe_dims* dims, const k3moe_mx_experts* src,
+                                 const k3moe_mx_experts* dst, void* stream);
+
+/* k3moe_layer_forward with the experts in the packed layout (same arguments and results to
+ * rounding; bf16 activations, no block mode). The expert matmuls run as grouped GEMMs on the
+ * block-scaled FP4 x FP8 MFMA (token as two FP8 terms, h as three) for any token count, every
+ * weight tile step read as 1 KB contiguous. K3MOE_EUNSUPPORTED for shapes or activations
+ * outside the above. */
+K3MOE_API int k3moe_layer_forward_packed(const k3moe_dims* dims, int32_t T, const void* x,
+                                         int x_dtype, const uint16_t* w_router,
+                                         const float* logit_bias,
+                                         const k3moe_mx_experts* experts,
+                                         const k3moe_block* blk, float* y, uint16_t* y_bf16,
+                                         int32_t* topk_ids, float* topk_gates, void* ws,
+                                         size_t ws_bytes, void* stream);
+
 /* Bytes of the static device scratch behind k3moe_layer_forward_noalloc (one copy per GPU
  * the library runs on). 64 MiB: T <= 64 tokens on the K3 layer (d_model 7168, d_ff 1536,
  * 896 experts, top-16) need at most 45 MiB. */

@@ -46,6 +46,11 @@ class _Block(ctypes.Structure):
                 ("sh_down", ctypes.c_void_p)]
 
 
+class PackedBytes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")]
+
+
 class CacheStats(ctypes.Structure):
     _fields_ = [("hits", ctypes.c_int64), ("misses", ctypes.c_int64),
                 ("bytes_copied", ctypes.c_int64), ("distinct", ctypes.c_int32)]
@@ -121,6 +126,16 @@ def lib() -> ctypes.CDLL:
         L.k3moe_layer_forward_noalloc.argtypes = [D, i32, vp, ctypes.c_int, vp, vp,
                                                   ctypes.POINTER(_MxExperts),
                                                   ctypes.POINTER(_Block), vp, vp, vp, vp, vp]
+        L.k3moe_packed_expert_bytes.restype = ctypes.c_int
+        L.k3moe_packed_expert_bytes.argtypes = [D, ctypes.POINTER(PackedBytes)]
+        L.k3moe_pack_experts.restype = ctypes.c_int
+        L.k3moe_pack_experts.argtypes = [D, ctypes.POINTER(_MxExperts),
+                                         ctypes.POINTER(_MxExperts), vp]
+        L.k3moe_layer_forward_packed.restype = ctypes.c_int
+        L.k3moe_layer_forward_packed.argtypes = [D, i32, vp, ctypes.c_int, vp, vp,
+                                                 ctypes.POINTER(_MxExperts),
+                                                 ctypes.POINTER(_Block), vp, vp, vp, vp, vp, sz,
+                                                 vp]
         L.k3moe_release.restype = ctypes.c_int
         L.k3moe_release.argtypes = []
         _lib = L
@@ -185,17 +200,43 @@ def make_workspace(dims: Dims, max_tokens: int, device="cuda") -> torch.Tensor:
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def _experts_struct(dims: Dims, ex: MxExperts) -> _MxExperts:
+def _experts_struct(dims: Dims, ex: MxExperts, packed: bool = False) -> _MxExperts:
     E, d, f = dims.n_experts, dims.d_model, dims.d_ff
-    shapes = {"gate_q": (E, f, d // 2), "gate_s": (E, f, d // 32), "up_q": (E, f, d // 2),
-              "up_s": (E, f, d // 32), "down_q": (E, d, f // 2), "down_s": (E, d, f // 32)}
+    if packed:
+        pb = packed_expert_bytes(dims)
+        sizes = {n: E * pb[n] for n in pb}
+    else:
+        sizes = {"gate_q": E * f * (d // 2), "gate_s": E * f * (d // 32),
+                 "up_q": E * f * (d // 2), "up_s": E * f * (d // 32),
+                 "down_q": E * d * (f // 2), "down_s": E * d * (f // 32)}
     s = _MxExperts()
-    for n, shp in shapes.items():
+    for n, size in sizes.items():
         t = _dev(getattr(ex, n), f"experts.{n}", torch.uint8)
-        if t.numel() != shp[0] * shp[1] * shp[2]:
-            raise ValueError(f"experts.{n} has {t.numel()} bytes, expected {shp}")
+        if t.numel() != size:
+            raise ValueError(f"experts.{n} has {t.numel()} bytes, expected {size}")
         setattr(s, n, t.data_ptr())
     return s
+
+
+def packed_expert_bytes(dims: Dims) -> dict:
+    """Per-expert bytes of each tensor in the packed tile layout (k3moe_packed_expert_bytes)."""
+    pb = PackedBytes()
+    _check(lib().k3moe_packed_expert_bytes(ctypes.byref(dims), ctypes.byref(pb)))
+    return {n: int(getattr(pb, n)) for n, _ in PackedBytes._fields_}
+
+
+def pack_experts(dims: Dims, experts: MxExperts, stream=None) -> MxExperts:
+    """Packed copy (k3moe_pack_experts) of row-major experts, as new uint8 device tensors of
+    shape [E][bytes per expert]; enqueued on the stream."""
+    pb = packed_expert_bytes(dims)
+    dev = experts.gate_q.device
+    out = MxExperts(**{n: torch.empty((dims.n_experts, pb[n]), dtype=torch.uint8, device=dev)
+                       for n in pb})
+    src = _experts_struct(dims, experts)
+    dst = _experts_struct(dims, out, packed=True)
+    _check(lib().k3moe_pack_experts(ctypes.byref(dims), ctypes.byref(src), ctypes.byref(dst),
+                                    _stream(stream)))
+    return out
 
 
 def _ws(dims: Dims, T: int, ws: Optional[torch.Tensor], device) -> torch.Tensor:
@@ -307,6 +348,37 @@ def layer_forward(dims: Dims, x: torch.Tensor, w_router: torch.Tensor,
                                      _ptr(logit_bias), ctypes.byref(es), blk_ref, _ptr(y),
                                      _ptr(y_bf16), _ptr(ids), _ptr(gates), _ptr(w), w.numel(),
                                      _stream(stream)))
+    return y
+
+
+def layer_forward_packed(dims: Dims, x: torch.Tensor, w_router: torch.Tensor,
+                         logit_bias: Optional[torch.Tensor], experts: MxExperts, *,
+                         y: Optional[torch.Tensor] = None,
+                         y_bf16: Optional[torch.Tensor] = None,
+                         ids: Optional[torch.Tensor] = None,
+                         gates: Optional[torch.Tensor] = None, ws=None,
+                         stream=None) -> torch.Tensor:
+    """layer_forward with `experts` in the packed tile layout (pack_experts)."""
+    T = x.shape[0]
+    d, E, k = dims.d_model, dims.n_experts, dims.top_k
+    _dev(x, "x", (torch.bfloat16,), (T, d))
+    _dev(w_router, "w_router", (torch.bfloat16, torch.int16), (d, E))
+    if logit_bias is not None:
+        _dev(logit_bias, "logit_bias", torch.float32, (E,))
+    y = torch.empty((T, d), dtype=torch.float32, device=x.device) if y is None else \
+        _dev(y, "y", torch.float32, (T, d))
+    if y_bf16 is not None:
+        _dev(y_bf16, "y_bf16", (torch.bfloat16, torch.int16), (T, d))
+    if ids is not None:
+        _dev(ids, "ids", torch.int32, (T, k))
+    if gates is not None:
+        _dev(gates, "gates", torch.float32, (T, k))
+    es = _experts_struct(dims, experts, packed=True)
+    w = _ws(dims, T, ws, x.device)
+    _check(lib().k3moe_layer_forward_packed(ctypes.byref(dims), T, _ptr(x), _x_dtype(x),
+                                            _ptr(w_router), _ptr(logit_bias), ctypes.byref(es),
+                                            None, _ptr(y), _ptr(y_bf16), _ptr(ids), _ptr(gates),
+                                            _ptr(w), w.numel(), _stream(stream)))
     return y
 
 

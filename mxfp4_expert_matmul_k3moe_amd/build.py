@@ -14,7 +14,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libk3moe.so")
 
 SOURCES = ["router.hip", "bucket.hip", "ffn_gemv.hip", "ffn_mfma.hip", "block.hip",
-           "k3moe_api.cpp", "expert_cache.cpp"]
+           "pack.hip", "k3moe_api.cpp", "expert_cache.cpp"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
          "-Wno-unused-function", "-fvisibility=hidden",
          # no packed fp32 instructions in any generated code

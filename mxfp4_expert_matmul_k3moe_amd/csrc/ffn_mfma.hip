@@ -141,6 +141,7 @@ struct MfmaArgs {
   const uint8_t *q0, *s0, *q1, *s1;  // gate/up: G and U; down: D (q1 unused)
   const int32_t *offsets, *rows, *act, *n_act, *mtile_off;
   int nblk_n;
+  int packed;    // weights in the packed tile layout (pack.hip)
   uint8_t* h8;   // h as three E4M3 terms [P][3][f], bucket order (gate/up out, down in)
   uint8_t* hs8;  // their E8M0 scales [P][3][f/32], one per term and 32-element block
   float* z_out;  // down output
@@ -242,10 +243,10 @@ __device__ __forceinline__ void mx_gateup_tile(const MfmaArgs& a, uint8_t* lds, 
 template <int MT>
 __device__ __forceinline__ void mx_gateup_tile_sr(const MfmaArgs& a, uint8_t* lds, int e, int p0,
                                                   int pn, int nb);
-template <int MT>
+template <int MT, bool PK>
 __device__ __forceinline__ void mx_gateup_tile_rw(const MfmaArgs& a, uint8_t* lds, int e, int p0,
                                                   int pn, int nb);
-template <int MT, bool SG4>
+template <int MT, bool SG4, bool PK = false>
 __device__ __forceinline__ void mx_down_tile(const MfmaArgs& a, uint8_t* lds, int e, int p0, int pn,
                                              int nb);
 
@@ -276,10 +277,14 @@ __global__ __launch_bounds__(512) void mfma_ffn_kernel(MfmaArgs a) {
                    ((reinterpret_cast<uintptr_t>(a.s0) |
                      reinterpret_cast<uintptr_t>(GATEUP ? a.s1 : a.s0)) & 15u) == 0;
   if (GATEUP) {
-    if (sg4 && a.d % (kScaleSteps * BK) == 0) {
-      if (cnt <= 16) mx_gateup_tile_rw<1>(a, lds, e, p0, pn, nb);
-      else if (cnt <= 32) mx_gateup_tile_rw<2>(a, lds, e, p0, pn, nb);
-      else mx_gateup_tile_rw<4>(a, lds, e, p0, pn, nb);
+    if (a.packed) {
+      if (cnt <= 16) mx_gateup_tile_rw<1, true>(a, lds, e, p0, pn, nb);
+      else if (cnt <= 32) mx_gateup_tile_rw<2, true>(a, lds, e, p0, pn, nb);
+      else mx_gateup_tile_rw<4, true>(a, lds, e, p0, pn, nb);
+    } else if (sg4 && a.d % (kScaleSteps * BK) == 0) {
+      if (cnt <= 16) mx_gateup_tile_rw<1, false>(a, lds, e, p0, pn, nb);
+      else if (cnt <= 32) mx_gateup_tile_rw<2, false>(a, lds, e, p0, pn, nb);
+      else mx_gateup_tile_rw<4, false>(a, lds, e, p0, pn, nb);
     } else if (sg4) {
       if (cnt <= 16) mx_gateup_tile_sr<1>(a, lds, e, p0, pn, nb);
       else if (cnt <= 32) mx_gateup_tile_sr<2>(a, lds, e, p0, pn, nb);
@@ -291,7 +296,11 @@ __global__ __launch_bounds__(512) void mfma_ffn_kernel(MfmaArgs a) {
     }
     return;
   }
-  if (sg4) {
+  if (a.packed) {
+    if (cnt <= 16) mx_down_tile<1, true, true>(a, lds, e, p0, pn, nb);
+    else if (cnt <= 32) mx_down_tile<2, true, true>(a, lds, e, p0, pn, nb);
+    else mx_down_tile<4, true, true>(a, lds, e, p0, pn, nb);
+  } else if (sg4) {
     if (cnt <= 16) mx_down_tile<1, true>(a, lds, e, p0, pn, nb);
     else if (cnt <= 32) mx_down_tile<2, true>(a, lds, e, p0, pn, nb);
     else mx_down_tile<4, true>(a, lds, e, p0, pn, nb);
@@ -616,7 +625,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uin
                                            0x00020000);
 }
 
-template <int MT>
+template <int MT, bool PK>
 __device__ __forceinline__ void mx_gateup_tile_rw(const MfmaArgs& a, uint8_t* lds, int e, int p0,
                                                   int pn, int nb) {
   constexpr int S = kTokStages, AB = MT * 4 * 1024;
@@ -650,21 +659,31 @@ __device__ __forceinline__ void mx_gateup_tile_rw(const MfmaArgs& a, uint8_t* ld
   // expert e's G and U (weights, scales) as buffer resources; tiles 0, 1: rows +0..15,
   // +16..31 of G; tiles 2, 3: the same rows of U (rows past the end read the last row again;
   // their results are never stored)
+  // packed layout: tile t's step s is 1 KB at (t nk + s) KB, its scale chunk c 512 B at
+  // (t nch + c) 512 B, both in lane order; row-major: lane (ln, g) reads 16 bytes of its row
+  const uint32_t sbytes = PK ? (uint32_t)(NR / 16) * nch * 512u : (uint32_t)(NR * KB);
   const size_t eoff = (size_t)e * NR;
   const __amdgpu_buffer_rsrc_t rq_g = buf_rsrc(a.q0 + eoff * rq, (uint32_t)NR * rq);
   const __amdgpu_buffer_rsrc_t rq_u = buf_rsrc(a.q1 + eoff * rq, (uint32_t)NR * rq);
-  const __amdgpu_buffer_rsrc_t rs_g = buf_rsrc(a.s0 + eoff * KB, (uint32_t)(NR * KB));
-  const __amdgpu_buffer_rsrc_t rs_u = buf_rsrc(a.s1 + eoff * KB, (uint32_t)(NR * KB));
+  const __amdgpu_buffer_rsrc_t rs_g = buf_rsrc(a.s0 + (size_t)e * sbytes, sbytes);
+  const __amdgpu_buffer_rsrc_t rs_u = buf_rsrc(a.s1 + (size_t)e * sbytes, sbytes);
+  constexpr int QSTEP = PK ? 1024 : 64, SCHUNK = PK ? 512 : 32;
   uint32_t vq[NT], vs[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const uint32_t r = (uint32_t)min(nb * 256 + wave * 32 + (nt & 1) * 16 + ln, NR - 1);
-    vq[nt] = r * rq + 16u * g;
-    vs[nt] = r * (uint32_t)KB + 8u * g;
+    if constexpr (PK) {
+      const uint32_t t = (uint32_t)min(nb * 16 + wave * 2 + (nt & 1), NR / 16 - 1);
+      vq[nt] = (t * (uint32_t)nk * 64u + (uint32_t)lane) * 16u;
+      vs[nt] = (t * (uint32_t)nch * 64u + (uint32_t)lane) * 8u;
+    } else {
+      const uint32_t r = (uint32_t)min(nb * 256 + wave * 32 + (nt & 1) * 16 + ln, NR - 1);
+      vq[nt] = r * rq + 16u * g;
+      vs[nt] = r * (uint32_t)KB + 8u * g;
+    }
   }
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  auto sload = [&](int nt, int c) {  // this lane's 8 bytes of scale chunk c of its row
-    return __builtin_amdgcn_raw_buffer_load_b64(nt < 2 ? rs_g : rs_u, vs[nt], 32 * c, 0);
+  auto sload = [&](int nt, int c) {  // this lane's 8 bytes of scale chunk c
+    return __builtin_amdgcn_raw_buffer_load_b64(nt < 2 ? rs_g : rs_u, vs[nt], SCHUNK * c, 0);
   };
 
   f32x4 acc[MT][NT];
@@ -683,7 +702,7 @@ __device__ __forceinline__ void mx_gateup_tile_rw(const MfmaArgs& a, uint8_t* ld
     auto issue = [&](int ks, u32x4 (&dst)[NT]) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        dst[nt] = __builtin_amdgcn_raw_buffer_load_b128(nt < 2 ? rq_g : rq_u, vq[nt], ks * 64, 0);
+        dst[nt] = __builtin_amdgcn_raw_buffer_load_b128(nt < 2 ? rq_g : rq_u, vq[nt], ks * QSTEP, 0);
       asm volatile("" ::: "memory");
       if constexpr (HA) {
         uint8_t* st = lds + (ks % S) * AB;
@@ -728,8 +747,11 @@ __device__ __forceinline__ void mx_gateup_tile_rw(const MfmaArgs& a, uint8_t* ld
         typedef int i32x4v __attribute__((ext_vector_type(4)));
         const i32x4v wi = __builtin_bit_cast(i32x4v, wr[u % kWRing][nt]);
         wop[nt] = __builtin_shufflevector(wi, wi, 0, 1, 2, 3, -1, -1, -1, -1);
-        wsc[nt] = (int)(((uint32_t)__builtin_amdgcn_ds_bpermute(baddr, (int)scur[nt][u & 1]) >>
-                         (8 * g)) & 0xFFu);
+        if constexpr (PK)  // this lane's own byte of step u of the chunk
+          wsc[nt] = (int)((scur[nt][u >> 2] >> (8 * (u & 3))) & 0xFFu);
+        else
+          wsc[nt] = (int)(((uint32_t)__builtin_amdgcn_ds_bpermute(baddr, (int)scur[nt][u & 1]) >>
+                           (8 * g)) & 0xFFu);
       }
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
@@ -792,22 +814,27 @@ __device__ __forceinline__ void mx_gateup_tile_rw(const MfmaArgs& a, uint8_t* ld
 // in the FP8 operand lane order, and each pair's 4 scale bytes of every term), its 4
 // weight tiles and their scales; each wave waits on its own DMA count. 3 MFMAs per
 // (M subtile, N tile, step).
-template <int MT, bool SG4>
+// Packed weights (PK): each tile's step is one contiguous 1-KB DMA; each wave's scale bytes
+// of its 4 tiles for 8 steps come in two 1-KB DMAs into a 2-KB slot, two groups in the ring.
+constexpr int kPkSGroup = kWaves * 2048;
+
+template <int MT, bool SG4, bool PK = false>
 struct MxDownPipe {
   static constexpr int ADATA = MT * 6 * 1024;      // [m][term][half] 1-KB blocks
   static constexpr int ABYTES = ADATA + MT * 256;  // + scale words [m][term x 16 pairs]
   static constexpr int BYTES = ABYTES + kBStage + (SG4 ? 0 : kSStage);
-  static constexpr int RING = SG4 ? 2 * kSGroup : 0;
+  static constexpr int RING = PK ? 2 * kPkSGroup : (SG4 ? 2 * kSGroup : 0);
   static constexpr int S0 = (kLdsBytes - RING) / BYTES;
   static constexpr int S = S0 < 4 ? S0 : 4;
   static_assert(S >= 2, "pipeline needs two stages");
   static constexpr int A_PER_WAVE = (6 * MT + kWaves - 1) / kWaves;
 };
 
-template <int MT, bool SG4>
+template <int MT, bool SG4, bool PK>
 __device__ __forceinline__ void mx_down_tile(const MfmaArgs& a, uint8_t* lds, int e, int p0, int pn,
                                              int nb) {
-  using PP = MxDownPipe<MT, SG4>;
+  static_assert(!PK || SG4, "packed scales use the ring");
+  using PP = MxDownPipe<MT, SG4, PK>;
   constexpr int S = PP::S, SB = PP::BYTES, AB = PP::ABYTES, AW = PP::A_PER_WAVE;
   const int P = a.T * a.k;
   const int K = a.f, NR = a.d, KB = K >> 5;
@@ -826,16 +853,34 @@ __device__ __forceinline__ void mx_down_tile(const MfmaArgs& a, uint8_t* lds, in
   // scale-word lanes: pair ln, term lane >> 4 (the fourth group repeats term 2)
   const int sw_t = min(lane >> 4, 2);
   const uint8_t* bsrc[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int r = min(nb * 512 + wave * 64 + nt * 16 + ln, NR - 1);
-    bsrc[nt] = a.q0 + ((size_t)e * NR + r) * rq + 16 * g;
-  }
   const uint8_t* ssrc;
-  {
+  const int nch = (nk + 7) >> 3;
+  if constexpr (PK) {
+    // tile t's step ks is 1 KB at (t nk + ks) KB in lane order; its scale chunk c is 512 B at
+    // (t nch + c) 512 B, 8 bytes per lane
+    const size_t qb = (size_t)NR * rq, sbytes = (size_t)(NR / 16) * nch * 512;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const size_t t = (size_t)min(nb * 32 + wave * 4 + nt, NR / 16 - 1);
+      bsrc[nt] = a.q0 + (size_t)e * qb + (t * nk * 64 + lane) * 16;
+    }
+    // scale DMA lane l of copy q: tile 2 q + (l >> 5), lanes 2 (l & 31) and 2 (l & 31) + 1
+    const size_t t0 = (size_t)min(nb * 32 + wave * 4 + (lane >> 5), NR / 16 - 1);
+    ssrc = a.s0 + (size_t)e * sbytes + (t0 * nch * 64 + 2 * (lane & 31)) * 8;
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int r = min(nb * 512 + wave * 64 + nt * 16 + ln, NR - 1);
+      bsrc[nt] = a.q0 + ((size_t)e * NR + r) * rq + 16 * g;
+    }
     const int r = min(nb * 512 + wave * 64 + (lane >> 4) * 16 + (lane & 15), NR - 1);
     ssrc = a.s0 + ((size_t)e * NR + r) * KB;
   }
+  // the scale DMA of copy 1 (tiles 2, 3) of the packed layout: tile t0 + 2
+  const size_t s_pk_next =
+      PK ? ((size_t)min(nb * 32 + wave * 4 + 2 + (lane >> 5), NR / 16 - 1) -
+            (size_t)min(nb * 32 + wave * 4 + (lane >> 5), NR / 16 - 1)) * nch * 512
+         : 0;
   auto issue = [&](int ks, int slotno) {
     uint8_t* st = lds + slotno * SB;
 #pragma unroll
@@ -852,8 +897,14 @@ __device__ __forceinline__ void mx_down_tile(const MfmaArgs& a, uint8_t* lds, in
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-      dma16(bsrc[nt] + (size_t)ks * 64, st + AB + (wave * NT + nt) * 1024);
-    if (SG4) {
+      dma16(bsrc[nt] + (size_t)ks * (PK ? 1024 : 64), st + AB + (wave * NT + nt) * 1024);
+    if (PK) {
+      if ((ks & 7) == 0) {
+        uint8_t* slot = sring + ((ks >> 3) & 1) * kPkSGroup + wave * 2048;
+        dma16(ssrc + (size_t)(ks >> 3) * 512, slot);
+        dma16(ssrc + s_pk_next + (size_t)(ks >> 3) * 512, slot + 1024);
+      }
+    } else if (SG4) {
       if ((ks & 3) == 0) dma16(ssrc + ks * 4, sring + ((ks >> 2) & 1) * kSGroup + wave * 1024);
     } else {
       dma4(ssrc + ks * 4, st + AB + kBStage + wave * 256);
@@ -869,7 +920,8 @@ __device__ __forceinline__ void mx_down_tile(const MfmaArgs& a, uint8_t* lds, in
       wait_vm<0>();
       return;
     }
-    const int extra = SG4 ? ((ks + S - 2) >> 2) - (ks >> 2) : 0;
+    const int extra = PK ? 2 * (((ks + S - 2) >> 3) - (ks >> 3))
+                         : (SG4 ? ((ks + S - 2) >> 2) - (ks >> 2) : 0);
     wait_vm_n((S - 2) * ops + extra);
   };
 
@@ -895,8 +947,11 @@ __device__ __forceinline__ void mx_down_tile(const MfmaArgs& a, uint8_t* lds, in
     for (int nt = 0; nt < NT; ++nt) {
       const u32x4 q = *reinterpret_cast<const u32x4*>(st + AB + (wave * NT + nt) * 1024 + lane * 16);
       wop[nt] = i32x8{(int)q[0], (int)q[1], (int)q[2], (int)q[3], 0, 0, 0, 0};
-      wsc[nt] = SG4 ? sring[((ks >> 2) & 1) * kSGroup + wave * 1024 + 16 * (nt * 16 + ln) + 4 * (ks & 3) + g]
-                    : st[AB + kBStage + wave * 256 + 4 * (nt * 16 + ln) + g];
+      if (PK)  // this lane's byte of step ks in tile nt's 8-byte entry
+        wsc[nt] = sring[((ks >> 3) & 1) * kPkSGroup + wave * 2048 + nt * 512 + lane * 8 + (ks & 7)];
+      else
+        wsc[nt] = SG4 ? sring[((ks >> 2) & 1) * kSGroup + wave * 1024 + 16 * (nt * 16 + ln) + 4 * (ks & 3) + g]
+                      : st[AB + kBStage + wave * 256 + 4 * (nt * 16 + ln) + g];
     }
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -1247,13 +1302,14 @@ hipError_t launch_gateup_mfma(int T, int d, int f, int E, int k, const uint16_t*
                               const MxPtrs& w, const int32_t* offsets, const int32_t* rows,
                               const int32_t* act, const int32_t* n_act,
                               const int32_t* mtile_off, uint8_t* h8, uint8_t* hs8, uint8_t* x8,
-                              uint8_t* xs8, hipStream_t s) {
+                              uint8_t* xs8, hipStream_t s, bool packed) {
   x8_prep_kernel<<<T, 256, 0, s>>>(d, x, x8, xs8);
   MfmaArgs a{};
   a.T = T; a.d = d; a.f = f; a.k = k; a.x8 = x8; a.xs8 = xs8;
   a.q0 = w.gate_q; a.s0 = w.gate_s; a.q1 = w.up_q; a.s1 = w.up_s;
   a.offsets = offsets; a.rows = rows; a.act = act; a.n_act = n_act; a.mtile_off = mtile_off;
   a.nblk_n = (f + 255) / 256;
+  a.packed = packed ? 1 : 0;
   a.h8 = h8;
   a.hs8 = hs8;
   dim3 grid((unsigned)(mfma_mtiles_bound(T, E, k) * a.nblk_n));
@@ -1261,11 +1317,14 @@ hipError_t launch_gateup_mfma(int T, int d, int f, int E, int k, const uint16_t*
   return hipGetLastError();
 }
 
+bool packed_shape_supported(int d, int f) { return d % 1024 == 0 && f % 512 == 0; }
+
 hipError_t launch_down_mfma(int T, int d, int f, int E, int k, const MxPtrs& w,
                             const uint8_t* h8, const uint8_t* hs8, const int32_t* offsets,
                             const int32_t* rows, const int32_t* act, const int32_t* n_act,
-                            const int32_t* mtile_off, float* z, hipStream_t s) {
+                            const int32_t* mtile_off, float* z, hipStream_t s, bool packed) {
   MfmaArgs a{};
+  a.packed = packed ? 1 : 0;
   a.T = T; a.d = d; a.f = f; a.k = k;
   a.h8 = const_cast<uint8_t*>(h8);
   a.hs8 = const_cast<uint8_t*>(hs8);

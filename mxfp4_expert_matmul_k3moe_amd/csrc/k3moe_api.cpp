@@ -319,7 +319,8 @@ int run_router(const k3moe_dims& dm, int32_t T, const void* x, int xf32, const u
 int run_ffn(const k3moe_dims& dm, int32_t T, const void* x, int xf32,
             const k3moe_mx_experts* ex, const int32_t* offsets, const int32_t* rows,
             const float* gates, const float* resid, const float* shared, float* y,
-            uint16_t* y_bf16, const Ws& ws, hipStream_t s, hipEvent_t shared_ready = nullptr) {
+            uint16_t* y_bf16, const Ws& ws, hipStream_t s, hipEvent_t shared_ready = nullptr,
+            bool packed = false) {
   auto join = [&]() -> int {
     return shared_ready ? hip_check(hipStreamWaitEvent(s, shared_ready, 0), "join shared expert")
                         : 0;
@@ -333,6 +334,34 @@ int run_ffn(const k3moe_dims& dm, int32_t T, const void* x, int xf32,
   const bool scales4 = ((reinterpret_cast<uintptr_t>(ex->gate_s) |
                          reinterpret_cast<uintptr_t>(ex->up_s) |
                          reinterpret_cast<uintptr_t>(ex->down_s)) & 3u) == 0;
+  if (packed) {
+    // packed tile layout: grouped GEMMs on the block-scaled MFMA for every token count (the
+    // shapes and the bf16 activations were checked by the entry point)
+    uint8_t* h8 = ws.at<uint8_t>(R_H);
+    uint8_t* hs8 = h8 + (size_t)P * 3 * f;
+    float* z = ws.at<float>(R_Z);
+    {
+      Probe probe(K3MOE_KERNEL_GATE_UP, s);
+      rc = hip_check(k3moe::launch_gateup_mfma(T, d, f, E, k, static_cast<const uint16_t*>(x), w,
+                                               offsets, rows, ws.at<int32_t>(R_ACT),
+                                               ws.at<int32_t>(R_NACT), ws.at<int32_t>(R_MTILE),
+                                               h8, hs8, ws.at<uint8_t>(R_X8),
+                                               ws.at<uint8_t>(R_XS), s, true),
+                     "gate/up (MFMA, packed)");
+    }
+    if (rc) return rc;
+    {
+      Probe probe(K3MOE_KERNEL_DOWN, s);
+      rc = hip_check(k3moe::launch_down_mfma(T, d, f, E, k, w, h8, hs8, offsets, rows,
+                                             ws.at<int32_t>(R_ACT), ws.at<int32_t>(R_NACT),
+                                             ws.at<int32_t>(R_MTILE), z, s, true),
+                     "down (MFMA, packed)");
+    }
+    if (rc || (rc = join())) return rc;
+    return hip_check(k3moe::launch_combine(T, d, k, z, gates, ws.at<int32_t>(R_PPOS), resid,
+                                           shared, y, y_bf16, s),
+                     "combine");
+  }
   if (T >= kMfmaMinTokens && !xf32 && scales4 && k3moe::mfma_shape_supported(d, f)) {
     // many tokens per expert: grouped GEMMs on the block-scaled FP4 x FP8 MFMA, h kept as
     // three E4M3 terms [P][3][f] with per-32-block scales [P][3][f/32] (in the h region)
@@ -701,7 +730,8 @@ int check_layer(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
 int run_layer(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
               const uint16_t* w_router, const float* logit_bias, const k3moe_mx_experts* experts,
               const k3moe_block* blk, float* y, uint16_t* y_bf16, int32_t* topk_ids,
-              float* topk_gates, const Ws& w, hipStream_t s, bool side_ok) {
+              float* topk_gates, const Ws& w, hipStream_t s, bool side_ok,
+              bool packed = false) {
   int rc;
   const int d = dims->d_model;
   int32_t* ids = topk_ids ? topk_ids : w.at<int32_t>(R_IDS);
@@ -757,7 +787,19 @@ int run_layer(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
     if (rc) return rc;
   }
   return run_ffn(*dims, T, xin, xf32, experts, offs, rows, gates, resid, shared, y, y_bf16, w, s,
-                 joined);
+                 joined, packed);
+}
+
+// Shapes and activations the packed-layout kernels take.
+int check_packed(const k3moe_dims& dm, int x_dtype) {
+  if (!k3moe::packed_shape_supported(dm.d_model, dm.d_ff))
+    return fail(K3MOE_EUNSUPPORTED,
+                "packed layout needs d_model %% 1024 == 0 and d_ff %% 512 == 0 (d_model=%d, "
+                "d_ff=%d)",
+                dm.d_model, dm.d_ff);
+  if (x_dtype != K3MOE_BF16)
+    return fail(K3MOE_EUNSUPPORTED, "the packed-layout kernels take bf16 activations");
+  return K3MOE_OK;
 }
 
 
@@ -809,6 +851,64 @@ int k3moe_layer_forward(const k3moe_dims* dims, int32_t T, const void* x, int x_
   if ((rc = get_ws(*dims, T, ws, ws_bytes, &w))) return rc;
   return run_layer(dims, T, x, x_dtype, w_router, logit_bias, experts, blk, y, y_bf16, topk_ids,
                    topk_gates, w, (hipStream_t)stream, true);
+}
+
+int k3moe_packed_expert_bytes(const k3moe_dims* dims, k3moe_packed_bytes* per_expert) {
+  int rc;
+  if ((rc = check_dims(dims))) return rc;
+  if (!per_expert) return fail(K3MOE_EINVAL, "per_expert is NULL");
+  if ((rc = check_packed(*dims, K3MOE_BF16))) return rc;
+  const size_t d = (size_t)dims->d_model, f = (size_t)dims->d_ff;
+  per_expert->gate_q = per_expert->up_q = f * d / 2;
+  per_expert->down_q = d * f / 2;
+  per_expert->gate_s = per_expert->up_s = k3moe::packed_scale_bytes((int)f, (int)d);
+  per_expert->down_s = k3moe::packed_scale_bytes((int)d, (int)f);
+  return K3MOE_OK;
+}
+
+int k3moe_pack_experts(const k3moe_dims* dims, const k3moe_mx_experts* src,
+                       const k3moe_mx_experts* dst, void* stream) {
+  int rc;
+  k3moe_packed_bytes pb;
+  if ((rc = k3moe_packed_expert_bytes(dims, &pb))) return rc;
+  if ((rc = check_experts(src)) || (rc = check_experts(dst))) return rc;
+  if ((reinterpret_cast<uintptr_t>(dst->gate_s) | reinterpret_cast<uintptr_t>(dst->up_s) |
+       reinterpret_cast<uintptr_t>(dst->down_s)) & 7u)
+    return fail(K3MOE_EINVAL, "packed scale arrays must be 8-byte aligned");
+  const int d = dims->d_model, f = dims->d_ff, E = dims->n_experts;
+  hipStream_t s = (hipStream_t)stream;
+  if ((rc = hip_check(k3moe::launch_pack_matrix(f, d, E, src->gate_q, src->gate_s,
+                                                const_cast<uint8_t*>(dst->gate_q),
+                                                const_cast<uint8_t*>(dst->gate_s), s),
+                      "pack gate")) ||
+      (rc = hip_check(k3moe::launch_pack_matrix(f, d, E, src->up_q, src->up_s,
+                                                const_cast<uint8_t*>(dst->up_q),
+                                                const_cast<uint8_t*>(dst->up_s), s),
+                      "pack up")))
+    return rc;
+  return hip_check(k3moe::launch_pack_matrix(d, f, E, src->down_q, src->down_s,
+                                             const_cast<uint8_t*>(dst->down_q),
+                                             const_cast<uint8_t*>(dst->down_s), s),
+                   "pack down");
+}
+
+int k3moe_layer_forward_packed(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
+                               const uint16_t* w_router, const float* logit_bias,
+                               const k3moe_mx_experts* experts, const k3moe_block* blk, float* y,
+                               uint16_t* y_bf16, int32_t* topk_ids, float* topk_gates, void* ws,
+                               size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_layer(dims, T, x, x_dtype, w_router, experts, blk, y))) return rc;
+  if (T == 0) return K3MOE_OK;
+  if ((rc = check_packed(*dims, blk ? K3MOE_BF16 : x_dtype))) return rc;
+  if (blk) return fail(K3MOE_EUNSUPPORTED, "block mode is not available on the packed layout");
+  if (((reinterpret_cast<uintptr_t>(experts->gate_s) | reinterpret_cast<uintptr_t>(experts->up_s) |
+        reinterpret_cast<uintptr_t>(experts->down_s)) & 7u))
+    return fail(K3MOE_EINVAL, "packed scale arrays must be 8-byte aligned");
+  Ws w;
+  if ((rc = get_ws(*dims, T, ws, ws_bytes, &w))) return rc;
+  return run_layer(dims, T, x, x_dtype, w_router, logit_bias, experts, blk, y, y_bf16, topk_ids,
+                   topk_gates, w, (hipStream_t)stream, true, true);
 }
 
 int k3moe_layer_forward_noalloc(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,

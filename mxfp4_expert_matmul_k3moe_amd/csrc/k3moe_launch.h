@@ -106,16 +106,29 @@ bool mfma_shape_supported(int d, int f);
 // h = silu(G x) * (U x) for every (expert, token) pair, bucket order, as three E4M3 terms
 // h8 [P][3][f] with their E8M0 scales hs8 [P][3][f/32] (one per term and 32-block); x8
 // [T][2][d] and xs8 [T][2] receive the tokens' own FP8 terms on the way.
+// packed: G and U in the packed tile layout (pack.hip; needs d % 1024 == 0, f % 16 == 0).
 hipError_t launch_gateup_mfma(int T, int d, int f, int E, int k, const uint16_t* x,
                               const MxPtrs& w, const int32_t* offsets, const int32_t* rows,
                               const int32_t* act, const int32_t* n_act,
                               const int32_t* mtile_off, uint8_t* h8, uint8_t* hs8, uint8_t* x8,
-                              uint8_t* xs8, hipStream_t s);
-// z (fp32 [P][d], pair-indexed) = D h from the three terms of h.
+                              uint8_t* xs8, hipStream_t s, bool packed = false);
+// Shapes the packed-layout grouped GEMMs take (d: whole 8-step scale chunks; f: the down
+// kernel's scale groups).
+bool packed_shape_supported(int d, int f);
+// z (fp32 [P][d], pair-indexed) = D h from the three terms of h; packed: D in the packed tile
+// layout (weights streamed per M tile, each tile step one 1-KB DMA).
 hipError_t launch_down_mfma(int T, int d, int f, int E, int k, const MxPtrs& w,
                             const uint8_t* h8, const uint8_t* hs8, const int32_t* offsets,
                             const int32_t* rows, const int32_t* act, const int32_t* n_act,
-                            const int32_t* mtile_off, float* z, hipStream_t s);
+                            const int32_t* mtile_off, float* z, hipStream_t s,
+                            bool packed = false);
+
+// ---- packed tile layout (pack.hip) ----------------------------------------------------
+// Bytes of the packed scales of one [R][K] matrix (the packed codes take R K / 2, as before).
+size_t packed_scale_bytes(int R, int K);
+// n_mat stacked [R][K] matrices (codes q, scales s) -> packed codes pq and scales ps.
+hipError_t launch_pack_matrix(int R, int K, int n_mat, const uint8_t* q, const uint8_t* s,
+                              uint8_t* pq, uint8_t* ps, hipStream_t st);
 
 // ---- block extras (block.hip) ---------------------------------------------------------
 hipError_t launch_rmsnorm(int T, int d, const float* h, const uint16_t* gamma, float eps,

@@ -31,7 +31,9 @@ def test_exports_every_declared_symbol():
                           "k3moe_last_error", "k3moe_time_next_kernel",
                           "k3moe_cache_state_bytes", "k3moe_cache_init", "k3moe_cache_plan",
                           "k3moe_cache_stats_get", "k3moe_layer_forward_cached",
-                          "k3moe_release", "k3moe_layer_forward_noalloc"}
+                          "k3moe_release", "k3moe_layer_forward_noalloc",
+                          "k3moe_packed_expert_bytes", "k3moe_pack_experts",
+                          "k3moe_layer_forward_packed"}
     L = k3.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -178,3 +180,16 @@ def test_noalloc_rejects_beyond_its_scratch():
                                          None) == k3.EINVAL
     assert L.k3moe_layer_forward_noalloc(ctypes.byref(K3), 0, None, 0, None, None, None, None,
                                          None, None, None, None, None) == k3.OK
+
+
+def test_packed_sizes_and_shape_checks():
+    """Packed sizes are host arithmetic: codes keep R K / 2 bytes, scales are padded to whole
+    chunks of 8 K steps (16 rows x 64 lanes x 8 bytes per chunk and tile)."""
+    pb = k3.packed_expert_bytes(K3)
+    assert pb["gate_q"] == pb["up_q"] == 1536 * 7168 // 2
+    assert pb["down_q"] == 7168 * 1536 // 2
+    assert pb["gate_s"] == pb["up_s"] == (1536 // 16) * 7 * 512 == 1536 * 7168 // 32
+    assert pb["down_s"] == (7168 // 16) * 2 * 512  # 12 steps -> 2 chunks (4 steps of padding)
+    with pytest.raises(k3.K3MoEError) as ei:
+        k3.packed_expert_bytes(k3.make_dims(512, 256, 32, 4))  # d_model not a multiple of 1024
+    assert ei.value.code == k3.EUNSUPPORTED

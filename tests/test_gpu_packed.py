@@ -1,0 +1,154 @@
+"""The packed tile layout of the expert weights (k3moe_pack_experts) and the layer on it
+(k3moe_layer_forward_packed), through the C ABI.
+
+- The pack call is checked byte for byte against the layout as include/k3moe.h states it,
+  built here with numpy index arithmetic (a permutation: no arithmetic of the method).
+- The layer on packed experts is checked against the fp64 oracle with the bars of
+  test_gpu_parity.py (routing bit-exact, per-token relative L2 and element bounds), on small
+  ragged shapes (16-, 32- and 64-row tiles, partial row slices, experts with one to many
+  subtiles) and on the K3 layer: every token of the 32-token batch, and routing-chosen tile
+  edges of the 2048-token prefill chunk.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_expert_matmul_k3moe_amd as k3
+import oracle
+from k3gen import device as gdev
+from k3gen.workloads import BATCHED, PREFILL, Workload
+from oracle import harness
+
+from test_gpu_parity import ELEM_FACTOR, K3_TOL, TOL, check_routing, rel_elem, rel_l2, \
+    tile_probe_tokens
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def pack_reference(q: np.ndarray, s: np.ndarray, R: int, K: int):
+    """The packed layout of one [R][K] matrix, from the row-major codes q [R][K/2] and
+    scales s [R][K/32], by index arithmetic."""
+    nk, nch = K // 128, (K // 128 + 7) // 8
+    # codes: (t, step, lane = i + 16 g) -> 16 bytes of row 16 t + i at 64 step + 16 g
+    qr = q.reshape(R // 16, 16, nk, 4, 16)               # [t][i][step][g][16 B]
+    pq = qr.transpose(0, 2, 3, 1, 4).reshape(-1)         # [t][step][g][i][16 B]
+    # scales: (t, c, lane) byte j -> block 4 (8 c + j) + g of row 16 t + i, 0 past nk
+    sp = np.zeros((R // 16, 16, nch * 8, 4), dtype=np.uint8)  # [t][i][step][g]
+    sp[:, :, :nk, :] = s.reshape(R // 16, 16, nk, 4)
+    ps = sp.reshape(R // 16, 16, nch, 8, 4).transpose(0, 2, 4, 1, 3).reshape(-1)
+    return pq, ps
+
+
+SMALL = [
+    # one 8-step chunk of d, f = 512 (4 down steps), mixed 16/32/64-row tiles
+    Workload("pk_d1024", 61, d=1024, f=512, E=12, k=3, T=40, zipf_alpha=0.6),
+    # three chunks of d, down with 12 steps (f = 1536), hot experts over several M tiles
+    Workload("pk_mixed", 62, d=3072, f=1536, E=24, k=4, T=150, zipf_alpha=0.9),
+    # f = 1024 (8 down steps), one token (every expert one tile), two tokens
+    Workload("pk_t1", 63, d=2048, f=1024, E=16, k=4, T=1),
+    Workload("pk_t2", 64, d=2048, f=1024, E=16, k=4, T=2),
+]
+
+
+def test_pack_matches_layout(dev):
+    for w in SMALL[:2]:
+        say(f"pack {w.name} d={w.d} f={w.f} E={w.E}")
+        dims = k3.make_dims(w.d, w.f, w.E, w.k)
+        ex = gdev.experts(w, 0, dev)
+        pk = k3.pack_experts(dims, k3.MxExperts(**ex))
+        torch.cuda.synchronize()
+        for e in (0, w.E - 1):
+            h = w.expert_host(0, e)
+            for name, R, K in (("gate", w.f, w.d), ("up", w.f, w.d), ("down", w.d, w.f)):
+                pq, ps = pack_reference(h[name + "_q"], h[name + "_s"], R, K)
+                assert np.array_equal(getattr(pk, name + "_q")[e].cpu().numpy(), pq), (name, e)
+                assert np.array_equal(getattr(pk, name + "_s")[e].cpu().numpy(), ps), (name, e)
+
+
+def run_packed(w: Workload, x_np, dev, packed):
+    dims = k3.make_dims(w.d, w.f, w.E, w.k)
+    x = gdev.bf16_tensor(x_np, dev)
+    T = x.shape[0]
+    ids = torch.empty((T, w.k), dtype=torch.int32, device=dev)
+    gates = torch.empty((T, w.k), dtype=torch.float32, device=dev)
+    ybf = torch.empty((T, w.d), dtype=torch.bfloat16, device=dev)
+    y = k3.layer_forward_packed(dims, x, gdev.router_w(w, 0, dev), gdev.bias(w, 0, dev), packed,
+                                y_bf16=ybf, ids=ids, gates=gates)
+    torch.cuda.synchronize()
+    return {"y": y, "ybf": ybf, "ids": ids.cpu().numpy(), "gates": gates.cpu().numpy()}
+
+
+def check(g, ref, rows=None, tol=TOL):
+    ids_g, gates_g = g["ids"], g["gates"]
+    yg = g["y"].cpu().double().numpy()
+    if rows is not None:
+        ids_g, gates_g, yg = ids_g[rows], gates_g[rows], yg[rows]
+    check_routing(ids_g, gates_g, ref["ids"], ref["gates"])
+    assert np.isfinite(yg).all()
+    err, el = rel_l2(yg, ref["y"]), rel_elem(yg, ref["y"])
+    print(f"    max rel L2 err {err.max():.3e}, max elem err / row rms {el.max():.3e}  "
+          f"(tokens {len(err)})", flush=True)
+    assert err.max() <= tol and el.max() <= ELEM_FACTOR * tol
+    assert torch.equal(g["ybf"], g["y"].to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[s.name for s in SMALL])
+def test_packed_layer_matches_oracle(dev, w):
+    say(f"packed layer {w.name} d={w.d} f={w.f} E={w.E} k={w.k} T={w.T}")
+    dims = k3.make_dims(w.d, w.f, w.E, w.k)
+    packed = k3.pack_experts(dims, k3.MxExperts(**gdev.experts(w, 0, dev)))
+    x = w.x_bf16()
+    g = run_packed(w, x, dev, packed)
+    check(g, harness.run_layer(w, x), tol=1e-4)
+
+
+def test_packed_repeat_runs_bit_identical(dev):
+    w = SMALL[1]
+    say(f"packed determinism {w.name}")
+    dims = k3.make_dims(w.d, w.f, w.E, w.k)
+    packed = k3.pack_experts(dims, k3.MxExperts(**gdev.experts(w, 0, dev)))
+    x = w.x_bf16()
+    a = run_packed(w, x, dev, packed)
+    b = run_packed(w, x, dev, packed)
+    assert torch.equal(a["y"], b["y"]) and np.array_equal(a["ids"], b["ids"])
+
+
+def test_packed_batched_k3(dev):
+    w = BATCHED
+    say("packed batched decode: T=32, every token")
+    dims = k3.make_dims(w.d, w.f, w.E, w.k)
+    ex = gdev.experts(w, 0, dev)
+    packed = k3.pack_experts(dims, k3.MxExperts(**ex))
+    del ex
+    x = w.x_bf16()
+    g = run_packed(w, x, dev, packed)
+    check(g, harness.run_layer(w, x), tol=K3_TOL)
+    del packed
+    torch.cuda.empty_cache()
+
+
+def test_packed_prefill_k3(dev):
+    w = PREFILL
+    say("packed prefill: T=2048 with Zipf(1.1) logit bias")
+    dims = k3.make_dims(w.d, w.f, w.E, w.k)
+    ex = gdev.experts(w, 0, dev)
+    packed = k3.pack_experts(dims, k3.MxExperts(**ex))
+    del ex
+    x = w.x_bf16()
+    g = run_packed(w, x, dev, packed)
+    ids_all, gates_all, _, _ = oracle.layer_route(x, w.router_w(0), w.bias(0), w.k)
+    check_routing(g["ids"], g["gates"], ids_all, gates_all)
+    rows = tile_probe_tokens(ids_all, w.E, seed=2)
+    check(g, harness.run_layer(w, x, tokens=rows), rows=rows, tol=K3_TOL)
+    del packed
+    torch.cuda.empty_cache()
