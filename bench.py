@@ -356,7 +356,8 @@ def decode_like_fields(w, m, traffic, packed=False):
     dn_bytes = m["sel"] * w.d * (w.f // 2 + w.f // 32)
     ach = gu_bytes / (m["gate_up_ms"] * 1e-3) / 1e9
     if w.T == 1:
-        kname = "gateup_decode_kernel (MXFP4 gate/up GEMV + SwiGLU)"
+        kname = ("gateup_decode_packed_kernel (MXFP4 gate/up GEMV + SwiGLU, packed tile layout)"
+                 if packed else "gateup_decode_kernel (MXFP4 gate/up GEMV + SwiGLU)")
     elif w.T >= MFMA_MIN_TOKENS or packed:
         kname = grouped_label(packed)
     else:
@@ -501,7 +502,8 @@ def main() -> int:
     leg = LayerLeg(args, w, dev, packed=use_packed(args, w))
     m = leg.measure(args.repeats)
     if w.T <= 64:
-        traffic = decode_traffic() if args.workload == "decode" and not args.tokens else None
+        traffic = (decode_traffic(leg.packed) if args.workload == "decode" and not args.tokens
+                   else None)
         value, unit, roof, extra = decode_like_fields(w, m, traffic, leg.packed)
     else:
         value, unit, roof, extra = prefill_fields(w, m, grouped_traffic(w, leg.packed),
@@ -552,11 +554,13 @@ def _read_record(name: str) -> dict:
     return tr
 
 
-def decode_traffic():
-    """HBM bytes per launch of the T=1 gate/up kernel from the committed FETCH_SIZE /
-    WRITE_SIZE record, used only while the kernel source it was measured on is unchanged."""
-    tr = _read_record("gateup_decode_traffic.txt")
-    if not tr or tr.get("kernel_source_hash") != _kernel_hash():
+def decode_traffic(packed=False):
+    """HBM bytes per launch of the T=1 gate/up kernel of that layout from the committed
+    FETCH_SIZE / WRITE_SIZE record, used only while the kernel source it was measured on is
+    unchanged."""
+    tr = _read_record("gateup_decode_packed_traffic.txt" if packed
+                      else "gateup_decode_traffic.txt")
+    if not tr or tr.get("kernel_source_hash") != _kernel_hash(packed):
         return None
     return int(tr["bytes_per_launch"])
 
@@ -802,16 +806,21 @@ def _function_text(src: str, marker: str) -> str:
     return src[start:end]
 
 
-def _kernel_hash() -> str:
-    """Hash of the T=1 gate/up kernel's own source: its template, its launcher and the
-    device helpers it uses (the traffic record holds while these are unchanged)."""
+def _kernel_hash(packed=False) -> str:
+    """Hash of the T=1 gate/up kernel's own source (row-major or packed layout): its template,
+    its launcher and the device helpers it uses (the traffic record holds while these are
+    unchanged)."""
     import hashlib
     csrc = os.path.join(ROOT, "mxfp4_expert_matmul_k3moe_amd", "csrc")
     with open(os.path.join(csrc, "ffn_gemv.hip")) as fh:
         src = fh.read()
     h = hashlib.sha256()
-    h.update(_function_text(src, "void gateup_decode_kernel(").encode())
-    h.update(_function_text(src, "hipError_t launch_gateup_decode(").encode())
+    if packed:
+        h.update(_function_text(src, "void gateup_decode_packed_kernel(").encode())
+        h.update(_function_text(src, "hipError_t launch_gateup_decode_packed(").encode())
+    else:
+        h.update(_function_text(src, "void gateup_decode_kernel(").encode())
+        h.update(_function_text(src, "hipError_t launch_gateup_decode(").encode())
     with open(os.path.join(csrc, "k3moe_device.h"), "rb") as fh:
         h.update(fh.read())
     return h.hexdigest()[:16]

@@ -459,6 +459,129 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int d, int k, const
   }
 }
 
+// ---- gate/up, T == 1, packed tile layout ---------------------------------------------------
+// One wave per (slot, 16-row tile): k * f/16 work items, two waves per block (768 blocks on the
+// K3 layer, three per CU). Lane (i, g) owns row i of the tile and K block 4 s + g of step s:
+// each step is one contiguous 1-KB load of G and one of U per wave, whose 32 codes each are
+// converted in registers and dotted with the token's block (read once from LDS, the same 64
+// bytes for the 16 lanes of a group), each scaled once by its block's E8M0 byte. After the
+// last step the four lanes of a row add their sums (fixed tree) and the row's
+// h = silu(gate) * up goes to h[pos][f], pos the slot's bucket position. The weights are never
+// written anywhere decoded.
+constexpr int kPkAhead = 8;  // steps of loads in flight per wave and matrix
+
+struct GateUpPackedArgs {
+  int d, f, k;
+  const void* x;
+  const uint8_t *gq, *gs, *uq, *us;  // packed G and U
+  const int32_t *pair_pos, *pair_exp;
+  float* h;  // [k][f] by bucket position
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <bool XF32>
+__global__ __launch_bounds__(128) void gateup_decode_packed_kernel(GateUpPackedArgs a) {
+  extern __shared__ __attribute__((aligned(16))) u32x4 xs[];
+  constexpr int Q = XF32 ? 8 : 4;  // 16-byte pieces per 32-element block
+  const int d = a.d, f = a.f, NB = d >> 5;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, i = lane & 15;
+  // 1. the token into LDS by asynchronous copies (1 KB per wave copy, natural order)
+  const int nchunk = (NB * Q * 16) >> 10;  // d % 1024 == 0: whole kilobytes
+  for (int c = wave; c < nchunk; c += 2)
+    __builtin_amdgcn_global_load_lds(static_cast<const uint8_t*>(a.x) + (size_t)c * 1024 + lane * 16,
+                                     (lds_void_t*)(reinterpret_cast<uint8_t*>(xs) + c * 1024), 16, 0,
+                                     0);
+  // 2. the wave's work item (slot, tile); its slot read with scalar loads
+  const int ntile = f >> 4, nk = d / 128, nch = nk >> 3;
+  const int item = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 2 + wave);
+  bool work = item < a.k * ntile;
+  int q = 0, t = 0, pos = -1, e = -1;
+  if (work) {
+    q = item / ntile;
+    t = item - q * ntile;
+    pos = __builtin_amdgcn_readfirstlane(a.pair_pos[q]);
+    e = __builtin_amdgcn_readfirstlane(a.pair_exp[q]);
+    work = pos >= 0 && e >= 0;
+  }
+  // 3. the first chunk of the tile in G and U (ring slot j holds step 8 c + j) and its scale
+  //    entries; then the barrier (its wait covers these loads too)
+  const size_t qb = (size_t)f * (d >> 1), sb = (size_t)(f >> 4) * nch * 512;
+  const size_t qo = (size_t)(work ? e : 0) * qb + ((size_t)t * nk * 64 + lane) * 16;
+  const size_t so = (size_t)(work ? e : 0) * sb + ((size_t)t * nch * 64 + lane) * 8;
+  const uint8_t *gq = a.gq + qo, *uq = a.uq + qo, *gsc = a.gs + so, *usc = a.us + so;
+  u32x4 wg[kPkAhead], wu[kPkAhead];
+  uint64_t sg_next = 0, su_next = 0;
+  if (work) {
+#pragma unroll
+    for (int j = 0; j < kPkAhead; ++j) {  // nk >= 8
+      wg[j] = load_u32x4_nt(gq + (size_t)j * 1024);
+      wu[j] = load_u32x4_nt(uq + (size_t)j * 1024);
+    }
+    sg_next = *reinterpret_cast<const uint64_t*>(gsc);
+    su_next = *reinterpret_cast<const uint64_t*>(usc);
+  }
+  __syncthreads();
+  if (!work) return;
+
+  // 4. the K loop: slot j, after its step of chunk c, is refilled with the same step of chunk
+  //    c + 1 (the last chunk again at the end: cache hits, and no conditional load for the
+  //    compiler to wait on); scale entry c + 1 arrives during chunk c
+  float ga = 0.0f, ua = 0.0f;
+  for (int c = 0; c < nch; ++c) {
+    const uint64_t sg = sg_next, su = su_next;
+    const int cn = min(c + 1, nch - 1);
+    sg_next = *reinterpret_cast<const uint64_t*>(gsc + (size_t)cn * 512);
+    su_next = *reinterpret_cast<const uint64_t*>(usc + (size_t)cn * 512);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kPkAhead; ++j) {
+      const uint32_t gb = (uint32_t)(sg >> (8 * j)) & 0xFFu;
+      const uint32_t ub = (uint32_t)(su >> (8 * j)) & 0xFFu;
+      const u32x4* xb = xs + (size_t)(4 * (8 * c + j) + g) * Q;  // block 4 s + g of the token
+      float gd, ud;
+      if constexpr (XF32) {
+        float xv[32];
+#pragma unroll
+        for (int qq = 0; qq < 8; ++qq) {
+          const u32x4 v = xb[qq];
+          xv[4 * qq + 0] = __uint_as_float(v[0]);
+          xv[4 * qq + 1] = __uint_as_float(v[1]);
+          xv[4 * qq + 2] = __uint_as_float(v[2]);
+          xv[4 * qq + 3] = __uint_as_float(v[3]);
+        }
+        gd = block_dot_f32(wg[j], xv);
+        ud = block_dot_f32(wu[j], xv);
+      } else {
+        uint32_t xp[16];
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const u32x4 v = xb[qq];
+          xp[4 * qq + 0] = v[0];
+          xp[4 * qq + 1] = v[1];
+          xp[4 * qq + 2] = v[2];
+          xp[4 * qq + 3] = v[3];
+        }
+        gd = block_dot_bf16(wg[j], xp);
+        ud = block_dot_bf16(wu[j], xp);
+      }
+      ga = fmaf(e8m0_to_f32(gb), gd, ga);
+      ua = fmaf(e8m0_to_f32(ub), ud, ua);
+      const size_t nx = (size_t)(8 * cn + j) * 1024;
+      wg[j] = load_u32x4_nt(gq + nx);
+      wu[j] = load_u32x4_nt(uq + nx);
+      __builtin_amdgcn_sched_barrier(0);  // each refill stays behind its own step
+    }
+  }
+  ga += __shfl_xor(ga, 16, 64);
+  ua += __shfl_xor(ua, 16, 64);
+  ga += __shfl_xor(ga, 32, 64);
+  ua += __shfl_xor(ua, 32, 64);
+  if (g == 0) a.h[(size_t)pos * f + 16 * t + i] = silu_f32(ga) * ua;
+}
+
 int bpl_of(int nb) { return nb / lanes_per_row(nb); }
 
 constexpr int kMaxDecodeBpl = 8;
@@ -519,6 +642,21 @@ hipError_t launch_gateup_gemv(int T, int d, int f, int E, int k, const void* x, 
   }
 #undef K3_GU_B
 #undef K3_GU
+  return hipGetLastError();
+}
+
+hipError_t launch_gateup_decode_packed(int d, int f, int k, const void* x, int xf32,
+                                       const MxPtrs& w, const int32_t* pair_pos,
+                                       const int32_t* pair_exp, float* h, hipStream_t s) {
+  GateUpPackedArgs a;
+  a.d = d; a.f = f; a.k = k; a.x = x;
+  a.gq = w.gate_q; a.gs = w.gate_s; a.uq = w.up_q; a.us = w.up_s;
+  a.pair_pos = pair_pos; a.pair_exp = pair_exp; a.h = h;
+  const int items = k * (f / 16);
+  const dim3 grid((unsigned)((items + 1) / 2));
+  const size_t lds = (size_t)d * (xf32 ? 4 : 2);
+  if (xf32) gateup_decode_packed_kernel<true><<<grid, 128, lds, s>>>(a);
+  else gateup_decode_packed_kernel<false><<<grid, 128, lds, s>>>(a);
   return hipGetLastError();
 }
 

@@ -1127,7 +1127,7 @@ struct DownDecMArgs {
   int rpb;  // output rows per block
 };
 
-template <int NK>
+template <int NK, bool PK>
 __global__ __launch_bounds__(1024) void down_decode_mfma_kernel(DownDecMArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t tb[kDecMfmaSlots][kDecTermBytes];
   __shared__ float zs[2][kDecMfmaSlots][16];
@@ -1146,8 +1146,8 @@ __global__ __launch_bounds__(1024) void down_decode_mfma_kernel(DownDecMArgs a) 
   // h of the slot first (four values per lane and round), so that waiting for it later
   // leaves the weight loads behind it in flight
   constexpr int NR = (NK * BK / 4 + 63) / 64;
-  const float* hr = a.h + (size_t)(sv ? pos : 0) * F;
   f32x4 hv[NR];
+  const float* hr = a.h + (size_t)(sv ? pos : 0) * F;
 #pragma unroll
   for (int v0 = 0; v0 < NR; ++v0) {
     const int c = v0 * 64 + lane;
@@ -1157,18 +1157,38 @@ __global__ __launch_bounds__(1024) void down_decode_mfma_kernel(DownDecMArgs a) 
   // 1. weights of one tile's 16 rows; lanes of rows past the block's range read the last row
   //    of the range again (same addresses as a lane in the same load, so no extra traffic;
   //    their results are never combined). Unconditional loads keep the wait counts exact.
-  const uint8_t* wq0 = a.dq + (size_t)(sv ? e : 0) * a.d * (size_t)(F >> 1) + 16 * g;
-  const uint8_t* ws0 = a.ds + (size_t)(sv ? e : 0) * a.d * (size_t)FB;
+  //    Packed layout: the block's rows are whole 16-row tiles, a tile step is one 1-KB piece
+  //    in lane order and a lane's scale bytes of 8 steps are one 8-byte entry.
+  constexpr int NCH = (NK + 7) / 8;
+  constexpr int NSW = PK ? 2 * NCH : NK;
+  const uint8_t* wq0 = PK ? a.dq + (size_t)(sv ? e : 0) * a.d * (size_t)(F >> 1) + 16 * lane
+                          : a.dq + (size_t)(sv ? e : 0) * a.d * (size_t)(F >> 1) + 16 * g;
+  const uint8_t* ws0 = PK ? a.ds + (size_t)(sv ? e : 0) * (a.d >> 4) * (size_t)(NCH * 512) + 8 * lane
+                          : a.ds + (size_t)(sv ? e : 0) * a.d * (size_t)FB;
   u32x4 w[NK];
-  uint32_t sw[NK];
+  uint32_t sw[NSW];
   auto load_tile = [&](int rt) {
-    const int row = min(rt + ln, rb1 - 1);
-    const uint8_t* wq = wq0 + (size_t)row * (size_t)(F >> 1);
-    const uint32_t* wsc = reinterpret_cast<const uint32_t*>(ws0 + (size_t)row * (size_t)FB);
+    if constexpr (PK) {
+      const int tt = rt >> 4;
+      const uint2* wsc = reinterpret_cast<const uint2*>(ws0 + (size_t)tt * (NCH * 512));
 #pragma unroll
-    for (int s = 0; s < NK; ++s) sw[s] = wsc[s];  // scales first: step s waits for block s only
+      for (int c = 0; c < NCH; ++c) {
+        const uint2 v = wsc[c * 64];
+        sw[2 * c] = v.x;
+        sw[2 * c + 1] = v.y;
+      }
+      const uint8_t* wq = wq0 + (size_t)tt * NK * 1024;
 #pragma unroll
-    for (int s = 0; s < NK; ++s) w[s] = load_u32x4_nt(wq + 64 * s);
+      for (int s = 0; s < NK; ++s) w[s] = load_u32x4_nt(wq + 1024 * s);
+    } else {
+      const int row = min(rt + ln, rb1 - 1);
+      const uint8_t* wq = wq0 + (size_t)row * (size_t)(F >> 1);
+      const uint32_t* wsc = reinterpret_cast<const uint32_t*>(ws0 + (size_t)row * (size_t)FB);
+#pragma unroll
+      for (int s = 0; s < NK; ++s) sw[s] = wsc[s];  // scales first: step s waits for block s only
+#pragma unroll
+      for (int s = 0; s < NK; ++s) w[s] = load_u32x4_nt(wq + 64 * s);
+    }
   };
   load_tile(r0);  // every block has at least one row
 
@@ -1251,7 +1271,8 @@ __global__ __launch_bounds__(1024) void down_decode_mfma_kernel(DownDecMArgs a) 
       const i32x8 aop = __builtin_shufflevector(wi, wi, 0, 1, 2, 3, -1, -1, -1, -1);
       const i32x8 bop = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
                          (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
-      const int asc = (int)((sw[s] >> (8 * g)) & 0xFFu);
+      const int asc = PK ? (int)((sw[2 * (s >> 3) + ((s & 7) >> 2)] >> (8 * (s & 3))) & 0xFFu)
+                         : (int)((sw[s] >> (8 * g)) & 0xFFu);
       acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop, acc, 4, 0, 0, asc, 0, bsc);
       b0 = n0;
       b1 = n1;
@@ -1345,20 +1366,27 @@ bool down_decode_mfma_supported(int d, int f, int k) {
 hipError_t launch_down_decode_mfma(int d, int f, int k, const MxPtrs& w, const float* h,
                                    const int32_t* pair_pos, const int32_t* pair_exp,
                                    const float* gates, const float* resid, const float* shared,
-                                   float* y, uint16_t* y_bf16, int n_cu, hipStream_t s) {
+                                   float* y, uint16_t* y_bf16, int n_cu, hipStream_t s,
+                                   bool packed) {
   DownDecMArgs a;
   a.d = d; a.f = f; a.k = k; a.dq = w.down_q; a.ds = w.down_s; a.h = h;
   a.pair_pos = pair_pos; a.pair_exp = pair_exp; a.gates = gates;
   a.resid = resid; a.shared = shared; a.y = y; a.y_bf16 = y_bf16;
-  // equal row ranges for one block per CU (16 rows at least)
+  // equal row ranges for one block per CU (16 rows at least; whole tiles when packed)
   const int nb = n_cu > 0 ? n_cu : 1;
-  a.rpb = (d + nb - 1) / nb;
+  if (packed)
+    a.rpb = 16 * ((d / 16 + nb - 1) / nb);
+  else
+    a.rpb = (d + nb - 1) / nb;
   if (a.rpb < 16) a.rpb = 16;
   const dim3 grid((unsigned)((d + a.rpb - 1) / a.rpb)), block((unsigned)(64 * k));
   switch (f / BK) {
-#define K3_DM(N)                                               \
-  case N:                                                      \
-    down_decode_mfma_kernel<N><<<grid, block, 0, s>>>(a);      \
+#define K3_DM(N)                                                   \
+  case N:                                                          \
+    if (packed)                                                    \
+      down_decode_mfma_kernel<N, true><<<grid, block, 0, s>>>(a);  \
+    else                                                           \
+      down_decode_mfma_kernel<N, false><<<grid, block, 0, s>>>(a); \
     break;
     K3_DM(1) K3_DM(2) K3_DM(3) K3_DM(4) K3_DM(5) K3_DM(6)
     K3_DM(7) K3_DM(8) K3_DM(9) K3_DM(10) K3_DM(11) K3_DM(12)

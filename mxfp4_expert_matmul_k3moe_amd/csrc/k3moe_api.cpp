@@ -334,6 +334,23 @@ int run_ffn(const k3moe_dims& dm, int32_t T, const void* x, int xf32,
   const bool scales4 = ((reinterpret_cast<uintptr_t>(ex->gate_s) |
                          reinterpret_cast<uintptr_t>(ex->up_s) |
                          reinterpret_cast<uintptr_t>(ex->down_s)) & 3u) == 0;
+  if (packed && T == 1 && k3moe::down_decode_mfma_supported(d, f, k)) {
+    // packed tile layout, one token: h per (slot, 16-row tile), then the decode down kernel
+    // adds the slots in order
+    {
+      Probe probe(K3MOE_KERNEL_GATE_UP, s);
+      rc = hip_check(k3moe::launch_gateup_decode_packed(d, f, k, x, xf32, w,
+                                                        ws.at<int32_t>(R_PPOS),
+                                                        ws.at<int32_t>(R_PEXP), h, s),
+                     "gate/up (decode, packed)");
+    }
+    if (rc || (rc = join())) return rc;
+    Probe probe(K3MOE_KERNEL_DOWN, s);
+    return hip_check(k3moe::launch_down_decode_mfma(d, f, k, w, h, ws.at<int32_t>(R_PPOS),
+                                                    ws.at<int32_t>(R_PEXP), gates, resid, shared,
+                                                    y, y_bf16, cu_count(), s, true),
+                     "down+combine (decode, packed)");
+  }
   if (packed) {
     // packed tile layout: grouped GEMMs on the block-scaled MFMA for every token count (the
     // shapes and the bf16 activations were checked by the entry point)

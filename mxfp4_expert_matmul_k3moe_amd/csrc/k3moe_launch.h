@@ -83,12 +83,19 @@ hipError_t launch_down_decode(int d, int f, int k, const MxPtrs& w, const float*
 // T == 1 down projection + ordered combine on the block-scaled MFMA (ffn_mfma.hip): one
 // persistent block per CU walking its equal share of output rows in 16-row tiles, one wave
 // per slot; needs d % 16 == 0, f % 128 == 0, f <= 1536 and k <= 16. launch_down_decode takes
-// it whenever the shape allows.
+// it whenever the shape allows. packed: down in the packed tile layout.
 bool down_decode_mfma_supported(int d, int f, int k);
 hipError_t launch_down_decode_mfma(int d, int f, int k, const MxPtrs& w, const float* h,
                                    const int32_t* pair_pos, const int32_t* pair_exp,
                                    const float* gates, const float* resid, const float* shared,
-                                   float* y, uint16_t* y_bf16, int n_cu, hipStream_t s);
+                                   float* y, uint16_t* y_bf16, int n_cu, hipStream_t s,
+                                   bool packed = false);
+// One token, packed tile layout (d % 1024 == 0, f % 16 == 0): h = silu(G x) * (U x) of every
+// slot as fp32 into h [k][f] at the slot's bucket position; one wave per (slot, 16-row tile).
+// x is bf16 (xf32 == 0) or fp32 [d].
+hipError_t launch_gateup_decode_packed(int d, int f, int k, const void* x, int xf32,
+                                       const MxPtrs& w, const int32_t* pair_pos,
+                                       const int32_t* pair_exp, float* h, hipStream_t s);
 // Any T: per-expert down projection into z [P][d] (pair-indexed).
 hipError_t launch_down_gemv(int T, int d, int f, int E, int k, const MxPtrs& w,
                             const float* h, const int32_t* offsets, const int32_t* rows,

@@ -6,8 +6,9 @@
 - The layer on packed experts is checked against the fp64 oracle with the bars of
   test_gpu_parity.py (routing bit-exact, per-token relative L2 and element bounds), on small
   ragged shapes (16-, 32- and 64-row tiles, partial row slices, experts with one to many
-  subtiles) and on the K3 layer: every token of the 32-token batch, and routing-chosen tile
-  edges of the 2048-token prefill chunk.
+  subtiles; one-token cases on the decode kernels) and on the K3 layer: two single tokens,
+  every token of the 32-token batch, and routing-chosen tile edges of the 2048-token prefill
+  chunk.
 """
 import numpy as np
 import pytest
@@ -16,7 +17,7 @@ import torch
 import mxfp4_expert_matmul_k3moe_amd as k3
 import oracle
 from k3gen import device as gdev
-from k3gen.workloads import BATCHED, PREFILL, Workload
+from k3gen.workloads import BATCHED, DECODE, PREFILL, Workload
 from oracle import harness
 
 from test_gpu_parity import ELEM_FACTOR, K3_TOL, TOL, check_routing, rel_elem, rel_l2, \
@@ -54,9 +55,14 @@ SMALL = [
     Workload("pk_d1024", 61, d=1024, f=512, E=12, k=3, T=40, zipf_alpha=0.6),
     # three chunks of d, down with 12 steps (f = 1536), hot experts over several M tiles
     Workload("pk_mixed", 62, d=3072, f=1536, E=24, k=4, T=150, zipf_alpha=0.9),
-    # f = 1024 (8 down steps), one token (every expert one tile), two tokens
+    # f = 1024 (8 down steps), one token (the one-token kernels: a wave per slot tile of
+    # G and U, decode down on whole tiles), two tokens (grouped GEMMs)
     Workload("pk_t1", 63, d=2048, f=1024, E=16, k=4, T=1),
     Workload("pk_t2", 64, d=2048, f=1024, E=16, k=4, T=2),
+    # one token: three 8-step chunks of d and 12 down steps with 16 slots; one chunk of d
+    # (the scale prefetch clamps at once) with two slots
+    Workload("pk_t1_k16", 65, d=3072, f=1536, E=40, k=16, T=1),
+    Workload("pk_t1_d1024", 66, d=1024, f=512, E=8, k=2, T=1),
 ]
 
 
@@ -121,6 +127,23 @@ def test_packed_repeat_runs_bit_identical(dev):
     a = run_packed(w, x, dev, packed)
     b = run_packed(w, x, dev, packed)
     assert torch.equal(a["y"], b["y"]) and np.array_equal(a["ids"], b["ids"])
+
+
+def test_packed_decode_k3(dev):
+    w = DECODE
+    say("packed decode: d=7168 f=1536 E=896 k=16 T=1, two tokens")
+    dims = k3.make_dims(w.d, w.f, w.E, w.k)
+    ex = gdev.experts(w, 0, dev)
+    packed = k3.pack_experts(dims, k3.MxExperts(**ex))
+    del ex
+    for ts in (0, 1):
+        x = w.x_bf16(token_set=ts)
+        g = run_packed(w, x, dev, packed)
+        check(g, harness.run_layer(w, x), tol=K3_TOL)
+        g2 = run_packed(w, x, dev, packed)
+        assert torch.equal(g["y"], g2["y"])
+    del packed
+    torch.cuda.empty_cache()
 
 
 def test_packed_batched_k3(dev):
