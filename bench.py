@@ -414,7 +414,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "batched", "prefill", "stack8", "cached"])
+                    choices=["decode", "batched", "batched_zipf", "prefill", "stack8",
+                             "cached"])
     ap.add_argument("--slots", type=int, default=128,
                     help="cached workload: HBM expert slots (the other experts stay in "
                          "pinned host memory)")
@@ -430,6 +431,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="decode: leave out the prefill leg of the default line")
+    ap.add_argument("--hot-tokens", type=int, default=None,
+                    help="k3moe_set_hot_tokens before the run: experts with fewer tokens in a "
+                         "step read their weights non-temporally in the grouped kernels "
+                         "(0..16; the library's default is 16)")
     ap.add_argument("--layout", choices=["rowmajor", "packed"], default=None,
                     help="expert weight layout of a single-workload run (default: packed "
                          "for the grouped-GEMM workloads, row-major for one token)")
@@ -460,6 +465,9 @@ def main() -> int:
     from k3gen.workloads import WORKLOADS
 
     w = WORKLOADS["decode" if args.workload == "cached" else args.workload]
+    if args.hot_tokens is not None:
+        import mxfp4_expert_matmul_k3moe_amd as k3
+        k3.set_hot_tokens(args.hot_tokens)
     if args.tokens:
         w = w.with_(T=args.tokens)
     if args.workload == "cached":
@@ -526,6 +534,7 @@ def main() -> int:
                    "bytes_per_step": int(round(m["bytes_timed"] / args.steps)),
                    "token_sets": leg.nsets, "hip_graph": bool(args.graph),
                    "expert_layout": "packed" if leg.packed else "row-major",
+                   "hot_tokens": _hot_tokens(),
                    "preceded_by": ("the prefill leg below, then " if prefill_obj else "") +
                    "a 6 GB read-only sweep (no dirty lines from input generation in the "
                    "caches; none of the layer's weights in them)"},
@@ -540,6 +549,11 @@ def main() -> int:
         out["prefill"] = prefill_obj
     print(json.dumps(out), flush=True)
     return 0
+
+
+def _hot_tokens() -> int:
+    import mxfp4_expert_matmul_k3moe_amd as k3
+    return k3.hot_tokens()
 
 
 def _read_record(name: str) -> dict:

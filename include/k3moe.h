@@ -326,6 +326,17 @@ K3MOE_API int k3moe_time_next_kernel(int which, void* ev_start, void* ev_stop);
 /* Message describing the calling thread's last non-OK status ("" if none). */
 K3MOE_API const char* k3moe_last_error(void);
 
+/* Cache policy of the expert weight reads in the grouped (many-token) kernels, process-wide:
+ * an expert with fewer than `hot_tokens` tokens in a call reads its weights non-temporally
+ * (streamed past the caches), one with more keeps the normal policy, so that the weights of
+ * experts that many tokens choose can stay in the caches for their other 64-token tiles and,
+ * under skewed routing, for later calls ("Kimi K3 纯 C 语言 CPU 推理实战" §1.3, obstacle 3: keep
+ * loaded experts in the last-level cache; §6.2: a small hot set is chosen far more often).
+ * 0 <= hot_tokens <= 16 (0: normal policy for every expert); default 16. Results do not
+ * depend on it. K3MOE_EINVAL outside the range. k3moe_hot_tokens() returns the setting. */
+K3MOE_API int k3moe_set_hot_tokens(int32_t hot_tokens);
+K3MOE_API int32_t k3moe_hot_tokens(void);
+
 /* Teardown of what the library keeps between calls: synchronises and destroys, on every
  * device where they exist, the block-mode side stream and the slot cache's copy streams,
  * and destroys the CALLING thread's fork/join events (other threads' events stay until the

@@ -1,12 +1,14 @@
 """Synthetic workloads: shapes, value distributions and stream keys.
 
 Nothing here computes any part of the MoE layer; it only says which numbers
-go in. The five named workloads are:
+go in. The named workloads are:
 
   toy      d=512,  f=256,  E=32,  k=4,  T=1
   decode   d=7168, f=1536, E=896, k=16, T=1
   batched  same layer, T=32 independent tokens
   prefill  same layer, T=2048, Zipf(1.1) logit bias
+  batched_zipf  same layer, T=32, Zipf(1.1) logit bias (a hot set of experts that every
+           step routes to again; about 165 distinct experts per step)
   stack8   8 blocks (RMSNorm -> routed MoE + bf16 shared SwiGLU -> residual), T=1
 
 Value distributions (all workloads): x ~ bf16(N(0,1)); router weight
@@ -126,5 +128,6 @@ BATCHED = Workload("batched", 3, d=7168, f=1536, E=896, k=16, T=32)
 PREFILL = Workload("prefill", 4, d=7168, f=1536, E=896, k=16, T=2048, zipf_alpha=1.1)
 STACK8 = Workload("stack8", 5, d=7168, f=1536, E=896, k=16, T=1, layers=8, block=True)
 TINY = Workload("tiny", 6, d=64, f=32, E=8, k=2, T=3)
+BATCHED_ZIPF = Workload("batched_zipf", 7, d=7168, f=1536, E=896, k=16, T=32, zipf_alpha=1.1)
 
-WORKLOADS = {w.name: w for w in (TOY, DECODE, BATCHED, PREFILL, STACK8, TINY)}
+WORKLOADS = {w.name: w for w in (TOY, DECODE, BATCHED, PREFILL, STACK8, TINY, BATCHED_ZIPF)}

@@ -138,6 +138,10 @@ def lib() -> ctypes.CDLL:
                                                  vp]
         L.k3moe_release.restype = ctypes.c_int
         L.k3moe_release.argtypes = []
+        L.k3moe_set_hot_tokens.restype = ctypes.c_int
+        L.k3moe_set_hot_tokens.argtypes = [i32]
+        L.k3moe_hot_tokens.restype = i32
+        L.k3moe_hot_tokens.argtypes = []
         _lib = L
         # streams and events the library keeps are released while the HIP runtime is
         # still up (Python's exit handlers run before the runtime's own finalisers)
@@ -177,6 +181,16 @@ def _x_dtype(x: torch.Tensor) -> int:
     if x.dtype == torch.float32:
         return F32
     raise ValueError(f"x must be bf16 or fp32, got {x.dtype}")
+
+
+def set_hot_tokens(n: int) -> None:
+    """k3moe_set_hot_tokens: experts with fewer than n tokens in a call read their weights
+    non-temporally in the grouped kernels (0 <= n <= 16)."""
+    _check(lib().k3moe_set_hot_tokens(int(n)))
+
+
+def hot_tokens() -> int:
+    return int(lib().k3moe_hot_tokens())
 
 
 def time_next_kernel(which: int, ev_start, ev_stop) -> None:

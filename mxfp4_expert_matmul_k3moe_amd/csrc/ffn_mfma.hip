@@ -15,6 +15,7 @@
 // Every term is one more MFMA into the same fp32 accumulator; no instruction decodes a
 // weight. K is walked in steps of 128 (4 scale blocks). Source of the form: "Kimi K3 纯
 // C 语言 CPU 推理实战" (chenxutan.com/d/5901.html) §1.2, §2.3.
+#include <atomic>
 #include <type_traits>
 
 #include "k3moe_device.h"
@@ -38,6 +39,17 @@ constexpr int kSGroup = kWaves * 1024;       // scale groups: 16 B per lane = 4 
 constexpr int kWRing = 4;       // weight steps held per wave: the current one and 3 ahead
 constexpr int kTokStages = 4;   // token stages in LDS
 constexpr int kScaleSteps = 8;  // K steps per scale chunk (32 bytes of a row)
+// Cache policy of the weight reads of one expert tile. An expert with fewer than hot_tokens
+// tokens in the call reads its weights non-temporally (one pass, nothing to keep); one with
+// more keeps the normal policy, so that its weights can stay cached for its other M tiles and,
+// under skewed routing, for the next call that routes to it again ("Kimi K3 纯 C 语言 CPU
+// 推理实战" §1.3, obstacle 3, and §6.2: a small set of hot experts is chosen far more often
+// than the rest, and loaded experts are worth keeping in the last-level cache).
+// The threshold is a launch argument (set_hot_tokens), at most kHotTokensMax = 16 so that only
+// single-subtile experts (at most 16 tokens) can be cold; the default is 16.
+constexpr int kHotTokensMax = 16;
+constexpr int kCpNormal = 0, kCpStream = 2;  // load cache-policy bits: normal, non-temporal
+std::atomic<int> g_hot_tokens{kHotTokensMax};
 static_assert(kTokStages - 1 == 3, "the last scale chunk of the K loop peels three steps");
 
 // Gate/up on the gfx950 block-scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4): the MXFP4
@@ -85,6 +97,10 @@ __device__ __forceinline__ int tile_expert_blocks(const int32_t* mtile_off, int 
 // (or dst + 4 l). dst must be the same for the whole wave.
 __device__ __forceinline__ void dma16(const void* src, uint8_t* dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+}
+template <int CP>
+__device__ __forceinline__ void dma16p(const void* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, CP);
 }
 __device__ __forceinline__ void dma4(const void* src, uint8_t* dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 4, 0, 0);
@@ -145,6 +161,7 @@ struct MfmaArgs {
   uint8_t* h8;   // h as three E4M3 terms [P][3][f], bucket order (gate/up out, down in)
   uint8_t* hs8;  // their E8M0 scales [P][3][f/32], one per term and 32-element block
   float* z_out;  // down output
+  int hot_tokens;  // experts with fewer tokens read their weights non-temporally
 };
 
 
@@ -243,10 +260,10 @@ __device__ __forceinline__ void mx_gateup_tile(const MfmaArgs& a, uint8_t* lds, 
 template <int MT>
 __device__ __forceinline__ void mx_gateup_tile_sr(const MfmaArgs& a, uint8_t* lds, int e, int p0,
                                                   int pn, int nb);
-template <int MT, bool PK>
+template <int MT, bool PK, int CP = kCpNormal>
 __device__ __forceinline__ void mx_gateup_tile_rw(const MfmaArgs& a, uint8_t* lds, int e, int p0,
                                                   int pn, int nb);
-template <int MT, bool SG4, bool PK = false>
+template <int MT, bool SG4, bool PK = false, int CP = kCpNormal>
 __device__ __forceinline__ void mx_down_tile(const MfmaArgs& a, uint8_t* lds, int e, int p0, int pn,
                                              int nb);
 
@@ -277,12 +294,15 @@ __global__ __launch_bounds__(512) void mfma_ffn_kernel(MfmaArgs a) {
                    ((reinterpret_cast<uintptr_t>(a.s0) |
                      reinterpret_cast<uintptr_t>(GATEUP ? a.s1 : a.s0)) & 15u) == 0;
   if (GATEUP) {
+    // (hot_tokens <= 16: only single-subtile experts can be cold)
     if (a.packed) {
-      if (cnt <= 16) mx_gateup_tile_rw<1, true>(a, lds, e, p0, pn, nb);
+      if (cnt < a.hot_tokens) mx_gateup_tile_rw<1, true, kCpStream>(a, lds, e, p0, pn, nb);
+      else if (cnt <= 16) mx_gateup_tile_rw<1, true>(a, lds, e, p0, pn, nb);
       else if (cnt <= 32) mx_gateup_tile_rw<2, true>(a, lds, e, p0, pn, nb);
       else mx_gateup_tile_rw<4, true>(a, lds, e, p0, pn, nb);
     } else if (sg4 && a.d % (kScaleSteps * BK) == 0) {
-      if (cnt <= 16) mx_gateup_tile_rw<1, false>(a, lds, e, p0, pn, nb);
+      if (cnt < a.hot_tokens) mx_gateup_tile_rw<1, false, kCpStream>(a, lds, e, p0, pn, nb);
+      else if (cnt <= 16) mx_gateup_tile_rw<1, false>(a, lds, e, p0, pn, nb);
       else if (cnt <= 32) mx_gateup_tile_rw<2, false>(a, lds, e, p0, pn, nb);
       else mx_gateup_tile_rw<4, false>(a, lds, e, p0, pn, nb);
     } else if (sg4) {
@@ -297,11 +317,13 @@ __global__ __launch_bounds__(512) void mfma_ffn_kernel(MfmaArgs a) {
     return;
   }
   if (a.packed) {
-    if (cnt <= 16) mx_down_tile<1, true, true>(a, lds, e, p0, pn, nb);
+    if (cnt < a.hot_tokens) mx_down_tile<1, true, true, kCpStream>(a, lds, e, p0, pn, nb);
+    else if (cnt <= 16) mx_down_tile<1, true, true>(a, lds, e, p0, pn, nb);
     else if (cnt <= 32) mx_down_tile<2, true, true>(a, lds, e, p0, pn, nb);
     else mx_down_tile<4, true, true>(a, lds, e, p0, pn, nb);
   } else if (sg4) {
-    if (cnt <= 16) mx_down_tile<1, true>(a, lds, e, p0, pn, nb);
+    if (cnt < a.hot_tokens) mx_down_tile<1, true, false, kCpStream>(a, lds, e, p0, pn, nb);
+    else if (cnt <= 16) mx_down_tile<1, true>(a, lds, e, p0, pn, nb);
     else if (cnt <= 32) mx_down_tile<2, true>(a, lds, e, p0, pn, nb);
     else mx_down_tile<4, true>(a, lds, e, p0, pn, nb);
   } else {
@@ -625,7 +647,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uin
                                            0x00020000);
 }
 
-template <int MT, bool PK>
+template <int MT, bool PK, int CP>
 __device__ __forceinline__ void mx_gateup_tile_rw(const MfmaArgs& a, uint8_t* lds, int e, int p0,
                                                   int pn, int nb) {
   constexpr int S = kTokStages, AB = MT * 4 * 1024;
@@ -683,7 +705,7 @@ __device__ __forceinline__ void mx_gateup_tile_rw(const MfmaArgs& a, uint8_t* ld
   }
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   auto sload = [&](int nt, int c) {  // this lane's 8 bytes of scale chunk c
-    return __builtin_amdgcn_raw_buffer_load_b64(nt < 2 ? rs_g : rs_u, vs[nt], SCHUNK * c, 0);
+    return __builtin_amdgcn_raw_buffer_load_b64(nt < 2 ? rs_g : rs_u, vs[nt], SCHUNK * c, CP);
   };
 
   f32x4 acc[MT][NT];
@@ -702,7 +724,7 @@ __device__ __forceinline__ void mx_gateup_tile_rw(const MfmaArgs& a, uint8_t* ld
     auto issue = [&](int ks, u32x4 (&dst)[NT]) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        dst[nt] = __builtin_amdgcn_raw_buffer_load_b128(nt < 2 ? rq_g : rq_u, vq[nt], ks * QSTEP, 0);
+        dst[nt] = __builtin_amdgcn_raw_buffer_load_b128(nt < 2 ? rq_g : rq_u, vq[nt], ks * QSTEP, CP);
       asm volatile("" ::: "memory");
       if constexpr (HA) {
         uint8_t* st = lds + (ks % S) * AB;
@@ -830,7 +852,7 @@ struct MxDownPipe {
   static constexpr int A_PER_WAVE = (6 * MT + kWaves - 1) / kWaves;
 };
 
-template <int MT, bool SG4, bool PK>
+template <int MT, bool SG4, bool PK, int CP>
 __device__ __forceinline__ void mx_down_tile(const MfmaArgs& a, uint8_t* lds, int e, int p0, int pn,
                                              int nb) {
   static_assert(!PK || SG4, "packed scales use the ring");
@@ -897,7 +919,7 @@ __device__ __forceinline__ void mx_down_tile(const MfmaArgs& a, uint8_t* lds, in
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-      dma16(bsrc[nt] + (size_t)ks * (PK ? 1024 : 64), st + AB + (wave * NT + nt) * 1024);
+      dma16p<CP>(bsrc[nt] + (size_t)ks * (PK ? 1024 : 64), st + AB + (wave * NT + nt) * 1024);
     if (PK) {
       if ((ks & 7) == 0) {
         uint8_t* slot = sring + ((ks >> 3) & 1) * kPkSGroup + wave * 2048;
@@ -1331,12 +1353,20 @@ hipError_t launch_gateup_mfma(int T, int d, int f, int E, int k, const uint16_t*
   a.offsets = offsets; a.rows = rows; a.act = act; a.n_act = n_act; a.mtile_off = mtile_off;
   a.nblk_n = (f + 255) / 256;
   a.packed = packed ? 1 : 0;
+  a.hot_tokens = g_hot_tokens.load(std::memory_order_relaxed);
   a.h8 = h8;
   a.hs8 = hs8;
   dim3 grid((unsigned)(mfma_mtiles_bound(T, E, k) * a.nblk_n));
   mfma_ffn_kernel<true><<<grid, 512, 0, s>>>(a);
   return hipGetLastError();
 }
+
+bool set_hot_tokens(int n) {
+  if (n < 0 || n > kHotTokensMax) return false;
+  g_hot_tokens.store(n, std::memory_order_relaxed);
+  return true;
+}
+int hot_tokens() { return g_hot_tokens.load(std::memory_order_relaxed); }
 
 bool packed_shape_supported(int d, int f) { return d % 1024 == 0 && f % 512 == 0; }
 
@@ -1346,6 +1376,7 @@ hipError_t launch_down_mfma(int T, int d, int f, int E, int k, const MxPtrs& w,
                             const int32_t* mtile_off, float* z, hipStream_t s, bool packed) {
   MfmaArgs a{};
   a.packed = packed ? 1 : 0;
+  a.hot_tokens = g_hot_tokens.load(std::memory_order_relaxed);
   a.T = T; a.d = d; a.f = f; a.k = k;
   a.h8 = const_cast<uint8_t*>(h8);
   a.hs8 = const_cast<uint8_t*>(hs8);

@@ -51,7 +51,6 @@ constexpr int kMaxE = 4096;
 constexpr int kMaxK = 32;
 constexpr int kMaxT = 1 << 20;
 constexpr int kMaxWidth = 16384;
-// Above this many tokens, bf16 activations go through the MFMA grouped GEMMs.
 // From this many tokens on (bf16 activations) the expert matmuls run as grouped MFMA GEMMs;
 // below, as per-expert GEMVs. At 32 tokens the MFMA path's down projection already streams
 // twice as fast as the GEMV one.
@@ -465,6 +464,14 @@ int k3moe_time_next_kernel(int which, void* ev_start, void* ev_stop) {
 }
 
 const char* k3moe_last_error(void) { return g_err.c_str(); }
+
+int k3moe_set_hot_tokens(int32_t hot_tokens) {
+  if (!k3moe::set_hot_tokens(hot_tokens))
+    return fail(K3MOE_EINVAL, "hot_tokens must be in [0, 16] (got %d)", (int)hot_tokens);
+  return K3MOE_OK;
+}
+
+int32_t k3moe_hot_tokens(void) { return k3moe::hot_tokens(); }
 
 int k3moe_release(void) {
   if (!g_created.load()) return K3MOE_OK;

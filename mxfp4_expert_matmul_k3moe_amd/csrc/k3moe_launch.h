@@ -122,6 +122,11 @@ hipError_t launch_gateup_mfma(int T, int d, int f, int E, int k, const uint16_t*
 // Shapes the packed-layout grouped GEMMs take (d: whole 8-step scale chunks; f: the down
 // kernel's scale groups).
 bool packed_shape_supported(int d, int f);
+// Grouped GEMMs: experts with fewer than n tokens in a call read their weights
+// non-temporally, the others with the normal cache policy (0 <= n <= 16; default 16).
+// Returns false (and changes nothing) for n outside that range.
+bool set_hot_tokens(int n);
+int hot_tokens();
 // z (fp32 [P][d], pair-indexed) = D h from the three terms of h; packed: D in the packed tile
 // layout (weights streamed per M tile, each tile step one 1-KB DMA).
 hipError_t launch_down_mfma(int T, int d, int f, int E, int k, const MxPtrs& w,

@@ -33,7 +33,8 @@ def test_exports_every_declared_symbol():
                           "k3moe_cache_stats_get", "k3moe_layer_forward_cached",
                           "k3moe_release", "k3moe_layer_forward_noalloc",
                           "k3moe_packed_expert_bytes", "k3moe_pack_experts",
-                          "k3moe_layer_forward_packed"}
+                          "k3moe_layer_forward_packed", "k3moe_set_hot_tokens",
+                          "k3moe_hot_tokens"}
     L = k3.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -42,6 +43,22 @@ def test_exports_every_declared_symbol():
     assert L.k3moe_time_next_kernel(k3.KERNEL_GATE_UP, None, None) == k3.OK  # disarm
     # nothing created yet: release touches no HIP state and succeeds
     assert L.k3moe_release() == k3.OK
+
+
+def test_hot_tokens_setting_range():
+    """The grouped kernels' cache-policy threshold: default 16, settable in [0, 16], anything
+    else rejected with the setting unchanged (host state only, no GPU)."""
+    L = k3.lib()
+    assert L.k3moe_hot_tokens() == 16
+    try:
+        for n in (0, 1, 15, 16):
+            assert L.k3moe_set_hot_tokens(n) == k3.OK and L.k3moe_hot_tokens() == n
+        for n in (-1, 17, 1 << 30):
+            assert L.k3moe_set_hot_tokens(n) == k3.EINVAL
+            assert b"hot_tokens" in L.k3moe_last_error()
+            assert L.k3moe_hot_tokens() == 16
+    finally:
+        assert L.k3moe_set_hot_tokens(16) == k3.OK
 
 
 def test_workspace_bytes_monotone_and_zero_for_bad_dims():

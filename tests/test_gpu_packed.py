@@ -21,7 +21,7 @@ from k3gen.workloads import BATCHED, DECODE, PREFILL, Workload
 from oracle import harness
 
 from test_gpu_parity import ELEM_FACTOR, K3_TOL, TOL, check_routing, rel_elem, rel_l2, \
-    tile_probe_tokens
+    run_gpu_layer, tile_probe_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -144,6 +144,28 @@ def test_packed_decode_k3(dev):
         assert torch.equal(g["y"], g2["y"])
     del packed
     torch.cuda.empty_cache()
+
+
+def test_hot_tokens_policy_keeps_results(dev):
+    """The cache policy of the grouped kernels' weight reads (experts below the threshold
+    read non-temporally) changes no result: both layouts, bit for bit, with the threshold at
+    0 (every expert normal), 16 (the default) and 9, on a skewed batch that has experts
+    below and above every threshold."""
+    w = SMALL[1]  # pk_mixed: Zipf(0.9), T=150, experts with 2 to 115 tokens
+    say(f"cache policy invariance {w.name}")
+    dims = k3.make_dims(w.d, w.f, w.E, w.k)
+    ex = gdev.experts(w, 0, dev)
+    packed = k3.pack_experts(dims, k3.MxExperts(**ex))
+    x = w.x_bf16()
+    got = {}
+    try:
+        for n in (0, 16, 9):
+            k3.set_hot_tokens(n)
+            got[n] = (run_gpu_layer(w, x, dev, experts=ex)["y"], run_packed(w, x, dev, packed)["y"])
+    finally:
+        k3.set_hot_tokens(16)
+    for n in (16, 9):
+        assert torch.equal(got[n][0], got[0][0]) and torch.equal(got[n][1], got[0][1]), n
 
 
 def test_packed_batched_k3(dev):
