@@ -437,7 +437,8 @@ def main() -> int:
                          "(0..16; the library's default is 16)")
     ap.add_argument("--layout", choices=["rowmajor", "packed"], default=None,
                     help="expert weight layout of a single-workload run (default: packed "
-                         "for the grouped-GEMM workloads, row-major for one token)")
+                         "for the grouped-GEMM workloads and the 8-block stack, row-major for "
+                         "the one-token layer)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one HIP graph per token set (captured on the "
                          "caller's stream) instead of eager calls")
@@ -616,9 +617,20 @@ def bench_stack(args, w) -> int:
 
     dev = torch.device("cuda:0")
     dims = k3.make_dims(w.d, w.f, w.E, w.k)
+    # packed by default: the fp32-token gate/up of the packed layout holds 128 registers,
+    # the row-major one 177
+    packed = args.layout == "packed" or (args.layout is None and w.d % 1024 == 0 and
+                                          w.f % 512 == 0)
+    fwd = k3.layer_forward_packed if packed else k3.layer_forward
     layers = []
     for l in range(w.layers):
         ex = k3.MxExperts(**gdev.experts(w, l, dev))
+        if packed:  # the packed copy, made once per layer (weight preparation, not timed)
+            rm = ex
+            ex = k3.pack_experts(dims, rm)
+            torch.cuda.synchronize()
+            del rm
+            torch.cuda.empty_cache()
         b = gdev.block_extras(w, l, dev)
         blk = k3.BlockWeights(b["rms_gamma"], b["sh_gate"], b["sh_up"], b["sh_down"], 1e-6)
         layers.append((gdev.router_w(w, l, dev), gdev.bias(w, l, dev), ex, blk))
@@ -633,7 +645,7 @@ def bench_stack(args, w) -> int:
         h = h0[i % nsets]
         for l, (wr, bias, ex, blk) in enumerate(layers):
             y = hb[l % 2]
-            k3.layer_forward(dims, h, wr, bias, ex, blk, y=y, ids=ids[l], gates=gates, ws=ws)
+            fwd(dims, h, wr, bias, ex, blk, y=y, ids=ids[l], gates=gates, ws=ws)
             h = y
 
     clean_sweep()
@@ -679,11 +691,15 @@ def bench_stack(args, w) -> int:
         "config": {"workload": f"stack8: {workload_desc(w)} layers={w.layers}, block "
                                "(RMSNorm, shared expert, residual)",
                    "bytes_per_step": int(bytes_step), "token_sets": nsets,
-                   "hip_graph": bool(args.graph)},
+                   "hip_graph": bool(args.graph),
+                   "expert_layout": "packed" if packed else "row-major"},
         "roofline": {"bound": "hbm",
-                     "kernel": "gateup_decode_kernel (MXFP4 gate/up GEMV + SwiGLU)",
+                     "kernel": ("gateup_decode_packed_kernel<fp32 x> (MXFP4 gate/up GEMV + "
+                                "SwiGLU, packed tile layout)" if packed else
+                                "gateup_decode_kernel<fp32 x> (MXFP4 gate/up GEMV + SwiGLU)"),
                      "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": decode_traffic(),
+                     # the counter record was taken on the bf16-token instantiation
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": int(gu_bytes),
                      "avg_launch_us": round(kern["gate_up"] * 1e3, 2)},
         "kernels": {"down_us": round(kern["down"] * 1e3, 2),

@@ -315,6 +315,20 @@ def expert_ffn(dims: Dims, x: torch.Tensor, experts: MxExperts, offsets: torch.T
     return y
 
 
+def _block_struct(dims: Dims, block: Optional[BlockWeights]):
+    """ctypes reference to a k3moe_block for ``block`` (None for no block mode)."""
+    if block is None:
+        return None
+    d, f = dims.d_model, dims.d_ff
+    _dev(block.rms_gamma, "rms_gamma", (torch.bfloat16, torch.int16), (d,))
+    _dev(block.sh_gate, "sh_gate", (torch.bfloat16, torch.int16), (f, d))
+    _dev(block.sh_up, "sh_up", (torch.bfloat16, torch.int16), (f, d))
+    _dev(block.sh_down, "sh_down", (torch.bfloat16, torch.int16), (d, f))
+    b = _Block(block.rms_gamma.data_ptr(), float(block.rms_eps), block.sh_gate.data_ptr(),
+               block.sh_up.data_ptr(), block.sh_down.data_ptr())
+    return ctypes.byref(b)
+
+
 def layer_forward(dims: Dims, x: torch.Tensor, w_router: torch.Tensor,
                   logit_bias: Optional[torch.Tensor], experts: MxExperts,
                   block: Optional[BlockWeights] = None, *, y: Optional[torch.Tensor] = None,
@@ -340,15 +354,7 @@ def layer_forward(dims: Dims, x: torch.Tensor, w_router: torch.Tensor,
         _dev(ids, "ids", torch.int32, (T, k))
     if gates is not None:
         _dev(gates, "gates", torch.float32, (T, k))
-    blk_ref = None
-    if block is not None:
-        _dev(block.rms_gamma, "rms_gamma", (torch.bfloat16, torch.int16), (d,))
-        _dev(block.sh_gate, "sh_gate", (torch.bfloat16, torch.int16), (f, d))
-        _dev(block.sh_up, "sh_up", (torch.bfloat16, torch.int16), (f, d))
-        _dev(block.sh_down, "sh_down", (torch.bfloat16, torch.int16), (d, f))
-        b = _Block(block.rms_gamma.data_ptr(), float(block.rms_eps), block.sh_gate.data_ptr(),
-                   block.sh_up.data_ptr(), block.sh_down.data_ptr())
-        blk_ref = ctypes.byref(b)
+    blk_ref = _block_struct(dims, block)
     es = _experts_struct(dims, experts)
     if ws is False:  # the allocation-free entry point: static device scratch
         _check(lib().k3moe_layer_forward_noalloc(ctypes.byref(dims), T, _ptr(x), _x_dtype(x),
@@ -366,16 +372,18 @@ def layer_forward(dims: Dims, x: torch.Tensor, w_router: torch.Tensor,
 
 
 def layer_forward_packed(dims: Dims, x: torch.Tensor, w_router: torch.Tensor,
-                         logit_bias: Optional[torch.Tensor], experts: MxExperts, *,
+                         logit_bias: Optional[torch.Tensor], experts: MxExperts,
+                         block: Optional[BlockWeights] = None, *,
                          y: Optional[torch.Tensor] = None,
                          y_bf16: Optional[torch.Tensor] = None,
                          ids: Optional[torch.Tensor] = None,
                          gates: Optional[torch.Tensor] = None, ws=None,
                          stream=None) -> torch.Tensor:
-    """layer_forward with `experts` in the packed tile layout (pack_experts)."""
+    """layer_forward with `experts` in the packed tile layout (pack_experts). fp32 tokens
+    and ``block`` only for one token (the library refuses them otherwise)."""
     T = x.shape[0]
-    d, E, k = dims.d_model, dims.n_experts, dims.top_k
-    _dev(x, "x", (torch.bfloat16,), (T, d))
+    d, E, k, f = dims.d_model, dims.n_experts, dims.top_k, dims.d_ff
+    _dev(x, "x", (torch.bfloat16, torch.float32), (T, d))
     _dev(w_router, "w_router", (torch.bfloat16, torch.int16), (d, E))
     if logit_bias is not None:
         _dev(logit_bias, "logit_bias", torch.float32, (E,))
@@ -387,12 +395,13 @@ def layer_forward_packed(dims: Dims, x: torch.Tensor, w_router: torch.Tensor,
         _dev(ids, "ids", torch.int32, (T, k))
     if gates is not None:
         _dev(gates, "gates", torch.float32, (T, k))
+    blk_ref = _block_struct(dims, block)
     es = _experts_struct(dims, experts, packed=True)
     w = _ws(dims, T, ws, x.device)
     _check(lib().k3moe_layer_forward_packed(ctypes.byref(dims), T, _ptr(x), _x_dtype(x),
                                             _ptr(w_router), _ptr(logit_bias), ctypes.byref(es),
-                                            None, _ptr(y), _ptr(y_bf16), _ptr(ids), _ptr(gates),
-                                            _ptr(w), w.numel(), _stream(stream)))
+                                            blk_ref, _ptr(y), _ptr(y_bf16), _ptr(ids),
+                                            _ptr(gates), _ptr(w), w.numel(), _stream(stream)))
     return y
 
 

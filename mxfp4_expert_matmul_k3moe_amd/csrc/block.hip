@@ -110,8 +110,10 @@ __host__ __device__ inline int gemv_lanes(int nch) {
 // out[t][r] = sum_c W[r][c] * x[t][c], one row group (rpw rows) per wave; two weight
 // matrices at once when W2 is given (gate and up share the activation). Epilogue:
 // SWIGLU ? silu(a)*b : a. A lane takes chunks sub, sub + lpr, ... in rounds of
-// kGemvChunks whose loads all go out before their math; the first round is requested
-// before the token is staged in LDS, since the weights do not depend on it.
+// kGemvChunks whose loads all go out before their math. The grid may
+// be smaller than the row groups: blocks then walk groups gridDim.x apart (the shared
+// expert runs beside the routed path and is given a fraction of the CUs, so that the
+// latency-bound router and top-k find room on every CU).
 constexpr int kGemvChunks = 8;
 template <bool SWIGLU>
 __global__ __launch_bounds__(256, 2) void bf16_gemv_kernel(int T, int nrows, int ncols,
@@ -124,43 +126,46 @@ __global__ __launch_bounds__(256, 2) void bf16_gemv_kernel(int T, int nrows, int
   const int lpr = gemv_lanes(nch), cpl = nch / lpr, rpw = 64 / lpr;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane & (lpr - 1), rsel = lane / lpr;
-  const int r = (blockIdx.x * 4 + wave) * rpw + rsel;
-  const bool rv = r < nrows;
-  const int rr = rv ? r : nrows - 1;  // loads stay in bounds; results of !rv are dropped
-  const uint16_t* w1 = W1 + (size_t)rr * ncols + (size_t)sub * 8;
-  const uint16_t* w2 = SWIGLU ? W2 + (size_t)rr * ncols + (size_t)sub * 8 : nullptr;
+  const int ngroups = (nrows + 4 * rpw - 1) / (4 * rpw);  // row groups of 4 waves
   for (int t = 0; t < T; ++t) {
-    u32x4 v1[kGemvChunks], v2[kGemvChunks];
-    auto load_round = [&](int i0) {
-#pragma unroll
-      for (int i = 0; i < kGemvChunks; ++i) {
-        if (i0 + i < cpl) {
-          const size_t off = (size_t)lpr * (i0 + i) * 8;
-          v1[i] = load_u32x4_nt(reinterpret_cast<const uint8_t*>(w1 + off));
-          if (SWIGLU) v2[i] = load_u32x4_nt(reinterpret_cast<const uint8_t*>(w2 + off));
-        }
-      }
-    };
-    load_round(0);
+    // the token is staged once per block and token; every group of the block uses it
     __syncthreads();  // the previous token's LDS reads are done
     stage_row(x + (size_t)t * ncols, ncols, lpr, xs);
     __syncthreads();
-    float a1 = 0.0f, a2 = 0.0f;
-    for (int i0 = 0; i0 < cpl; i0 += kGemvChunks) {
-      if (i0 > 0) load_round(i0);
+    for (int grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
+      const int r = (grp * 4 + wave) * rpw + rsel;
+      const bool rv = r < nrows;
+      const int rr = rv ? r : nrows - 1;  // loads stay in bounds; results of !rv are dropped
+      const uint16_t* w1 = W1 + (size_t)rr * ncols + (size_t)sub * 8;
+      const uint16_t* w2 = SWIGLU ? W2 + (size_t)rr * ncols + (size_t)sub * 8 : nullptr;
+      u32x4 v1[kGemvChunks], v2[kGemvChunks];
+      auto load_round = [&](int i0) {
 #pragma unroll
-      for (int i = 0; i < kGemvChunks; ++i) {
-        if (i0 + i < cpl) {
-          const int c = sub + lpr * (i0 + i);
-          const f32x4 xa = xs[xs_slot(c, 0, lpr)], xb = xs[xs_slot(c, 1, lpr)];
-          a1 = bf16x8_dot(v1[i], xa, xb, a1);
-          if (SWIGLU) a2 = bf16x8_dot(v2[i], xa, xb, a2);
+        for (int i = 0; i < kGemvChunks; ++i) {
+          if (i0 + i < cpl) {
+            const size_t off = (size_t)lpr * (i0 + i) * 8;
+            v1[i] = load_u32x4_nt(reinterpret_cast<const uint8_t*>(w1 + off));
+            if (SWIGLU) v2[i] = load_u32x4_nt(reinterpret_cast<const uint8_t*>(w2 + off));
+          }
+        }
+      };
+      float a1 = 0.0f, a2 = 0.0f;
+      for (int i0 = 0; i0 < cpl; i0 += kGemvChunks) {
+        load_round(i0);
+#pragma unroll
+        for (int i = 0; i < kGemvChunks; ++i) {
+          if (i0 + i < cpl) {
+            const int c = sub + lpr * (i0 + i);
+            const f32x4 xa = xs[xs_slot(c, 0, lpr)], xb = xs[xs_slot(c, 1, lpr)];
+            a1 = bf16x8_dot(v1[i], xa, xb, a1);
+            if (SWIGLU) a2 = bf16x8_dot(v2[i], xa, xb, a2);
+          }
         }
       }
+      a1 = group_sum_rt(a1, lpr);
+      if (SWIGLU) a2 = group_sum_rt(a2, lpr);
+      if (rv && sub == 0) out[(size_t)t * nrows + r] = SWIGLU ? silu_f32(a1) * a2 : a1;
     }
-    a1 = group_sum_rt(a1, lpr);
-    if (SWIGLU) a2 = group_sum_rt(a2, lpr);
-    if (rv && sub == 0) out[(size_t)t * nrows + r] = SWIGLU ? silu_f32(a1) * a2 : a1;
   }
 }
 
@@ -174,16 +179,20 @@ hipError_t launch_rmsnorm(int T, int d, const float* h, const uint16_t* gamma, f
 
 hipError_t launch_dense_swiglu(int T, int d, int f, const float* x, const uint16_t* wg,
                                const uint16_t* wu, const uint16_t* wd, float* hbuf, float* out,
-                               hipStream_t s) {
-  // one row group per wave: at d = 7168, f = 1536 that is 384 and 448 blocks
+                               hipStream_t s, int max_blocks) {
+  // one row group per wave: at d = 7168, f = 1536 that is 384 and 448 groups of 4 waves,
+  // walked by at most max_blocks blocks (0: one block per group)
+  auto blocks = [&](int groups) {
+    return (unsigned)(max_blocks > 0 && groups > max_blocks ? max_blocks : groups);
+  };
   {
     const int rows = 4 * (64 / gemv_lanes(d >> 3));
-    dim3 grid((unsigned)((f + rows - 1) / rows));
+    dim3 grid(blocks((f + rows - 1) / rows));
     bf16_gemv_kernel<true><<<grid, 256, (size_t)d * 4, s>>>(T, f, d, x, wg, wu, hbuf);
   }
   {
     const int rows = 4 * (64 / gemv_lanes(f >> 3));
-    dim3 grid((unsigned)((d + rows - 1) / rows));
+    dim3 grid(blocks((d + rows - 1) / rows));
     bf16_gemv_kernel<false><<<grid, 256, (size_t)f * 4, s>>>(T, d, f, hbuf, wd, nullptr, out);
   }
   return hipGetLastError();

@@ -786,9 +786,14 @@ int run_layer(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
           (rc = hip_check(hipStreamWaitEvent(s2, fork, 0), "fork shared expert")))
         return rc;
     }
+    // beside the routed path each shared-expert GEMV runs one block per CU (it has until the
+    // down launch to finish), so the latency-bound router and top-k find room on every CU:
+    // at d = 7168 the 8-block stack took 0.749 ms per token so, 0.76-0.80 ms with one block
+    // per row group (384 and 448 blocks), 0.80 ms with 128 blocks and 0.96 ms with 64
     rc = hip_check(k3moe::launch_dense_swiglu(T, d, dims->d_ff, static_cast<const float*>(xin),
                                               blk->sh_gate, blk->sh_up, blk->sh_down,
-                                              w.at<float>(R_HSH), ssh, s2 ? s2 : s),
+                                              w.at<float>(R_HSH), ssh, s2 ? s2 : s,
+                                              s2 ? cu_count() : 0),
                    "shared expert");
     if (rc) return rc;
     if (s2 && (rc = hip_check(hipEventRecord(joined, s2), "join shared expert"))) return rc;
@@ -815,14 +820,21 @@ int run_layer(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
 }
 
 // Shapes and activations the packed-layout kernels take.
-int check_packed(const k3moe_dims& dm, int x_dtype) {
+// One token on the packed layout runs the one-token kernels, which also take fp32 tokens
+// (and so block mode, whose RMSNorm output is fp32).
+bool packed_one_token(const k3moe_dims& dm, int32_t T) {
+  return T == 1 && k3moe::down_decode_mfma_supported(dm.d_model, dm.d_ff, dm.top_k);
+}
+
+int check_packed(const k3moe_dims& dm, int32_t T, int x_dtype) {
   if (!k3moe::packed_shape_supported(dm.d_model, dm.d_ff))
     return fail(K3MOE_EUNSUPPORTED,
                 "packed layout needs d_model %% 1024 == 0 and d_ff %% 512 == 0 (d_model=%d, "
                 "d_ff=%d)",
                 dm.d_model, dm.d_ff);
-  if (x_dtype != K3MOE_BF16)
-    return fail(K3MOE_EUNSUPPORTED, "the packed-layout kernels take bf16 activations");
+  if (x_dtype != K3MOE_BF16 && !packed_one_token(dm, T))
+    return fail(K3MOE_EUNSUPPORTED,
+                "the packed-layout kernels take bf16 activations (fp32 only for one token)");
   return K3MOE_OK;
 }
 
@@ -881,7 +893,7 @@ int k3moe_packed_expert_bytes(const k3moe_dims* dims, k3moe_packed_bytes* per_ex
   int rc;
   if ((rc = check_dims(dims))) return rc;
   if (!per_expert) return fail(K3MOE_EINVAL, "per_expert is NULL");
-  if ((rc = check_packed(*dims, K3MOE_BF16))) return rc;
+  if ((rc = check_packed(*dims, 1, K3MOE_BF16))) return rc;
   const size_t d = (size_t)dims->d_model, f = (size_t)dims->d_ff;
   per_expert->gate_q = per_expert->up_q = f * d / 2;
   per_expert->down_q = d * f / 2;
@@ -924,8 +936,8 @@ int k3moe_layer_forward_packed(const k3moe_dims* dims, int32_t T, const void* x,
   int rc;
   if ((rc = check_layer(dims, T, x, x_dtype, w_router, experts, blk, y))) return rc;
   if (T == 0) return K3MOE_OK;
-  if ((rc = check_packed(*dims, blk ? K3MOE_BF16 : x_dtype))) return rc;
-  if (blk) return fail(K3MOE_EUNSUPPORTED, "block mode is not available on the packed layout");
+  // block mode feeds the experts the fp32 RMSNorm output
+  if ((rc = check_packed(*dims, T, blk ? K3MOE_F32 : x_dtype))) return rc;
   if (((reinterpret_cast<uintptr_t>(experts->gate_s) | reinterpret_cast<uintptr_t>(experts->up_s) |
         reinterpret_cast<uintptr_t>(experts->down_s)) & 7u))
     return fail(K3MOE_EINVAL, "packed scale arrays must be 8-byte aligned");

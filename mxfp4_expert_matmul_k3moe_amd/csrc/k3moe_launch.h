@@ -145,9 +145,10 @@ hipError_t launch_pack_matrix(int R, int K, int n_mat, const uint8_t* q, const u
 // ---- block extras (block.hip) ---------------------------------------------------------
 hipError_t launch_rmsnorm(int T, int d, const float* h, const uint16_t* gamma, float eps,
                           float* xhat, hipStream_t s);
-// Dense bf16 SwiGLU: out [T][d] = Wd (silu(Wg x) * (Wu x)); hbuf [T][f] scratch.
+// Dense bf16 SwiGLU: out [T][d] = Wd (silu(Wg x) * (Wu x)); hbuf [T][f] scratch. Each GEMV
+// runs on at most max_blocks blocks (0: one per row group of 4 waves).
 hipError_t launch_dense_swiglu(int T, int d, int f, const float* x, const uint16_t* wg,
                                const uint16_t* wu, const uint16_t* wd, float* hbuf,
-                               float* out, hipStream_t s);
+                               float* out, hipStream_t s, int max_blocks = 0);
 
 }  // namespace k3moe

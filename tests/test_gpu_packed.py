@@ -17,7 +17,7 @@ import torch
 import mxfp4_expert_matmul_k3moe_amd as k3
 import oracle
 from k3gen import device as gdev
-from k3gen.workloads import BATCHED, DECODE, PREFILL, Workload
+from k3gen.workloads import BATCHED, DECODE, PREFILL, STACK8, Workload
 from oracle import harness
 
 from test_gpu_parity import ELEM_FACTOR, K3_TOL, TOL, check_routing, rel_elem, rel_l2, \
@@ -166,6 +166,69 @@ def test_hot_tokens_policy_keeps_results(dev):
         k3.set_hot_tokens(16)
     for n in (16, 9):
         assert torch.equal(got[n][0], got[0][0]) and torch.equal(got[n][1], got[0][1]), n
+
+
+def run_packed_block(w: Workload, h: torch.Tensor, layer: int, packed, dev):
+    """One block (RMSNorm -> routed MoE on packed experts + shared expert -> residual) on the
+    fp32 residual h [1][d]."""
+    dims = k3.make_dims(w.d, w.f, w.E, w.k)
+    b = gdev.block_extras(w, layer, dev)
+    blk = k3.BlockWeights(b["rms_gamma"], b["sh_gate"], b["sh_up"], b["sh_down"], 1e-6)
+    ids = torch.empty((1, w.k), dtype=torch.int32, device=dev)
+    y = k3.layer_forward_packed(dims, h, gdev.router_w(w, layer, dev), gdev.bias(w, layer, dev),
+                                packed, blk, ids=ids)
+    torch.cuda.synchronize()
+    return y, ids.cpu().numpy()
+
+
+def packed_layer(w: Workload, layer: int, dev):
+    """Layer `layer`'s experts in the packed layout (the row-major copy freed)."""
+    dims = k3.make_dims(w.d, w.f, w.E, w.k)
+    ex = gdev.experts(w, layer, dev)
+    pk = k3.pack_experts(dims, k3.MxExperts(**ex))
+    torch.cuda.synchronize()
+    del ex
+    return pk
+
+
+def test_packed_block_mode_small_chain(dev):
+    """Block mode on packed experts (one token, fp32 residual): three chained blocks with
+    packed-layout shapes (two 8-step chunks of d, 8 down steps) against the oracle's stack."""
+    w = Workload("pk_block", 67, d=2048, f=1024, E=16, k=4, T=1, layers=3, block=True)
+    say("packed block mode, 3 chained blocks d=2048 f=1024")
+    h0 = w.resid0()
+    ref = harness.run_stack(w, h0)
+    h = torch.from_numpy(h0).to(dev)
+    for layer in range(w.layers):
+        h, ids = run_packed_block(w, h, layer, packed_layer(w, layer, dev), dev)
+        assert np.array_equal(ids, ref["ids"][layer]), f"routing differs at layer {layer}"
+    yg = h.cpu().double().numpy()
+    err, el = rel_l2(yg, ref["y"]), rel_elem(yg, ref["y"])
+    print(f"    max rel L2 err {err.max():.3e}, max elem err / rms {el.max():.3e}", flush=True)
+    assert err.max() <= 1e-4 and el.max() <= ELEM_FACTOR * 1e-4
+
+
+def test_packed_stack8_k3(dev):
+    """The 8-block K3 stack on packed experts (fp32 tokens on the one-token kernels), one
+    token, routed exactly as the oracle at every block; the final residual within the K3 bar
+    in L2 and element-wise."""
+    w = STACK8
+    say("packed 8 stacked blocks, T=1, ~126 GB of packed MXFP4 experts resident")
+    h0 = w.resid0()
+    ref = harness.run_stack(w, h0)
+    layers = [packed_layer(w, l, dev) for l in range(w.layers)]
+    torch.cuda.empty_cache()
+    h = torch.from_numpy(h0).to(dev)
+    for l in range(w.layers):
+        h, ids = run_packed_block(w, h, l, layers[l], dev)
+        assert np.array_equal(ids, ref["ids"][l]), f"routing differs at layer {l}"
+    yg = h.cpu().double().numpy()
+    err, el = rel_l2(yg, ref["y"]), rel_elem(yg, ref["y"])
+    print(f"    max rel L2 err after 8 blocks {err.max():.3e}, max elem err / rms {el.max():.3e}",
+          flush=True)
+    assert err.max() <= K3_TOL and el.max() <= ELEM_FACTOR * K3_TOL
+    del layers
+    torch.cuda.empty_cache()
 
 
 def test_packed_batched_k3(dev):
