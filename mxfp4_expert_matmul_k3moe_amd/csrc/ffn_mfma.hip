@@ -17,6 +17,7 @@
 // C 语言 CPU 推理实战" (chenxutan.com/d/5901.html) §1.2, §2.3.
 #include <atomic>
 #include <type_traits>
+#include <utility>
 
 #include "k3moe_device.h"
 #include "k3moe_launch.h"
@@ -263,6 +264,14 @@ __device__ __forceinline__ void mx_gateup_tile_sr(const MfmaArgs& a, uint8_t* ld
 template <int MT, bool PK, int CP = kCpNormal>
 __device__ __forceinline__ void mx_gateup_tile_rw(const MfmaArgs& a, uint8_t* lds, int e, int p0,
                                                   int pn, int nb);
+template <int MT, int NK, int CP>
+__device__ __forceinline__ void mx_down_tile_rw(const MfmaArgs& a, uint8_t* lds, int e, int p0,
+                                                int pn, int nb);
+// f(integral_constant<int, I>) for I = 0, 1, ... in order (a compile-time unrolled loop)
+template <int... I, class F>
+__device__ __forceinline__ void for_each_const(std::integer_sequence<int, I...>, F&& f) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
 template <int MT, bool SG4, bool PK = false, int CP = kCpNormal>
 __device__ __forceinline__ void mx_down_tile(const MfmaArgs& a, uint8_t* lds, int e, int p0, int pn,
                                              int nb);
@@ -316,7 +325,22 @@ __global__ __launch_bounds__(512) void mfma_ffn_kernel(MfmaArgs a) {
     }
     return;
   }
-  if (a.packed) {
+  if (a.packed && a.f % 512 == 0 && a.f <= 16 * BK) {
+    // register-fed weights, compile-time K steps (f = 512, 1024, 1536 or 2048)
+    switch (a.f / BK) {
+#define K3_DRW(NKV)                                                                     \
+  case NKV:                                                                              \
+    if (cnt < a.hot_tokens) mx_down_tile_rw<1, NKV, kCpStream>(a, lds, e, p0, pn, nb);   \
+    else if (cnt <= 16) mx_down_tile_rw<1, NKV, kCpNormal>(a, lds, e, p0, pn, nb);       \
+    else if (cnt <= 32) mx_down_tile_rw<2, NKV, kCpNormal>(a, lds, e, p0, pn, nb);       \
+    else mx_down_tile_rw<4, NKV, kCpNormal>(a, lds, e, p0, pn, nb);                      \
+    break;
+      K3_DRW(4) K3_DRW(8) K3_DRW(12) K3_DRW(16)
+#undef K3_DRW
+      default:
+        break;
+    }
+  } else if (a.packed) {
     if (cnt < a.hot_tokens) mx_down_tile<1, true, true, kCpStream>(a, lds, e, p0, pn, nb);
     else if (cnt <= 16) mx_down_tile<1, true, true>(a, lds, e, p0, pn, nb);
     else if (cnt <= 32) mx_down_tile<2, true, true>(a, lds, e, p0, pn, nb);
@@ -990,6 +1014,167 @@ __device__ __forceinline__ void mx_down_tile(const MfmaArgs& a, uint8_t* lds, in
       }
     }
   }
+
+  // epilogue: lane (ln, g) holds output rows 4 g .. 4 g + 3 of each tile for pair row ln
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int row = 16 * m + ln;
+    if (row >= pn) continue;
+    const int pair = a.rows[p0 + row];
+    if (pair < 0 || pair >= P) continue;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int i0 = nb * 512 + wave * 64 + nt * 16 + 4 * g;  // d % 4 == 0: all four or none
+      if (i0 < a.d) *reinterpret_cast<f32x4*>(a.z_out + (size_t)pair * a.d + i0) = acc[m][nt];
+    }
+  }
+}
+
+// Down projection of one tile on the packed layout with the weights fed straight into the
+// MFMA's FP4 operand registers: each wave owns NT 16-row tiles of D (64 output rows; the
+// block 512), and for K step ks loads its tiles' 1-KB steps with buffer loads into a ring of
+// S steps, issued S - 1 steps ahead. Only h passes through LDS: each stage holds the tile's
+// three E4M3 terms of h for one K step (MT 16-pair subtiles x 3 terms x 2 x 1 KB) and their
+// E8M0 words, S = 4 stages. Every wave issues the same number of h copies per step (the
+// last copies are repeated by the waves that have no block of their own: same source, same
+// LDS bytes), so each wave's wait for step ks is one compile-time count: its own loads issued
+// after those of step ks (steps ks + 1 .. ks + S - 2, and the next scale entries when they
+// were loaded in between), then a barrier for the other waves' copies. The K loop is
+// unrolled over its NK steps. The weights' scale bytes come 8 steps at a time, 8 bytes per
+// lane and tile (the packed scale entry), loaded one chunk ahead.
+template <int MT, int NK, int CP>
+__device__ __forceinline__ void mx_down_tile_rw(const MfmaArgs& a, uint8_t* lds, int e, int p0,
+                                                int pn, int nb) {
+  constexpr int S = 4;
+  constexpr int ADATA = MT * 6 * 1024;            // [m][term][half] 1-KB blocks
+  constexpr int SB = ADATA + MT * 256;            // + scale words [m][term x 16 pairs]
+  static_assert(S * SB <= kLdsBytes, "h stages exceed LDS");
+  constexpr int NA = (6 * MT + kWaves - 1) / kWaves;  // h blocks per wave and step
+  constexpr int OPS = NT + NA + 1;                 // loads per wave and step
+  constexpr int NCH = (NK + 7) / 8;                // packed scale entries per tile
+  static_assert(NK >= S - 1, "the prologue issues S - 1 steps");
+  const int P = a.T * a.k;
+  const int K = a.f, NR = a.d, KB = K >> 5;
+  const size_t F = (size_t)K;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ln = lane & 15, g = lane >> 4;
+
+  // h term rows (x3) of this lane's pair in each M subtile; rows past the tile's end repeat
+  // its last row (their results are never stored)
+  size_t hrow[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) hrow[m] = (size_t)(p0 + min(16 * m + ln, pn - 1)) * 3;
+  const uint8_t* hlane = a.h8 + 32 * (g >> 1) + 16 * (g & 1);
+  // this wave's h copies: blocks b = wave + 8 j (block b = m 6 + 2 t + hh); past 6 MT, the
+  // copy of block b mod 6 MT again. Scale words: subtile wave mod MT, term lane >> 4 (the
+  // fourth group repeats term 2).
+  const int sw_m = wave % MT, sw_t = min(lane >> 4, 2);
+  const uint8_t* swsrc = a.hs8 + ((size_t)(p0 + min(16 * sw_m + ln, pn - 1)) * 3 + sw_t) * KB;
+  const uint8_t* hsrc[NA];
+  int hdst[NA];
+#pragma unroll
+  for (int j = 0; j < NA; ++j) {
+    const int b = (wave + kWaves * j) % (6 * MT);
+    const int m = b / 6, t = (b % 6) >> 1, hh = b & 1;
+    hsrc[j] = hlane + (hrow[m] + t) * F + 64 * hh;
+    hdst[j] = b * 1024;
+  }
+  // expert e's D in the packed layout: tile t, step ks at (t NK + ks) KB, lane order; scale
+  // chunk c of tile t at (t NCH + c) 512 B, 8 bytes per lane
+  const size_t qb = (size_t)NR * (K >> 1), sbytes = (size_t)(NR / 16) * NCH * 512;
+  const __amdgpu_buffer_rsrc_t rq = buf_rsrc(a.q0 + (size_t)e * qb, (uint32_t)qb);
+  const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a.s0 + (size_t)e * sbytes, (uint32_t)sbytes);
+  uint32_t vq[NT], vs[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const uint32_t t = (uint32_t)min(nb * 32 + wave * 4 + nt, NR / 16 - 1);
+    vq[nt] = (t * (uint32_t)NK * 64u + (uint32_t)lane) * 16u;
+    vs[nt] = (t * (uint32_t)NCH * 64u + (uint32_t)lane) * 8u;
+  }
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  u32x4 wr[S][NT];
+  u32x2 scur[NT], snxt[NT];
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // step ks: its weights (ring slot ks mod S), then its h copies into stage ks mod S
+  auto issue = [&](auto ks_c) {
+    constexpr int KS = decltype(ks_c)::value;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      wr[KS % S][nt] = __builtin_amdgcn_raw_buffer_load_b128(rq, vq[nt], KS * 1024, CP);
+    asm volatile("" ::: "memory");
+    uint8_t* st = lds + (KS % S) * SB;
+#pragma unroll
+    for (int j = 0; j < NA; ++j) dma16(hsrc[j] + KS * BK, st + hdst[j]);
+    dma4(swsrc + 4 * KS, st + ADATA + sw_m * 256);
+    asm volatile("" ::: "memory");
+  };
+  auto sload = [&](int nt, int c) {
+    return __builtin_amdgcn_raw_buffer_load_b64(rs, vs[nt], 512 * c, CP);
+  };
+  auto step = [&](auto ks_c) {
+    constexpr int KS = decltype(ks_c)::value;
+    constexpr int U = KS & 7, C = KS >> 3;
+    // loads issued after step KS's: steps KS + 1 .. KS + S - 2 (those issued) and the scale
+    // entries of chunk C + 1 when they were loaded (at step 8 C) after step KS's loads
+    constexpr int LATER = (NK - 1 - KS) < (S - 2) ? (NK - 1 - KS) : (S - 2);
+    constexpr int EXTRA = (U >= 1 && U <= S - 2 && C + 1 < NCH) ? NT : 0;
+    wait_vm_known<LATER * OPS + EXTRA>();
+    if constexpr (U == 0 && C > 0) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) scur[nt] = snxt[nt];  // loaded 8 steps ago
+    }
+    barrier_no_fence();
+    if constexpr (U == 0 && C + 1 < NCH) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) snxt[nt] = sload(nt, C + 1);
+      asm volatile("" ::: "memory");
+    }
+    if constexpr (KS + S - 1 < NK) issue(std::integral_constant<int, KS + S - 1>{});
+    const uint8_t* st = lds + (KS % S) * SB;
+    i32x8 wop[NT];
+    int wsc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      // an FP4 operand takes the low four registers of the tuple; the upper four are left
+      // undefined so that no zero registers are kept per tile
+      typedef int i32x4v __attribute__((ext_vector_type(4)));
+      const i32x4v wi = __builtin_bit_cast(i32x4v, wr[KS % S][nt]);
+      wop[nt] = __builtin_shufflevector(wi, wi, 0, 1, 2, 3, -1, -1, -1, -1);
+      wsc[nt] = (int)((scur[nt][U >> 2] >> (8 * (U & 3))) & 0xFFu);
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        const uint8_t* xb = st + ((m * 3 + t) * 2) * 1024 + lane * 16;
+        const u32x4 h0 = *reinterpret_cast<const u32x4*>(xb), h1 = *reinterpret_cast<const u32x4*>(xb + 1024);
+        const i32x8 xop = {(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
+        const int xsc = st[ADATA + m * 256 + (ln + 16 * t) * 4 + g];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          acc[m][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wop[nt], xop, acc[m][nt], 4, 0, 0,
+                                                                         wsc[nt], 0, xsc);
+          // ties each MFMA to this point, and the next term's LDS reads below it: left free,
+          // the scheduler gathers the MFMAs of many steps at the end and holds every operand
+          // read before them
+          asm volatile("" : "+v"(acc[m][nt])::"memory");
+        }
+      }
+    }
+  };
+
+  // prologue: scale chunk 0 (taken over at step 0), then steps 0 .. S - 2
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) scur[nt] = sload(nt, 0);
+  asm volatile("" ::: "memory");
+  for_each_const(std::make_integer_sequence<int, S - 1>{}, issue);
+  for_each_const(std::make_integer_sequence<int, NK>{}, step);
 
   // epilogue: lane (ln, g) holds output rows 4 g .. 4 g + 3 of each tile for pair row ln
 #pragma unroll
