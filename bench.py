@@ -229,11 +229,13 @@ def dtype_of(w) -> str:
 
 def use_packed(args, w) -> bool:
     """Expert layout of a layer leg: --layout if given (the default line's prefill leg
-    follows it too), else the packed tile layout wherever its grouped GEMMs run (more than
-    one token) and the row-major layout for one token."""
+    follows it too), else the packed tile layout wherever the shape allows it (d % 1024 and
+    f % 512; for one token also f <= 1536 and k <= 16, the one-token kernels' range)."""
     if args.layout:
         return args.layout == "packed"
-    return w.T > 1 and w.d % 1024 == 0 and w.f % 512 == 0
+    if w.d % 1024 or w.f % 512:
+        return False
+    return w.T > 1 or (w.f <= 1536 and w.k <= 16)
 
 
 def spread(vals):
@@ -356,7 +358,8 @@ def decode_like_fields(w, m, traffic, packed=False):
     dn_bytes = m["sel"] * w.d * (w.f // 2 + w.f // 32)
     ach = gu_bytes / (m["gate_up_ms"] * 1e-3) / 1e9
     if w.T == 1:
-        kname = ("gateup_decode_packed_kernel (MXFP4 gate/up GEMV + SwiGLU, packed tile layout)"
+        kname = ("gateup_decode_packed_ks_kernel (MXFP4 gate/up GEMV + SwiGLU, packed tile "
+                 "layout, one wave per 8-step K chunk)"
                  if packed else "gateup_decode_kernel (MXFP4 gate/up GEMV + SwiGLU)")
     elif w.T >= MFMA_MIN_TOKENS or packed:
         kname = grouped_label(packed)
@@ -437,8 +440,7 @@ def main() -> int:
                          "(0..16; the library's default is 16)")
     ap.add_argument("--layout", choices=["rowmajor", "packed"], default=None,
                     help="expert weight layout of a single-workload run (default: packed "
-                         "for the grouped-GEMM workloads and the 8-block stack, row-major for "
-                         "the one-token layer)")
+                         "wherever the shape allows it)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one HIP graph per token set (captured on the "
                          "caller's stream) instead of eager calls")
@@ -694,7 +696,7 @@ def bench_stack(args, w) -> int:
                    "hip_graph": bool(args.graph),
                    "expert_layout": "packed" if packed else "row-major"},
         "roofline": {"bound": "hbm",
-                     "kernel": ("gateup_decode_packed_kernel<fp32 x> (MXFP4 gate/up GEMV + "
+                     "kernel": ("gateup_decode_packed_ks_kernel<fp32 x> (MXFP4 gate/up GEMV + "
                                 "SwiGLU, packed tile layout)" if packed else
                                 "gateup_decode_kernel<fp32 x> (MXFP4 gate/up GEMV + SwiGLU)"),
                      "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -846,7 +848,7 @@ def _kernel_hash(packed=False) -> str:
         src = fh.read()
     h = hashlib.sha256()
     if packed:
-        h.update(_function_text(src, "void gateup_decode_packed_kernel(").encode())
+        h.update(_function_text(src, "void gateup_decode_packed_ks_kernel(").encode())
         h.update(_function_text(src, "hipError_t launch_gateup_decode_packed(").encode())
     else:
         h.update(_function_text(src, "void gateup_decode_kernel(").encode())

@@ -215,13 +215,13 @@ K3MOE_API int k3moe_pack_experts(const k3moe_dims* dims, const k3moe_mx_experts*
                                  const k3moe_mx_experts* dst, void* stream);
 
 /* k3moe_layer_forward with the experts in the packed layout (same arguments and results to
- * rounding). Activations bf16; for one token (T == 1, d_ff <= 1536, top_k <= 16) also fp32,
- * and block mode (whose experts take the fp32 RMSNorm output). Every weight tile step is read as 1 KB
- * contiguous. One token (T == 1, d_ff <= 1536, top_k <= 16): gate/up as a GEMV, one wave per
- * (slot, 16-row tile) in fp32, then the one-token down kernel on the block-scaled MFMA (h as
- * three FP8 terms) with the gate-weighted sum in slot order. More tokens: grouped GEMMs on the
- * block-scaled FP4 x FP8 MFMA (token as two FP8 terms, h as three). K3MOE_EUNSUPPORTED for
- * shapes or activations outside the above. */
+ * rounding). Every weight tile step is read as 1 KB contiguous. Activations are bf16; for one
+ * token (T == 1, d_ff <= 1536, top_k <= 16) also fp32, and block mode (whose experts take the
+ * fp32 RMSNorm output). One token: gate/up as a GEMV in fp32, one block per (slot, 16-row
+ * tile) and one wave per 8 K steps, then the one-token down kernel on the block-scaled MFMA
+ * (h as three FP8 terms) with the gate-weighted sum in slot order. More tokens: grouped GEMMs
+ * on the block-scaled FP4 x FP8 MFMA (token as two FP8 terms, h as three).
+ * K3MOE_EUNSUPPORTED for shapes or activations outside the above. */
 K3MOE_API int k3moe_layer_forward_packed(const k3moe_dims* dims, int32_t T, const void* x,
                                          int x_dtype, const uint16_t* w_router,
                                          const float* logit_bias,

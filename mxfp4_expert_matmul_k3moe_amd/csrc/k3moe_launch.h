@@ -90,9 +90,9 @@ hipError_t launch_down_decode_mfma(int d, int f, int k, const MxPtrs& w, const f
                                    const float* gates, const float* resid, const float* shared,
                                    float* y, uint16_t* y_bf16, int n_cu, hipStream_t s,
                                    bool packed = false);
-// One token, packed tile layout (d % 1024 == 0, f % 16 == 0): h = silu(G x) * (U x) of every
-// slot as fp32 into h [k][f] at the slot's bucket position; one wave per (slot, 16-row tile).
-// x is bf16 (xf32 == 0) or fp32 [d].
+// One token, packed tile layout (d % 1024 == 0, d <= 16384, f % 16 == 0): h = silu(G x) * (U x)
+// of every slot as fp32 into h [k][f] at the slot's bucket position; one block per (slot,
+// 16-row tile), one wave per 8-step K chunk. x is bf16 (xf32 == 0) or fp32 [d].
 hipError_t launch_gateup_decode_packed(int d, int f, int k, const void* x, int xf32,
                                        const MxPtrs& w, const int32_t* pair_pos,
                                        const int32_t* pair_exp, float* h, hipStream_t s);
