@@ -652,8 +652,12 @@ hipError_t launch_gateup_decode_packed(int d, int f, int k, const void* x, int x
   const int nch = d / 1024;
   if (nch < 1 || nch > kPkKsMaxWaves) return hipErrorInvalidValue;
   const size_t lds = (size_t)d * (xf32 ? 4 : 2);
-  if (xf32) gateup_decode_packed_ks_kernel<true><<<items, 64 * nch, lds, s>>>(a);
-  else gateup_decode_packed_ks_kernel<false><<<items, 64 * nch, lds, s>>>(a);
+  if (xf32)
+    launch_timed(gateup_decode_packed_ks_kernel<true>, dim3(items), dim3(64 * nch), (uint32_t)lds,
+                 s, a);
+  else
+    launch_timed(gateup_decode_packed_ks_kernel<false>, dim3(items), dim3(64 * nch),
+                 (uint32_t)lds, s, a);
   return hipGetLastError();
 }
 
@@ -677,7 +681,8 @@ hipError_t launch_gateup_decode(int d, int f, int k, const void* x, int xf32, co
   if (grid > cap) grid = cap;
   if (bpl > kMaxDecodeBpl) return hipErrorInvalidValue;  // see gateup_decode_supported
   const size_t lds = (size_t)d * (xf32 ? 4 : 2);
-#define K3_GD(XF, B) gateup_decode_kernel<XF, B><<<grid, 256, lds, s>>>(a)
+#define K3_GD(XF, B) \
+  launch_timed(gateup_decode_kernel<XF, B>, dim3(grid), dim3(256), (uint32_t)lds, s, a)
 #define K3_GD_B(XF)                   \
   switch (bpl) {                      \
     case 1: K3_GD(XF, 1); break;      \

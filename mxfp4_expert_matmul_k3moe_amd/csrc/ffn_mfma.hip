@@ -1542,7 +1542,7 @@ hipError_t launch_gateup_mfma(int T, int d, int f, int E, int k, const uint16_t*
   a.h8 = h8;
   a.hs8 = hs8;
   dim3 grid((unsigned)(mfma_mtiles_bound(T, E, k) * a.nblk_n));
-  mfma_ffn_kernel<true><<<grid, 512, 0, s>>>(a);
+  launch_timed(mfma_ffn_kernel<true>, grid, dim3(512), 0u, s, a);
   return hipGetLastError();
 }
 
@@ -1570,7 +1570,7 @@ hipError_t launch_down_mfma(int T, int d, int f, int E, int k, const MxPtrs& w,
   a.nblk_n = (d + 511) / 512;
   a.z_out = z;
   dim3 grid((unsigned)(mfma_mtiles_bound(T, E, k) * a.nblk_n));
-  mfma_ffn_kernel<false><<<grid, 512, 0, s>>>(a);
+  launch_timed(mfma_ffn_kernel<false>, grid, dim3(512), 0u, s, a);
   return hipGetLastError();
 }
 
@@ -1597,12 +1597,12 @@ hipError_t launch_down_decode_mfma(int d, int f, int k, const MxPtrs& w, const f
   if (a.rpb < 16) a.rpb = 16;
   const dim3 grid((unsigned)((d + a.rpb - 1) / a.rpb)), block((unsigned)(64 * k));
   switch (f / BK) {
-#define K3_DM(N)                                                   \
-  case N:                                                          \
-    if (packed)                                                    \
-      down_decode_mfma_kernel<N, true><<<grid, block, 0, s>>>(a);  \
-    else                                                           \
-      down_decode_mfma_kernel<N, false><<<grid, block, 0, s>>>(a); \
+#define K3_DM(N)                                                              \
+  case N:                                                                     \
+    if (packed)                                                               \
+      launch_timed(down_decode_mfma_kernel<N, true>, grid, block, 0u, s, a);  \
+    else                                                                      \
+      launch_timed(down_decode_mfma_kernel<N, false>, grid, block, 0u, s, a); \
     break;
     K3_DM(1) K3_DM(2) K3_DM(3) K3_DM(4) K3_DM(5) K3_DM(6)
     K3_DM(7) K3_DM(8) K3_DM(9) K3_DM(10) K3_DM(11) K3_DM(12)

@@ -14,6 +14,10 @@
 #include "k3moe_cache.h"
 #include "k3moe_launch.h"
 
+namespace k3moe {
+thread_local LaunchTiming* t_launch_timing = nullptr;
+}  // namespace k3moe
+
 namespace {
 
 thread_local std::string g_err;
@@ -22,16 +26,25 @@ thread_local std::string g_err;
 thread_local int g_probe_which = 0;
 thread_local hipEvent_t g_probe_start = nullptr, g_probe_stop = nullptr;
 
-struct Probe {  // records around one launch when armed for `which`
+// Times one launch when armed for `which`: the launcher stamps the kernel's own begin and end
+// (launch_timed); a launcher that does not time its kernel leaves events recorded around
+// its launches.
+struct Probe {
   int which;
   hipStream_t s;
   bool armed;
+  k3moe::LaunchTiming lt;
   Probe(int w, hipStream_t st) : which(w), s(st), armed(g_probe_which == w) {
-    if (armed) (void)hipEventRecord(g_probe_start, s);
+    if (armed) {
+      (void)hipEventRecord(g_probe_start, s);
+      lt = {g_probe_start, g_probe_stop, false};
+      k3moe::t_launch_timing = &lt;
+    }
   }
   ~Probe() {
     if (armed) {
-      (void)hipEventRecord(g_probe_stop, s);
+      k3moe::t_launch_timing = nullptr;
+      if (!lt.used) (void)hipEventRecord(g_probe_stop, s);
       g_probe_which = 0;
     }
   }

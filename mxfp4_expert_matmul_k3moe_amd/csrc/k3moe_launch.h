@@ -1,11 +1,35 @@
 // k3moe_launch.h — host-side launch wrappers of the gfx950 kernels (internal).
 // Every wrapper enqueues on `stream` and returns hipGetLastError().
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace k3moe {
+
+// Event pair of k3moe_time_next_kernel, set on the calling thread while the probed launch is
+// being enqueued. The launcher of a timed kernel passes the events to hipExtLaunchKernel,
+// which stamps the kernel's own begin and end (events recorded around the launch would also
+// take in the wait for the kernel before it), and marks them used.
+struct LaunchTiming {
+  hipEvent_t start, stop;
+  bool used;
+};
+extern thread_local LaunchTiming* t_launch_timing;
+
+// kernel<<<grid, block, lds, s>>>(args...), with the pending timing events if there are any.
+template <typename... Args, typename F>
+inline void launch_timed(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t s,
+                         Args... args) {
+  LaunchTiming* lt = t_launch_timing;
+  if (lt && !lt->used) {
+    lt->used = true;
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, lt->start, lt->stop, 0u, args...);
+  } else {
+    kernel<<<grid, block, lds, s>>>(args...);
+  }
+}
 
 // ---- router (router.hip) -------------------------------------------------------
 // Rows of W handled per partial-sum chunk of the small-T router.
