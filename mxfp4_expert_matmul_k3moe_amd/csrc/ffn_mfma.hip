@@ -1398,6 +1398,18 @@ __global__ __launch_bounds__(1024) void down_decode_mfma_kernel(DownDecMArgs a) 
     }
   };
   load_tile(r0);  // every block has at least one row
+  // residual and shared-expert values of this thread's row in the current tile, requested a
+  // tile ahead of the combine that adds them (behind that tile's weight loads, so waiting for
+  // them leaves the next tile's weights in flight)
+  float res_r = 0.0f, res_s = 0.0f;
+  auto fetch_res = [&](int rt) {
+    if (a.resid && tid < 16) {
+      const int r = min(rt + tid, rb1 - 1);
+      res_r = a.resid[r];
+      res_s = a.shared ? a.shared[r] : 0.0f;
+    }
+  };
+  fetch_res(r0);
 
   // 2. three E4M3 terms of h with one E8M0 scale per term for the whole slot: 2^(s0-127)
   //    puts the slot maximum in [128, 256), term t has scale s0 - 4t. RNE to E4M3 leaves a
@@ -1507,12 +1519,13 @@ __global__ __launch_bounds__(1024) void down_decode_mfma_kernel(DownDecMArgs a) 
       float s2 = 0.0f;
       for (int j = 0; j < a.k; ++j) s2 = fmaf(gsh[j], zb[j][tid], s2);
       float out = s2;
-      if (a.resid) out = (a.resid[r] + (a.shared ? a.shared[r] : 0.0f)) + s2;
+      if (a.resid) out = (res_r + res_s) + s2;
       a.y[r] = out;
       if (a.y_bf16) a.y_bf16[r] = f32_to_bf16_rne(out);
     }
     if (!more) break;
     r0 = next;
+    fetch_res(r0);
   }
 }
 

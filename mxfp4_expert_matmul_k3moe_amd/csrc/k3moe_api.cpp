@@ -784,6 +784,27 @@ int run_layer(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
     xin = xhat;
     xf32 = 1;
   }
+  int32_t* offs = w.at<int32_t>(R_OFFS);
+  int32_t* rows = w.at<int32_t>(R_ROWS);
+  const k3moe::BucketOut bo = bucket_out(w, offs, rows);
+  // One token: the shared expert's two GEMVs ride in the router and top-k launches (which
+  // also write the token's bucket), all on `s`.
+  if (blk && T == 1 &&
+      k3moe::route_shared_supported(d, dims->n_experts, dims->top_k, w_router)) {
+    float* ssh = w.at<float>(R_SSH);
+    {
+      Probe probe(K3MOE_KERNEL_ROUTER, s);
+      rc = hip_check(k3moe::launch_route_shared(
+                         d, dims->d_ff, dims->n_experts, dims->top_k,
+                         static_cast<const float*>(xin), w_router, logit_bias,
+                         w.at<double>(R_PART), blk->sh_gate, blk->sh_up, blk->sh_down,
+                         w.at<float>(R_HSH), ssh, ids, gates, bo, 0, s),
+                     "router + shared expert");
+    }
+    if (rc) return rc;
+    return run_ffn(*dims, T, xin, xf32, experts, offs, rows, gates,
+                   static_cast<const float*>(x), ssh, y, y_bf16, w, s, nullptr, packed);
+  }
   // The shared expert needs only xhat: it runs on a side stream, overlapping the router,
   // top-k and gate/up, and the launch that adds it into y waits for it (per-call events).
   const float* resid = nullptr;
@@ -814,9 +835,6 @@ int run_layer(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
     resid = static_cast<const float*>(x);
     shared = ssh;
   }
-  int32_t* offs = w.at<int32_t>(R_OFFS);
-  int32_t* rows = w.at<int32_t>(R_ROWS);
-  const k3moe::BucketOut bo = bucket_out(w, offs, rows);
   // a single token's bucket is written by the top-k kernel itself
   if ((rc = run_router(*dims, T, xin, xf32, w_router, logit_bias, ids, gates, w, s,
                        T == 1 ? &bo : nullptr)))

@@ -72,6 +72,18 @@ struct BucketOut {
 hipError_t launch_route_topk(int T, int E, int k, const double* part, int nsum,
                              const float* bias, int32_t* ids, float* gates,
                              const BucketOut* bucket1, hipStream_t s);
+// Block mode, one token: the router GEMV (fp32 token x) and the shared expert's gate/up GEMV
+// (hsh = silu(G x) * (U x)) in one launch, then the top-k with the token's bucket and the
+// shared expert's down GEMV (ssh = D hsh) in a second; every value as from the standalone
+// kernels. Needs route_shared_supported (E % 8 == 0, 256 < E <= 4096, 16-byte aligned router
+// weights); gateup_blocks > 0 caps the shared gate/up blocks.
+bool route_shared_supported(int d, int E, int k, const uint16_t* w_router);
+hipError_t launch_route_shared(int d, int f, int E, int k, const float* x,
+                               const uint16_t* w_router, const float* bias, double* part,
+                               const uint16_t* sh_gate, const uint16_t* sh_up,
+                               const uint16_t* sh_down, float* hsh, float* ssh, int32_t* ids,
+                               float* gates, const BucketOut& bucket1, int gateup_blocks,
+                               hipStream_t s);
 hipError_t launch_bucket(int T, int E, int k, const int32_t* ids, const BucketOut& o,
                          uint32_t* hist, uint32_t* base, uint64_t* masks, hipStream_t s);
 // From caller-supplied offsets/rows (k3moe_expert_ffn): act, n_act, pair_pos, pair_exp.

@@ -7,6 +7,7 @@
 // Every product bf16*bf16 or bf16*fp32 is exact in fp64, and the sums are carried in
 // fp64, so the ranking is that of the exact logits barring ties closer than fp64
 // rounding.
+#include "gemv_bf16.h"
 #include "k3moe_device.h"
 #include "k3moe_launch.h"
 
@@ -89,20 +90,21 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(int T, int d, int E,
 // columns 8*(l%8) .. +7 of rows l/8, l/8 + 8, ... (16 rows per lane, all loads issued
 // before the first FMA). Row sums: per lane in row order, then a fixed xor tree over
 // the 8 lanes sharing a column group, then the four waves in order. Needs E % 8 == 0.
+// (chunk, cblk): the block's row chunk and column block (the grid's x and y). Needs 256
+// threads.
 template <bool XF32, int NT>
-__global__ __launch_bounds__(256) void router_gemv_vec_kernel(int T, int d, int E,
-                                                              const void* __restrict__ x,
-                                                              const uint16_t* __restrict__ w,
-                                                              double* __restrict__ part) {
+__device__ __forceinline__ void router_gemv_vec_block(int chunk, int cblk, int T, int d, int E,
+                                                      const void* __restrict__ x,
+                                                      const uint16_t* __restrict__ w,
+                                                      double* __restrict__ part) {
   constexpr int RPL = kRouterRows / 4 / 8;  // rows per lane (16)
   __shared__ double xs[kRouterRows][NT];
   __shared__ double wsum[4][NT][kRouterCols];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int chunk = blockIdx.x;
   const int k0 = chunk * kRouterRows;
   const int nrows = min(kRouterRows, d - k0);
   const int cg = lane & 7, rl = lane >> 3;
-  const int col0 = blockIdx.y * kRouterCols + cg * 8;
+  const int col0 = cblk * kRouterCols + cg * 8;
   const bool cv = col0 < E;
   u32x4 wv[RPL];
   if constexpr (NT > 1) {
@@ -219,13 +221,21 @@ __global__ __launch_bounds__(256) void router_gemv_vec_kernel(int T, int d, int 
     __syncthreads();
     for (int i = threadIdx.x; i < nt * kRouterCols; i += 256) {
       const int tt = i / kRouterCols, c = i % kRouterCols;
-      const int col = blockIdx.y * kRouterCols + c;
+      const int col = cblk * kRouterCols + c;
       if (col < E) {
         const double s = ((wsum[0][tt][c] + wsum[1][tt][c]) + wsum[2][tt][c]) + wsum[3][tt][c];
         part[((size_t)chunk * T + t0 + tt) * E + col] = s;
       }
     }
   }
+}
+
+template <bool XF32, int NT>
+__global__ __launch_bounds__(256) void router_gemv_vec_kernel(int T, int d, int E,
+                                                              const void* __restrict__ x,
+                                                              const uint16_t* __restrict__ w,
+                                                              double* __restrict__ part) {
+  router_gemv_vec_block<XF32, NT>(blockIdx.x, blockIdx.y, T, d, E, x, w, part);
 }
 
 // Several tokens: the K reduction stays inside each lane (no cross-lane sums). A work item
@@ -552,12 +562,13 @@ __device__ __forceinline__ double key_to_double(uint64_t kv) {
   return __longlong_as_double((long long)b);
 }
 
+// Token t of the block; WIDE needs 1024 threads, the other form at most 256.
 template <int KPT, bool WIDE>
-__global__ __launch_bounds__(WIDE ? 1024 : 256) void route_topk_kernel(int T, int E, int k,
-                                                          const double* __restrict__ part,
-                                                          int nsum, const float* __restrict__ bias,
-                                                          int32_t* __restrict__ ids,
-                                                          float* __restrict__ gates, Bucket1 bk) {
+__device__ __forceinline__ void route_topk_block(int t, int T, int E, int k,
+                                                 const double* __restrict__ part, int nsum,
+                                                 const float* __restrict__ bias,
+                                                 int32_t* __restrict__ ids,
+                                                 float* __restrict__ gates, Bucket1 bk) {
   __shared__ uint64_t keys[kMaxE];
   __shared__ uint64_t ckey[kMaxCand];
   __shared__ int cid[kMaxCand];
@@ -565,7 +576,6 @@ __global__ __launch_bounds__(WIDE ? 1024 : 256) void route_topk_kernel(int T, in
   __shared__ int w_ok[kTopkMaxWaves], w_cnt[kTopkMaxWaves], w_nan[kTopkMaxWaves];
   __shared__ double w_sum[kTopkMaxWaves];
   __shared__ int s_ids[kMaxSlots];
-  const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int NT = WIDE ? 256 : blockDim.x, nw = NT >> 6;
 
@@ -802,6 +812,61 @@ __global__ __launch_bounds__(WIDE ? 1024 : 256) void route_topk_kernel(int T, in
   }
 }
 
+template <int KPT, bool WIDE>
+__global__ __launch_bounds__(WIDE ? 1024 : 256) void route_topk_kernel(int T, int E, int k,
+                                                          const double* __restrict__ part,
+                                                          int nsum, const float* __restrict__ bias,
+                                                          int32_t* __restrict__ ids,
+                                                          float* __restrict__ gates, Bucket1 bk) {
+  route_topk_block<KPT, WIDE>(blockIdx.x, T, E, k, part, nsum, bias, ids, gates, bk);
+}
+
+// ---- block mode, one token: the routing launches carry the shared expert ------------------
+// The shared expert's two bf16 GEMVs need only the normalised token. Rather than running on
+// a second stream (whose fork and join cost more than the GEMVs themselves at this size),
+// they ride in the two routing launches, which are latency-bound and leave most of the HBM
+// bandwidth idle: blocks [0, nrb) of the first launch are the router GEMV's (chunk, column
+// block) in the standalone grid's order, the others walk the shared gate/up row groups
+// (silu(G x) * (U x) into hsh); block 0 of the second launch is the top-k's (with the token's
+// bucket), the others walk the shared down row groups (D hsh into ssh). Each part runs the
+// code of its standalone kernel, so every value is the same bit for bit.
+struct RouteSharedArgs {
+  int d, f, E, k;
+  const float* x;            // normalised token [d]
+  const uint16_t* w_router;  // [d][E]
+  double* part;              // router partial sums [nchunk][E]
+  int nchunk, nrb;           // router chunks; router blocks (chunks x column blocks)
+  const uint16_t *sh_gate, *sh_up, *sh_down;
+  float *hsh, *ssh;          // shared expert's h [f] and output [d]
+  const float* bias;
+  int32_t* ids;
+  float* gates;
+  Bucket1 bk;
+};
+
+__global__ __launch_bounds__(256) void router_shared_gateup_kernel(RouteSharedArgs a) {
+  extern __shared__ __attribute__((aligned(16))) f32x4 xs[];
+  const int b = blockIdx.x;
+  if (b < a.nrb) {  // block-uniform
+    router_gemv_vec_block<true, 1>(b % a.nchunk, b / a.nchunk, 1, a.d, a.E, a.x, a.w_router,
+                                   a.part);
+    return;
+  }
+  bf16_gemv_rows<true>(b - a.nrb, (int)gridDim.x - a.nrb, 1, a.f, a.d, a.x, a.sh_gate, a.sh_up,
+                       a.hsh, xs);
+}
+
+template <int KPT>
+__global__ __launch_bounds__(1024) void topk_shared_down_kernel(RouteSharedArgs a) {
+  extern __shared__ __attribute__((aligned(16))) f32x4 xs[];
+  if (blockIdx.x == 0) {
+    route_topk_block<KPT, true>(0, 1, a.E, a.k, a.part, a.nchunk, a.bias, a.ids, a.gates, a.bk);
+    return;
+  }
+  bf16_gemv_rows<false>((int)blockIdx.x - 1, (int)gridDim.x - 1, 1, a.d, a.f, a.hsh, a.sh_down,
+                        nullptr, a.ssh, xs);
+}
+
 }  // namespace
 
 int router_chunk_rows(int) { return kRouterRows; }
@@ -894,6 +959,42 @@ hipError_t launch_route_topk(int T, int E, int k, const double* part, int nsum,
   else if (kpt <= 4) route_topk_kernel<4, false><<<T, nt, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
   else if (kpt <= 8) route_topk_kernel<8, false><<<T, nt, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
   else route_topk_kernel<16, false><<<T, nt, 0, s>>>(T, E, k, part, nsum, bias, ids, gates, b);
+  return hipGetLastError();
+}
+
+bool route_shared_supported(int d, int E, int k, const uint16_t* w_router) {
+  return d % 8 == 0 && E % 8 == 0 && E > 256 && E <= kMaxE && k >= 1 && k <= kMaxSlots &&
+         k <= E && (reinterpret_cast<uintptr_t>(w_router) & 15u) == 0;
+}
+
+hipError_t launch_route_shared(int d, int f, int E, int k, const float* x,
+                               const uint16_t* w_router, const float* bias, double* part,
+                               const uint16_t* sh_gate, const uint16_t* sh_up,
+                               const uint16_t* sh_down, float* hsh, float* ssh, int32_t* ids,
+                               float* gates, const BucketOut& bucket1, int gateup_blocks,
+                               hipStream_t s) {
+  if (!route_shared_supported(d, E, k, w_router)) return hipErrorInvalidValue;
+  RouteSharedArgs a;
+  a.d = d; a.f = f; a.E = E; a.k = k; a.x = x; a.w_router = w_router; a.part = part;
+  a.nchunk = router_num_chunks(d);
+  a.nrb = a.nchunk * ((E + kRouterCols - 1) / kRouterCols);
+  a.sh_gate = sh_gate; a.sh_up = sh_up; a.sh_down = sh_down; a.hsh = hsh; a.ssh = ssh;
+  a.bias = bias; a.ids = ids; a.gates = gates;
+  a.bk = Bucket1{bucket1.offsets, bucket1.rows, bucket1.act, bucket1.n_act, bucket1.pair_pos,
+                 bucket1.pair_exp, bucket1.mtile_off};
+  // shared gate/up: one block per row group of 4 waves (gateup_blocks > 0 caps the count);
+  // shared down: one block per row group of the top-k block's 16 waves
+  const int rows_gu = gemv_group_rows(d, 4), rows_dn = gemv_group_rows(f, 16);
+  int nsb = (f + rows_gu - 1) / rows_gu;
+  if (gateup_blocks > 0 && nsb > gateup_blocks) nsb = gateup_blocks;
+  router_shared_gateup_kernel<<<a.nrb + nsb, 256, (size_t)d * 4, s>>>(a);
+  const int ndb = (d + rows_dn - 1) / rows_dn;
+  const int kpt = (E + 255) / 256;
+  const size_t lds = (size_t)f * 4;
+  if (kpt <= 2) topk_shared_down_kernel<2><<<1 + ndb, 1024, lds, s>>>(a);
+  else if (kpt <= 4) topk_shared_down_kernel<4><<<1 + ndb, 1024, lds, s>>>(a);
+  else if (kpt <= 8) topk_shared_down_kernel<8><<<1 + ndb, 1024, lds, s>>>(a);
+  else topk_shared_down_kernel<16><<<1 + ndb, 1024, lds, s>>>(a);
   return hipGetLastError();
 }
 

@@ -208,6 +208,23 @@ def test_packed_block_mode_small_chain(dev):
     assert err.max() <= 1e-4 and el.max() <= ELEM_FACTOR * 1e-4
 
 
+def test_packed_block_mode_wide_router_chain(dev):
+    """Block mode on packed experts with more than 256 experts (the shared expert's GEMVs
+    ride in the router and top-k launches): three chained blocks against the oracle."""
+    w = Workload("pk_block_e320", 68, d=2048, f=1024, E=320, k=4, T=1, layers=3, block=True)
+    say("packed block mode, 3 chained blocks d=2048 f=1024 E=320")
+    h0 = w.resid0()
+    ref = harness.run_stack(w, h0)
+    h = torch.from_numpy(h0).to(dev)
+    for layer in range(w.layers):
+        h, ids = run_packed_block(w, h, layer, packed_layer(w, layer, dev), dev)
+        assert np.array_equal(ids, ref["ids"][layer]), f"routing differs at layer {layer}"
+    yg = h.cpu().double().numpy()
+    err, el = rel_l2(yg, ref["y"]), rel_elem(yg, ref["y"])
+    print(f"    max rel L2 err {err.max():.3e}, max elem err / rms {el.max():.3e}", flush=True)
+    assert err.max() <= 1e-4 and el.max() <= ELEM_FACTOR * 1e-4
+
+
 def test_packed_stack8_k3(dev):
     """The 8-block K3 stack on packed experts (fp32 tokens on the one-token kernels), one
     token, routed exactly as the oracle at every block; the final residual within the K3 bar

@@ -399,6 +399,24 @@ def test_block_mode_small_chain(dev):
     assert err.max() < 1e-4
 
 
+def test_block_mode_wide_router_chain(dev):
+    """Block mode with more than 256 experts at one token, where the shared expert's GEMVs
+    ride in the router and top-k launches: three chained blocks against the oracle's stack,
+    routed exactly as the oracle at every block."""
+    w = Workload("block_e264", 23, d=512, f=256, E=264, k=4, T=1, layers=3, block=True)
+    say("block mode, 3 chained blocks, E=264, T=1")
+    h0 = w.resid0()
+    ref = harness.run_stack(w, h0)
+    h = torch.from_numpy(h0).to(dev)
+    for layer in range(w.layers):
+        g = run_gpu_layer(w, h.cpu().numpy(), dev, layer=layer, block=True, x_dtype="f32")
+        assert np.array_equal(g["ids"], ref["ids"][layer]), f"routing differs at layer {layer}"
+        h = g["y"]
+    err = rel_l2(h.cpu().double().numpy(), ref["y"])
+    print(f"    max rel L2 err {err.max():.3e}", flush=True)
+    assert err.max() < 1e-4
+
+
 def test_workspace_too_small_reports(dev):
     w = TOY
     dims = dims_of(w)
