@@ -7,44 +7,48 @@
 // FareedKhan-dev/kimi-k3-in-c", architecture section). Both are HBM-streaming GEMVs at
 // decode: bf16 weights are read once with 16-byte loads, widened to fp32 and
 // multiplied against an fp32 activation staged in LDS.
-#include "gemv_bf16.h"
+#include "block_dev.h"
 #include "k3moe_device.h"
 #include "k3moe_launch.h"
 
 namespace k3moe {
 namespace {
 
-// xhat = h / sqrt(mean(h^2) + eps) * gamma; the sum of squares runs in fp64 with a
-// fixed per-thread order and reduction tree. Each thread holds its 4-element pieces of
-// the row (16-byte loads, all in flight at once) through both passes.
-constexpr int kNormPieces = 8;  // rows up to 256 * 4 * 8 = 8192 elements stay in registers
+// xhat = h / sqrt(mean(h^2) + eps) * gamma, one block of 256 threads per row; rows up to
+// kNormMaxD elements stay in registers between the two passes (norm_load / norm_inv), longer
+// ones are read again with the same per-thread order and reduction tree.
 __global__ __launch_bounds__(256) void rmsnorm_kernel(int d, const float* __restrict__ h,
                                                       const uint16_t* __restrict__ gamma,
                                                       float eps, float* __restrict__ xhat) {
   __shared__ double red[4];
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const f32x4* ht = reinterpret_cast<const f32x4*>(h + (size_t)t * d);  // d % 8 == 0
+  const float* ht = h + (size_t)t * d;  // d % 8 == 0
+  f32x4* out = reinterpret_cast<f32x4*>(xhat + (size_t)t * d);
   const int nq = d >> 2;
-  const bool cached = nq <= 256 * kNormPieces;
-  f32x4 v[kNormPieces];
-  uint32_t gm[kNormPieces][4];  // gamma of the same pieces, requested with them
-  if (cached) {
+  if (d <= kNormMaxD) {
+    NormPieces p;
+    norm_load(ht, gamma, d, p);
+    const double inv = norm_inv(p.v, d, eps, red);
 #pragma unroll
     for (int c = 0; c < kNormPieces; ++c) {
       const int q = tid + 256 * c;
-      const int qc = q < nq ? q : 0;
-      v[c] = q < nq ? ht[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+      if (q < nq) {
+        f32x4 o;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) gm[c][i] = gamma[4 * qc + i];
+        for (int i = 0; i < 4; ++i) o[i] = norm_out(p, c, i, inv);
+        out[q] = o;
+      }
     }
+    return;
   }
+  const f32x4* h4 = reinterpret_cast<const f32x4*>(ht);
   double ss = 0.0;
   for (int q0 = 0; q0 < nq; q0 += 256 * kNormPieces)
 #pragma unroll
     for (int c = 0; c < kNormPieces; ++c) {
       const int q = q0 + tid + 256 * c;
       if (q < nq) {
-        const f32x4 a = cached ? v[c] : ht[q];
+        const f32x4 a = h4[q];
 #pragma unroll
         for (int i = 0; i < 4; ++i) ss += (double)a[i] * (double)a[i];
       }
@@ -53,18 +57,15 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(int d, const float* __rest
   if (lane == 0) red[wave] = ss;
   __syncthreads();
   const double inv = 1.0 / sqrt(((red[0] + red[1]) + (red[2] + red[3])) / (double)d + (double)eps);
-  f32x4* out = reinterpret_cast<f32x4*>(xhat + (size_t)t * d);
   for (int q0 = 0; q0 < nq; q0 += 256 * kNormPieces)
 #pragma unroll
     for (int c = 0; c < kNormPieces; ++c) {
       const int q = q0 + tid + 256 * c;
       if (q < nq) {
-        const f32x4 a = cached ? v[c] : ht[q];
+        const f32x4 a = h4[q];
         f32x4 o;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          o[i] = (float)((double)a[i] * inv *
-                         (double)bf16_bits_to_f32(cached ? gm[c][i] : gamma[4 * q + i]));
+        for (int i = 0; i < 4; ++i) o[i] = norm_value(a[i], gamma[4 * q + i], inv);
         out[q] = o;
       }
     }
@@ -81,7 +82,8 @@ __global__ __launch_bounds__(256, 2) void bf16_gemv_kernel(int T, int nrows, int
                                                            const uint16_t* __restrict__ W2,
                                                            float* __restrict__ out) {
   extern __shared__ __attribute__((aligned(16))) f32x4 xs[];
-  bf16_gemv_rows<SWIGLU>(blockIdx.x, gridDim.x, T, nrows, ncols, x, W1, W2, out, xs);
+  StageRow stg{x, ncols};
+  bf16_gemv_rows<SWIGLU>(blockIdx.x, gridDim.x, T, nrows, ncols, stg, W1, W2, out, xs);
 }
 
 }  // namespace

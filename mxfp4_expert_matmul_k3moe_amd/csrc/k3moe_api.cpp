@@ -775,6 +775,28 @@ int run_layer(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
   float* gates = topk_gates ? topk_gates : w.at<float>(R_GATES);
   const void* xin = x;
   int xf32 = x_dtype == K3MOE_F32;
+  int32_t* offs = w.at<int32_t>(R_OFFS);
+  int32_t* rows = w.at<int32_t>(R_ROWS);
+  const k3moe::BucketOut bo = bucket_out(w, offs, rows);
+  // One token: the RMSNorm and the shared expert's two GEMVs ride in the router and top-k
+  // launches (which also write the token's bucket), all on `s`.
+  if (blk && T == 1 &&
+      k3moe::route_shared_supported(d, dims->n_experts, dims->top_k, w_router)) {
+    float* xhat = w.at<float>(R_XHAT);
+    float* ssh = w.at<float>(R_SSH);
+    {
+      Probe probe(K3MOE_KERNEL_ROUTER, s);
+      rc = hip_check(k3moe::launch_route_shared(
+                         d, dims->d_ff, dims->n_experts, dims->top_k,
+                         static_cast<const float*>(x), blk->rms_gamma, blk->rms_eps, xhat,
+                         w_router, logit_bias, w.at<double>(R_PART), blk->sh_gate, blk->sh_up,
+                         blk->sh_down, w.at<float>(R_HSH), ssh, ids, gates, bo, 0, s),
+                     "rmsnorm + router + shared expert");
+    }
+    if (rc) return rc;
+    return run_ffn(*dims, T, xhat, 1, experts, offs, rows, gates, static_cast<const float*>(x),
+                   ssh, y, y_bf16, w, s, nullptr, packed);
+  }
   if (blk) {
     float* xhat = w.at<float>(R_XHAT);
     rc = hip_check(k3moe::launch_rmsnorm(T, d, static_cast<const float*>(x), blk->rms_gamma,
@@ -783,27 +805,6 @@ int run_layer(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
     if (rc) return rc;
     xin = xhat;
     xf32 = 1;
-  }
-  int32_t* offs = w.at<int32_t>(R_OFFS);
-  int32_t* rows = w.at<int32_t>(R_ROWS);
-  const k3moe::BucketOut bo = bucket_out(w, offs, rows);
-  // One token: the shared expert's two GEMVs ride in the router and top-k launches (which
-  // also write the token's bucket), all on `s`.
-  if (blk && T == 1 &&
-      k3moe::route_shared_supported(d, dims->n_experts, dims->top_k, w_router)) {
-    float* ssh = w.at<float>(R_SSH);
-    {
-      Probe probe(K3MOE_KERNEL_ROUTER, s);
-      rc = hip_check(k3moe::launch_route_shared(
-                         d, dims->d_ff, dims->n_experts, dims->top_k,
-                         static_cast<const float*>(xin), w_router, logit_bias,
-                         w.at<double>(R_PART), blk->sh_gate, blk->sh_up, blk->sh_down,
-                         w.at<float>(R_HSH), ssh, ids, gates, bo, 0, s),
-                     "router + shared expert");
-    }
-    if (rc) return rc;
-    return run_ffn(*dims, T, xin, xf32, experts, offs, rows, gates,
-                   static_cast<const float*>(x), ssh, y, y_bf16, w, s, nullptr, packed);
   }
   // The shared expert needs only xhat: it runs on a side stream, overlapping the router,
   // top-k and gate/up, and the launch that adds it into y waits for it (per-call events).

@@ -72,13 +72,15 @@ struct BucketOut {
 hipError_t launch_route_topk(int T, int E, int k, const double* part, int nsum,
                              const float* bias, int32_t* ids, float* gates,
                              const BucketOut* bucket1, hipStream_t s);
-// Block mode, one token: the router GEMV (fp32 token x) and the shared expert's gate/up GEMV
-// (hsh = silu(G x) * (U x)) in one launch, then the top-k with the token's bucket and the
-// shared expert's down GEMV (ssh = D hsh) in a second; every value as from the standalone
-// kernels. Needs route_shared_supported (E % 8 == 0, 256 < E <= 4096, 16-byte aligned router
-// weights); gateup_blocks > 0 caps the shared gate/up blocks.
+// Block mode, one token: the RMSNorm of the residual h (into xhat), the router GEMV on it and
+// the shared expert's gate/up GEMV (hsh = silu(G xhat) * (U xhat)) in one launch, then the
+// top-k with the token's bucket and the shared expert's down GEMV (ssh = D hsh) in a second;
+// every value as from the standalone kernels. Needs route_shared_supported (d % 8 == 0,
+// d <= 8192, E % 8 == 0, 256 < E <= 4096, 16-byte aligned router weights); gateup_blocks > 0
+// caps the shared gate/up blocks.
 bool route_shared_supported(int d, int E, int k, const uint16_t* w_router);
-hipError_t launch_route_shared(int d, int f, int E, int k, const float* x,
+hipError_t launch_route_shared(int d, int f, int E, int k, const float* h,
+                               const uint16_t* gamma, float eps, float* xhat,
                                const uint16_t* w_router, const float* bias, double* part,
                                const uint16_t* sh_gate, const uint16_t* sh_up,
                                const uint16_t* sh_down, float* hsh, float* ssh, int32_t* ids,

@@ -7,7 +7,7 @@
 // Every product bf16*bf16 or bf16*fp32 is exact in fp64, and the sums are carried in
 // fp64, so the ranking is that of the exact logits barring ties closer than fp64
 // rounding.
-#include "gemv_bf16.h"
+#include "block_dev.h"
 #include "k3moe_device.h"
 #include "k3moe_launch.h"
 
@@ -91,11 +91,27 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(int T, int d, int E,
 // before the first FMA). Row sums: per lane in row order, then a fixed xor tree over
 // the 8 lanes sharing a column group, then the four waves in order. Needs E % 8 == 0.
 // (chunk, cblk): the block's row chunk and column block (the grid's x and y). Needs 256
-// threads.
-template <bool XF32, int NT>
+// threads. One token: xl supplies the chunk's activations: issue(t, ra, rb) before the
+// weight loads (rows ra, rb of the chunk, in range), get(xa, xb) after them (XRow reads
+// x; the block-mode launch's form normalises the residual there).
+template <bool XF32>
+struct XRow {
+  const void* x;
+  int d, k0;
+  double xa, xb;
+  __device__ __forceinline__ void issue(int t, int ra, int rb) {
+    xa = load_x<XF32>(x, (size_t)t * d + k0 + ra);
+    xb = load_x<XF32>(x, (size_t)t * d + k0 + rb);
+  }
+  __device__ __forceinline__ void get(double& a, double& b) {
+    a = xa;
+    b = xb;
+  }
+};
+
+template <bool XF32, int NT, class XL>
 __device__ __forceinline__ void router_gemv_vec_block(int chunk, int cblk, int T, int d, int E,
-                                                      const void* __restrict__ x,
-                                                      const uint16_t* __restrict__ w,
+                                                      XL& xl, const uint16_t* __restrict__ w,
                                                       double* __restrict__ part) {
   constexpr int RPL = kRouterRows / 4 / 8;  // rows per lane (16)
   __shared__ double xs[kRouterRows][NT];
@@ -124,14 +140,15 @@ __device__ __forceinline__ void router_gemv_vec_block(int chunk, int cblk, int T
       // loads land and the barrier waits only for LDS, so all weight loads stay in flight
       if (t0 > 0) __syncthreads();
       const int ra = threadIdx.x, rb = threadIdx.x + 256;
-      const double xa = load_x<XF32>(x, (size_t)t0 * d + k0 + min(ra, nrows - 1));
-      const double xb = load_x<XF32>(x, (size_t)t0 * d + k0 + min(rb, nrows - 1));
+      xl.issue(t0, min(ra, nrows - 1), min(rb, nrows - 1));
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int u = 0; u < RPL; ++u) {
         const int r = min(wave * (kRouterRows / 4) + rl + 8 * u, nrows - 1);
         wv[u] = *reinterpret_cast<const u32x4*>(w + (size_t)(k0 + r) * E + (cv ? col0 : 0));
       }
+      double xa, xb;
+      xl.get(xa, xb);
       xs[ra][0] = ra < nrows ? xa : 0.0;
       xs[rb][0] = rb < nrows ? xb : 0.0;
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -144,6 +161,7 @@ __device__ __forceinline__ void router_gemv_vec_block(int chunk, int cblk, int T
       // step, all issued before any is used (one element per load made every element its
       // own round trip to L2); x rows and the chunk start are 16-byte aligned and nrows is
       // a multiple of 32
+      const void* x = xl.x;
       constexpr int VPL = XF32 ? 4 : 8;
       constexpr int LPT = kRouterRows / VPL;              // loads per token
       constexpr int ITER = (NT * LPT + 255) / 256;        // loads per thread
@@ -235,7 +253,8 @@ __global__ __launch_bounds__(256) void router_gemv_vec_kernel(int T, int d, int 
                                                               const void* __restrict__ x,
                                                               const uint16_t* __restrict__ w,
                                                               double* __restrict__ part) {
-  router_gemv_vec_block<XF32, NT>(blockIdx.x, blockIdx.y, T, d, E, x, w, part);
+  XRow<XF32> xl{x, d, (int)blockIdx.x * kRouterRows, 0.0, 0.0};
+  router_gemv_vec_block<XF32, NT>(blockIdx.x, blockIdx.y, T, d, E, xl, w, part);
 }
 
 // Several tokens: the K reduction stays inside each lane (no cross-lane sums). A work item
@@ -535,7 +554,6 @@ __device__ __forceinline__ bool better(uint64_t ka, int ia, uint64_t kb, int ib)
 
 constexpr int kMaxE = 4096;
 constexpr int kMaxSlots = 32;
-constexpr int kMaxChunks = 32;  // d <= 16384 in 512-row chunks
 constexpr int kMaxCand = 2048;  // candidate buffer; the exact ranking covers any count
 
 // One block per token of NT = blockDim.x threads (a multiple of 64, at most 256): thread t
@@ -821,18 +839,60 @@ __global__ __launch_bounds__(WIDE ? 1024 : 256) void route_topk_kernel(int T, in
   route_topk_block<KPT, WIDE>(blockIdx.x, T, E, k, part, nsum, bias, ids, gates, bk);
 }
 
+// One token of block mode: the router's chunk rows are the RMSNorm of the residual h, formed
+// in every router block (the sum of squares over the whole row as in the standalone RMSNorm,
+// so every block gets the same values); the blocks of column block 0 also store their chunk
+// of xhat for the expert kernels.
+struct XNormRow {
+  const float* h;
+  const uint16_t* gamma;
+  float* xhat;  // nullable: where to store the chunk's rows
+  int d, k0;
+  float eps;
+  double* red;  // 4 doubles of LDS
+  f32x4 v[kNormPieces];  // this thread's pieces of h, for the sum of squares
+  float ha, hb;
+  uint32_t ga, gb;
+  int rowa, rowb;
+  __device__ __forceinline__ void issue(int, int ra, int rb) {
+    norm_load_h(h, d, v);
+    rowa = k0 + ra;
+    rowb = k0 + rb;
+    ha = h[rowa];
+    hb = h[rowb];
+    ga = gamma[rowa];
+    gb = gamma[rowb];
+  }
+  __device__ __forceinline__ void get(double& a, double& b) {
+    const double inv = norm_inv(v, d, eps, red);
+    const float xa = norm_value(ha, ga, inv), xb = norm_value(hb, gb, inv);
+    if (xhat) {  // rows past the chunk's end are clamped to its last row: same value
+      xhat[rowa] = xa;
+      xhat[rowb] = xb;
+    }
+    a = (double)xa;
+    b = (double)xb;
+  }
+};
+
 // ---- block mode, one token: the routing launches carry the shared expert ------------------
 // The shared expert's two bf16 GEMVs need only the normalised token. Rather than running on
 // a second stream (whose fork and join cost more than the GEMVs themselves at this size),
 // they ride in the two routing launches, which are latency-bound and leave most of the HBM
-// bandwidth idle: blocks [0, nrb) of the first launch are the router GEMV's (chunk, column
-// block) in the standalone grid's order, the others walk the shared gate/up row groups
-// (silu(G x) * (U x) into hsh); block 0 of the second launch is the top-k's (with the token's
-// bucket), the others walk the shared down row groups (D hsh into ssh). Each part runs the
-// code of its standalone kernel, so every value is the same bit for bit.
+// bandwidth idle, and the RMSNorm rides in the first: blocks [0, nrb) of the first launch
+// are the router GEMV's (chunk, column block), in the standalone grid's order, each forming
+// its chunk of xhat itself (XNormRow; column block 0 also stores it for the expert kernels);
+// the others walk the shared gate/up row groups (silu(G xhat) * (U xhat) into hsh) on a
+// token they normalise themselves (StageNormRow). Block 0 of the second launch is the
+// top-k's (with the token's bucket), the others walk the shared down row groups (D hsh into
+// ssh). Each part runs the code of its standalone kernel, so every value is the same bit for
+// bit as with the separate launches.
 struct RouteSharedArgs {
   int d, f, E, k;
-  const float* x;            // normalised token [d]
+  const float* h;            // residual [d] (block input)
+  const uint16_t* gamma;     // RMSNorm weight [d]
+  float eps;
+  float* xhat;               // normalised token [d] (written)
   const uint16_t* w_router;  // [d][E]
   double* part;              // router partial sums [nchunk][E]
   int nchunk, nrb;           // router chunks; router blocks (chunks x column blocks)
@@ -844,15 +904,22 @@ struct RouteSharedArgs {
   Bucket1 bk;
 };
 
-__global__ __launch_bounds__(256) void router_shared_gateup_kernel(RouteSharedArgs a) {
+// Three waves per SIMD (168 registers, two of them spilled): the 196 router and 384 shared
+// blocks of the K3 layer are then all resident at once (two waves per SIMD left 68 blocks for
+// a second round; 0.649-0.654 against 0.657-0.660 ms per token on the 8-block stack).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void
+router_shared_gateup_kernel(RouteSharedArgs a) {
   extern __shared__ __attribute__((aligned(16))) f32x4 xs[];
+  __shared__ double red[4];
   const int b = blockIdx.x;
   if (b < a.nrb) {  // block-uniform
-    router_gemv_vec_block<true, 1>(b % a.nchunk, b / a.nchunk, 1, a.d, a.E, a.x, a.w_router,
-                                   a.part);
+    const int chunk = b % a.nchunk, cblk = b / a.nchunk;
+    XNormRow xl{a.h, a.gamma, cblk == 0 ? a.xhat : nullptr, a.d, chunk * kRouterRows, a.eps, red};
+    router_gemv_vec_block<true, 1>(chunk, cblk, 1, a.d, a.E, xl, a.w_router, a.part);
     return;
   }
-  bf16_gemv_rows<true>(b - a.nrb, (int)gridDim.x - a.nrb, 1, a.f, a.d, a.x, a.sh_gate, a.sh_up,
+  StageNormRow stg{a.h, a.gamma, a.d, a.eps, red};
+  bf16_gemv_rows<true>(b - a.nrb, (int)gridDim.x - a.nrb, 1, a.f, a.d, stg, a.sh_gate, a.sh_up,
                        a.hsh, xs);
 }
 
@@ -863,7 +930,8 @@ __global__ __launch_bounds__(1024) void topk_shared_down_kernel(RouteSharedArgs 
     route_topk_block<KPT, true>(0, 1, a.E, a.k, a.part, a.nchunk, a.bias, a.ids, a.gates, a.bk);
     return;
   }
-  bf16_gemv_rows<false>((int)blockIdx.x - 1, (int)gridDim.x - 1, 1, a.d, a.f, a.hsh, a.sh_down,
+  StageRow stg{a.hsh, a.f};
+  bf16_gemv_rows<false>((int)blockIdx.x - 1, (int)gridDim.x - 1, 1, a.d, a.f, stg, a.sh_down,
                         nullptr, a.ssh, xs);
 }
 
@@ -963,11 +1031,12 @@ hipError_t launch_route_topk(int T, int E, int k, const double* part, int nsum,
 }
 
 bool route_shared_supported(int d, int E, int k, const uint16_t* w_router) {
-  return d % 8 == 0 && E % 8 == 0 && E > 256 && E <= kMaxE && k >= 1 && k <= kMaxSlots &&
-         k <= E && (reinterpret_cast<uintptr_t>(w_router) & 15u) == 0;
+  return d % 8 == 0 && d <= kNormMaxD && E % 8 == 0 && E > 256 && E <= kMaxE && k >= 1 &&
+         k <= kMaxSlots && k <= E && (reinterpret_cast<uintptr_t>(w_router) & 15u) == 0;
 }
 
-hipError_t launch_route_shared(int d, int f, int E, int k, const float* x,
+hipError_t launch_route_shared(int d, int f, int E, int k, const float* h,
+                               const uint16_t* gamma, float eps, float* xhat,
                                const uint16_t* w_router, const float* bias, double* part,
                                const uint16_t* sh_gate, const uint16_t* sh_up,
                                const uint16_t* sh_down, float* hsh, float* ssh, int32_t* ids,
@@ -975,7 +1044,8 @@ hipError_t launch_route_shared(int d, int f, int E, int k, const float* x,
                                hipStream_t s) {
   if (!route_shared_supported(d, E, k, w_router)) return hipErrorInvalidValue;
   RouteSharedArgs a;
-  a.d = d; a.f = f; a.E = E; a.k = k; a.x = x; a.w_router = w_router; a.part = part;
+  a.d = d; a.f = f; a.E = E; a.k = k; a.h = h; a.gamma = gamma; a.eps = eps; a.xhat = xhat;
+  a.w_router = w_router; a.part = part;
   a.nchunk = router_num_chunks(d);
   a.nrb = a.nchunk * ((E + kRouterCols - 1) / kRouterCols);
   a.sh_gate = sh_gate; a.sh_up = sh_up; a.sh_down = sh_down; a.hsh = hsh; a.ssh = ssh;
