@@ -358,8 +358,8 @@ def decode_like_fields(w, m, traffic, packed=False):
     dn_bytes = m["sel"] * w.d * (w.f // 2 + w.f // 32)
     ach = gu_bytes / (m["gate_up_ms"] * 1e-3) / 1e9
     if w.T == 1:
-        kname = ("gateup_decode_packed_ks_kernel (MXFP4 gate/up GEMV + SwiGLU, packed tile "
-                 "layout, one wave per 8-step K chunk)"
+        kname = ("gateup_decode_packed_kernel (MXFP4 gate/up + SwiGLU, one token, packed tile "
+                 "layout, block-scaled FP4 x FP8 MFMA on the token's E4M3 terms)"
                  if packed else "gateup_decode_kernel (MXFP4 gate/up GEMV + SwiGLU)")
     elif w.T >= MFMA_MIN_TOKENS or packed:
         kname = grouped_label(packed)
@@ -696,7 +696,7 @@ def bench_stack(args, w) -> int:
                    "hip_graph": bool(args.graph),
                    "expert_layout": "packed" if packed else "row-major"},
         "roofline": {"bound": "hbm",
-                     "kernel": ("gateup_decode_packed_ks_kernel<fp32 x> (MXFP4 gate/up GEMV + "
+                     "kernel": ("gateup_decode_packed_kernel<fp32 x> (MXFP4 gate/up + "
                                 "SwiGLU, packed tile layout)" if packed else
                                 "gateup_decode_kernel<fp32 x> (MXFP4 gate/up GEMV + SwiGLU)"),
                      "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -844,11 +844,11 @@ def _kernel_hash(packed=False) -> str:
     unchanged)."""
     import hashlib
     csrc = os.path.join(ROOT, "mxfp4_expert_matmul_k3moe_amd", "csrc")
-    with open(os.path.join(csrc, "ffn_gemv.hip")) as fh:
+    with open(os.path.join(csrc, "ffn_mfma.hip" if packed else "ffn_gemv.hip")) as fh:
         src = fh.read()
     h = hashlib.sha256()
     if packed:
-        h.update(_function_text(src, "void gateup_decode_packed_ks_kernel(").encode())
+        h.update(_function_text(src, "void gateup_decode_packed_kernel(").encode())
         h.update(_function_text(src, "hipError_t launch_gateup_decode_packed(").encode())
     else:
         h.update(_function_text(src, "void gateup_decode_kernel(").encode())

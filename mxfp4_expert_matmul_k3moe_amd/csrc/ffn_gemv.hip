@@ -459,125 +459,6 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int d, int k, const
   }
 }
 
-// ---- gate/up, T == 1, packed tile layout ---------------------------------------------------
-struct GateUpPackedArgs {
-  int d, f, k;
-  const void* x;
-  const uint8_t *gq, *gs, *uq, *us;  // packed G and U
-  const int32_t *pair_pos, *pair_exp;
-  float* h;  // [k][f] by bucket position
-};
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// One block per (slot, 16-row tile), one wave per chunk of 8 K steps (d / 1024 waves; lane
-// (i, g) owns row i of the tile and K block 4 s + g of step s, as the packed layout stores
-// them). A wave copies its chunk of the token into LDS (asynchronous
-// copies), issues all 8 steps of G and of U and its two scale entries at once, and dots them;
-// the waves of a block read the tile's consecutive 8-KB pieces side by side. The per-row
-// partial sums go through LDS and wave 0 adds them in chunk order (fixed order: results are
-// the same from run to run) and writes h = silu(gate) * up. The weights are never written
-// anywhere decoded. One wave streaming a whole tile (3072 streams of 56 KB on the K3 layer,
-// 8 steps in flight each) took 39.4-40.2 us against 35.7-36.8 us for this form; a timing
-// copy of it without the dot products still took 36.6 us, so the read pattern was the limit.
-constexpr int kPkKsMaxWaves = 16;  // d <= 16384
-template <bool XF32>
-__global__ __launch_bounds__(64 * kPkKsMaxWaves) void gateup_decode_packed_ks_kernel(
-    GateUpPackedArgs a) {
-  extern __shared__ __attribute__((aligned(16))) u32x4 xs[];  // [wave][8 steps x 4 blocks x Q]
-  __shared__ float part[kPkKsMaxWaves][2][16];
-  constexpr int Q = XF32 ? 8 : 4;  // 16-byte pieces per 32-element block
-  const int d = a.d, f = a.f;
-  const int lane = threadIdx.x & 63;
-  const int c = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // this wave's chunk
-  const int g = lane >> 4, i = lane & 15;
-  const int ntile = f >> 4, nk = d / 128, nch = nk >> 3;
-  const int q = blockIdx.x / ntile, t = blockIdx.x - (blockIdx.x / ntile) * ntile;
-  const int pos = __builtin_amdgcn_readfirstlane(a.pair_pos[q]);
-  const int e = __builtin_amdgcn_readfirstlane(a.pair_exp[q]);
-  if (pos < 0 || e < 0) return;  // block-uniform
-  // 1. the chunk's 1024 token elements into this wave's LDS area (1 KB per copy)
-  u32x4* xw = xs + (size_t)c * (32 * Q);
-  constexpr int NCOPY = 2 * Q / 4;  // 2 (bf16) or 4 (fp32) KB
-#pragma unroll
-  for (int u = 0; u < NCOPY; ++u)
-    __builtin_amdgcn_global_load_lds(static_cast<const uint8_t*>(a.x) + ((size_t)c * NCOPY + u) * 1024 +
-                                         lane * 16,
-                                     (lds_void_t*)(reinterpret_cast<uint8_t*>(xw) + u * 1024), 16, 0, 0);
-  asm volatile("" ::: "memory");  // the copies stay the oldest loads
-  // 2. the chunk's two scale entries and its 8 steps of G and U (1 KB each), all at once, in
-  //    the order they are used
-  const size_t qb = (size_t)f * (d >> 1), sb = (size_t)(f >> 4) * nch * 512;
-  const size_t qo = (size_t)e * qb + (((size_t)t * nk + 8 * c) * 64 + lane) * 16;
-  const size_t so = (size_t)e * sb + (((size_t)t * nch + c) * 64 + lane) * 8;
-  const uint64_t sg = *reinterpret_cast<const uint64_t*>(a.gs + so);
-  const uint64_t su = *reinterpret_cast<const uint64_t*>(a.us + so);
-  asm volatile("" ::: "memory");
-  u32x4 wg[8], wu[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    wg[j] = load_u32x4_nt(a.gq + qo + (size_t)j * 1024);
-    wu[j] = load_u32x4_nt(a.uq + qo + (size_t)j * 1024);
-  }
-  asm volatile("" ::: "memory");
-  // the token copies are the oldest loads: waiting for them leaves the other 18 in flight
-  asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-  __builtin_amdgcn_wave_barrier();
-  asm volatile("" ::: "memory");
-  float ga = 0.0f, ua = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t gb = (uint32_t)(sg >> (8 * j)) & 0xFFu;
-    const uint32_t ub = (uint32_t)(su >> (8 * j)) & 0xFFu;
-    const u32x4* xb = xw + (size_t)(4 * j + g) * Q;  // block 4 j + g of the chunk
-    float gd, ud;
-    if constexpr (XF32) {
-      float xv[32];
-#pragma unroll
-      for (int qq = 0; qq < 8; ++qq) {
-        const u32x4 v = xb[qq];
-        xv[4 * qq + 0] = __uint_as_float(v[0]);
-        xv[4 * qq + 1] = __uint_as_float(v[1]);
-        xv[4 * qq + 2] = __uint_as_float(v[2]);
-        xv[4 * qq + 3] = __uint_as_float(v[3]);
-      }
-      gd = block_dot_f32(wg[j], xv);
-      ud = block_dot_f32(wu[j], xv);
-    } else {
-      uint32_t xp[16];
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const u32x4 v = xb[qq];
-        xp[4 * qq + 0] = v[0];
-        xp[4 * qq + 1] = v[1];
-        xp[4 * qq + 2] = v[2];
-        xp[4 * qq + 3] = v[3];
-      }
-      gd = block_dot_bf16(wg[j], xp);
-      ud = block_dot_bf16(wu[j], xp);
-    }
-    ga = fmaf(e8m0_to_f32(gb), gd, ga);
-    ua = fmaf(e8m0_to_f32(ub), ud, ua);
-  }
-  ga += __shfl_xor(ga, 16, 64);
-  ua += __shfl_xor(ua, 16, 64);
-  ga += __shfl_xor(ga, 32, 64);
-  ua += __shfl_xor(ua, 32, 64);
-  if (g == 0) {
-    part[c][0][i] = ga;
-    part[c][1][i] = ua;
-  }
-  __syncthreads();
-  if (c == 0 && lane < 16) {
-    float gs2 = part[0][0][lane], us2 = part[0][1][lane];
-    for (int c2 = 1; c2 < nch; ++c2) {
-      gs2 += part[c2][0][lane];
-      us2 += part[c2][1][lane];
-    }
-    a.h[(size_t)pos * f + 16 * t + lane] = silu_f32(gs2) * us2;
-  }
-}
-
 int bpl_of(int nb) { return nb / lanes_per_row(nb); }
 
 constexpr int kMaxDecodeBpl = 8;
@@ -638,26 +519,6 @@ hipError_t launch_gateup_gemv(int T, int d, int f, int E, int k, const void* x, 
   }
 #undef K3_GU_B
 #undef K3_GU
-  return hipGetLastError();
-}
-
-hipError_t launch_gateup_decode_packed(int d, int f, int k, const void* x, int xf32,
-                                       const MxPtrs& w, const int32_t* pair_pos,
-                                       const int32_t* pair_exp, float* h, hipStream_t s) {
-  GateUpPackedArgs a;
-  a.d = d; a.f = f; a.k = k; a.x = x;
-  a.gq = w.gate_q; a.gs = w.gate_s; a.uq = w.up_q; a.us = w.up_s;
-  a.pair_pos = pair_pos; a.pair_exp = pair_exp; a.h = h;
-  const int items = k * (f / 16);
-  const int nch = d / 1024;
-  if (nch < 1 || nch > kPkKsMaxWaves) return hipErrorInvalidValue;
-  const size_t lds = (size_t)d * (xf32 ? 4 : 2);
-  if (xf32)
-    launch_timed(gateup_decode_packed_ks_kernel<true>, dim3(items), dim3(64 * nch), (uint32_t)lds,
-                 s, a);
-  else
-    launch_timed(gateup_decode_packed_ks_kernel<false>, dim3(items), dim3(64 * nch),
-                 (uint32_t)lds, s, a);
   return hipGetLastError();
 }
 

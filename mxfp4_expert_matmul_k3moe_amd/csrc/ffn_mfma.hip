@@ -1529,6 +1529,185 @@ __global__ __launch_bounds__(1024) void down_decode_mfma_kernel(DownDecMArgs a) 
   }
 }
 
+// ---- gate/up of one token on the packed layout, block-scaled MFMA --------------------------
+// One block per (slot, 16-row tile of f), one wave per chunk of 8 K steps (1024 elements of d;
+// d / 1024 waves). Wave c:
+//  1. copies its chunk of the token into LDS (asynchronous copies) and issues all 8 steps of
+//     the tile in G and in U (1 KB each: lane (i, g) = row i, MXFP4 block 4 s + g, as the
+//     packed layout stores them) and its two packed scale entries, all at once;
+//  2. splits the chunk into NTM E4M3 terms with one E8M0 scale per term and 32-element block
+//     (lane l takes elements 16 l .. 16 l + 15, two lanes per block): term 0 puts the block
+//     maximum in [128, 256), each further term codes what the previous ones left against its
+//     own maximum. Two terms carry a bf16 token exactly (to about 2^-22 of the block maximum),
+//     three an fp32 one to about 2^-13 of it. The terms overwrite the chunk in LDS (each lane
+//     has read its elements first), natural order, scales behind them;
+//  3. runs one MFMA per step and matrix with the weights as the FP4 operand as stored and the
+//     terms as FP8 B columns 0 .. NTM - 1 (the other columns repeat term 0 and are not read),
+//     so column t of the result is term t's share of the row's dot product: (C0 + C1) (+ C2).
+// The per-row chunk sums go through LDS and wave 0 adds them in chunk order and writes
+// h = silu(gate) * up, so results are the same from run to run. The weights are never
+// decoded: the dot products of the one-token GEMV become 16 MFMAs per wave.
+struct GateUpPackedArgs {
+  int d, f, k;
+  const void* x;
+  const uint8_t *gq, *gs, *uq, *us;  // packed G and U
+  const int32_t *pair_pos, *pair_exp;
+  float* h;  // [k][f] by bucket position
+};
+constexpr int kPkMaxWaves = 16;  // d <= 16384
+// LDS bytes per wave: the chunk as copied, or its terms and their scales if that is more
+__host__ __device__ constexpr int pk_wave_lds(bool xf32) {
+  return xf32 ? 4096 : 2048 + 2 * 32;
+}
+
+template <bool XF32>
+__global__ __launch_bounds__(64 * kPkMaxWaves) void gateup_decode_packed_kernel(
+    GateUpPackedArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
+  __shared__ float part[kPkMaxWaves][2][16];
+  constexpr int NTM = XF32 ? 3 : 2;  // E4M3 terms of the token
+  constexpr int AREA = pk_wave_lds(XF32);
+  const int d = a.d, f = a.f;
+  const int lane = threadIdx.x & 63;
+  const int c = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // this wave's chunk
+  const int g = lane >> 4, ln = lane & 15;
+  const int ntile = f >> 4, nk = d / 128, nch = nk >> 3;
+  const int q = blockIdx.x / ntile, t = blockIdx.x - (blockIdx.x / ntile) * ntile;
+  const int pos = __builtin_amdgcn_readfirstlane(a.pair_pos[q]);
+  const int e = __builtin_amdgcn_readfirstlane(a.pair_exp[q]);
+  if (pos < 0 || e < 0) return;  // block-uniform
+  uint8_t* xw = xl + c * AREA;
+  // 1. the chunk's 1024 token elements into this wave's LDS area (1 KB per copy), then the
+  //    two scale entries and the 8 steps of G and U, in the order they are used
+  constexpr int NCOPY = XF32 ? 4 : 2;
+#pragma unroll
+  for (int u = 0; u < NCOPY; ++u)
+    __builtin_amdgcn_global_load_lds(static_cast<const uint8_t*>(a.x) + ((size_t)c * NCOPY + u) * 1024 +
+                                         lane * 16,
+                                     (lds_void*)(xw + u * 1024), 16, 0, 0);
+  asm volatile("" ::: "memory");  // the copies stay the oldest loads
+  const size_t qb = (size_t)f * (d >> 1), sb = (size_t)(f >> 4) * nch * 512;
+  const size_t qo = (size_t)e * qb + (((size_t)t * nk + 8 * c) * 64 + lane) * 16;
+  const size_t so = (size_t)e * sb + (((size_t)t * nch + c) * 64 + lane) * 8;
+  const uint64_t sg = *reinterpret_cast<const uint64_t*>(a.gs + so);
+  const uint64_t su = *reinterpret_cast<const uint64_t*>(a.us + so);
+  asm volatile("" ::: "memory");
+  u32x4 wg[8], wu[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    wg[j] = load_u32x4_nt(a.gq + qo + (size_t)j * 1024);
+    wu[j] = load_u32x4_nt(a.uq + qo + (size_t)j * 1024);
+  }
+  asm volatile("" ::: "memory");
+  // the token copies are the oldest loads: waiting for them leaves the other 18 in flight
+  asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+
+  // 2. terms of this lane's 16 elements
+  float y[16];
+  if constexpr (XF32) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const u32x4 w4 = *reinterpret_cast<const u32x4*>(xw + 64 * lane + 16 * v);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[4 * v + i] = __uint_as_float(w4[i]);
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const u32x4 w4 = *reinterpret_cast<const u32x4*>(xw + 32 * lane + 16 * v);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        y[8 * v + 2 * i] = __uint_as_float(w4[i] << 16);
+        y[8 * v + 2 * i + 1] = __uint_as_float(w4[i] & 0xFFFF0000u);
+      }
+    }
+  }
+  // every lane holds its elements before any term overwrites the chunk
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  auto bmax = [](float m) { return fmaxf(m, __shfl_xor(m, 1, 64)); };  // the block's two lanes
+  float mx = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(y[i]));
+  mx = bmax(mx);
+  const int e0 = top_exp(mx);
+  const bool bad = e0 == kExpBad;
+  const int s0 = bad ? 255 : min(max(e0 + 127, 0), 254);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) y[i] = ldexpf(y[i], 127 - s0);  // exact: the maximum below 256
+#pragma unroll
+  for (int tm = 0; tm < NTM; ++tm) {
+    int sc = s0, er = 0;  // term scale and its exponent relative to term 0
+    if (tm > 0) {
+      float rm = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) rm = fmaxf(rm, fabsf(y[i]));
+      rm = bmax(rm);
+      const int ex = top_exp(rm);
+      sc = bad ? 255 : min(max(s0 + max(ex, -300), 0), 254);
+      er = sc - s0;
+    }
+    u32x4 codes = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int cq = e4m3_code(ldexpf(y[i], -er));
+      y[i] -= ldexpf(e4m3_value(cq), er);
+      codes[i >> 2] |= (uint32_t)cq << (8 * (i & 3));
+    }
+    *reinterpret_cast<u32x4*>(xw + tm * 1024 + 16 * lane) = codes;
+    if ((lane & 1) == 0) xw[NTM * 1024 + tm * 32 + (lane >> 1)] = (uint8_t)sc;
+  }
+  // the wave reads back what its own lanes wrote (LDS operations of a wave are in order)
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+
+  // 3. one MFMA per step and matrix
+  const int tt = ln < NTM ? ln : 0;  // this lane's term (B column)
+  const uint8_t* tb = xw + tt * 1024 + 16 * g;
+  const uint8_t* ts = xw + NTM * 1024 + tt * 32 + g;
+  f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const u32x4 b0 = *reinterpret_cast<const u32x4*>(tb + 128 * j);
+    const u32x4 b1 = *reinterpret_cast<const u32x4*>(tb + 128 * j + 64);
+    const int bsc = ts[4 * j];
+    const i32x8 bop = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                       (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+    // an FP4 operand takes the low four registers of the tuple; the upper four are undefined
+    typedef int i32x4v __attribute__((ext_vector_type(4)));
+    const i32x4v wgi = __builtin_bit_cast(i32x4v, wg[j]), wui = __builtin_bit_cast(i32x4v, wu[j]);
+    const i32x8 ag = __builtin_shufflevector(wgi, wgi, 0, 1, 2, 3, -1, -1, -1, -1);
+    const i32x8 au = __builtin_shufflevector(wui, wui, 0, 1, 2, 3, -1, -1, -1, -1);
+    const int gsc = (int)((sg >> (8 * j)) & 0xFFu), usc = (int)((su >> (8 * j)) & 0xFFu);
+    accg = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ag, bop, accg, 4, 0, 0, gsc, 0, bsc);
+    accu = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(au, bop, accu, 4, 0, 0, usc, 0, bsc);
+  }
+  // lane (ln, g) holds column ln (term ln) of tile rows 4 g .. 4 g + 3
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float gs = accg[r] + __shfl_down(accg[r], 1, 64);
+    float us = accu[r] + __shfl_down(accu[r], 1, 64);
+    if (NTM == 3) {
+      gs += __shfl_down(accg[r], 2, 64);
+      us += __shfl_down(accu[r], 2, 64);
+    }
+    if (ln == 0) {
+      part[c][0][4 * g + r] = gs;
+      part[c][1][4 * g + r] = us;
+    }
+  }
+  __syncthreads();
+  if (c == 0 && lane < 16) {
+    float gs2 = part[0][0][lane], us2 = part[0][1][lane];
+    for (int c2 = 1; c2 < nch; ++c2) {
+      gs2 += part[c2][0][lane];
+      us2 += part[c2][1][lane];
+    }
+    a.h[(size_t)pos * f + 16 * t + lane] = silu_f32(gs2) * us2;
+  }
+}
+
 }  // namespace
 
 int mfma_mtiles_bound(int T, int E, int k) {
@@ -1623,6 +1802,26 @@ hipError_t launch_down_decode_mfma(int d, int f, int k, const MxPtrs& w, const f
     default:
       return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gateup_decode_packed(int d, int f, int k, const void* x, int xf32,
+                                       const MxPtrs& w, const int32_t* pair_pos,
+                                       const int32_t* pair_exp, float* h, hipStream_t s) {
+  if (d % 1024 != 0 || f % 16 != 0) return hipErrorInvalidValue;
+  const int nch = d / 1024;
+  if (nch < 1 || nch > kPkMaxWaves) return hipErrorInvalidValue;
+  GateUpPackedArgs a;
+  a.d = d; a.f = f; a.k = k; a.x = x;
+  a.gq = w.gate_q; a.gs = w.gate_s; a.uq = w.up_q; a.us = w.up_s;
+  a.pair_pos = pair_pos; a.pair_exp = pair_exp; a.h = h;
+  const dim3 grid((unsigned)(k * (f / 16))), block((unsigned)(64 * nch));
+  if (xf32)
+    launch_timed(gateup_decode_packed_kernel<true>, grid, block,
+                 (uint32_t)(nch * pk_wave_lds(true)), s, a);
+  else
+    launch_timed(gateup_decode_packed_kernel<false>, grid, block,
+                 (uint32_t)(nch * pk_wave_lds(false)), s, a);
   return hipGetLastError();
 }
 

@@ -129,8 +129,9 @@ hipError_t launch_down_decode_mfma(int d, int f, int k, const MxPtrs& w, const f
                                    float* y, uint16_t* y_bf16, int n_cu, hipStream_t s,
                                    bool packed = false);
 // One token, packed tile layout (d % 1024 == 0, d <= 16384, f % 16 == 0): h = silu(G x) * (U x)
-// of every slot as fp32 into h [k][f] at the slot's bucket position; one block per (slot,
-// 16-row tile), one wave per 8-step K chunk. x is bf16 (xf32 == 0) or fp32 [d].
+// of every slot as fp32 into h [k][f] at the slot's bucket position, on the block-scaled MFMA
+// (ffn_mfma.hip; the token split into E4M3 terms per 32-element block inside the kernel); one
+// block per (slot, 16-row tile), one wave per 8-step K chunk. x is bf16 (xf32 == 0) or fp32.
 hipError_t launch_gateup_decode_packed(int d, int f, int k, const void* x, int xf32,
                                        const MxPtrs& w, const int32_t* pair_pos,
                                        const int32_t* pair_exp, float* h, hipStream_t s);
