@@ -1423,8 +1423,12 @@ __global__ __launch_bounds__(1024) void down_decode_mfma_kernel(DownDecMArgs a) 
   for (int v0 = 0; v0 < NR; ++v0)
     mx = fmaxf(mx, fmaxf(fmaxf(fabsf(hv[v0][0]), fabsf(hv[v0][1])),
                          fmaxf(fabsf(hv[v0][2]), fabsf(hv[v0][3]))));
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  mx = fmaxf(mx, lane_xor_f<1>(mx, lane));
+  mx = fmaxf(mx, lane_xor_f<2>(mx, lane));
+  mx = fmaxf(mx, lane_xor_f<4>(mx, lane));
+  mx = fmaxf(mx, lane_xor_f<8>(mx, lane));
+  mx = fmaxf(mx, lane_xor_f<16>(mx, lane));
+  mx = fmaxf(mx, lane_xor_f<32>(mx, lane));
   const int e0 = top_exp(mx);
   const bool bad = e0 == kExpBad;
   const int s0 = bad ? 255 : min(max(e0 + 127, 0), 254);
@@ -1506,8 +1510,9 @@ __global__ __launch_bounds__(1024) void down_decode_mfma_kernel(DownDecMArgs a) 
     float (*zb)[16] = zs[it & 1];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float c1 = __shfl_down(acc[i], 1, 64);
-      const float c2 = __shfl_down(acc[i], 2, 64);
+      // lane (0, g) takes columns 1 and 2 from lanes (1, g) and (2, g)
+      const float c1 = lane_xor_f<1>(acc[i], lane);
+      const float c2 = lane_xor_f<2>(acc[i], lane);
       if (ln == 0) zb[q][4 * g + i] = sv ? (acc[i] + c1) + c2 : 0.0f;
     }
     // barrier without draining the next tile's loads: only LDS writes must be complete
@@ -1599,8 +1604,9 @@ __global__ __launch_bounds__(64 * kPkMaxWaves) void gateup_decode_packed_kernel(
     wu[j] = load_u32x4_nt(a.uq + qo + (size_t)j * 1024);
   }
   asm volatile("" ::: "memory");
-  // the token copies are the oldest loads: waiting for them leaves the other 18 in flight
-  asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+  // the token copies are the oldest loads: waiting for them leaves the other 18 in flight (as
+  // the builtin, so that the compiler's own waits for the weights stay per step)
+  wait_vm_known<18>();
   __builtin_amdgcn_wave_barrier();
   asm volatile("" ::: "memory");
 
@@ -1626,7 +1632,7 @@ __global__ __launch_bounds__(64 * kPkMaxWaves) void gateup_decode_packed_kernel(
   }
   // every lane holds its elements before any term overwrites the chunk
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  auto bmax = [](float m) { return fmaxf(m, __shfl_xor(m, 1, 64)); };  // the block's two lanes
+  auto bmax = [&](float m) { return fmaxf(m, lane_xor_f<1>(m, lane)); };  // the block's two lanes
   float mx = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(y[i]));
@@ -1686,11 +1692,12 @@ __global__ __launch_bounds__(64 * kPkMaxWaves) void gateup_decode_packed_kernel(
   // lane (ln, g) holds column ln (term ln) of tile rows 4 g .. 4 g + 3
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    float gs = accg[r] + __shfl_down(accg[r], 1, 64);
-    float us = accu[r] + __shfl_down(accu[r], 1, 64);
+    // lane (0, g) takes columns 1 (and 2) from lanes (1, g) (and (2, g))
+    float gs = accg[r] + lane_xor_f<1>(accg[r], lane);
+    float us = accu[r] + lane_xor_f<1>(accu[r], lane);
     if (NTM == 3) {
-      gs += __shfl_down(accg[r], 2, 64);
-      us += __shfl_down(accu[r], 2, 64);
+      gs += lane_xor_f<2>(accg[r], lane);
+      us += lane_xor_f<2>(accu[r], lane);
     }
     if (ln == 0) {
       part[c][0][4 * g + r] = gs;

@@ -88,17 +88,77 @@ __device__ __forceinline__ u32x4 load_u32x4_nt(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// The value that lane (lane ^ M) of the wave holds, M in {1, 2, 4, 8, 16, 32}: DPP moves within
+// rows of 16 lanes (quad permutations, the half-row mirror, a row rotation by 8) and the
+// gfx950 permlane swaps across rows, all VALU operations, so a butterfly stage costs no LDS
+// round trip (a bpermute does). lane = this thread's lane in the wave.
+template <int M>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v, int lane) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "butterfly stage");
+  if constexpr (M == 1) {
+    return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  } else if constexpr (M == 2) {
+    return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  } else if constexpr (M == 4) {
+    // lane ^ 7 within each half-row, then ^ 3 within each quad
+    const uint32_t t = __builtin_amdgcn_update_dpp(0u, v, 0x141, 0xF, 0xF, false);
+    return __builtin_amdgcn_update_dpp(0u, t, 0x1B, 0xF, 0xF, false);
+  } else if constexpr (M == 8) {
+    return __builtin_amdgcn_update_dpp(0u, v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else if constexpr (M == 16) {
+    // rows 0,2 receive rows 1,3 in the second result, rows 1,3 rows 0,2 in the first
+    const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane & 16) ? p[0] : p[1];
+  } else {
+    // lanes 0-31 receive lanes 32-63 in the second result, lanes 32-63 lanes 0-31 in the first
+    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane & 32) ? p[0] : p[1];
+  }
+}
+template <int M>
+__device__ __forceinline__ float lane_xor_f(float v, int lane) {
+  return __uint_as_float(lane_xor<M>(__float_as_uint(v), lane));
+}
+template <int M>
+__device__ __forceinline__ double lane_xor_d(double v, int lane) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint64_t lo = lane_xor<M>((uint32_t)b, lane), hi = lane_xor<M>((uint32_t)(b >> 32), lane);
+  return __longlong_as_double((long long)(lo | (hi << 32)));
+}
+// Lane (lane ^ m) for a wave-uniform m that the caller's unrolled loop makes a constant.
+__device__ __forceinline__ uint32_t lane_xor_rt(uint32_t v, int m, int lane) {
+  switch (m) {
+    case 1: return lane_xor<1>(v, lane);
+    case 2: return lane_xor<2>(v, lane);
+    case 4: return lane_xor<4>(v, lane);
+    case 8: return lane_xor<8>(v, lane);
+    case 16: return lane_xor<16>(v, lane);
+    default: return lane_xor<32>(v, lane);
+  }
+}
+
 // Sum over aligned groups of `G` lanes (G a power of two <= 64); every lane of a
 // group ends with the group's total. The reduction tree is fixed, so results are
 // identical from run to run.
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int off = 1; off < G; off <<= 1) v += __shfl_xor(v, off, kWave);
+  const int lane = (int)(threadIdx.x & (kWave - 1));
+  if (G > 1) v += lane_xor_f<1>(v, lane);
+  if (G > 2) v += lane_xor_f<2>(v, lane);
+  if (G > 4) v += lane_xor_f<4>(v, lane);
+  if (G > 8) v += lane_xor_f<8>(v, lane);
+  if (G > 16) v += lane_xor_f<16>(v, lane);
+  if (G > 32) v += lane_xor_f<32>(v, lane);
   return v;
 }
 __device__ __forceinline__ float group_sum_rt(float v, int G) {
-  for (int off = 1; off < G; off <<= 1) v += __shfl_xor(v, off, kWave);
+  const int lane = (int)(threadIdx.x & (kWave - 1));
+  if (G > 1) v += lane_xor_f<1>(v, lane);
+  if (G > 2) v += lane_xor_f<2>(v, lane);
+  if (G > 4) v += lane_xor_f<4>(v, lane);
+  if (G > 8) v += lane_xor_f<8>(v, lane);
+  if (G > 16) v += lane_xor_f<16>(v, lane);
+  if (G > 32) v += lane_xor_f<32>(v, lane);
   return v;
 }
 

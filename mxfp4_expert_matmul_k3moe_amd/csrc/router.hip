@@ -225,9 +225,9 @@ __device__ __forceinline__ void router_gemv_vec_block(int chunk, int cblk, int T
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         double v = acc[tt][c];
-        v += __shfl_xor(v, 8, 64);
-        v += __shfl_xor(v, 16, 64);
-        v += __shfl_xor(v, 32, 64);
+        v += lane_xor_d<8>(v, lane);
+        v += lane_xor_d<16>(v, lane);
+        v += lane_xor_d<32>(v, lane);
         acc[tt][c] = v;
       }
     if (rl == 0) {
@@ -566,7 +566,7 @@ constexpr int kMaxCand = 2048;  // candidate buffer; the exact ranking covers an
 //     lanes): the k-th best of them is at most the upper bits of the k-th best of all E,
 //     so the best such bound over the waves is a valid threshold, and every top-k element
 //     has its upper bits at or above it;
-//  3. candidates at or above the threshold are compacted into LDS (wave scans) and ranked
+//  3. candidates at or above the threshold are compacted into LDS (ballot counts) and ranked
 //     exactly against each other; the softmax denominator is a per-thread ordered sum and
 //     a fixed reduction tree.
 // With `bk` (T == 1) the same block also writes the expert bucket of the single token.
@@ -684,9 +684,11 @@ __device__ __forceinline__ void route_topk_block(int t, int T, int E, int k,
   //    best and lane k-1 its k-th best
   {
     uint32_t sk = (bi >= 0) ? (uint32_t)(bkey >> 32) : 0u;
+#pragma unroll
     for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
       for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        const uint32_t pk = (uint32_t)__shfl_xor((int)sk, stride, 64);
+        const uint32_t pk = lane_xor_rt(sk, stride, lane);  // a constant stride once unrolled
         const bool desc = (lane & size) == 0;  // this run of `size` lanes sorts best-first
         const bool low = (lane & stride) == 0;
         sk = (low == desc) ? (pk > sk ? pk : sk) : (pk < sk ? pk : sk);
@@ -726,14 +728,26 @@ __device__ __forceinline__ void route_topk_block(int t, int T, int E, int k,
       se += exp(key_to_double(key[j]) - m);
     }
   }
-  int pre = mine;
-  for (int off = 1; off < 64; off <<= 1) {
-    const int v = __shfl_up(pre, off, 64);
-    if (lane >= off) pre += v;
+  // exclusive prefix of `mine` (at most KPT) over the wave's lanes and the wave's total, from
+  // the ballots of its bits
+  int pre = 0, wtot = 0;
+#pragma unroll
+  for (int bit = 0; (1 << bit) <= KPT; ++bit) {
+    const uint64_t bm = __ballot((mine >> bit) & 1);
+    pre += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u)) << bit;
+    wtot += __popcll(bm) << bit;
   }
-  for (int off = 32; off >= 1; off >>= 1) se += __shfl_xor(se, off, 64);
-  if (lane == 63) w_cnt[wave] = pre;
-  if (lane == 0) w_sum[wave] = se;
+  se += lane_xor_d<32>(se, lane);
+  se += lane_xor_d<16>(se, lane);
+  se += lane_xor_d<8>(se, lane);
+  se += lane_xor_d<4>(se, lane);
+  se += lane_xor_d<2>(se, lane);
+  se += lane_xor_d<1>(se, lane);
+  if (lane == 0) {
+    w_cnt[wave] = wtot;
+    w_sum[wave] = se;
+  }
   __syncthreads();
   int base = 0, total = 0;
   double wsum = 0.0;
@@ -743,7 +757,7 @@ __device__ __forceinline__ void route_topk_block(int t, int T, int E, int k,
     wsum += w_sum[w];
   }
   const double sum = anynan ? __builtin_nan("") : wsum;
-  pre = base + pre - mine;
+  pre += base;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int e = tid + NT * j;
@@ -769,8 +783,8 @@ __device__ __forceinline__ void route_topk_block(int t, int T, int E, int k,
 #pragma unroll 4
       for (int j = part; j < total; j += 4) r += better(ckey[j], cid[j], kv, id) ? 1 : 0;
     }
-    r += __shfl_xor(r, 1, 64);
-    r += __shfl_xor(r, 2, 64);
+    r += (int)lane_xor<1>((uint32_t)r, lane);
+    r += (int)lane_xor<2>((uint32_t)r, lane);
     if (has && part == 0 && r < k) {
       ids[(size_t)t * k + r] = id;
       gates[(size_t)t * k + r] = (float)(exp(key_to_double(kv) - m) / sum);
