@@ -674,6 +674,11 @@ def bench_stack(args, w) -> int:
         kern[name] = sum(times) / len(times)
     gu_bytes = w.k * 2 * w.f * (w.d // 2 + w.d // 32)
     dn_bytes = w.k * w.d * (w.f // 2 + w.f // 32)
+    # packed experts at these shapes: the gate/up launch also runs the shared expert's bf16
+    # down GEMV (its d x f weights are part of that launch's bytes)
+    shared_in_gu = packed and 256 < w.E <= 4096 and w.E % 8 == 0 and w.d <= 8192
+    if shared_in_gu:
+        gu_bytes += w.d * w.f * 2
     value = bytes_step * args.steps / (t1 - t0) / 1e9
     ach = gu_bytes / (kern["gate_up"] * 1e-3) / 1e9
     out = {
@@ -696,7 +701,11 @@ def bench_stack(args, w) -> int:
                    "hip_graph": bool(args.graph),
                    "expert_layout": "packed" if packed else "row-major"},
         "roofline": {"bound": "hbm",
-                     "kernel": ("gateup_decode_packed_kernel<fp32 x> (MXFP4 gate/up + "
+                     "kernel": ("gateup_packed_shared_down_kernel<fp32 x> (MXFP4 gate/up + "
+                                "SwiGLU on the block-scaled MFMA, packed tile layout, and the "
+                                "shared expert's bf16 down GEMV in the same launch)"
+                                if shared_in_gu else
+                                "gateup_decode_packed_kernel<fp32 x> (MXFP4 gate/up + "
                                 "SwiGLU, packed tile layout)" if packed else
                                 "gateup_decode_kernel<fp32 x> (MXFP4 gate/up GEMV + SwiGLU)"),
                      "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

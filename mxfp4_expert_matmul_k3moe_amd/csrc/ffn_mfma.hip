@@ -19,6 +19,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "block_dev.h"
 #include "k3moe_device.h"
 #include "k3moe_launch.h"
 
@@ -1565,11 +1566,11 @@ __host__ __device__ constexpr int pk_wave_lds(bool xf32) {
   return xf32 ? 4096 : 2048 + 2 * 32;
 }
 
+// Work item `item` = (slot, tile) of the block; xl: the dynamic LDS (nch * AREA bytes);
+// part: per-chunk row sums.
 template <bool XF32>
-__global__ __launch_bounds__(64 * kPkMaxWaves) void gateup_decode_packed_kernel(
-    GateUpPackedArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
-  __shared__ float part[kPkMaxWaves][2][16];
+__device__ __forceinline__ void gateup_packed_item(int item, const GateUpPackedArgs& a,
+                                                   uint8_t* xl, float (*part)[2][16]) {
   constexpr int NTM = XF32 ? 3 : 2;  // E4M3 terms of the token
   constexpr int AREA = pk_wave_lds(XF32);
   const int d = a.d, f = a.f;
@@ -1577,7 +1578,7 @@ __global__ __launch_bounds__(64 * kPkMaxWaves) void gateup_decode_packed_kernel(
   const int c = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // this wave's chunk
   const int g = lane >> 4, ln = lane & 15;
   const int ntile = f >> 4, nk = d / 128, nch = nk >> 3;
-  const int q = blockIdx.x / ntile, t = blockIdx.x - (blockIdx.x / ntile) * ntile;
+  const int q = item / ntile, t = item - (item / ntile) * ntile;
   const int pos = __builtin_amdgcn_readfirstlane(a.pair_pos[q]);
   const int e = __builtin_amdgcn_readfirstlane(a.pair_exp[q]);
   if (pos < 0 || e < 0) return;  // block-uniform
@@ -1715,6 +1716,38 @@ __global__ __launch_bounds__(64 * kPkMaxWaves) void gateup_decode_packed_kernel(
   }
 }
 
+template <bool XF32>
+__global__ __launch_bounds__(64 * kPkMaxWaves) void gateup_decode_packed_kernel(
+    GateUpPackedArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
+  __shared__ float part[kPkMaxWaves][2][16];
+  gateup_packed_item<XF32>(blockIdx.x, a, xl, part);
+}
+
+// Block mode: the expert items, then the shared expert's down GEMV (out = W hsh, bf16 W
+// [d][f]) in the blocks after them, one row group of the block's waves each; its 22 MB at the
+// K3 shapes fill the tail of the expert stream.
+struct SharedDownArgs {
+  int d, f;
+  const float* hsh;
+  const uint16_t* w;
+  float* out;
+};
+template <bool XF32>
+__global__ __launch_bounds__(64 * kPkMaxWaves) void gateup_packed_shared_down_kernel(
+    GateUpPackedArgs a, SharedDownArgs sd) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
+  __shared__ float part[kPkMaxWaves][2][16];
+  const int items = a.k * (a.f >> 4);
+  if ((int)blockIdx.x < items) {  // block-uniform
+    gateup_packed_item<XF32>(blockIdx.x, a, xl, part);
+    return;
+  }
+  StageRow stg{sd.hsh, sd.f};
+  bf16_gemv_rows<false>((int)blockIdx.x - items, (int)gridDim.x - items, 1, sd.d, sd.f, stg, sd.w,
+                        nullptr, sd.out, reinterpret_cast<f32x4*>(xl));
+}
+
 }  // namespace
 
 int mfma_mtiles_bound(int T, int E, int k) {
@@ -1814,7 +1847,8 @@ hipError_t launch_down_decode_mfma(int d, int f, int k, const MxPtrs& w, const f
 
 hipError_t launch_gateup_decode_packed(int d, int f, int k, const void* x, int xf32,
                                        const MxPtrs& w, const int32_t* pair_pos,
-                                       const int32_t* pair_exp, float* h, hipStream_t s) {
+                                       const int32_t* pair_exp, float* h, hipStream_t s,
+                                       const SharedDown* shared) {
   if (d % 1024 != 0 || f % 16 != 0) return hipErrorInvalidValue;
   const int nch = d / 1024;
   if (nch < 1 || nch > kPkMaxWaves) return hipErrorInvalidValue;
@@ -1822,13 +1856,26 @@ hipError_t launch_gateup_decode_packed(int d, int f, int k, const void* x, int x
   a.d = d; a.f = f; a.k = k; a.x = x;
   a.gq = w.gate_q; a.gs = w.gate_s; a.uq = w.up_q; a.us = w.up_s;
   a.pair_pos = pair_pos; a.pair_exp = pair_exp; a.h = h;
-  const dim3 grid((unsigned)(k * (f / 16))), block((unsigned)(64 * nch));
+  const int items = k * (f / 16);
+  const dim3 block((unsigned)(64 * nch));
+  const uint32_t lds = (uint32_t)(nch * pk_wave_lds(xf32 != 0));
+  if (shared) {
+    // the shared down's staged hsh (f floats) fits the expert items' LDS: f <= 16 d / 4
+    if ((size_t)f * 4 > lds || f % 8 != 0) return hipErrorInvalidValue;
+    SharedDownArgs sd{d, f, shared->hsh, shared->w, shared->out};
+    const int rows = gemv_group_rows(f, nch);
+    const dim3 grid((unsigned)(items + (d + rows - 1) / rows));
+    if (xf32)
+      launch_timed(gateup_packed_shared_down_kernel<true>, grid, block, lds, s, a, sd);
+    else
+      launch_timed(gateup_packed_shared_down_kernel<false>, grid, block, lds, s, a, sd);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)items);
   if (xf32)
-    launch_timed(gateup_decode_packed_kernel<true>, grid, block,
-                 (uint32_t)(nch * pk_wave_lds(true)), s, a);
+    launch_timed(gateup_decode_packed_kernel<true>, grid, block, lds, s, a);
   else
-    launch_timed(gateup_decode_packed_kernel<false>, grid, block,
-                 (uint32_t)(nch * pk_wave_lds(false)), s, a);
+    launch_timed(gateup_decode_packed_kernel<false>, grid, block, lds, s, a);
   return hipGetLastError();
 }
 

@@ -332,7 +332,7 @@ int run_ffn(const k3moe_dims& dm, int32_t T, const void* x, int xf32,
             const k3moe_mx_experts* ex, const int32_t* offsets, const int32_t* rows,
             const float* gates, const float* resid, const float* shared, float* y,
             uint16_t* y_bf16, const Ws& ws, hipStream_t s, hipEvent_t shared_ready = nullptr,
-            bool packed = false) {
+            bool packed = false, const k3moe::SharedDown* shared_down = nullptr) {
   auto join = [&]() -> int {
     return shared_ready ? hip_check(hipStreamWaitEvent(s, shared_ready, 0), "join shared expert")
                         : 0;
@@ -347,13 +347,15 @@ int run_ffn(const k3moe_dims& dm, int32_t T, const void* x, int xf32,
                          reinterpret_cast<uintptr_t>(ex->up_s) |
                          reinterpret_cast<uintptr_t>(ex->down_s)) & 3u) == 0;
   if (packed && T == 1 && k3moe::down_decode_mfma_supported(d, f, k)) {
-    // packed tile layout, one token: h per (slot, 16-row tile), then the decode down kernel
-    // adds the slots in order
+    // packed tile layout, one token: h per (slot, 16-row tile) (and, in block mode, the shared
+    // expert's down GEMV in the same launch), then the decode down kernel adds the slots in
+    // order
     {
       Probe probe(K3MOE_KERNEL_GATE_UP, s);
       rc = hip_check(k3moe::launch_gateup_decode_packed(d, f, k, x, xf32, w,
                                                         ws.at<int32_t>(R_PPOS),
-                                                        ws.at<int32_t>(R_PEXP), h, s),
+                                                        ws.at<int32_t>(R_PEXP), h, s,
+                                                        shared_down),
                      "gate/up (decode, packed)");
     }
     if (rc || (rc = join())) return rc;
@@ -363,6 +365,9 @@ int run_ffn(const k3moe_dims& dm, int32_t T, const void* x, int xf32,
                                                     y, y_bf16, cu_count(), s, true),
                      "down+combine (decode, packed)");
   }
+  if (shared_down)  // only the one-token packed launch runs it; callers check the shape first
+    return fail(K3MOE_EUNSUPPORTED, "the shared expert's down GEMV rides only in the one-token "
+                                    "packed gate/up launch");
   if (packed) {
     // packed tile layout: grouped GEMMs on the block-scaled MFMA for every token count (the
     // shapes and the bf16 activations were checked by the entry point)
@@ -761,6 +766,12 @@ int check_layer(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
   return K3MOE_OK;
 }
 
+// One token on the packed layout runs the one-token kernels, which also take fp32 tokens
+// (and so block mode, whose RMSNorm output is fp32).
+bool packed_one_token(const k3moe_dims& dm, int32_t T) {
+  return T == 1 && k3moe::down_decode_mfma_supported(dm.d_model, dm.d_ff, dm.top_k);
+}
+
 // The layer on a carved workspace. side_ok: block mode's shared expert may run on the
 // library's side stream (created on first use); otherwise it runs in order on `s` (same
 // kernels, same buffers, so the same results bit for bit).
@@ -784,6 +795,23 @@ int run_layer(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
       k3moe::route_shared_supported(d, dims->n_experts, dims->top_k, w_router)) {
     float* xhat = w.at<float>(R_XHAT);
     float* ssh = w.at<float>(R_SSH);
+    if (packed && packed_one_token(*dims, T)) {
+      // packed experts: the shared gate/up rides with the top-k, the shared down with the
+      // expert gate/up
+      {
+        Probe probe(K3MOE_KERNEL_ROUTER, s);
+        rc = hip_check(k3moe::launch_route_norm_shared_gateup(
+                           d, dims->d_ff, dims->n_experts, dims->top_k,
+                           static_cast<const float*>(x), blk->rms_gamma, blk->rms_eps, xhat,
+                           w_router, logit_bias, w.at<double>(R_PART), blk->sh_gate,
+                           blk->sh_up, w.at<float>(R_HSH), ids, gates, bo, s),
+                       "rmsnorm + router, top-k + shared gate/up");
+      }
+      if (rc) return rc;
+      const k3moe::SharedDown sdn{w.at<float>(R_HSH), blk->sh_down, ssh};
+      return run_ffn(*dims, T, xhat, 1, experts, offs, rows, gates,
+                     static_cast<const float*>(x), ssh, y, y_bf16, w, s, nullptr, packed, &sdn);
+    }
     {
       Probe probe(K3MOE_KERNEL_ROUTER, s);
       rc = hip_check(k3moe::launch_route_shared(
@@ -851,12 +879,7 @@ int run_layer(const k3moe_dims* dims, int32_t T, const void* x, int x_dtype,
                  joined, packed);
 }
 
-// Shapes and activations the packed-layout kernels take.
-// One token on the packed layout runs the one-token kernels, which also take fp32 tokens
-// (and so block mode, whose RMSNorm output is fp32).
-bool packed_one_token(const k3moe_dims& dm, int32_t T) {
-  return T == 1 && k3moe::down_decode_mfma_supported(dm.d_model, dm.d_ff, dm.top_k);
-}
+// Shapes and activations the packed-layout kernels take (packed_one_token above).
 
 int check_packed(const k3moe_dims& dm, int32_t T, int x_dtype) {
   if (!k3moe::packed_shape_supported(dm.d_model, dm.d_ff))

@@ -86,6 +86,16 @@ hipError_t launch_route_shared(int d, int f, int E, int k, const float* h,
                                const uint16_t* sh_down, float* hsh, float* ssh, int32_t* ids,
                                float* gates, const BucketOut& bucket1, int gateup_blocks,
                                hipStream_t s);
+// Same shapes, packed experts (whose one-token gate/up launch takes the shared down, see
+// launch_gateup_decode_packed): the RMSNorm and the router GEMV in one launch, then the top-k
+// with the token's bucket and the shared gate/up GEMV (on the stored xhat) in a second.
+hipError_t launch_route_norm_shared_gateup(int d, int f, int E, int k, const float* h,
+                                           const uint16_t* gamma, float eps, float* xhat,
+                                           const uint16_t* w_router, const float* bias,
+                                           double* part, const uint16_t* sh_gate,
+                                           const uint16_t* sh_up, float* hsh, int32_t* ids,
+                                           float* gates, const BucketOut& bucket1,
+                                           hipStream_t s);
 hipError_t launch_bucket(int T, int E, int k, const int32_t* ids, const BucketOut& o,
                          uint32_t* hist, uint32_t* base, uint64_t* masks, hipStream_t s);
 // From caller-supplied offsets/rows (k3moe_expert_ffn): act, n_act, pair_pos, pair_exp.
@@ -132,9 +142,17 @@ hipError_t launch_down_decode_mfma(int d, int f, int k, const MxPtrs& w, const f
 // of every slot as fp32 into h [k][f] at the slot's bucket position, on the block-scaled MFMA
 // (ffn_mfma.hip; the token split into E4M3 terms per 32-element block inside the kernel); one
 // block per (slot, 16-row tile), one wave per 8-step K chunk. x is bf16 (xf32 == 0) or fp32.
+// shared (nullable, block mode): the same launch also runs the shared expert's down GEMV,
+// out[r] = W[r] . hsh for the d rows of the bf16 [d][f] W, in blocks after the expert ones.
+struct SharedDown {
+  const float* hsh;
+  const uint16_t* w;
+  float* out;
+};
 hipError_t launch_gateup_decode_packed(int d, int f, int k, const void* x, int xf32,
                                        const MxPtrs& w, const int32_t* pair_pos,
-                                       const int32_t* pair_exp, float* h, hipStream_t s);
+                                       const int32_t* pair_exp, float* h, hipStream_t s,
+                                       const SharedDown* shared = nullptr);
 // Any T: per-expert down projection into z [P][d] (pair-indexed).
 hipError_t launch_down_gemv(int T, int d, int f, int E, int k, const MxPtrs& w,
                             const float* h, const int32_t* offsets, const int32_t* rows,

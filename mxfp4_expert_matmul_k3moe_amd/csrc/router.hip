@@ -554,7 +554,6 @@ __device__ __forceinline__ bool better(uint64_t ka, int ia, uint64_t kb, int ib)
 
 constexpr int kMaxE = 4096;
 constexpr int kMaxSlots = 32;
-constexpr int kMaxCand = 2048;  // candidate buffer; the exact ranking covers any count
 
 // One block per token of NT = blockDim.x threads (a multiple of 64, at most 256): thread t
 // holds the logits of experts t + NT*j (j < KPT) in registers. WIDE: the block has 1024
@@ -587,9 +586,11 @@ __device__ __forceinline__ void route_topk_block(int t, int T, int E, int k,
                                                  const float* __restrict__ bias,
                                                  int32_t* __restrict__ ids,
                                                  float* __restrict__ gates, Bucket1 bk) {
-  __shared__ uint64_t keys[kMaxE];
-  __shared__ uint64_t ckey[kMaxCand];
-  __shared__ int cid[kMaxCand];
+  // every expert's key, and room for every candidate (E <= 256 KPT)
+  constexpr int NKEY = 256 * KPT;
+  __shared__ uint64_t keys[NKEY];
+  __shared__ uint64_t ckey[NKEY];
+  __shared__ int cid[NKEY];
   __shared__ uint32_t w_tk[kTopkMaxWaves], w_mk[kTopkMaxWaves];
   __shared__ int w_ok[kTopkMaxWaves], w_cnt[kTopkMaxWaves], w_nan[kTopkMaxWaves];
   __shared__ double w_sum[kTopkMaxWaves];
@@ -762,10 +763,8 @@ __device__ __forceinline__ void route_topk_block(int t, int T, int E, int k,
   for (int j = 0; j < KPT; ++j) {
     const int e = tid + NT * j;
     if (e < E && (uint32_t)(key[j] >> 32) >= tk) {
-      if (pre < kMaxCand) {
-        cid[pre] = e;
-        ckey[pre] = key[j];
-      }
+      cid[pre] = e;
+      ckey[pre] = key[j];
       ++pre;
     }
   }
@@ -790,7 +789,7 @@ __device__ __forceinline__ void route_topk_block(int t, int T, int E, int k,
       gates[(size_t)t * k + r] = (float)(exp(key_to_double(kv) - m) / sum);
       if (bk.offsets) s_ids[r] = id;
     }
-  } else if (total <= kMaxCand) {
+  } else {
     for (int c = tid; c < total; c += NT) {
       const int id = cid[c];
       const uint64_t kv = ckey[c];
@@ -801,19 +800,6 @@ __device__ __forceinline__ void route_topk_block(int t, int T, int E, int k,
         ids[(size_t)t * k + r] = id;
         gates[(size_t)t * k + r] = (float)(exp(key_to_double(kv) - m) / sum);
         if (bk.offsets) s_ids[r] = id;
-      }
-    }
-  } else {
-    // very many exact ties: rank every candidate against all logits
-    for (int e = tid; e < E; e += NT) {
-      const uint64_t kv = keys[e];
-      if ((uint32_t)(kv >> 32) < tk) continue;
-      int r = 0;
-      for (int j = 0; j < E; ++j) r += better(keys[j], j, kv, e) ? 1 : 0;
-      if (r < k) {
-        ids[(size_t)t * k + r] = e;
-        gates[(size_t)t * k + r] = (float)(exp(key_to_double(kv) - m) / sum);
-        if (bk.offsets) s_ids[r] = e;
       }
     }
   }
@@ -949,6 +935,32 @@ __global__ __launch_bounds__(1024) void topk_shared_down_kernel(RouteSharedArgs 
                         nullptr, a.ssh, xs);
 }
 
+// Packed experts at one token: the router launch carries only the RMSNorm (router_norm_kernel),
+// the top-k launch the shared gate/up (topk_shared_gateup_kernel: block 0 the top-k of 256
+// threads, the others the shared gate/up row groups on the xhat the router blocks stored), and
+// the shared down rides in the expert gate/up launch (ffn_mfma.hip): the top-k leaves a whole
+// launch of HBM bandwidth idle that the 44 MB of shared gate/up weights fill, and the router
+// launch, the critical one, no longer waits for them.
+__global__ __launch_bounds__(256) void router_norm_kernel(RouteSharedArgs a) {
+  __shared__ double red[4];
+  const int b = blockIdx.x;
+  const int chunk = b % a.nchunk, cblk = b / a.nchunk;
+  XNormRow xl{a.h, a.gamma, cblk == 0 ? a.xhat : nullptr, a.d, chunk * kRouterRows, a.eps, red};
+  router_gemv_vec_block<true, 1>(chunk, cblk, 1, a.d, a.E, xl, a.w_router, a.part);
+}
+
+template <int KPT>
+__global__ __launch_bounds__(256) void topk_shared_gateup_kernel(RouteSharedArgs a) {
+  extern __shared__ __attribute__((aligned(16))) f32x4 xs[];
+  if (blockIdx.x == 0) {
+    route_topk_block<KPT, false>(0, 1, a.E, a.k, a.part, a.nchunk, a.bias, a.ids, a.gates, a.bk);
+    return;
+  }
+  StageRow stg{a.xhat, a.d};
+  bf16_gemv_rows<true>((int)blockIdx.x - 1, (int)gridDim.x - 1, 1, a.f, a.d, stg, a.sh_gate,
+                       a.sh_up, a.hsh, xs);
+}
+
 }  // namespace
 
 int router_chunk_rows(int) { return kRouterRows; }
@@ -1049,14 +1061,13 @@ bool route_shared_supported(int d, int E, int k, const uint16_t* w_router) {
          k <= kMaxSlots && k <= E && (reinterpret_cast<uintptr_t>(w_router) & 15u) == 0;
 }
 
-hipError_t launch_route_shared(int d, int f, int E, int k, const float* h,
-                               const uint16_t* gamma, float eps, float* xhat,
-                               const uint16_t* w_router, const float* bias, double* part,
-                               const uint16_t* sh_gate, const uint16_t* sh_up,
-                               const uint16_t* sh_down, float* hsh, float* ssh, int32_t* ids,
-                               float* gates, const BucketOut& bucket1, int gateup_blocks,
-                               hipStream_t s) {
-  if (!route_shared_supported(d, E, k, w_router)) return hipErrorInvalidValue;
+namespace {
+RouteSharedArgs route_shared_args(int d, int f, int E, int k, const float* h,
+                                  const uint16_t* gamma, float eps, float* xhat,
+                                  const uint16_t* w_router, const float* bias, double* part,
+                                  const uint16_t* sh_gate, const uint16_t* sh_up,
+                                  const uint16_t* sh_down, float* hsh, float* ssh, int32_t* ids,
+                                  float* gates, const BucketOut& bucket1) {
   RouteSharedArgs a;
   a.d = d; a.f = f; a.E = E; a.k = k; a.h = h; a.gamma = gamma; a.eps = eps; a.xhat = xhat;
   a.w_router = w_router; a.part = part;
@@ -1066,6 +1077,21 @@ hipError_t launch_route_shared(int d, int f, int E, int k, const float* h,
   a.bias = bias; a.ids = ids; a.gates = gates;
   a.bk = Bucket1{bucket1.offsets, bucket1.rows, bucket1.act, bucket1.n_act, bucket1.pair_pos,
                  bucket1.pair_exp, bucket1.mtile_off};
+  return a;
+}
+}  // namespace
+
+hipError_t launch_route_shared(int d, int f, int E, int k, const float* h,
+                               const uint16_t* gamma, float eps, float* xhat,
+                               const uint16_t* w_router, const float* bias, double* part,
+                               const uint16_t* sh_gate, const uint16_t* sh_up,
+                               const uint16_t* sh_down, float* hsh, float* ssh, int32_t* ids,
+                               float* gates, const BucketOut& bucket1, int gateup_blocks,
+                               hipStream_t s) {
+  if (!route_shared_supported(d, E, k, w_router)) return hipErrorInvalidValue;
+  const RouteSharedArgs a = route_shared_args(d, f, E, k, h, gamma, eps, xhat, w_router, bias,
+                                              part, sh_gate, sh_up, sh_down, hsh, ssh, ids,
+                                              gates, bucket1);
   // shared gate/up: one block per row group of 4 waves (gateup_blocks > 0 caps the count);
   // shared down: one block per row group of the top-k block's 16 waves
   const int rows_gu = gemv_group_rows(d, 4), rows_dn = gemv_group_rows(f, 16);
@@ -1079,6 +1105,29 @@ hipError_t launch_route_shared(int d, int f, int E, int k, const float* h,
   else if (kpt <= 4) topk_shared_down_kernel<4><<<1 + ndb, 1024, lds, s>>>(a);
   else if (kpt <= 8) topk_shared_down_kernel<8><<<1 + ndb, 1024, lds, s>>>(a);
   else topk_shared_down_kernel<16><<<1 + ndb, 1024, lds, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_norm_shared_gateup(int d, int f, int E, int k, const float* h,
+                                           const uint16_t* gamma, float eps, float* xhat,
+                                           const uint16_t* w_router, const float* bias,
+                                           double* part, const uint16_t* sh_gate,
+                                           const uint16_t* sh_up, float* hsh, int32_t* ids,
+                                           float* gates, const BucketOut& bucket1,
+                                           hipStream_t s) {
+  if (!route_shared_supported(d, E, k, w_router)) return hipErrorInvalidValue;
+  const RouteSharedArgs a = route_shared_args(d, f, E, k, h, gamma, eps, xhat, w_router, bias,
+                                              part, sh_gate, sh_up, nullptr, hsh, nullptr, ids,
+                                              gates, bucket1);
+  router_norm_kernel<<<a.nrb, 256, 0, s>>>(a);
+  const int rows_gu = gemv_group_rows(d, 4);
+  const int nsb = (f + rows_gu - 1) / rows_gu;
+  const int kpt = (E + 255) / 256;
+  const size_t lds = (size_t)d * 4;
+  if (kpt <= 2) topk_shared_gateup_kernel<2><<<1 + nsb, 256, lds, s>>>(a);
+  else if (kpt <= 4) topk_shared_gateup_kernel<4><<<1 + nsb, 256, lds, s>>>(a);
+  else if (kpt <= 8) topk_shared_gateup_kernel<8><<<1 + nsb, 256, lds, s>>>(a);
+  else topk_shared_gateup_kernel<16><<<1 + nsb, 256, lds, s>>>(a);
   return hipGetLastError();
 }
 
