@@ -208,11 +208,13 @@ def test_packed_block_mode_small_chain(dev):
     assert err.max() <= 1e-4 and el.max() <= ELEM_FACTOR * 1e-4
 
 
-def test_packed_block_mode_wide_router_chain(dev):
-    """Block mode on packed experts with more than 256 experts (the shared expert's GEMVs
-    ride in the router and top-k launches): three chained blocks against the oracle."""
-    w = Workload("pk_block_e320", 68, d=2048, f=1024, E=320, k=4, T=1, layers=3, block=True)
-    say("packed block mode, 3 chained blocks d=2048 f=1024 E=320")
+@pytest.mark.parametrize("E", [320, 1032])
+def test_packed_block_mode_wide_router_chain(dev, E):
+    """Block mode on packed experts with more than 256 experts (the shared gate/up rides in
+    the top-k launch, the shared down in the expert gate/up launch; E = 1032: five keys per
+    top-k thread): three chained blocks against the oracle."""
+    w = Workload(f"pk_block_e{E}", 68, d=2048, f=1024, E=E, k=4, T=1, layers=3, block=True)
+    say(f"packed block mode, 3 chained blocks d=2048 f=1024 E={E}")
     h0 = w.resid0()
     ref = harness.run_stack(w, h0)
     h = torch.from_numpy(h0).to(dev)

@@ -399,12 +399,13 @@ def test_block_mode_small_chain(dev):
     assert err.max() < 1e-4
 
 
-def test_block_mode_wide_router_chain(dev):
+@pytest.mark.parametrize("E", [264, 1032])
+def test_block_mode_wide_router_chain(dev, E):
     """Block mode with more than 256 experts at one token, where the shared expert's GEMVs
-    ride in the router and top-k launches: three chained blocks against the oracle's stack,
-    routed exactly as the oracle at every block."""
-    w = Workload("block_e264", 23, d=512, f=256, E=264, k=4, T=1, layers=3, block=True)
-    say("block mode, 3 chained blocks, E=264, T=1")
+    ride in the router and top-k launches (E = 1032: five keys per top-k thread): three
+    chained blocks against the oracle's stack, routed exactly as the oracle at every block."""
+    w = Workload(f"block_e{E}", 23, d=512, f=256, E=E, k=4, T=1, layers=3, block=True)
+    say(f"block mode, 3 chained blocks, E={E}, T=1")
     h0 = w.resid0()
     ref = harness.run_stack(w, h0)
     h = torch.from_numpy(h0).to(dev)
