@@ -415,21 +415,24 @@ __global__ __launch_bounds__(64 * NW) void router_tok_kernel(int T, int d, int E
 // Many-token router on fp64 MFMA: part[c][t][e] = sum over the c-th K chunk of
 // x[t][k] * W[k][e], with v_mfma_f64_16x16x4_f64 (fp64 products and sums, like the
 // scalar paths). Block: 64 tokens x 64 experts x one K chunk, 4 waves of 32 x 32
-// (2 x 2 MFMA tiles). Operands are converted to fp64 once, when staged in LDS;
-// K advances 32 per stage, double-buffered, the next stage's global loads in flight
-// while the MFMAs of the current one run. Within a stage, lane group g = lane/16 feeds
-// k = 4 j + g to the j-th MFMA of every tile (A and B alike).
+// (2 x 2 MFMA tiles). Both operands (bf16, or fp32 tokens) are exact in fp32, so LDS holds
+// them as fp32 (four blocks fit on a CU) and each MFMA operand is widened to fp64 as it is
+// read. K advances 32 per stage, double-buffered: the next stage's global loads go out as raw
+// words before the current stage's MFMAs and are converted and stored after them, one block
+// barrier per stage. Within a stage, lane group g = lane/16 feeds k = 4 j + g to the j-th
+// MFMA of every tile (A and B alike).
 typedef double f64x4 __attribute__((ext_vector_type(4)));
-constexpr int kRmBK = 32;             // K per stage
-constexpr int kRmAP = kRmBK + 1;      // A row pitch in doubles (16 rows hit distinct banks)
+constexpr int kRmBK = 32;        // K per stage
+constexpr int kRmAP = kRmBK + 4; // A: token-major, pitch 36 floats (lane (ln, g) -> bank 4 ln + g)
+constexpr int kRmBP = 64 + 16;   // B: k-major, pitch 80 floats (lane groups 16 banks apart)
 
 template <bool XF32>
 __global__ __launch_bounds__(256) void router_mfma_kernel(int T, int d, int E, int kc,
                                                           const void* __restrict__ x,
                                                           const uint16_t* __restrict__ w,
                                                           double* __restrict__ part) {
-  __shared__ double As[2][64 * kRmAP];
-  __shared__ double Bs[2][kRmBK * 64];
+  __shared__ __align__(16) float As[2][64 * kRmAP];
+  __shared__ __align__(16) float Bs[2][kRmBK * kRmBP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 15, g = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
@@ -441,57 +444,66 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(int T, int d, int E, i
   // staging: thread -> (A row ar, 8 k at ak) and (B k-row bk, 8 experts at be)
   const int ar = tid >> 2, ak = (tid & 3) * 8;
   const int bk = tid >> 3, be = (tid & 7) * 8;
+  const int arow = min(t0 + ar, T - 1);  // rows past T load row T - 1 and store zeros
   const bool arow_ok = t0 + ar < T;
-  double av[8], bv[8];
   // 16-byte loads where the 8 values are contiguous and aligned (k chunks are multiples
   // of 32 and x rows are 16-byte aligned; W rows need E % 8 == 0 and an aligned base)
   const bool wvec = (E % 8) == 0 && (reinterpret_cast<uintptr_t>(w) & 15u) == 0;
+  // raw words of the next stage: A as 8 fp32 (qa0, qa1) or 8 bf16 (qa0); B as 8 bf16
+  u32x4 qa0, qa1 = u32x4{0u, 0u, 0u, 0u}, qb;
+  bool aok, bok;
   auto load = [&](int st) {
     const int k = kbeg + st * kRmBK;
-    const int ka = k + ak;
-    if (arow_ok && ka < kend) {
-      if (XF32) {
-        const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) +
-                                                          (size_t)(t0 + ar) * d + ka);
-        const f32x4 p0 = src[0], p1 = src[1];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          av[u] = (double)p0[u];
-          av[4 + u] = (double)p1[u];
-        }
-      } else {
-        const u32x4 q = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) +
-                                                        (size_t)(t0 + ar) * d + ka);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          av[2 * u] = (double)__uint_as_float(q[u] << 16);
-          av[2 * u + 1] = (double)__uint_as_float(q[u] & 0xFFFF0000u);
-        }
-      }
+    const int ka = k + ak, kb = k + bk;
+    aok = arow_ok && ka < kend;
+    // out-of-range pieces read an in-range address and are zeroed when stored, so no load
+    // sits behind a branch that would make the compiler wait for it there
+    const size_t aoff = (size_t)arow * d + (ka < kend ? ka : kbeg);
+    if (XF32) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const float*>(x) + aoff);
+      qa0 = src[0];
+      qa1 = src[1];
     } else {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) av[u] = 0.0;
+      qa0 = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + aoff);
     }
-    const int kb = k + bk, eb = e0 + be;
-    if (kb < kend && wvec && eb + 8 <= E) {
-      const u32x4 q = *reinterpret_cast<const u32x4*>(w + (size_t)kb * E + eb);
+    const int eb = e0 + be;
+    if (wvec) {
+      bok = kb < kend && eb + 8 <= E;
+      qb = *reinterpret_cast<const u32x4*>(w + (size_t)(kb < kend ? kb : kbeg) * E +
+                                           (eb + 8 <= E ? eb : 0));
+    } else {
+      bok = true;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        bv[2 * u] = (double)__uint_as_float(q[u] << 16);
-        bv[2 * u + 1] = (double)__uint_as_float(q[u] & 0xFFFF0000u);
+        const uint32_t lo = (kb < kend && eb + 2 * u < E) ? w[(size_t)kb * E + eb + 2 * u] : 0u;
+        const uint32_t hi =
+            (kb < kend && eb + 2 * u + 1 < E) ? w[(size_t)kb * E + eb + 2 * u + 1] : 0u;
+        qb[u] = lo | (hi << 16);
       }
-    } else {
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        bv[u] = (kb < kend && eb + u < E) ? (double)bf16_bits_to_f32(w[(size_t)kb * E + eb + u]) : 0.0;
     }
   };
   auto store = [&](int buf) {
+    f32x4 a0, a1, b0, b1;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      As[buf][ar * kRmAP + ak + u] = av[u];
-      Bs[buf][bk * 64 + be + u] = bv[u];
+    for (int u = 0; u < 4; ++u) {
+      if (XF32) {
+        a0[u] = __uint_as_float(qa0[u]);
+        a1[u] = __uint_as_float(qa1[u]);
+      } else {
+        const uint32_t q = qa0[u >> 1] >> (16 * (u & 1)), r = qa0[2 + (u >> 1)] >> (16 * (u & 1));
+        a0[u] = __uint_as_float(q << 16);
+        a1[u] = __uint_as_float(r << 16);
+      }
+      b0[u] = __uint_as_float((qb[u >> 1] >> (16 * (u & 1))) << 16);
+      b1[u] = __uint_as_float((qb[2 + (u >> 1)] >> (16 * (u & 1))) << 16);
     }
+    const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4* ad = reinterpret_cast<f32x4*>(&As[buf][ar * kRmAP + ak]);
+    f32x4* bd = reinterpret_cast<f32x4*>(&Bs[buf][bk * kRmBP + be]);
+    ad[0] = aok ? a0 : z;
+    ad[1] = aok ? a1 : z;
+    bd[0] = bok ? b0 : z;
+    bd[1] = bok ? b1 : z;
   };
 
   f64x4 acc[2][2];
@@ -511,17 +523,18 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(int T, int d, int E, i
       const int kk = 4 * j + g;
       double a[2], b[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = As[buf][(wm * 32 + i * 16 + ln) * kRmAP + kk];
+      for (int i = 0; i < 2; ++i) a[i] = (double)As[buf][(wm * 32 + i * 16 + ln) * kRmAP + kk];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) b[i] = Bs[buf][kk * 64 + wn * 32 + i * 16 + ln];
+      for (int i = 0; i < 2; ++i) b[i] = (double)Bs[buf][kk * kRmBP + wn * 32 + i * 16 + ln];
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
     }
+    // buffer buf ^ 1 was last read in stage st - 1, before every wave passed the previous
+    // barrier, so it can be refilled without another one
     if (st + 1 < nst) {
-      __syncthreads();
       store(buf ^ 1);
       __syncthreads();
     }
