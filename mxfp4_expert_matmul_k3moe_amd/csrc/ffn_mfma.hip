@@ -1149,14 +1149,31 @@ __device__ __forceinline__ void mx_down_tile_rw(const MfmaArgs& a, uint8_t* lds,
       wop[nt] = __builtin_shufflevector(wi, wi, 0, 1, 2, 3, -1, -1, -1, -1);
       wsc[nt] = (int)((scur[nt][U >> 2] >> (8 * (U & 3))) & 0xFFu);
     }
+    // the step's h scale bytes are read first; then the h operand of the next (m, t) is read
+    // before the MFMAs of this one are issued (the scheduling barrier keeps the read there:
+    // left free, the scheduler sinks it to just before its own MFMAs and the LDS latency
+    // stalls every group). Each accumulator still takes terms 0, 1, 2 in order.
+    int xsa[3 * MT];
+#pragma unroll
+    for (int mt = 0; mt < 3 * MT; ++mt)
+      xsa[mt] = st[ADATA + (mt / 3) * 256 + (ln + 16 * (mt % 3)) * 4 + g];
+    u32x4 hb0[2], hb1[2];
+    auto rd = [&](int mt, int p) {
+      const uint8_t* xb = st + mt * 2048 + lane * 16;
+      hb0[p] = *reinterpret_cast<const u32x4*>(xb);
+      hb1[p] = *reinterpret_cast<const u32x4*>(xb + 1024);
+    };
+    rd(0, 0);
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
-        const uint8_t* xb = st + ((m * 3 + t) * 2) * 1024 + lane * 16;
-        const u32x4 h0 = *reinterpret_cast<const u32x4*>(xb), h1 = *reinterpret_cast<const u32x4*>(xb + 1024);
+        const int mt = m * 3 + t, p = mt & 1;
+        const u32x4 h0 = hb0[p], h1 = hb1[p];
+        if (mt + 1 < 3 * MT) rd(mt + 1, p ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
         const i32x8 xop = {(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
-        const int xsc = st[ADATA + m * 256 + (ln + 16 * t) * 4 + g];
+        const int xsc = xsa[mt];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           acc[m][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wop[nt], xop, acc[m][nt], 4, 0, 0,
