@@ -158,18 +158,24 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(int NB, int E,
                                                            BucketOut o) {
   __shared__ int cnt[kMaxE];
   __shared__ int s_wave[17];
+  // totals first (independent loads, eight blocks' counts in flight at once), then the
+  // offsets, then each block's base in one pass: no read-modify-write chains on base
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     int run = 0;
-    for (int b = 0; b < NB; ++b) {
-      base[(size_t)b * E + e] = (uint32_t)run;
-      run += (int)hist[(size_t)b * E + e];
-    }
+#pragma unroll 8
+    for (int b = 0; b < NB; ++b) run += (int)hist[(size_t)b * E + e];
     cnt[e] = run;
   }
   __syncthreads();
   offsets_and_active(E, cnt, o, s_wave);
-  for (int e = threadIdx.x; e < E; e += blockDim.x)
-    for (int b = 0; b < NB; ++b) base[(size_t)b * E + e] += (uint32_t)cnt[e];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    uint32_t run = (uint32_t)cnt[e];
+#pragma unroll 8
+    for (int b = 0; b < NB; ++b) {
+      base[(size_t)b * E + e] = run;
+      run += hist[(size_t)b * E + e];
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void bucket_place_kernel(int T, int E, int k,
