@@ -357,6 +357,11 @@ def test_repeat_runs_bit_identical(dev):
     (1024, 40, 8, 13, "bf16"),     # one column slab with 5 of 64 lanes in use
     (2080, 520, 16, 64, "f32"),    # last chunk 32 rows (one wave), second slab one lane wide
     (7168, 896, 16, 64, "f32"),
+    # more than 64 tokens: the fp64 MFMA router (64 x 64 tiles, K split into chunks)
+    (7168, 896, 16, 100, "bf16"),  # 8 K chunks of 896, second token tile 36 rows
+    (7008, 896, 16, 300, "bf16"),  # 8 K chunks, the last 736 deep; last token tile 44 rows
+    (2080, 520, 16, 130, "f32"),   # fp32 tokens, 5 K chunks of 416, last expert tile 8 wide
+    (1024, 44, 8, 70, "bf16"),     # E % 8 != 0: router weights read element by element
 ])
 def test_router_multi_token_shapes(dev, d, E, k, T, xdt):
     say(f"router, several tokens: d={d} E={E} k={k} T={T} x={xdt}")
