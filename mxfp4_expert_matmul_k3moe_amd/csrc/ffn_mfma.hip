@@ -1237,8 +1237,12 @@ __global__ __launch_bounds__(256) void x8_prep_kernel(int d, const uint16_t* __r
     if (m == 0.0f) return -0x7fffffff;
     return ilogbf(m) - 7;
   };
-  auto to_e4m3 = [](float v) { return __builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xFF; };
-  auto from_e4m3 = [](int q) { return __builtin_amdgcn_cvt_f32_fp8(q, 0); };
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  // four E4M3 codes (RNE) in one dword, byte i from v_i
+  auto pk_e4m3 = [](float v0, float v1, float v2, float v3) {
+    return __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false),
+                                           true);
+  };
   auto unpack = [](uint2 v, float f[4]) {
     f[0] = bf16_bits_to_f32(v.x & 0xFFFFu);
     f[1] = bf16_bits_to_f32(v.x >> 16);
@@ -1280,13 +1284,16 @@ __global__ __launch_bounds__(256) void x8_prep_kernel(int d, const uint16_t* __r
     for (int c = 0; c < kPrepChunks; ++c) {
       const int q = q0 + tid + 256 * c;
       if (q < nq) {
-        float f[4];
+        float f[4], y[4];
         unpack(piece(c, q), f);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float y = ldexpf(f[i], -eh);
-          rm = fmaxf(rm, fabsf(y - from_e4m3(to_e4m3(y))));
-        }
+        for (int i = 0; i < 4; ++i) y[i] = ldexpf(f[i], -eh);
+        // two values per conversion, each way (the same RNE codes as one at a time)
+        const int cq = pk_e4m3(y[0], y[1], y[2], y[3]);
+        const f32x2 b01 = __builtin_amdgcn_cvt_pk_f32_fp8(cq, false);
+        const f32x2 b23 = __builtin_amdgcn_cvt_pk_f32_fp8(cq, true);
+        rm = fmaxf(rm, fmaxf(fmaxf(fabsf(y[0] - b01[0]), fabsf(y[1] - b01[1])),
+                             fmaxf(fabsf(y[2] - b23[0]), fabsf(y[3] - b23[1]))));
       }
     }
   rm = block_max(rm);
@@ -1300,18 +1307,17 @@ __global__ __launch_bounds__(256) void x8_prep_kernel(int d, const uint16_t* __r
     for (int c = 0; c < kPrepChunks; ++c) {
       const int q = q0 + tid + 256 * c;
       if (q < nq) {
-        float f[4];
+        float f[4], y[4];
         unpack(piece(c, q), f);
-        uint32_t wh = 0, wl = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float y = ldexpf(f[i], -eh);
-          const int qh = to_e4m3(y);
-          wh |= (uint32_t)qh << (8 * i);
-          wl |= (uint32_t)to_e4m3(ldexpf(y - from_e4m3(qh), -er)) << (8 * i);
-        }
-        hi[q] = wh;
-        lo[q] = wl;
+        for (int i = 0; i < 4; ++i) y[i] = ldexpf(f[i], -eh);
+        const int wh = pk_e4m3(y[0], y[1], y[2], y[3]);
+        const f32x2 b01 = __builtin_amdgcn_cvt_pk_f32_fp8(wh, false);
+        const f32x2 b23 = __builtin_amdgcn_cvt_pk_f32_fp8(wh, true);
+        const int wl = pk_e4m3(ldexpf(y[0] - b01[0], -er), ldexpf(y[1] - b01[1], -er),
+                               ldexpf(y[2] - b23[0], -er), ldexpf(y[3] - b23[1], -er));
+        hi[q] = (uint32_t)wh;
+        lo[q] = (uint32_t)wl;
       }
     }
   if (tid == 0) {
