@@ -196,6 +196,46 @@ def test_layer_matches_oracle(dev, w):
     assert err.max() < 1e-4  # fp32 accumulation throughout these GEMV paths
 
 
+LIMIT_SHAPES = [
+    # 4096 experts and 32 slots: one token (fp32-FMA down, more than 16 slots), and 40
+    # tokens on the grouped MFMA GEMMs (about 1100 experts, each on a 16-row tile)
+    Workload("e4096_k32_t1", 28, d=256, f=64, E=4096, k=32, T=1),
+    Workload("e4096_k32_t40", 29, d=256, f=128, E=4096, k=32, T=40),
+    # d_model = 16384: 16 scale chunks of the register-fed gate/up, 64 down N slices
+    Workload("d16384_t1", 30, d=16384, f=128, E=8, k=2, T=1),
+    Workload("d16384_t20", 31, d=16384, f=128, E=8, k=2, T=20),
+    # d_ff = 8192, the widest the expert kernels take (256 scale blocks a row, 4 per lane)
+    Workload("f8192_t1", 32, d=256, f=8192, E=6, k=2, T=1),
+    Workload("f8192_t20", 33, d=256, f=8192, E=6, k=2, T=20),
+]
+
+
+@pytest.mark.parametrize("w", LIMIT_SHAPES, ids=[s.name for s in LIMIT_SHAPES])
+def test_layer_at_api_limits(dev, w):
+    say(f"layer at the limits {w.name} d={w.d} f={w.f} E={w.E} k={w.k} T={w.T}")
+    x = w.x_bf16()
+    g = run_gpu_layer(w, x, dev)
+    ref = harness.run_layer(w, x)
+    assert_layer(w, g, ref, tol=K3_TOL)
+
+
+def test_block_mode_widest_rows(dev):
+    """Block mode at d_model = 16384, above the rows the RMSNorm keeps in registers (8192):
+    the two-pass norm that reads h again, two chained blocks of three tokens."""
+    w = Workload("block_d16384", 34, d=16384, f=128, E=8, k=2, T=3, layers=2, block=True)
+    say(f"block mode, 2 chained blocks, d={w.d}, T={w.T}")
+    h0 = w.resid0()
+    ref = harness.run_stack(w, h0)
+    h = torch.from_numpy(h0).to(dev)
+    for layer in range(w.layers):
+        g = run_gpu_layer(w, h.cpu().numpy(), dev, layer=layer, block=True, x_dtype="f32")
+        assert np.array_equal(g["ids"], ref["ids"][layer]), f"routing differs at layer {layer}"
+        h = g["y"]
+    err = rel_l2(h.cpu().double().numpy(), ref["y"])
+    print(f"    max rel L2 err {err.max():.3e}", flush=True)
+    assert err.max() < 1e-4
+
+
 def test_entry_points_separately(dev):
     w = TOY.with_(T=9, name="toy9")
     say("router / route_bucket / expert_ffn separately on toy T=9")
@@ -243,7 +283,8 @@ def test_zero_input_routes_first_k(dev):
     assert_layer(w, g, ref)
 
 
-@pytest.mark.parametrize("E,k,T", [(32, 4, 1), (896, 16, 1), (896, 16, 80)])
+@pytest.mark.parametrize("E,k,T", [(32, 4, 1), (896, 16, 1), (896, 16, 80),
+                                   (4096, 32, 1), (4096, 32, 80)])
 def test_router_near_ties_below_upper_key_bits(dev, E, k, T):
     # x = 0, so every logit is exactly its fp32 bias. Clusters of biases that differ only
     # in the last fp32 mantissa bits share the upper 32 bits of their fp64 order keys, so
@@ -362,6 +403,13 @@ def test_repeat_runs_bit_identical(dev):
     (7008, 896, 16, 300, "bf16"),  # 8 K chunks, the last 736 deep; last token tile 44 rows
     (2080, 520, 16, 130, "f32"),   # fp32 tokens, 5 K chunks of 416, last expert tile 8 wide
     (1024, 44, 8, 70, "bf16"),     # E % 8 != 0: router weights read element by element
+    # the API's limits: 4096 experts (16 keys per top-k thread), 32 slots, d_model = 16384
+    (512, 4096, 32, 1, "bf16"),    # one token: the 1024-thread logit block, then top-32
+    (512, 4096, 32, 40, "bf16"),   # one logit block per token
+    (1024, 4096, 32, 100, "bf16"), # fp64 MFMA router, 256-thread top-k with 16 keys each
+    (512, 4095, 32, 3, "f32"),     # E % 8 != 0 at 16 keys per thread, last thread short
+    (16384, 128, 8, 1, "bf16"),    # widest d_model: 32 K chunks of 512 rows
+    (16384, 128, 8, 100, "f32"),   # widest d_model on the MFMA router
 ])
 def test_router_multi_token_shapes(dev, d, E, k, T, xdt):
     say(f"router, several tokens: d={d} E={E} k={k} T={T} x={xdt}")
@@ -404,13 +452,14 @@ def test_block_mode_small_chain(dev):
     assert err.max() < 1e-4
 
 
-@pytest.mark.parametrize("E", [264, 1032])
-def test_block_mode_wide_router_chain(dev, E):
+@pytest.mark.parametrize("E,k", [(264, 4), (1032, 4), (4096, 32)])
+def test_block_mode_wide_router_chain(dev, E, k):
     """Block mode with more than 256 experts at one token, where the shared expert's GEMVs
-    ride in the router and top-k launches (E = 1032: five keys per top-k thread): three
-    chained blocks against the oracle's stack, routed exactly as the oracle at every block."""
-    w = Workload(f"block_e{E}", 23, d=512, f=256, E=E, k=4, T=1, layers=3, block=True)
-    say(f"block mode, 3 chained blocks, E={E}, T=1")
+    ride in the router and top-k launches (E = 1032: five keys per top-k thread; E = 4096:
+    sixteen, with 32 slots): three chained blocks against the oracle's stack, routed exactly
+    as the oracle at every block."""
+    w = Workload(f"block_e{E}", 23, d=512, f=256, E=E, k=k, T=1, layers=3, block=True)
+    say(f"block mode, 3 chained blocks, E={E}, k={k}, T=1")
     h0 = w.resid0()
     ref = harness.run_stack(w, h0)
     h = torch.from_numpy(h0).to(dev)
