@@ -8,7 +8,8 @@
   ragged shapes (16-, 32- and 64-row tiles, partial row slices, experts with one to many
   subtiles; one-token cases on the decode kernels) and on the K3 layer: two single tokens,
   every token of the 32-token batch, and routing-chosen tile edges of the 2048-token prefill
-  chunk.
+  chunk; and at the API's limits (d_model 16384, d_ff 8192, 4096 experts with 32 slots, block
+  mode at d_model 16384).
 """
 import numpy as np
 import pytest
@@ -66,6 +67,22 @@ SMALL = [
 ]
 
 
+# the API's limits on the packed layout (d_model % 1024 == 0, d_ff % 512 == 0)
+LIMITS = [
+    # d_model = 16384: one token on the one-token kernels with 16 waves (one per 1024 of
+    # d_model, 1024 threads), and 20 tokens on the grouped GEMMs (16 scale chunks)
+    Workload("pk_d16384_t1", 69, d=16384, f=512, E=8, k=2, T=1),
+    Workload("pk_d16384_t20", 70, d=16384, f=512, E=8, k=2, T=20),
+    # d_ff = 8192: one token with d_ff above 1536 runs the grouped GEMMs (64 down K steps)
+    Workload("pk_f8192_t1", 71, d=1024, f=8192, E=6, k=2, T=1),
+    Workload("pk_f8192_t20", 72, d=1024, f=8192, E=6, k=2, T=20),
+    # 4096 experts with 32 slots: one token (more than 16 slots: grouped GEMMs, 32 experts
+    # of one row each) and 24 tokens (about 700 experts)
+    Workload("pk_e4096_k32_t1", 73, d=1024, f=512, E=4096, k=32, T=1),
+    Workload("pk_e4096_k32_t24", 74, d=1024, f=512, E=4096, k=32, T=24),
+]
+
+
 def test_pack_matches_layout(dev):
     for w in SMALL[:2]:
         say(f"pack {w.name} d={w.d} f={w.f} E={w.E}")
@@ -116,6 +133,18 @@ def test_packed_layer_matches_oracle(dev, w):
     x = w.x_bf16()
     g = run_packed(w, x, dev, packed)
     check(g, harness.run_layer(w, x), tol=1e-4)
+
+
+@pytest.mark.parametrize("w", LIMITS, ids=[s.name for s in LIMITS])
+def test_packed_layer_at_api_limits(dev, w):
+    say(f"packed layer at the limits {w.name} d={w.d} f={w.f} E={w.E} k={w.k} T={w.T}")
+    dims = k3.make_dims(w.d, w.f, w.E, w.k)
+    packed = k3.pack_experts(dims, k3.MxExperts(**gdev.experts(w, 0, dev)))
+    x = w.x_bf16()
+    g = run_packed(w, x, dev, packed)
+    check(g, harness.run_layer(w, x), tol=K3_TOL)
+    del packed
+    torch.cuda.empty_cache()
 
 
 def test_packed_repeat_runs_bit_identical(dev):
@@ -196,6 +225,24 @@ def test_packed_block_mode_small_chain(dev):
     packed-layout shapes (two 8-step chunks of d, 8 down steps) against the oracle's stack."""
     w = Workload("pk_block", 67, d=2048, f=1024, E=16, k=4, T=1, layers=3, block=True)
     say("packed block mode, 3 chained blocks d=2048 f=1024")
+    h0 = w.resid0()
+    ref = harness.run_stack(w, h0)
+    h = torch.from_numpy(h0).to(dev)
+    for layer in range(w.layers):
+        h, ids = run_packed_block(w, h, layer, packed_layer(w, layer, dev), dev)
+        assert np.array_equal(ids, ref["ids"][layer]), f"routing differs at layer {layer}"
+    yg = h.cpu().double().numpy()
+    err, el = rel_l2(yg, ref["y"]), rel_elem(yg, ref["y"])
+    print(f"    max rel L2 err {err.max():.3e}, max elem err / rms {el.max():.3e}", flush=True)
+    assert err.max() <= 1e-4 and el.max() <= ELEM_FACTOR * 1e-4
+
+
+def test_packed_block_mode_widest_rows(dev):
+    """Block mode on packed experts at d_model = 16384: the two-pass RMSNorm (rows above
+    8192), the shared expert on its own launches, and the fp32 one-token gate/up with 16
+    waves of 4 KB token chunks in LDS; two chained blocks against the oracle's stack."""
+    w = Workload("pk_block_d16384", 75, d=16384, f=512, E=8, k=2, T=1, layers=2, block=True)
+    say(f"packed block mode, 2 chained blocks d={w.d} f={w.f}")
     h0 = w.resid0()
     ref = harness.run_stack(w, h0)
     h = torch.from_numpy(h0).to(dev)
