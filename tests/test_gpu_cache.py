@@ -37,6 +37,9 @@ def _slot_experts(w: Workload, C: int, dev) -> k3.MxExperts:
     (TOY.with_(T=3, name="toy_t3"), 12),      # few tokens: GEMV kernels
     (TOY.with_(T=20, name="toy_t20"), 32),    # grouped MFMA GEMMs on slots
     (Workload("k3w_cache", 31, d=7168, f=1536, E=40, k=16, T=1), 20),  # K3 widths, MFMA down
+    # the limits: 4096 experts, 32 slots a token, and no more cache slots than one call's
+    # pairs (T * k = 64), so almost every step evicts
+    (Workload("e4096_cache", 32, d=256, f=128, E=4096, k=32, T=2), 64),
 ])
 def test_cached_layer_equals_resident(dev, w, C):
     say(f"cached layer {w.name} d={w.d} f={w.f} E={w.E} k={w.k} T={w.T} slots={C}")
