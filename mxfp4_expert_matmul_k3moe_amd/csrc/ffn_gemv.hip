@@ -409,11 +409,14 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int d, int k, const
                                                       const float* __restrict__ resid,
                                                       const float* __restrict__ shared,
                                                       float* __restrict__ y,
-                                                      uint16_t* __restrict__ y_bf16, int bf16_vec) {
+                                                      uint16_t* __restrict__ y_bf16, int bf16_vec,
+                                                      int nbx) {
   // four consecutive outputs per thread (16-byte loads of z); the z rows of up to 8 slots
-  // are requested before any of them is added, and slots are added in slot order
-  const int t = blockIdx.y;
-  const int i = (blockIdx.x * 256 + threadIdx.x) * 4;
+  // are requested before any of them is added, and slots are added in slot order. One
+  // grid dimension: token t takes blocks [t nbx, (t + 1) nbx), so T is not bound by the
+  // 65536 blocks the device reports for its other grid dimensions.
+  const int t = (int)(blockIdx.x / (unsigned)nbx);
+  const int i = ((int)(blockIdx.x - (unsigned)t * (unsigned)nbx) * 256 + threadIdx.x) * 4;
   if (i >= d) return;
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int s0 = 0; s0 < k; s0 += 8) {
@@ -629,10 +632,11 @@ hipError_t launch_combine(int T, int d, int k, const float* z, const float* gate
                           const int32_t* pair_pos, const float* resid, const float* shared,
                           float* y, uint16_t* y_bf16, hipStream_t s) {
   // d is a multiple of 32; y and resid are 16-byte aligned (checked at the boundary)
-  dim3 grid((unsigned)((d / 4 + 255) / 256), (unsigned)T);
+  const int nbx = (d / 4 + 255) / 256;
+  const dim3 grid((unsigned)nbx * (unsigned)T);  // T <= 2^20, nbx <= 16
   const int bf16_vec = (reinterpret_cast<uintptr_t>(y_bf16) & 7u) == 0;
   combine_kernel<<<grid, 256, 0, s>>>(T, d, k, z, gates, pair_pos, resid, shared, y, y_bf16,
-                                      bf16_vec);
+                                      bf16_vec, nbx);
   return hipGetLastError();
 }
 

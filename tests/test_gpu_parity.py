@@ -555,6 +555,21 @@ def test_prefill_k3_t8192(dev):
     torch.cuda.empty_cache()
 
 
+def test_tokens_past_65536(dev):
+    """70,000 tokens on a small layer (grouped GEMMs, fp64 MFMA router with 1094 token tiles):
+    every routed id against the oracle, outputs at tile edges and at tokens 65535, 65536 and
+    T-1, past the 65536 blocks the device reports for its second and third grid dimensions."""
+    w = Workload("t70000", 35, d=256, f=128, E=16, k=2, T=70000)
+    say(f"{w.T} tokens d={w.d} f={w.f} E={w.E} k={w.k}")
+    x = w.x_bf16()
+    g = run_gpu_layer(w, x, dev)
+    ids_all, gates_all, _, _ = oracle.layer_route(x, w.router_w(0), w.bias(0), w.k)
+    check_routing(g["ids"], g["gates"], ids_all, gates_all)
+    rows = sorted(set(tile_probe_tokens(ids_all, w.E)) | {65535, 65536, w.T - 1})
+    ref = harness.run_layer(w, x, tokens=rows)
+    assert_layer(w, g, ref, rows=rows, tol=K3_TOL)
+
+
 def test_stack8_k3(dev):
     w = STACK8
     say("8 stacked blocks, T=1, ~126 GB of MXFP4 experts resident")
